@@ -1,0 +1,9 @@
+"""CPU tests: the oracle against its pins (closed forms, library routines, brute force, invariants)."""
+import pytest
+
+import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
