@@ -1,0 +1,195 @@
+/*
+ * moe_decode.h -- C ABI of the MI355X (gfx950) quantized MoE decode layer.
+ *
+ * One decode step of a mixture-of-experts layer over group-wise
+ * affine-quantized expert weights, split into the three calls the layer is
+ * made of:
+ *
+ *   moe_decode_route       router logits, softmax, top-k, scores (+ shared gate)
+ *   moe_decode_expert_ffn  per selected expert: gate/up GEMV + SwiGLU -> act
+ *                          ("kernel A"), down GEMV * score -> partial ("kernel B")
+ *   moe_decode_tail        out = resid + (sum_k partial_k + shared * gate)
+ *
+ * Sources: mlxcel PR #276, "two-kernel decode-MoE that beats gather_qmm",
+ * section "What changed" step 2 (the act/partial split), "Scope / flags"
+ * (4- and 8-bit affine weights) and "Next" (6-bit and mixed-bit weights);
+ * Red Lite dev39, "fused expert tail (GPU-routed decode)", section "Change"
+ * (GPU routing, per-expert outputs exposed by the pool, the one-dispatch
+ * tail).
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; moe_qmat
+ *    and the call arguments themselves live on the host.  The library never
+ *    allocates, frees, copies to or from the host, synchronises, or prints.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the legacy
+ *    default stream).  Buffers must stay valid until the stream reaches the
+ *    enqueued work.  Calls may be captured into a HIP graph.
+ *  - Arguments are validated on the host before anything is enqueued; an
+ *    invalid call returns a status and enqueues nothing.  MOE_EHIP reports a
+ *    failed launch.
+ *  - Tensors are dense, row-major, with the shapes given below.
+ *  - Results are deterministic: repeated calls on the same inputs give
+ *    bit-identical outputs (no floating-point atomics are used).
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_DECODE_ABI_VERSION 1
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = 1,        /* null pointer, inconsistent shape, out-of-range size, misalignment */
+    MOE_EUNSUPPORTED = 2,  /* bit width, group size or dtype combination that is not built */
+    MOE_EHIP = 3           /* the HIP runtime reported an error when launching */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
+
+/*
+ * One stack of quantized projection matrices, one per expert.
+ * Expert e's matrix W_e has `rows` outputs and `cols` inputs (the
+ * contraction dimension).  Its weight is w[r][j] = scale[r][j/64] * q[r][j]
+ * + bias[r][j/64] (groups of 64 along the contraction dimension; mlxcel PR
+ * #276, "Scope / flags": affine quantization).
+ *   q       : uint32 [n_experts][rows][cols*bits/32]; code j of a row occupies
+ *             bits [bits*j, bits*j+bits) of the row's little-endian, LSB-first
+ *             bit stream (6-bit codes straddle words; 16 codes per 3 words).
+ *             Must be 16-byte aligned.
+ *   scales, biases : sb_dtype [n_experts][rows][cols/64].
+ *   bits       : 4, 6 or 8.      group_size : must be 64.
+ *   sb_dtype   : MOE_F16 or MOE_BF16.
+ *   cols must be a multiple of 64.
+ */
+typedef struct {
+    const uint32_t *q;
+    const void *scales;
+    const void *biases;
+    int32_t n_experts;
+    int32_t rows;
+    int32_t cols;
+    int32_t bits;
+    int32_t group_size;
+    moe_dtype sb_dtype;
+} moe_qmat;
+
+/* Limits checked by every call. */
+#define MOE_MAX_TOKENS 32
+#define MOE_MAX_TOP_K 32
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_DIM 8192
+
+/*
+ * Routing (Red Lite dev39, "Change": the layer is GPU-routed).  Per token t:
+ *   logits[e] = sum_j w_router[e][j] * x[t][j]           (fp32 accumulation)
+ *   p = softmax(logits) over all n_experts
+ *   expert_ids[t][0..top_k) = experts by descending logit, ties to the lower id
+ *   scores[t][k] = p[id_k] / sum_k' p[id_k']  if renormalize, else p[id_k]
+ *   shared_gate[t] = sigmoid(sum_j w_shared_gate[j] * x[t][j])  if w_shared_gate
+ * Arguments:
+ *   x           [n_tokens][d_in], dtype x_dtype (F32, F16 or BF16)
+ *   w_router    [n_experts][d_in], dtype w_router_dtype
+ *   w_shared_gate [d_in] or NULL, dtype w_shared_gate_dtype
+ *   expert_ids  out int32 [n_tokens][top_k]
+ *   scores      out float [n_tokens][top_k]
+ *   shared_gate out float [n_tokens]; must be NULL iff w_shared_gate is NULL
+ *   workspace   device scratch of at least moe_decode_route_workspace_bytes();
+ *               must be zero-filled before its first use; every call leaves it
+ *               zero-filled again when it completes.  Calls that may run
+ *               concurrently need separate workspaces.
+ * Limits: 1 <= n_tokens <= 32, 1 <= top_k <= min(n_experts, 32),
+ *         n_experts <= 1024, d_in a multiple of 64 and <= 8192.
+ */
+moe_status moe_decode_route(const void *x, moe_dtype x_dtype, int32_t n_tokens, int32_t d_in,
+                            const void *w_router, moe_dtype w_router_dtype,
+                            int32_t n_experts, int32_t top_k, int32_t renormalize,
+                            const void *w_shared_gate, moe_dtype w_shared_gate_dtype,
+                            int32_t *expert_ids, float *scores, float *shared_gate,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+size_t moe_decode_route_workspace_bytes(int32_t n_tokens, int32_t n_experts);
+
+/*
+ * Expert FFN (mlxcel PR #276, "What changed" step 2).  For every token t and
+ * slot k with e = expert_ids[t][k]:
+ *   act[t][k][r]     = silu(g_r) * u_r,  g = W_gate[e] x_t,  u = W_up[e] x_t   (kernel A)
+ *   partial[t][k][i] = score[t][k] * (W_down[e] act[t][k])[i]                  (kernel B)
+ * where silu(z) = z * sigmoid(z) and score = 1 when `scores` is NULL.
+ * An id outside [0, n_experts) yields all-zero act and partial rows.
+ * With n_tokens > 1, each touched expert's weights are read once and applied
+ * to all tokens routed to it.
+ * A shared expert is run through this same call with its own stacks,
+ * expert_ids[t][s] = s and scores = NULL; its partial is the `shared` input
+ * of moe_decode_tail.
+ * Arguments:
+ *   x        [n_tokens][d_in], dtype x_dtype; d_in = gate->cols
+ *   gate, up : stacks with rows = d_ff, cols = d_in; down: rows = d_in, cols = d_ff;
+ *              the same n_experts and sb_dtype; gate->bits == up->bits
+ *   expert_ids int32 [n_tokens][top_k]; scores float [n_tokens][top_k] or NULL
+ *   act      out float [n_tokens][top_k][d_ff]   (also read back by kernel B)
+ *   partial  out float [n_tokens][top_k][d_in]
+ *   workspace device scratch of moe_decode_expert_ffn_workspace_bytes() bytes
+ *             (0 bytes, and NULL allowed, when n_tokens == 1); no zeroing needed.
+ * Limits: as for moe_decode_route; d_in and d_ff multiples of 64, <= 8192.
+ */
+moe_status moe_decode_expert_ffn(const void *x, moe_dtype x_dtype, int32_t n_tokens,
+                                 const moe_qmat *gate, const moe_qmat *up, const moe_qmat *down,
+                                 const int32_t *expert_ids, const float *scores, int32_t top_k,
+                                 float *act, float *partial,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+size_t moe_decode_expert_ffn_workspace_bytes(int32_t n_tokens, int32_t top_k, int32_t n_experts);
+
+/*
+ * The two halves of moe_decode_expert_ffn as separate calls, for callers that
+ * schedule kernel A and kernel B themselves (mlxcel PR #276, "What changed"
+ * step 2: two dispatches with act staged in global memory between them).
+ * moe_decode_gate_up writes act exactly as moe_decode_expert_ffn does;
+ * moe_decode_down reads act [n_tokens][top_k][down->cols] and writes partial.
+ * Same limits, ownership and workspace rules as moe_decode_expert_ffn; with
+ * n_tokens > 1 each call regroups the pairs by expert in its workspace.
+ */
+moe_status moe_decode_gate_up(const void *x, moe_dtype x_dtype, int32_t n_tokens,
+                              const moe_qmat *gate, const moe_qmat *up,
+                              const int32_t *expert_ids, int32_t top_k, float *act,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+moe_status moe_decode_down(const float *act, int32_t n_tokens, const moe_qmat *down,
+                           const int32_t *expert_ids, const float *scores, int32_t top_k,
+                           float *partial, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Tail (Red Lite dev39, "Change": one dispatch, one thread per hidden
+ * element).  For every token t and hidden index i:
+ *   routed = (((partial[t][0][i] + partial[t][1][i]) + ...) + partial[t][top_k-1][i])
+ *   shared = shared[t][0][i] + ... + shared[t][n_shared-1][i]   (0 when n_shared == 0)
+ *   out[t][i] = residual[t][i] + (routed + shared * g),  g = shared_gate[t] or 1
+ * The sums run left to right in slot order in fp32.
+ * Arguments:
+ *   partial  [n_tokens][top_k][d_in] float
+ *   shared   [n_tokens][n_shared][d_in] float, or NULL iff n_shared == 0
+ *   shared_gate [n_tokens] float or NULL (gate 1)
+ *   residual [n_tokens][d_in], dtype residual_dtype
+ *   out      out float [n_tokens][d_in]; may not alias the inputs
+ */
+moe_status moe_decode_tail(const float *partial, int32_t n_tokens, int32_t top_k, int32_t d_in,
+                           const float *shared, int32_t n_shared, const float *shared_gate,
+                           const void *residual, moe_dtype residual_dtype, float *out,
+                           void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *moe_decode_status_string(moe_status s);
+
+/* MOE_DECODE_ABI_VERSION of the built library. */
+int32_t moe_decode_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_DECODE_H */

@@ -1,0 +1,32 @@
+// Host-side helpers for argument validation of the C ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_decode.h"
+
+namespace moe {
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline bool valid_dtype(int dt) { return dt == MOE_F32 || dt == MOE_F16 || dt == MOE_BF16; }
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks one projection stack in isolation.  Returns MOE_OK or the error.
+inline moe_status check_qmat(const moe_qmat *m) {
+    if (!m || !m->q || !m->scales || !m->biases) return MOE_EINVAL;
+    if (m->bits != 4 && m->bits != 6 && m->bits != 8) return MOE_EUNSUPPORTED;
+    if (m->group_size != 64) return MOE_EUNSUPPORTED;
+    if (m->sb_dtype != MOE_F16 && m->sb_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+    if (m->n_experts < 1 || m->n_experts > MOE_MAX_EXPERTS) return MOE_EINVAL;
+    if (m->rows < 64 || m->rows > MOE_MAX_DIM || m->rows % 64) return MOE_EINVAL;
+    if (m->cols < 64 || m->cols > MOE_MAX_DIM || m->cols % 64) return MOE_EINVAL;
+    if (!aligned16(m->q)) return MOE_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(m->scales) & 1u) || (reinterpret_cast<uintptr_t>(m->biases) & 1u))
+        return MOE_EINVAL;
+    return MOE_OK;
+}
+
+}  // namespace moe

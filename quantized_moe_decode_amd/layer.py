@@ -1,0 +1,116 @@
+"""One MoE decode layer on the device: weights, preallocated buffers, and the
+route -> expert FFN (routed, then shared) -> tail call sequence.
+
+No arithmetic happens here; every step is a call into libmoe_decode.so on the
+caller's stream.  Buffers are allocated once, so `forward` can be captured
+into a HIP graph (torch.cuda.CUDAGraph) and replayed.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import (QuantStack, expert_ffn_workspace_bytes, moe_decode_expert_ffn, moe_decode_route,
+               moe_decode_tail, route_workspace_bytes)
+
+_TORCH_16 = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def tensor_from_encoded(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Device tensor from an encoded host array (float32 values or uint16 bit patterns)."""
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+    return t.view(_TORCH_16[dtype]).to(device)
+
+
+def stack_to_device(stack, device) -> QuantStack:
+    """A QuantStack from a host stack with q (uint32), scales/biases (uint16 bits)."""
+    q = torch.from_numpy(np.ascontiguousarray(stack.q).view(np.int32)).to(device)
+    s = tensor_from_encoded(stack.scales, stack.sb_dtype, device)
+    b = tensor_from_encoded(stack.biases, stack.sb_dtype, device)
+    return QuantStack(q, s, b, stack.rows, stack.cols, stack.bits)
+
+
+class DecodeLayer:
+    """A quantized MoE layer resident on one GPU, for a fixed number of tokens per step."""
+
+    def __init__(self, router: torch.Tensor, top_k: int, renormalize: bool,
+                 gate: QuantStack, up: QuantStack, down: QuantStack,
+                 shared: Optional[Sequence[QuantStack]] = None,
+                 shared_gate_w: Optional[torch.Tensor] = None, n_tokens: int = 1):
+        dev = router.device
+        self.router, self.top_k, self.renormalize = router, top_k, renormalize
+        self.gate, self.up, self.down = gate, up, down
+        self.shared = tuple(shared) if shared is not None else None
+        self.shared_gate_w = shared_gate_w
+        self.n_tokens = T = n_tokens
+        E, d_in = router.shape
+        d_ff = gate.rows
+        self.d_in, self.d_ff, self.n_experts = d_in, d_ff, E
+        f32 = dict(device=dev, dtype=torch.float32)
+        self.ids = torch.zeros(T, top_k, device=dev, dtype=torch.int32)
+        self.scores = torch.zeros(T, top_k, **f32)
+        self.shared_gate = torch.zeros(T, **f32) if shared_gate_w is not None else None
+        self.act = torch.zeros(T, top_k, d_ff, **f32)
+        self.partial = torch.zeros(T, top_k, d_in, **f32)
+        self.route_ws = torch.zeros(route_workspace_bytes(T, E), device=dev, dtype=torch.uint8)
+        nb = expert_ffn_workspace_bytes(T, top_k, E)
+        self.ffn_ws = torch.zeros(max(nb, 1), device=dev, dtype=torch.uint8) if nb else None
+        if self.shared is not None:
+            S = self.shared[0].n_experts
+            self.n_shared = S
+            self.shared_ids = torch.arange(S, device=dev, dtype=torch.int32).repeat(T, 1).contiguous()
+            self.shared_act = torch.zeros(T, S, self.shared[0].rows, **f32)
+            self.shared_partial = torch.zeros(T, S, d_in, **f32)
+            nb = expert_ffn_workspace_bytes(T, S, S)
+            self.shared_ws = torch.zeros(max(nb, 1), device=dev, dtype=torch.uint8) if nb else None
+        else:
+            self.n_shared = 0
+
+    def route(self, x: torch.Tensor, stream=None) -> None:
+        moe_decode_route(x, self.router, self.top_k, self.renormalize, self.ids, self.scores,
+                         self.route_ws, self.shared_gate_w, self.shared_gate, stream)
+
+    def experts(self, x: torch.Tensor, stream=None) -> None:
+        moe_decode_expert_ffn(x, self.gate, self.up, self.down, self.ids, self.scores, self.act,
+                              self.partial, self.ffn_ws, stream)
+        if self.shared is not None:
+            g, u, d = self.shared
+            moe_decode_expert_ffn(x, g, u, d, self.shared_ids, None, self.shared_act,
+                                  self.shared_partial, self.shared_ws, stream)
+
+    def tail(self, resid: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+        moe_decode_tail(self.partial, resid, out,
+                        self.shared_partial if self.shared is not None else None,
+                        self.shared_gate, stream)
+
+    def forward(self, x: torch.Tensor, resid: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+        """out [T, d_in] fp32 = the layer applied to x [T, d_in] with residual resid."""
+        self.route(x, stream)
+        self.experts(x, stream)
+        self.tail(resid, out, stream)
+
+    def expert_bytes_per_step(self) -> int:
+        """Bytes of expert weight one step reads when its K selections are distinct (T = 1)."""
+        n = (self.gate.nbytes(self.top_k) + self.up.nbytes(self.top_k) + self.down.nbytes(self.top_k))
+        if self.shared is not None:
+            n += sum(s.nbytes(self.n_shared) for s in self.shared)
+        return n
+
+
+def layer_from_host(cfg, weights: dict, device, n_tokens: Optional[int] = None) -> DecodeLayer:
+    """Build a DecodeLayer from host weights in the generator's layout."""
+    router = tensor_from_encoded(weights["router"], cfg.router_dtype, device)
+    gate, up, down = (stack_to_device(weights[p], device) for p in ("gate", "up", "down"))
+    shared = None
+    if cfg.n_shared:
+        shared = [stack_to_device(weights[p], device)
+                  for p in ("shared_gate_proj", "shared_up", "shared_down")]
+    wg = None
+    if cfg.shared_gate:
+        wg = tensor_from_encoded(weights["shared_gate_w"], "bf16", device)
+    return DecodeLayer(router, cfg.top_k, cfg.renormalize, gate, up, down, shared, wg,
+                       n_tokens if n_tokens is not None else cfg.n_tokens)

@@ -1,0 +1,216 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and
+rejects invalid arguments on the host before anything is enqueued.
+
+Every call here carries at least one flaw that host validation catches, so no
+kernel is ever launched (the pointers are placeholders and are never read).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_moe_decode_amd as qmd
+from quantized_moe_decode_amd import (CQMat, MOE_BF16, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_F16,
+                                      MOE_F32, MOE_OK, lib)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_decode.h")
+
+P = 0x10000          # placeholder "device" address, 16-byte aligned, never dereferenced
+MIS = 0x10008        # misaligned placeholder
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_decode_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("moe_decode_route", "moe_decode_expert_ffn", "moe_decode_tail",
+              "moe_decode_gate_up", "moe_decode_down"):
+        assert n in names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports_declared_symbol(name):
+    assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert qmd.abi_version() == 1
+    for code in (0, 1, 2, 3):
+        assert qmd.status_string(code).startswith("MOE_")
+    assert "unknown" in qmd.status_string(99)
+
+
+def test_workspace_sizes():
+    assert qmd.route_workspace_bytes(1, 128) >= (128 + 1) * 4 + 4
+    assert qmd.route_workspace_bytes(32, 1024) >= 32 * 1025 * 4 + 32 * 4
+    assert qmd.route_workspace_bytes(0, 8) == 0
+    assert qmd.expert_ffn_workspace_bytes(1, 8, 128) == 0
+    mw = min(32 * 8, 128) + 1
+    assert qmd.expert_ffn_workspace_bytes(32, 8, 128) >= (1 + mw + mw + 1 + 256) * 4
+
+
+def _route(**kw):
+    a = dict(x=P, x_dt=MOE_BF16, T=1, d_in=2048, wr=P, wr_dt=MOE_BF16, E=128, K=8, renorm=1,
+             wg=None, wg_dt=MOE_BF16, ids=P, scores=P, gate=None, ws=P, ws_bytes=1 << 20)
+    a.update(kw)
+    return lib.moe_decode_route(a["x"], a["x_dt"], a["T"], a["d_in"], a["wr"], a["wr_dt"], a["E"],
+                                a["K"], a["renorm"], a["wg"], a["wg_dt"], a["ids"], a["scores"],
+                                a["gate"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), MOE_EINVAL),
+    (dict(ids=None), MOE_EINVAL),
+    (dict(ws=None), MOE_EINVAL),
+    (dict(T=0), MOE_EINVAL),
+    (dict(T=33), MOE_EINVAL),
+    (dict(K=0), MOE_EINVAL),
+    (dict(K=33), MOE_EINVAL),
+    (dict(E=4, K=5), MOE_EINVAL),
+    (dict(E=1025), MOE_EINVAL),
+    (dict(d_in=100), MOE_EINVAL),
+    (dict(d_in=8192 + 64), MOE_EINVAL),
+    (dict(wg=P), MOE_EINVAL),              # shared-gate vector without an output
+    (dict(gate=P), MOE_EINVAL),            # output without a shared-gate vector
+    (dict(x=MIS), MOE_EINVAL),
+    (dict(ws_bytes=16), MOE_EINVAL),
+    (dict(x_dt=7), MOE_EUNSUPPORTED),
+    (dict(wr_dt=-1), MOE_EUNSUPPORTED),
+])
+def test_route_rejects(kw, want):
+    assert _route(**kw) == want
+
+
+def _qm(**kw):
+    a = dict(q=P, s=P, b=P, E=128, rows=768, cols=2048, bits=4, gs=64, dt=MOE_BF16)
+    a.update(kw)
+    return CQMat(a["q"], a["s"], a["b"], a["E"], a["rows"], a["cols"], a["bits"], a["gs"], a["dt"])
+
+
+def _ffn(gate=None, up=None, down=None, **kw):
+    a = dict(x=P, x_dt=MOE_BF16, T=1, ids=P, scores=P, K=8, act=P, partial=P, ws=None, ws_bytes=0)
+    a.update(kw)
+    g = gate or _qm()
+    u = up or _qm()
+    d = down or _qm(rows=2048, cols=768)
+    return lib.moe_decode_expert_ffn(a["x"], a["x_dt"], a["T"], ctypes.byref(g), ctypes.byref(u),
+                                     ctypes.byref(d), a["ids"], a["scores"], a["K"], a["act"],
+                                     a["partial"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("case,want", [
+    (dict(x=None), MOE_EINVAL),
+    (dict(act=None), MOE_EINVAL),
+    (dict(T=0), MOE_EINVAL),
+    (dict(T=2), MOE_EINVAL),                                   # several tokens need a workspace
+    (dict(K=0), MOE_EINVAL),
+    (dict(K=40), MOE_EINVAL),
+    (dict(x=MIS), MOE_EINVAL),
+    (dict(x_dt=5), MOE_EUNSUPPORTED),
+    (dict(gate=_qm(bits=5)), MOE_EUNSUPPORTED),
+    (dict(gate=_qm(bits=2)), MOE_EUNSUPPORTED),
+    (dict(down=_qm(rows=2048, cols=768, gs=32)), MOE_EUNSUPPORTED),
+    (dict(down=_qm(rows=2048, cols=768, dt=MOE_F32)), MOE_EUNSUPPORTED),
+    (dict(up=_qm(bits=8)), MOE_EUNSUPPORTED),                  # gate and up must share bits
+    (dict(up=_qm(dt=MOE_F16)), MOE_EUNSUPPORTED),              # one scale dtype per call
+    (dict(up=_qm(rows=512)), MOE_EINVAL),
+    (dict(down=_qm(rows=2048, cols=512)), MOE_EINVAL),
+    (dict(down=_qm(rows=1024, cols=768)), MOE_EINVAL),
+    (dict(down=_qm(rows=2048, cols=768, E=64)), MOE_EINVAL),
+    (dict(gate=_qm(cols=2000), up=_qm(cols=2000)), MOE_EINVAL),
+    (dict(gate=_qm(q=MIS)), MOE_EINVAL),
+    (dict(gate=_qm(q=None)), MOE_EINVAL),
+    (dict(gate=_qm(E=0)), MOE_EINVAL),
+    (dict(gate=_qm(rows=16384), up=_qm(rows=16384)), MOE_EINVAL),
+])
+def test_expert_ffn_rejects(case, want):
+    assert _ffn(**case) == want
+
+
+def _gate_up(gate=None, up=None, **kw):
+    a = dict(x=P, x_dt=MOE_BF16, T=1, ids=P, K=8, act=P, ws=None, ws_bytes=0)
+    a.update(kw)
+    g, u = gate or _qm(), up or _qm()
+    return lib.moe_decode_gate_up(a["x"], a["x_dt"], a["T"], ctypes.byref(g), ctypes.byref(u),
+                                  a["ids"], a["K"], a["act"], a["ws"], a["ws_bytes"], None)
+
+
+def _down(down=None, **kw):
+    a = dict(act=P, T=1, ids=P, scores=P, K=8, partial=P, ws=None, ws_bytes=0)
+    a.update(kw)
+    d = down or _qm(rows=2048, cols=768)
+    return lib.moe_decode_down(a["act"], a["T"], ctypes.byref(d), a["ids"], a["scores"], a["K"],
+                               a["partial"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("case,want", [
+    (dict(x=None), MOE_EINVAL),
+    (dict(ids=None), MOE_EINVAL),
+    (dict(act=None), MOE_EINVAL),
+    (dict(act=MIS), MOE_EINVAL),
+    (dict(T=40), MOE_EINVAL),
+    (dict(T=3), MOE_EINVAL),
+    (dict(x_dt=9), MOE_EUNSUPPORTED),
+    (dict(up=_qm(bits=6)), MOE_EUNSUPPORTED),
+    (dict(up=_qm(rows=64)), MOE_EINVAL),
+    (dict(gate=_qm(gs=128)), MOE_EUNSUPPORTED),
+])
+def test_gate_up_rejects(case, want):
+    assert _gate_up(**case) == want
+
+
+@pytest.mark.parametrize("case,want", [
+    (dict(act=None), MOE_EINVAL),
+    (dict(partial=None), MOE_EINVAL),
+    (dict(ids=None), MOE_EINVAL),
+    (dict(K=0), MOE_EINVAL),
+    (dict(T=2, ws=P, ws_bytes=8), MOE_EINVAL),
+    (dict(down=_qm(rows=2048, cols=768, bits=7)), MOE_EUNSUPPORTED),
+    (dict(down=_qm(rows=2048, cols=768, q=MIS)), MOE_EINVAL),
+])
+def test_down_rejects(case, want):
+    assert _down(**case) == want
+
+
+def _tail(**kw):
+    a = dict(partial=P, T=1, K=8, D=2048, shared=None, S=0, gate=None, resid=P, rdt=MOE_BF16, out=P)
+    a.update(kw)
+    return lib.moe_decode_tail(a["partial"], a["T"], a["K"], a["D"], a["shared"], a["S"], a["gate"],
+                               a["resid"], a["rdt"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(partial=None), MOE_EINVAL),
+    (dict(out=None), MOE_EINVAL),
+    (dict(T=0), MOE_EINVAL),
+    (dict(K=0), MOE_EINVAL),
+    (dict(D=96), MOE_EINVAL),
+    (dict(S=1), MOE_EINVAL),             # shared count without the buffer
+    (dict(shared=P), MOE_EINVAL),        # buffer without a count
+    (dict(S=-1, shared=P), MOE_EINVAL),
+    (dict(rdt=3), MOE_EUNSUPPORTED),
+])
+def test_tail_rejects(kw, want):
+    assert _tail(**kw) == want
+
+
+def test_binding_raises_on_error():
+    """The Python layer turns a status into MoeError (host-side rejection, no launch)."""
+    import torch
+    x = torch.zeros(1, 100, dtype=torch.bfloat16)          # d_in not a multiple of 64
+    with pytest.raises(qmd.MoeError) as ei:
+        qmd.moe_decode_route(x, torch.zeros(8, 100, dtype=torch.bfloat16), 2, True,
+                             torch.zeros(1, 2, dtype=torch.int32), torch.zeros(1, 2),
+                             torch.zeros(4096, dtype=torch.uint8), stream=_FakeStream())
+    assert ei.value.status == MOE_EINVAL
+    assert MOE_OK == 0
+
+
+class _FakeStream:
+    cuda_stream = 0
