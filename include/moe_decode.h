@@ -100,9 +100,11 @@ typedef struct {
  *   scores      out float [n_tokens][top_k]
  *   shared_gate out float [n_tokens]; must be NULL iff w_shared_gate is NULL
  *   workspace   device scratch of at least moe_decode_route_workspace_bytes();
- *               must be zero-filled before its first use; every call leaves it
- *               zero-filled again when it completes.  Calls that may run
- *               concurrently need separate workspaces.
+ *               must be zero-filled before its first use and not written by
+ *               the caller afterwards: each call leaves it in the state the
+ *               next call expects (its per-token completion counters back at
+ *               zero).  Calls that may run concurrently need separate
+ *               workspaces.
  * Limits: 1 <= n_tokens <= 32, 1 <= top_k <= min(n_experts, 32),
  *         n_experts <= 1024, d_in a multiple of 64 and <= 8192.
  */

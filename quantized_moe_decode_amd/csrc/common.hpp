@@ -81,10 +81,9 @@ __device__ __forceinline__ void unpack(const Chunk<BITS> &c, float *q) {
     }
 }
 
-// Scale or bias element as float.
+// A 16-bit scale or bias bit pattern as float.
 template <int SB>
-__device__ __forceinline__ float load_sb(const uint16_t *p, int64_t i) {
-    const uint16_t h = p[i];
+__device__ __forceinline__ float sb_to_float(uint16_t h) {
     if constexpr (SB == MOE_BF16) {
         return __uint_as_float((uint32_t)h << 16);
     } else {
@@ -92,6 +91,11 @@ __device__ __forceinline__ float load_sb(const uint16_t *p, int64_t i) {
         __builtin_memcpy(&f, &h, 2);
         return (float)f;
     }
+}
+
+template <int SB>
+__device__ __forceinline__ float load_sb(const uint16_t *p, int64_t i) {
+    return sb_to_float<SB>(p[i]);
 }
 
 // Activation element of a given dtype as float.

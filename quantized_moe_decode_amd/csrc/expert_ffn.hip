@@ -79,26 +79,167 @@ __device__ __forceinline__ bool get_work(const FfnArgs &a, int w, Work &wk) {
 
 __device__ __forceinline__ int pair_at(const Work &wk, int i) { return wk.pairs ? wk.pairs[i] : wk.single; }
 
-// Stage nt input vectors of `cols` floats into LDS plus their per-chunk sums.
-// src(tt, c) gives element c of the tt-th vector of this pass.
-template <int CODES, typename Src>
-__device__ __forceinline__ void stage_inputs(float *xs, float *xsum, int nt, int cols, Src src) {
-    const int tid = threadIdx.x;
-    for (int i = tid; i < nt * cols; i += blockDim.x) xs[i] = src(i / cols, i % cols);
-    __syncthreads();
-    const int cpr = cols / CODES;
-    for (int i = tid; i < nt * cpr; i += blockDim.x) {
-        const float *p = xs + (i / cpr) * cols + (i % cpr) * CODES;
-        float s = 0.f;
+// Rows of one lane group processed together: the loads of all of them are
+// issued before any is consumed, so each lane keeps several 16-byte loads in
+// flight.
+constexpr int kNR = 4;
+
+// Input chunk of CODES consecutive values for a single token, read straight
+// from global memory (it is small and shared by every row: it stays in L2).
+template <int XT, int CODES>
+__device__ __forceinline__ void load_x_chunk(const void *x, int64_t off, float *xv) {
+    if constexpr (XT == MOE_F32) {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(x) + off);
 #pragma unroll
-        for (int q = 0; q < CODES; ++q) s += p[q];
-        xsum[i] = s;
+        for (int i = 0; i < CODES / 4; ++i) {
+            const f32x4 v = p[i];
+            xv[4 * i] = v.x; xv[4 * i + 1] = v.y; xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
+        }
+    } else {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(x) + off);
+#pragma unroll
+        for (int i = 0; i < CODES / 8; ++i) {
+            const u32x4 v = p[i];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (XT == MOE_BF16) {
+                    xv[8 * i + 2 * k] = __uint_as_float(v[k] << 16);
+                    xv[8 * i + 2 * k + 1] = __uint_as_float(v[k] & 0xFFFF0000u);
+                } else {
+                    _Float16 lo, hi;
+                    const uint16_t l16 = (uint16_t)(v[k] & 0xFFFFu), h16 = (uint16_t)(v[k] >> 16);
+                    __builtin_memcpy(&lo, &l16, 2);
+                    __builtin_memcpy(&hi, &h16, 2);
+                    xv[8 * i + 2 * k] = (float)lo;
+                    xv[8 * i + 2 * k + 1] = (float)hi;
+                }
+            }
+        }
+    }
+}
+
+// LDS layout for several tokens: token slot t, chunk c occupies floats
+// [(t*cpr + c)*(CODES+4), +CODES) with the chunk's input sum at +CODES.  The
+// 4-float pad makes the 16-byte LDS reads of consecutive chunks by
+// consecutive lanes fall in distinct banks.
+template <int CODES, typename Src>
+__device__ __forceinline__ void stage_inputs(float *xs, int nt, int cpr, Src src) {
+    constexpr int SLOT = CODES + 4;
+    const int tid = threadIdx.x;
+    const int per_tok = cpr * CODES;
+    for (int i = tid; i < nt * per_tok; i += blockDim.x) {
+        const int t = i / per_tok, rem = i - t * per_tok;
+        const int c = rem / CODES, q = rem - c * CODES;
+        xs[(t * cpr + c) * SLOT + q] = src(t, rem);
+    }
+    __syncthreads();
+    for (int i = tid; i < nt * cpr; i += blockDim.x) {
+        float *p = xs + i * SLOT;
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < CODES; ++q) sum += p[q];
+        p[CODES] = sum;
     }
     __syncthreads();
 }
 
+__device__ __forceinline__ float chunk_sum(const float *v, int n) {
+    float s = 0.f;
+    for (int i = 0; i < n; ++i) s += v[i];
+    return s;
+}
+
+// Dot products of kNR rows (rows r0, r0+rstep, ...) of NM matrices of expert
+// row base `erow0` with the inputs, accumulated per lane (to be combined over
+// the row's LR lanes by the caller).  MAXT == 1 reads the single token's input
+// chunk from global memory (x_src, dtype XT); MAXT > 1 reads the staged LDS copy.
+template <int BITS, int SB, int XT, int NM, int MAXT>
+__device__ __forceinline__ void row_block(const QM *mats, int64_t erow0, int r0, int rstep, int row_end,
+                                          int j, int lr, int cpr, const void *x_src, int64_t x_off,
+                                          const float *xs, int nt, float (&acc)[NM][kNR][MAXT]) {
+    using F = Fmt<BITS>;
+    constexpr int CODES = F::kCodes;
+    constexpr int SLOT = CODES + 4;
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int n = 0; n < kNR; ++n)
+#pragma unroll
+            for (int t = 0; t < MAXT; ++t) acc[m][n][t] = 0.f;
+
+    for (int c0 = 0; c0 < cpr; c0 += lr) {          // same trip count on every lane
+        const int c = c0 + j;
+        const bool okc = c < cpr;
+        const int cc = okc ? c : 0;
+        // Branch-free loads: rows past the tile and chunks past the row read a
+        // valid neighbour (same cache lines) and are masked out afterwards, so
+        // every load of the block is issued before the first wait.
+        Chunk<BITS> w[NM][kNR];
+        uint16_t sr[NM][kNR], br[NM][kNR];
+        bool live[kNR];
+#pragma unroll
+        for (int n = 0; n < kNR; ++n) live[n] = okc && (r0 + n * rstep < row_end);
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int n = 0; n < kNR; ++n) {
+                const int r = min(r0 + n * rstep, row_end - 1);
+                const int64_t row = erow0 + r;
+                w[m][n] = load_chunk<BITS>(mats[m].q + row * mats[m].wpr + cc * F::kWords);
+                const int64_t gi = row * mats[m].gpr + cc / F::kChunksPerGroup;
+                sr[m][n] = mats[m].s[gi];
+                br[m][n] = mats[m].b[gi];
+            }
+        float s[NM][kNR], b[NM][kNR];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int n = 0; n < kNR; ++n) {
+                s[m][n] = live[n] ? sb_to_float<SB>(sr[m][n]) : 0.f;
+                b[m][n] = live[n] ? sb_to_float<SB>(br[m][n]) : 0.f;
+            }
+        if constexpr (MAXT == 1) {
+            float xv[CODES];
+            load_x_chunk<XT, CODES>(x_src, x_off + (int64_t)cc * CODES, xv);
+            const float xsum = chunk_sum(xv, CODES);
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int n = 0; n < kNR; ++n) {
+                    float q[CODES];
+                    unpack<BITS>(w[m][n], q);
+                    float d = 0.f;
+#pragma unroll
+                    for (int i = 0; i < CODES; ++i) d += q[i] * xv[i];
+                    acc[m][n][0] += s[m][n] * d + b[m][n] * xsum;
+                }
+        } else {
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int n = 0; n < kNR; ++n) {
+                    float q[CODES];
+                    unpack<BITS>(w[m][n], q);
+#pragma unroll
+                    for (int t = 0; t < MAXT; ++t) {
+                        if (t < nt) {
+                            const f32x4 *xp = reinterpret_cast<const f32x4 *>(xs + (t * cpr + cc) * SLOT);
+                            float d = 0.f;
+#pragma unroll
+                            for (int i = 0; i < CODES / 4; ++i) {
+                                const f32x4 v = xp[i];
+                                d += q[4 * i] * v.x + q[4 * i + 1] * v.y + q[4 * i + 2] * v.z + q[4 * i + 3] * v.w;
+                            }
+                            acc[m][n][t] += s[m][n] * d + b[m][n] * xs[(t * cpr + cc) * SLOT + CODES];
+                        }
+                    }
+                }
+        }
+    }
+}
+
 // Kernel A: gate and up projections of one expert over a tile of rows, then SwiGLU.
-template <int BITS, int SB, int MAXT>
+template <int BITS, int SB, int XT, int MAXT>
 __global__ __launch_bounds__(256) void gate_up_kernel(FfnArgs a) {
     using F = Fmt<BITS>;
     extern __shared__ float lds[];
@@ -114,72 +255,47 @@ __global__ __launch_bounds__(256) void gate_up_kernel(FfnArgs a) {
         }
         return;
     }
-    const int cols = a.d_in, cpr = cols / F::kCodes;
-    float *xs = lds;
-    float *xsum = lds + a.tpp * cols;
-    const int LR = 1 << a.lr_shift, j = lane & (LR - 1), rsub = lane >> a.lr_shift, RPW = kWave >> a.lr_shift;
-    const int64_t ebase_q = (int64_t)wk.e * a.d_ff;   // row index of the expert's first row
-    const uint32_t *gq = a.gate.q + ebase_q * a.gate.wpr;
-    const uint32_t *uq = a.up.q + ebase_q * a.up.wpr;
-    const uint16_t *gs = a.gate.s + ebase_q * a.gate.gpr, *gb = a.gate.b + ebase_q * a.gate.gpr;
-    const uint16_t *us = a.up.s + ebase_q * a.up.gpr, *ub = a.up.b + ebase_q * a.up.gpr;
+    const int cpr = a.d_in / F::kCodes;
+    const int lr = 1 << a.lr_shift, j = lane & (lr - 1), rsub = lane >> a.lr_shift, rpw = kWave >> a.lr_shift;
+    const QM mats[2] = {a.gate, a.up};
+    const int64_t erow0 = (int64_t)wk.e * a.d_ff;
 
     for (int pb = 0; pb < wk.npairs; pb += a.tpp) {
         const int nt = min(a.tpp, wk.npairs - pb);
-        __syncthreads();
-        stage_inputs<F::kCodes>(xs, xsum, nt, cols, [&](int tt, int c) {
-            const int64_t tok = pair_at(wk, pb + tt) / a.K;
-            return load_act(a.x, a.x_dt, tok * cols + c);
-        });
-        for (int rb = row0 + wave * RPW; rb < row_end; rb += 4 * RPW) {
-            const int r = rb + rsub;
-            const bool live = r < row_end;
-            float g[MAXT], u[MAXT];
+        int64_t x_off = 0;
+        if constexpr (MAXT == 1) {
+            x_off = (int64_t)(pair_at(wk, pb) / a.K) * a.d_in;
+        } else {
+            __syncthreads();
+            stage_inputs<F::kCodes>(lds, nt, cpr, [&](int tt, int c) {
+                const int64_t tok = pair_at(wk, pb + tt) / a.K;
+                return load_act(a.x, a.x_dt, tok * a.d_in + c);
+            });
+        }
+        for (int rb = row0 + wave * rpw * kNR; rb < row_end; rb += 4 * rpw * kNR) {
+            const int r0 = rb + rsub;
+            float acc[2][kNR][MAXT];
+            row_block<BITS, SB, XT, 2, MAXT>(mats, erow0, r0, rpw, row_end, j, lr, cpr, a.x, x_off, lds, nt, acc);
 #pragma unroll
-            for (int t = 0; t < MAXT; ++t) g[t] = u[t] = 0.f;
-            if (live) {
-                const uint32_t *grow = gq + (int64_t)r * a.gate.wpr;
-                const uint32_t *urow = uq + (int64_t)r * a.up.wpr;
-                for (int c = j; c < cpr; c += LR) {
-                    const Chunk<BITS> cg = load_chunk<BITS>(grow + c * F::kWords);
-                    const Chunk<BITS> cu = load_chunk<BITS>(urow + c * F::kWords);
-                    const int64_t gi = (int64_t)r * a.gate.gpr + c / F::kChunksPerGroup;
-                    const float sg = load_sb<SB>(gs, gi), bg = load_sb<SB>(gb, gi);
-                    const float su = load_sb<SB>(us, gi), bu = load_sb<SB>(ub, gi);
-                    float qg[F::kCodes], qu[F::kCodes];
-                    unpack<BITS>(cg, qg);
-                    unpack<BITS>(cu, qu);
+            for (int n = 0; n < kNR; ++n)
 #pragma unroll
-                    for (int t = 0; t < MAXT; ++t) {
-                        if (t < nt) {
-                            const float *xv = xs + t * cols + c * F::kCodes;
-                            float dg = 0.f, du = 0.f;
+                for (int t = 0; t < MAXT; ++t) {
+                    acc[0][n][t] = group_sum(acc[0][n][t], lr);
+                    acc[1][n][t] = group_sum(acc[1][n][t], lr);
+                }
+            if (j == 0) {
 #pragma unroll
-                            for (int q = 0; q < F::kCodes; ++q) {
-                                dg += qg[q] * xv[q];
-                                du += qu[q] * xv[q];
+                for (int n = 0; n < kNR; ++n) {
+                    const int r = r0 + n * rpw;
+                    if (r < row_end) {
+#pragma unroll
+                        for (int t = 0; t < MAXT; ++t)
+                            if (t < nt) {
+                                const float g = acc[0][n][t], u = acc[1][n][t];
+                                a.act[(int64_t)pair_at(wk, pb + t) * a.d_ff + r] = g * sigmoidf_(g) * u;
                             }
-                            const float xsm = xsum[t * cpr + c];
-                            g[t] += sg * dg + bg * xsm;
-                            u[t] += su * du + bu * xsm;
-                        }
                     }
                 }
-            }
-#pragma unroll
-            for (int t = 0; t < MAXT; ++t) {
-                if (t < nt) {
-                    g[t] = group_sum(g[t], LR);
-                    u[t] = group_sum(u[t], LR);
-                }
-            }
-            if (live && j == 0) {
-#pragma unroll
-                for (int t = 0; t < MAXT; ++t)
-                    if (t < nt) {
-                        const int64_t p = pair_at(wk, pb + t);
-                        a.act[p * a.d_ff + r] = g[t] * sigmoidf_(g[t]) * u[t];
-                    }
             }
         }
     }
@@ -202,58 +318,44 @@ __global__ __launch_bounds__(256) void down_kernel(FfnArgs a) {
         }
         return;
     }
-    const int cols = a.d_ff, cpr = cols / F::kCodes;
-    float *xs = lds;
-    float *xsum = lds + a.tpp * cols;
-    const int LR = 1 << a.lr_shift, j = lane & (LR - 1), rsub = lane >> a.lr_shift, RPW = kWave >> a.lr_shift;
-    const int64_t ebase = (int64_t)wk.e * a.d_in;
-    const uint32_t *dq = a.down.q + ebase * a.down.wpr;
-    const uint16_t *ds = a.down.s + ebase * a.down.gpr, *db = a.down.b + ebase * a.down.gpr;
+    const int cpr = a.d_ff / F::kCodes;
+    const int lr = 1 << a.lr_shift, j = lane & (lr - 1), rsub = lane >> a.lr_shift, rpw = kWave >> a.lr_shift;
+    const QM mats[1] = {a.down};
+    const int64_t erow0 = (int64_t)wk.e * a.d_in;
 
     for (int pb = 0; pb < wk.npairs; pb += a.tpp) {
         const int nt = min(a.tpp, wk.npairs - pb);
-        __syncthreads();
-        stage_inputs<F::kCodes>(xs, xsum, nt, cols, [&](int tt, int c) {
-            const int64_t p = pair_at(wk, pb + tt);
-            return a.act[p * cols + c];
-        });
-        for (int rb = row0 + wave * RPW; rb < row_end; rb += 4 * RPW) {
-            const int r = rb + rsub;
-            const bool live = r < row_end;
-            float acc[MAXT];
+        int64_t x_off = 0;
+        if constexpr (MAXT == 1) {
+            x_off = (int64_t)pair_at(wk, pb) * a.d_ff;
+        } else {
+            __syncthreads();
+            stage_inputs<F::kCodes>(lds, nt, cpr, [&](int tt, int c) {
+                return a.act[(int64_t)pair_at(wk, pb + tt) * a.d_ff + c];
+            });
+        }
+        for (int rb = row0 + wave * rpw * kNR; rb < row_end; rb += 4 * rpw * kNR) {
+            const int r0 = rb + rsub;
+            float acc[1][kNR][MAXT];
+            row_block<BITS, SB, MOE_F32, 1, MAXT>(mats, erow0, r0, rpw, row_end, j, lr, cpr, a.act, x_off, lds, nt, acc);
 #pragma unroll
-            for (int t = 0; t < MAXT; ++t) acc[t] = 0.f;
-            if (live) {
-                const uint32_t *row = dq + (int64_t)r * a.down.wpr;
-                for (int c = j; c < cpr; c += LR) {
-                    const Chunk<BITS> cd = load_chunk<BITS>(row + c * F::kWords);
-                    const int64_t gi = (int64_t)r * a.down.gpr + c / F::kChunksPerGroup;
-                    const float s = load_sb<SB>(ds, gi), b = load_sb<SB>(db, gi);
-                    float qd[F::kCodes];
-                    unpack<BITS>(cd, qd);
+            for (int n = 0; n < kNR; ++n)
 #pragma unroll
-                    for (int t = 0; t < MAXT; ++t) {
-                        if (t < nt) {
-                            const float *xv = xs + t * cols + c * F::kCodes;
-                            float d = 0.f;
+                for (int t = 0; t < MAXT; ++t) acc[0][n][t] = group_sum(acc[0][n][t], lr);
+            if (j == 0) {
 #pragma unroll
-                            for (int q = 0; q < F::kCodes; ++q) d += qd[q] * xv[q];
-                            acc[t] += s * d + b * xsum[t * cpr + c];
-                        }
+                for (int n = 0; n < kNR; ++n) {
+                    const int r = r0 + n * rpw;
+                    if (r < row_end) {
+#pragma unroll
+                        for (int t = 0; t < MAXT; ++t)
+                            if (t < nt) {
+                                const int64_t p = pair_at(wk, pb + t);
+                                const float sc = a.scores ? a.scores[p] : 1.0f;
+                                a.partial[p * a.d_in + r] = sc * acc[0][n][t];
+                            }
                     }
                 }
-            }
-#pragma unroll
-            for (int t = 0; t < MAXT; ++t)
-                if (t < nt) acc[t] = group_sum(acc[t], LR);
-            if (live && j == 0) {
-#pragma unroll
-                for (int t = 0; t < MAXT; ++t)
-                    if (t < nt) {
-                        const int64_t p = pair_at(wk, pb + t);
-                        const float sc = a.scores ? a.scores[p] : 1.0f;
-                        a.partial[p * a.d_in + r] = sc * acc[t];
-                    }
             }
         }
     }
@@ -301,15 +403,34 @@ __global__ __launch_bounds__(256) void bucket_kernel(const int32_t *ids, int n_p
 
 using KernelFn = void (*)(FfnArgs);
 
-template <int BITS, int SB, int MAXT>
-static KernelFn pick_gate_up() { return gate_up_kernel<BITS, SB, MAXT>; }
-template <int BITS, int SB, int MAXT>
-static KernelFn pick_down() { return down_kernel<BITS, SB, MAXT>; }
+// Kernel A instantiations: bits x scale dtype x (single-token input dtype, or
+// staged multi-token inputs).
+template <int BITS, int SB>
+static KernelFn pick_gate_up(int x_dt, bool multi) {
+    if (multi) return gate_up_kernel<BITS, SB, -1, 8>;
+    switch (x_dt) {
+    case MOE_F32: return gate_up_kernel<BITS, SB, MOE_F32, 1>;
+    case MOE_F16: return gate_up_kernel<BITS, SB, MOE_F16, 1>;
+    default: return gate_up_kernel<BITS, SB, MOE_BF16, 1>;
+    }
+}
 
-template <bool GATE_UP, int MAXT>
-static KernelFn select_kernel(int bits, int sb) {
-#define MOE_PICK(B, S) \
-    if (bits == B && sb == S) return GATE_UP ? pick_gate_up<B, S, MAXT>() : pick_down<B, S, MAXT>();
+template <int BITS, int SB>
+static KernelFn pick_down(bool multi) {
+    return multi ? down_kernel<BITS, SB, 8> : down_kernel<BITS, SB, 1>;
+}
+
+static KernelFn select_gate_up(int bits, int sb, int x_dt, bool multi) {
+#define MOE_PICK(B, S) if (bits == B && sb == S) return pick_gate_up<B, S>(x_dt, multi);
+    MOE_PICK(4, MOE_BF16) MOE_PICK(4, MOE_F16)
+    MOE_PICK(6, MOE_BF16) MOE_PICK(6, MOE_F16)
+    MOE_PICK(8, MOE_BF16) MOE_PICK(8, MOE_F16)
+#undef MOE_PICK
+    return nullptr;
+}
+
+static KernelFn select_down(int bits, int sb, bool multi) {
+#define MOE_PICK(B, S) if (bits == B && sb == S) return pick_down<B, S>(multi);
     MOE_PICK(4, MOE_BF16) MOE_PICK(4, MOE_F16)
     MOE_PICK(6, MOE_BF16) MOE_PICK(6, MOE_F16)
     MOE_PICK(8, MOE_BF16) MOE_PICK(8, MOE_F16)
@@ -319,12 +440,11 @@ static KernelFn select_kernel(int bits, int sb) {
 
 static int codes_per_chunk(int bits) { return bits == 4 ? 32 : 16; }
 
-// Lanes per row: the largest power of two <= 64 dividing the chunk count,
-// unless that leaves more than 16 chunks per lane.
+// Lanes per row: the chunk count rounded up to a power of two, at most 64
+// (lanes past the row's last chunk stay idle; longer rows loop).
 static int pick_lr_shift(int cpr) {
     int s = 0;
-    while (s < 6 && (cpr % (2 << s)) == 0) ++s;
-    while (s < 6 && (cpr >> s) > 16) ++s;
+    while (s < 6 && (1 << s) < cpr) ++s;
     return s;
 }
 
@@ -407,13 +527,19 @@ static void launch_bucket(const Plan &p) {
                        const_cast<int32_t *>(p.a.pair_list), const_cast<int32_t *>(p.a.n_work));
 }
 
-// Kernel launch geometry for a projection with `cols` inputs of `bits` bits and `rows` outputs.
+// Kernel launch geometry for a projection with `cols` inputs of `bits` bits.
 static moe_status geometry(FfnArgs &a, int maxt, int cols, int bits, size_t &lds) {
-    const int cpr = cols / codes_per_chunk(bits);
+    const int codes = codes_per_chunk(bits);
+    const int cpr = cols / codes;
     a.lr_shift = pick_lr_shift(cpr);
     const int rpw = kWave >> a.lr_shift;
-    a.rows_per_wg = 4 * rpw * 2;
-    const size_t per_tok = (size_t)(cols + cpr) * sizeof(float);
+    a.rows_per_wg = 4 * rpw * kNR;
+    if (maxt == 1) {
+        a.tpp = 1;
+        lds = 0;
+        return MOE_OK;
+    }
+    const size_t per_tok = (size_t)cpr * (codes + 4) * sizeof(float);
     const int fit = (int)(kLdsBudget / per_tok);
     a.tpp = fit < maxt ? fit : maxt;
     if (a.tpp < 1) return MOE_EUNSUPPORTED;
@@ -422,8 +548,7 @@ static moe_status geometry(FfnArgs &a, int maxt, int cols, int bits, size_t &lds
 }
 
 static moe_status launch_a(Plan &p) {
-    KernelFn k = p.maxt > 1 ? select_kernel<true, 8>(p.a.gate.bits_, p.a.gate.sb_)
-                            : select_kernel<true, 1>(p.a.gate.bits_, p.a.gate.sb_);
+    KernelFn k = select_gate_up(p.a.gate.bits_, p.a.gate.sb_, p.a.x_dt, p.maxt > 1);
     if (!k) return MOE_EUNSUPPORTED;
     size_t lds;
     const moe_status st = geometry(p.a, p.maxt, p.a.d_in, p.a.gate.bits_, lds);
@@ -434,8 +559,7 @@ static moe_status launch_a(Plan &p) {
 }
 
 static moe_status launch_b(Plan &p) {
-    KernelFn k = p.maxt > 1 ? select_kernel<false, 8>(p.a.down.bits_, p.a.down.sb_)
-                            : select_kernel<false, 1>(p.a.down.bits_, p.a.down.sb_);
+    KernelFn k = select_down(p.a.down.bits_, p.a.down.sb_, p.maxt > 1);
     if (!k) return MOE_EUNSUPPORTED;
     size_t lds;
     const moe_status st = geometry(p.a, p.maxt, p.a.d_ff, p.a.down.bits_, lds);

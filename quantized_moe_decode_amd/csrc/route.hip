@@ -5,10 +5,12 @@
 // One launch.  Workgroups of four waves each compute four router logits
 // (one wave per router row, fp32 accumulation over the contraction with a
 // wave64 butterfly reduction).  The router matrix is read once, spread over
-// many CUs.  The last workgroup to finish a token (device-scope counter)
-// selects the top-k from that token's logits and computes its scores; the
-// counter is reset to zero by that workgroup, so the workspace stays clean
-// for the next call (and for graph replays).
+// many CUs.  Logits are published with device-coherent stores and a
+// device-scope counter per token; the last workgroup to arrive selects the
+// top-k from that token's logits (read with device-coherent loads) and
+// computes its scores.  No cache-wide fence is needed: only the logits and
+// the counter cross workgroups.  The last workgroup resets the counter, so
+// the workspace is ready for the next call (and for graph replays).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -32,81 +34,99 @@ struct RouteArgs {
     uint32_t *counters;      // workspace [T]
 };
 
-// Dot product of a d_in-long row (dtype dt) with x staged as fp32 in LDS.
-__device__ float row_dot(const void *w, int dt, int64_t row, int d_in, const float *xs, int lane) {
-    float acc = 0.f;
-    if (dt == MOE_F32) {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(w) + row * d_in);
-        for (int c = lane; c < d_in / 4; c += kWave) {
-            const f32x4 v = p[c];
-            acc += v.x * xs[4 * c] + v.y * xs[4 * c + 1] + v.z * xs[4 * c + 2] + v.w * xs[4 * c + 3];
-        }
+// Eight consecutive elements of a row as floats (one 16-byte load for 16-bit
+// dtypes, two for fp32).
+template <int DT>
+__device__ __forceinline__ void load8(const void *base, int64_t elem, float *v) {
+    if constexpr (DT == MOE_F32) {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(base) + elem);
+        const f32x4 a = p[0], b = p[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     } else {
-        const u32x4 *p = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(w) + row * d_in);
-        for (int c = lane; c < d_in / 8; c += kWave) {
-            const u32x4 v = p[c];
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(base) + elem);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if constexpr (DT == MOE_BF16) {
+                v[2 * k] = __uint_as_float(w[k] << 16);
+                v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+            } else {
+                _Float16 lo, hi;
+                const uint16_t l16 = (uint16_t)(w[k] & 0xFFFFu), h16 = (uint16_t)(w[k] >> 16);
+                __builtin_memcpy(&lo, &l16, 2);
+                __builtin_memcpy(&hi, &h16, 2);
+                v[2 * k] = (float)lo;
+                v[2 * k + 1] = (float)hi;
+            }
+        }
+    }
+}
+
+// One router (or shared-gate) row dotted with x: lane l takes the 8-element
+// chunks l, l+64, ...; up to four chunks' loads are in flight before use.
+template <int XT, int WT>
+__device__ float row_dot(const void *w, int64_t row, const void *x, int64_t xrow, int d_in, int lane) {
+    const int nch = d_in / 8;
+    float acc = 0.f;
+    for (int base = 0; base < nch; base += 4 * kWave) {
+        float wv[4][8], xv[4][8];
+        bool ok[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = base + u * kWave + lane;
+            ok[u] = c < nch;
+            const int cc = ok[u] ? c : 0;     // in-bounds address; masked below
+            load8<WT>(w, row * d_in + 8 * cc, wv[u]);
+            load8<XT>(x, xrow * d_in + 8 * cc, xv[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
             float part = 0.f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                float a, b;
-                if (dt == MOE_BF16) {
-                    a = __uint_as_float(v[k] << 16);
-                    b = __uint_as_float(v[k] & 0xFFFF0000u);
-                } else {
-                    _Float16 ha, hb;
-                    const uint16_t la = (uint16_t)(v[k] & 0xFFFFu), lb = (uint16_t)(v[k] >> 16);
-                    __builtin_memcpy(&ha, &la, 2);
-                    __builtin_memcpy(&hb, &lb, 2);
-                    a = (float)ha;
-                    b = (float)hb;
-                }
-                part += a * xs[8 * c + 2 * k] + b * xs[8 * c + 2 * k + 1];
-            }
-            acc += part;
+            for (int i = 0; i < 8; ++i) part += wv[u][i] * xv[u][i];
+            acc += ok[u] ? part : 0.f;
         }
     }
     return wave_sum(acc);
 }
 
+template <int XT, int WT, int GT>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
-    extern __shared__ float xs[];   // [d_in] fp32
     __shared__ int s_last;
     const int t = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int n_rows = a.E + (a.wg ? 1 : 0);
-
-    for (int j = tid; j < a.d_in; j += blockDim.x)
-        xs[j] = load_act(a.x, a.x_dt, (int64_t)t * a.d_in + j);
-    __syncthreads();
+    float *logits = a.logits + (int64_t)t * (a.E + 1);
 
     const int row = blockIdx.x * kRouteWaves + wave;
     if (row < n_rows) {
-        float v = (row < a.E) ? row_dot(a.wr, a.wr_dt, row, a.d_in, xs, lane)
-                              : row_dot(a.wg, a.wg_dt, 0, a.d_in, xs, lane);
-        if (lane == 0) a.logits[(int64_t)t * (a.E + 1) + row] = v;
+        const float v = (row < a.E) ? row_dot<XT, WT>(a.wr, row, a.x, t, a.d_in, lane)
+                                    : row_dot<XT, GT>(a.wg, 0, a.x, t, a.d_in, lane);
+        if (lane == 0) {
+            // device-coherent store, completed before this workgroup signals
+            __hip_atomic_store(logits + row, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_s_waitcnt(0);
+        }
     }
-
-    // Last-arriving workgroup of this token does the selection.
-    __threadfence();
     __syncthreads();
     if (tid == 0) {
-        const uint32_t prev = atomicAdd(&a.counters[t], 1u);
+        const uint32_t prev = __hip_atomic_fetch_add(&a.counters[t], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == gridDim.x - 1);
     }
     __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (wave != 0) return;
+    if (!s_last || wave != 0) return;
 
-    const float *l = a.logits + (int64_t)t * (a.E + 1);
-    // Each lane owns experts lane, lane+64, ... (at most 16 of them).
+    // Last workgroup of token t: top-k over the E logits in one wave.  Each
+    // lane owns experts lane, lane+64, ... (at most 16 of them).
     constexpr int kPer = MOE_MAX_EXPERTS / kWave;
     float mine[kPer];
     uint32_t taken = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int e = lane + i * kWave;
-        mine[i] = (e < a.E) ? l[e] : -INFINITY;
+        mine[i] = (e < a.E) ? __hip_atomic_load(logits + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            : -INFINITY;
     }
     int my_id = -1;           // lane k keeps the k-th selection
     float my_logit = 0.f, mx = 0.f;
@@ -136,7 +156,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
             my_id = bi;
             my_logit = bv;
         }
-        if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+        if ((bi & (kWave - 1)) == lane) taken |= 1u << ((bi / kWave) & 31);
     }
     // softmax over all experts, max-subtracted (the maximum is the first selection)
     float z = 0.f;
@@ -153,8 +173,40 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
         a.scores[t * a.K + lane] = a.renorm ? p / psum : p;
     }
     if (lane == 0) {
-        if (a.wg) a.gate[t] = 1.0f / (1.0f + expf(-l[a.E]));
-        a.counters[t] = 0u;   // leave the workspace zeroed for the next call
+        if (a.wg) {
+            const float gl = __hip_atomic_load(logits + a.E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            a.gate[t] = 1.0f / (1.0f + expf(-gl));
+        }
+        // leave the counter at zero for the next call
+        __hip_atomic_store(&a.counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+using RouteFn = void (*)(RouteArgs);
+
+template <int XT, int WT>
+static RouteFn pick_route_g(int gt) {
+    switch (gt) {
+    case MOE_F32: return route_kernel<XT, WT, MOE_F32>;
+    case MOE_F16: return route_kernel<XT, WT, MOE_F16>;
+    default: return route_kernel<XT, WT, MOE_BF16>;
+    }
+}
+
+template <int XT>
+static RouteFn pick_route_w(int wt, int gt) {
+    switch (wt) {
+    case MOE_F32: return pick_route_g<XT, MOE_F32>(gt);
+    case MOE_F16: return pick_route_g<XT, MOE_F16>(gt);
+    default: return pick_route_g<XT, MOE_BF16>(gt);
+    }
+}
+
+static RouteFn pick_route(int xt, int wt, int gt) {
+    switch (xt) {
+    case MOE_F32: return pick_route_w<MOE_F32>(wt, gt);
+    case MOE_F16: return pick_route_w<MOE_F16>(wt, gt);
+    default: return pick_route_w<MOE_BF16>(wt, gt);
     }
 }
 
@@ -199,7 +251,7 @@ extern "C" moe_status moe_decode_route(const void *x, moe_dtype x_dtype, int32_t
 
     const int n_rows = n_experts + (w_shared_gate ? 1 : 0);
     dim3 grid((n_rows + kRouteWaves - 1) / kRouteWaves, n_tokens);
-    hipLaunchKernelGGL(route_kernel, grid, dim3(256), d_in * sizeof(float),
-                       reinterpret_cast<hipStream_t>(stream), a);
+    RouteFn k = pick_route(x_dtype, w_router_dtype, w_shared_gate ? w_shared_gate_dtype : MOE_BF16);
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
