@@ -3,10 +3,12 @@
 
 One step = one decode token (or one batch of tokens for the batch config)
 through every layer of the workload: route -> expert FFN (kernel A, kernel B,
-shared experts) -> tail, for each layer in order on one stream.  Each
-distinct token's step is captured once into a HIP graph (torch.cuda.CUDAGraph
-over the library's launches) and replayed; all inputs and weights are
-resident in HBM before the timed region starts.
+shared experts) -> tail, for each layer in order on one stream; with one token
+per step each layer is the fused single-launch moe_decode_layer (the
+three-call path is timed beside it for comparison).  Each distinct token's
+step is captured once into a HIP graph (torch.cuda.CUDAGraph over the
+library's launches) and replayed; all inputs and weights are resident in HBM
+before the timed region starts.
 
 Throughput is expert-weight bytes per second: the packed codes plus scales
 and biases of every expert the step touches (each touched expert counted
@@ -18,10 +20,14 @@ launch/sync overhead of the bracket is far below 2% (the amortisation check
 re-times K/2 steps and reports the per-step ratio).
 
 Extra fields:
-  roofline      the dominant kernel (kernel A, gate/up + SwiGLU) against the
-                8 TB/s HBM peak: its algorithmic bytes per launch divided by
-                its average launch duration, from HIP events around graph
-                replays of that kernel alone over the same layers and tokens.
+  roofline      the dominant kernel against the 8 TB/s HBM peak: its
+                algorithmic bytes per launch divided by its average launch
+                duration.  Fused path: the layer kernel is the only kernel of
+                the step, so its average duration is the timed region over
+                the launches in it (HIP events on the replay stream); bytes are
+                the touched experts' weights plus the router matrix.
+                Three-call path: kernel A alone, from HIP events around graph
+                replays of its launches over the same layers and tokens.
   cpu_baseline  the CPU oracle (fp64, all host cores) on a bounded sample of
                 the same workload, in the same unit.
 """
@@ -53,7 +59,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--path", choices=("fused", "three-call"), default=None,
+                    help="fused single-launch layer (default for one token per step) or "
+                         "route + expert FFN + tail (default for several tokens per step)")
     return ap.parse_args()
 
 
@@ -106,9 +114,18 @@ def main():
     outs = [torch.zeros(T, cfg.d_in, device=dev) for _ in range(L)]
     torch.cuda.synchronize()
 
-    def step_eager(r):
+    path = args.path or ("fused" if T == 1 else "three-call")
+    if path == "fused" and T != 1:
+        print("the fused layer launch takes one token per step", file=sys.stderr)
+        sys.exit(2)
+
+    def step_eager(r, which=None):
+        fused = (which or path) == "fused"
         for li in range(L):
-            layers[li].forward(xs[r][li], rs[r][li], outs[li])
+            if fused:
+                layers[li].forward_fused(xs[r][li], rs[r][li], outs[li])
+            else:
+                layers[li].forward(xs[r][li], rs[r][li], outs[li])
 
     # ---- capture one graph per distinct token
     s = torch.cuda.Stream()
@@ -168,11 +185,24 @@ def main():
     secs_half = timed(half)
     amort = (secs_half / half) / (secs / args.steps)
 
-    # ---- roofline of the dominant kernel (kernel A) from its own graph replays
-    roofline = None
-    if not args.no_roofline:
-        a_graphs = []
-        a_bytes = []
+    # ---- roofline of the dominant kernel.  With the fused path every launch of
+    # the step is the layer kernel, so its average launch duration is the timed
+    # region divided by the launches in it; algorithmic bytes per launch are
+    # the touched experts' weights plus the router matrix.
+    router_bytes = layers[0].router.numel() * layers[0].router.element_size()
+    if path == "fused":
+        launches = args.steps * L
+        avg_us = secs / launches * 1e6
+        alg = (bytes_total + args.steps * L * router_bytes) / launches
+        roofline = {"kernel": "layer_kernel (route + kernel A + kernel B + tail, one launch per layer)",
+                    "bound": "hbm", "achieved": round(alg / (avg_us * 1e-6) / 1e9, 1),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(alg / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "traffic": None, "avg_launch_us": round(avg_us, 3),
+                    "bytes_per_launch": int(alg)}
+    else:
+        # kernel A alone, from graphs holding only its launches for the same tokens
+        a_graphs, a_bytes = [], []
         for r in range(R):
             graphs[r].replay()           # leaves token r's expert ids in every layer
             torch.cuda.synchronize()
@@ -196,15 +226,38 @@ def main():
         torch.cuda.synchronize()
         a_secs = ev0.elapsed_time(ev1) / 1000.0
         launches = reps * L
-        avg_us = a_secs / launches * 1e6
         a_total = sum(a_bytes[i % R] for i in range(reps))
         achieved = a_total / a_secs / 1e9
         roofline = {"kernel": "gate_up_kernel (kernel A: gate/up GEMV + SwiGLU)",
                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": None,
-                    "avg_launch_us": round(avg_us, 3),
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "avg_launch_us": round(a_secs / launches * 1e6, 3),
                     "bytes_per_launch": int(a_total / launches)}
+
+    # ---- the other path on the same tokens, for comparison (not the headline)
+    other = None
+    if T == 1:
+        which = "three-call" if path == "fused" else "fused"
+        og = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step_eager(r, which)
+            og.append(g)
+        for g in og:
+            g.replay()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        n_o = max(10, args.steps // 3)
+        ev0.record()
+        for i in range(n_o):
+            og[i % R].replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        o_secs = ev0.elapsed_time(ev1) / 1000.0
+        other = {"path": which, "GBps": round(sum(step_bytes[i % R] for i in range(n_o)) / o_secs / 1e9, 2),
+                 "ms_per_step": round(o_secs / n_o * 1e3, 4)}
 
     # ---- CPU oracle baseline on a bounded sample
     cpu = None
@@ -252,6 +305,8 @@ def main():
         "expert_bytes_per_step": int(np.mean(step_bytes)),
         "amortisation_ratio_half_vs_full": round(amort, 4),
         "wall_s_timed": round(wall, 4),
+        "path": path,
+        "other_path": other,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -185,6 +185,58 @@ moe_status moe_decode_tail(const float *partial, int32_t n_tokens, int32_t top_k
                            const void *residual, moe_dtype residual_dtype, float *out,
                            void *stream);
 
+/*
+ * The whole layer for ONE token in a single launch: route, kernel A and
+ * kernel B for the K selected experts and the S shared experts, and the tail,
+ * with the same arithmetic as moe_decode_route + moe_decode_expert_ffn (routed,
+ * then shared) + moe_decode_tail (sources as cited above).  Workgroups hand
+ * results to each other through the workspace and device-scope counters
+ * instead of kernel boundaries, so the down-projection weights stream while
+ * the gate/up projections run (the dependency [P1] "What changed" step 1
+ * describes, resolved inside one launch).
+ *
+ * moe_layer_weights (host struct; every pointer in it is a device pointer):
+ *   w_router [n_experts][d_in] in the dtype of x; n_experts == gate.n_experts
+ *   top_k, renormalize         as in moe_decode_route
+ *   gate, up, down             routed stacks (as in moe_decode_expert_ffn)
+ *   n_shared                   0..MOE_MAX_SHARED shared experts, summed in order
+ *   shared_gate/_up/_down      shared stacks (n_experts = n_shared; their own
+ *                              d_ff; same bit widths and scale dtype as the
+ *                              routed stacks); ignored when n_shared == 0
+ *   w_shared_gate              [d_in] in the dtype of x, or NULL (gate 1); only
+ *                              with n_shared > 0
+ * Arguments: x [d_in] and residual [d_in] (one token); out [d_in] fp32;
+ * expert_ids [top_k], scores [top_k], shared_gate [1]: optional outputs (NULL
+ * to skip); workspace of moe_decode_layer_workspace_bytes() bytes, 16-byte
+ * aligned, zero-filled before its first use and not written by the caller
+ * afterwards (each launch leaves it ready for the next).  Its first 4 bytes
+ * become nonzero, and stay so, if an internal wait ever timed out (results of
+ * that launch invalid); this cannot happen unless the device is shared with
+ * work that starves the launch for a long time.  Launches that may run
+ * concurrently need separate workspaces.
+ */
+#define MOE_MAX_SHARED 8
+
+typedef struct {
+    const void *w_router;
+    moe_dtype w_router_dtype;
+    int32_t n_experts;
+    int32_t top_k;
+    int32_t renormalize;
+    moe_qmat gate, up, down;
+    int32_t n_shared;
+    moe_qmat shared_gate, shared_up, shared_down;
+    const void *w_shared_gate;
+} moe_layer_weights;
+
+moe_status moe_decode_layer(const moe_layer_weights *weights, const void *x, moe_dtype x_dtype,
+                            const void *residual, moe_dtype residual_dtype, float *out,
+                            int32_t *expert_ids, float *scores, float *shared_gate,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* 0 when the weights are invalid or unsupported. */
+size_t moe_decode_layer_workspace_bytes(const moe_layer_weights *weights);
+
 /* Human-readable name of a status code (static storage). */
 const char *moe_decode_status_string(moe_status s);
 

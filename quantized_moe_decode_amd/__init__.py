@@ -42,6 +42,15 @@ class CQMat(ctypes.Structure):
                 ("bits", ctypes.c_int32), ("group_size", ctypes.c_int32), ("sb_dtype", ctypes.c_int32)]
 
 
+class CLayerWeights(ctypes.Structure):
+    """moe_layer_weights of the C ABI."""
+    _fields_ = [("w_router", ctypes.c_void_p), ("w_router_dtype", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("renormalize", ctypes.c_int32), ("gate", CQMat), ("up", CQMat), ("down", CQMat),
+                ("n_shared", ctypes.c_int32), ("shared_gate", CQMat), ("shared_up", CQMat),
+                ("shared_down", CQMat), ("w_shared_gate", ctypes.c_void_p)]
+
+
 def _load_library():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_moe_decode_amd.build`")
@@ -62,6 +71,11 @@ def _load_library():
     L.moe_decode_gate_up.restype = i32
     L.moe_decode_down.argtypes = [vp, i32, ctypes.POINTER(CQMat), vp, vp, i32, vp, vp, sz, vp]
     L.moe_decode_down.restype = i32
+    L.moe_decode_layer.argtypes = [ctypes.POINTER(CLayerWeights), vp, i32, vp, i32, vp, vp, vp, vp,
+                                   vp, sz, vp]
+    L.moe_decode_layer.restype = i32
+    L.moe_decode_layer_workspace_bytes.argtypes = [ctypes.POINTER(CLayerWeights)]
+    L.moe_decode_layer_workspace_bytes.restype = sz
     L.moe_decode_tail.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp]
     L.moe_decode_tail.restype = i32
     L.moe_decode_status_string.argtypes = [i32]
@@ -195,6 +209,36 @@ def moe_decode_down(act: torch.Tensor, down: QuantStack, expert_ids: torch.Tenso
     _check(st, "moe_decode_down")
 
 
+def layer_weights(w_router: torch.Tensor, top_k: int, renormalize: bool, gate: QuantStack,
+                  up: QuantStack, down: QuantStack, shared=None,
+                  w_shared_gate: Optional[torch.Tensor] = None) -> CLayerWeights:
+    """The moe_layer_weights struct for a layer (device tensors stay owned by the caller)."""
+    E = w_router.shape[0]
+    z = CQMat()
+    sh = tuple(shared) if shared is not None else None
+    return CLayerWeights(w_router.data_ptr(), _dt(w_router), E, top_k, int(bool(renormalize)),
+                         gate.cstruct(), up.cstruct(), down.cstruct(),
+                         0 if sh is None else sh[0].n_experts,
+                         *(z, z, z) if sh is None else tuple(m.cstruct() for m in sh),
+                         None if w_shared_gate is None else w_shared_gate.data_ptr())
+
+
+def layer_workspace_bytes(weights: CLayerWeights) -> int:
+    return lib.moe_decode_layer_workspace_bytes(ctypes.byref(weights))
+
+
+def moe_decode_layer(weights: CLayerWeights, x: torch.Tensor, residual: torch.Tensor,
+                     out: torch.Tensor, workspace: torch.Tensor,
+                     expert_ids: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
+                     shared_gate: Optional[torch.Tensor] = None, stream=None) -> None:
+    """The fused single-launch layer for one token: out [d_in] fp32."""
+    st = lib.moe_decode_layer(ctypes.byref(weights), _ptr(x), _dt(x), _ptr(residual), _dt(residual),
+                              _ptr(out), _ptr(expert_ids), _ptr(scores), _ptr(shared_gate),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream))
+    _check(st, "moe_decode_layer")
+
+
 def moe_decode_tail(partial: torch.Tensor, residual: torch.Tensor, out: torch.Tensor,
                     shared: Optional[torch.Tensor] = None,
                     shared_gate: Optional[torch.Tensor] = None, stream=None) -> None:
@@ -209,6 +253,7 @@ def moe_decode_tail(partial: torch.Tensor, residual: torch.Tensor, out: torch.Te
 from .layer import DecodeLayer  # noqa: E402  (needs the functions above)
 
 __all__ = ["QuantStack", "DecodeLayer", "moe_decode_route", "moe_decode_expert_ffn",
+           "moe_decode_layer", "layer_weights", "layer_workspace_bytes",
            "moe_decode_gate_up", "moe_decode_down",
            "moe_decode_tail", "route_workspace_bytes", "expert_ffn_workspace_bytes",
            "MoeError", "status_string", "abi_version", "lib"]

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmoe_decode.so")
-SOURCES = ["route.hip", "expert_ffn.hip", "tail.hip"]
+SOURCES = ["route.hip", "expert_ffn.hip", "tail.hip", "layer.hip", "layer_a4.hip", "layer_a6.hip",
+           "layer_a8.hip"]
 ARCH = "gfx950"
 
 

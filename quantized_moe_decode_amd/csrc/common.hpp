@@ -108,19 +108,45 @@ __device__ __forceinline__ float load_act(const void *p, int dt, int64_t i) {
     return (float)f;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
 // Sum over aligned groups of `width` lanes (a power of two <= 64); every lane
-// of the group ends with the same bits.
+// of the group ends with the same bits.  Distances 1 and 2 use quad
+// permutations, 4 and 8 the row half-mirror and row mirror (DPP, no LDS
+// traffic); 16 and 32 use lane shuffles.  Each step adds a value that is
+// uniform over the partner set, so all lanes of a group compute the same sum.
 __device__ __forceinline__ float group_sum(float v, int width) {
-    for (int m = width >> 1; m > 0; m >>= 1)
-        v += __shfl_xor(v, m, kWave);
+    if (width >= 2) v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+    if (width >= 4) v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+    if (width >= 8) v += dpp_f<0x141>(v);   // row_half_mirror
+    if (width >= 16) v += dpp_f<0x140>(v);  // row_mirror
+    if (width >= 32) v += __shfl_xor(v, 16, kWave);
+    if (width >= 64) v += __shfl_xor(v, 32, kWave);
     return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m > 0; m >>= 1)
-        v += __shfl_xor(v, m, kWave);
-    return v;
+__device__ __forceinline__ float wave_sum(float v) { return group_sum(v, kWave); }
+
+// Maximum over the wave with DPP row shifts and row broadcasts; every lane
+// gets the result.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float fmax_dpp(float v) {
+    const int o = __builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), CTRL, ROW_MASK,
+                                              0xf, false);
+    return fmaxf(v, __int_as_float(o));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmax_dpp<0x111, 0xf>(v);   // row_shr:1
+    v = fmax_dpp<0x112, 0xf>(v);   // row_shr:2
+    v = fmax_dpp<0x114, 0xf>(v);   // row_shr:4
+    v = fmax_dpp<0x118, 0xf>(v);   // row_shr:8  (lane 15 of each row: the row maximum)
+    v = fmax_dpp<0x142, 0xa>(v);   // row_bcast:15
+    v = fmax_dpp<0x143, 0xc>(v);   // row_bcast:31 (lane 63: the wave maximum)
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }

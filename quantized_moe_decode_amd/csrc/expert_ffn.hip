@@ -25,16 +25,9 @@
 
 #include "api.hpp"
 #include "common.hpp"
+#include "qgemv.hpp"
 
 namespace moe {
-
-struct QM {
-    const uint32_t *q;
-    const uint16_t *s;
-    const uint16_t *b;
-    int rows, cols, wpr, gpr;   // words and groups per row
-    int bits_, sb_;             // host-side kernel selection only
-};
 
 struct FfnArgs {
     const void *x;
@@ -84,157 +77,57 @@ __device__ __forceinline__ int pair_at(const Work &wk, int i) { return wk.pairs 
 // flight.
 constexpr int kNR = 4;
 
-// Input chunk of CODES consecutive values for a single token, read straight
-// from global memory (it is small and shared by every row: it stays in L2).
-template <int XT, int CODES>
-__device__ __forceinline__ void load_x_chunk(const void *x, int64_t off, float *xv) {
-    if constexpr (XT == MOE_F32) {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(x) + off);
-#pragma unroll
-        for (int i = 0; i < CODES / 4; ++i) {
-            const f32x4 v = p[i];
-            xv[4 * i] = v.x; xv[4 * i + 1] = v.y; xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
-        }
-    } else {
-        const u32x4 *p = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(x) + off);
-#pragma unroll
-        for (int i = 0; i < CODES / 8; ++i) {
-            const u32x4 v = p[i];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                if constexpr (XT == MOE_BF16) {
-                    xv[8 * i + 2 * k] = __uint_as_float(v[k] << 16);
-                    xv[8 * i + 2 * k + 1] = __uint_as_float(v[k] & 0xFFFF0000u);
-                } else {
-                    _Float16 lo, hi;
-                    const uint16_t l16 = (uint16_t)(v[k] & 0xFFFFu), h16 = (uint16_t)(v[k] >> 16);
-                    __builtin_memcpy(&lo, &l16, 2);
-                    __builtin_memcpy(&hi, &h16, 2);
-                    xv[8 * i + 2 * k] = (float)lo;
-                    xv[8 * i + 2 * k + 1] = (float)hi;
-                }
-            }
-        }
-    }
-}
-
-// LDS layout for several tokens: token slot t, chunk c occupies floats
-// [(t*cpr + c)*(CODES+4), +CODES) with the chunk's input sum at +CODES.  The
-// 4-float pad makes the 16-byte LDS reads of consecutive chunks by
-// consecutive lanes fall in distinct banks.
-template <int CODES, typename Src>
-__device__ __forceinline__ void stage_inputs(float *xs, int nt, int cpr, Src src) {
-    constexpr int SLOT = CODES + 4;
-    const int tid = threadIdx.x;
-    const int per_tok = cpr * CODES;
-    for (int i = tid; i < nt * per_tok; i += blockDim.x) {
-        const int t = i / per_tok, rem = i - t * per_tok;
-        const int c = rem / CODES, q = rem - c * CODES;
-        xs[(t * cpr + c) * SLOT + q] = src(t, rem);
-    }
-    __syncthreads();
-    for (int i = tid; i < nt * cpr; i += blockDim.x) {
-        float *p = xs + i * SLOT;
-        float sum = 0.f;
-#pragma unroll
-        for (int q = 0; q < CODES; ++q) sum += p[q];
-        p[CODES] = sum;
-    }
-    __syncthreads();
-}
-
-__device__ __forceinline__ float chunk_sum(const float *v, int n) {
-    float s = 0.f;
-    for (int i = 0; i < n; ++i) s += v[i];
-    return s;
-}
-
-// Dot products of kNR rows (rows r0, r0+rstep, ...) of NM matrices of expert
-// row base `erow0` with the inputs, accumulated per lane (to be combined over
-// the row's LR lanes by the caller).  MAXT == 1 reads the single token's input
-// chunk from global memory (x_src, dtype XT); MAXT > 1 reads the staged LDS copy.
+// Dot products of kNR rows (r0, r0+rstep, ...) of NM matrices of the expert
+// whose first row is erow0, accumulated per lane (the caller combines the
+// row's LR lanes).  MAXT == 1 reads the single token's input chunk from
+// global memory (x_src, dtype XT); MAXT > 1 reads the staged LDS copy.
 template <int BITS, int SB, int XT, int NM, int MAXT>
 __device__ __forceinline__ void row_block(const QM *mats, int64_t erow0, int r0, int rstep, int row_end,
                                           int j, int lr, int cpr, const void *x_src, int64_t x_off,
                                           const float *xs, int nt, float (&acc)[NM][kNR][MAXT]) {
-    using F = Fmt<BITS>;
-    constexpr int CODES = F::kCodes;
-    constexpr int SLOT = CODES + 4;
+    constexpr int CODES = Fmt<BITS>::kCodes;
+    float a1[NM][kNR];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int n = 0; n < kNR; ++n)
+        for (int n = 0; n < kNR; ++n) {
+            a1[m][n] = 0.f;
 #pragma unroll
             for (int t = 0; t < MAXT; ++t) acc[m][n][t] = 0.f;
-
+        }
     for (int c0 = 0; c0 < cpr; c0 += lr) {          // same trip count on every lane
-        const int c = c0 + j;
-        const bool okc = c < cpr;
-        const int cc = okc ? c : 0;
-        // Branch-free loads: rows past the tile and chunks past the row read a
-        // valid neighbour (same cache lines) and are masked out afterwards, so
-        // every load of the block is issued before the first wait.
-        Chunk<BITS> w[NM][kNR];
-        uint16_t sr[NM][kNR], br[NM][kNR];
-        bool live[kNR];
-#pragma unroll
-        for (int n = 0; n < kNR; ++n) live[n] = okc && (r0 + n * rstep < row_end);
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int n = 0; n < kNR; ++n) {
-                const int r = min(r0 + n * rstep, row_end - 1);
-                const int64_t row = erow0 + r;
-                w[m][n] = load_chunk<BITS>(mats[m].q + row * mats[m].wpr + cc * F::kWords);
-                const int64_t gi = row * mats[m].gpr + cc / F::kChunksPerGroup;
-                sr[m][n] = mats[m].s[gi];
-                br[m][n] = mats[m].b[gi];
-            }
-        float s[NM][kNR], b[NM][kNR];
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int n = 0; n < kNR; ++n) {
-                s[m][n] = live[n] ? sb_to_float<SB>(sr[m][n]) : 0.f;
-                b[m][n] = live[n] ? sb_to_float<SB>(br[m][n]) : 0.f;
-            }
+        BlockRegs<BITS, NM, kNR> R;
+        load_block<BITS, NM, kNR>(R, mats, erow0, r0, rstep, row_end, c0 + j, cpr);
         if constexpr (MAXT == 1) {
             float xv[CODES];
-            load_x_chunk<XT, CODES>(x_src, x_off + (int64_t)cc * CODES, xv);
-            const float xsum = chunk_sum(xv, CODES);
-#pragma unroll
-            for (int m = 0; m < NM; ++m)
-#pragma unroll
-                for (int n = 0; n < kNR; ++n) {
-                    float q[CODES];
-                    unpack<BITS>(w[m][n], q);
-                    float d = 0.f;
-#pragma unroll
-                    for (int i = 0; i < CODES; ++i) d += q[i] * xv[i];
-                    acc[m][n][0] += s[m][n] * d + b[m][n] * xsum;
-                }
+            load_x_chunk<XT, CODES>(x_src, x_off + (int64_t)R.cc * CODES, xv);
+            dot_block<BITS, SB, NM, kNR>(R, xv, sum_n<CODES>(xv), a1);
         } else {
 #pragma unroll
-            for (int m = 0; m < NM; ++m)
+            for (int t = 0; t < MAXT; ++t) {
+                if (t < nt) {
+                    const float *p = staged_chunk<CODES>(xs, t, cpr, R.cc);
+                    float xv[CODES];
+                    read_staged<CODES>(p, xv);
+                    float part[NM][kNR];
 #pragma unroll
-                for (int n = 0; n < kNR; ++n) {
-                    float q[CODES];
-                    unpack<BITS>(w[m][n], q);
+                    for (int m = 0; m < NM; ++m)
 #pragma unroll
-                    for (int t = 0; t < MAXT; ++t) {
-                        if (t < nt) {
-                            const f32x4 *xp = reinterpret_cast<const f32x4 *>(xs + (t * cpr + cc) * SLOT);
-                            float d = 0.f;
+                        for (int n = 0; n < kNR; ++n) part[m][n] = 0.f;
+                    dot_block<BITS, SB, NM, kNR>(R, xv, p[CODES], part);
 #pragma unroll
-                            for (int i = 0; i < CODES / 4; ++i) {
-                                const f32x4 v = xp[i];
-                                d += q[4 * i] * v.x + q[4 * i + 1] * v.y + q[4 * i + 2] * v.z + q[4 * i + 3] * v.w;
-                            }
-                            acc[m][n][t] += s[m][n] * d + b[m][n] * xs[(t * cpr + cc) * SLOT + CODES];
-                        }
-                    }
+                    for (int m = 0; m < NM; ++m)
+#pragma unroll
+                        for (int n = 0; n < kNR; ++n) acc[m][n][t] += part[m][n];
                 }
+            }
         }
+    }
+    if constexpr (MAXT == 1) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int n = 0; n < kNR; ++n) acc[m][n][0] = a1[m][n];
     }
 }
 

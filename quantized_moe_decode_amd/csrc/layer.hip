@@ -1,0 +1,189 @@
+// moe_decode_layer: the fused single-launch decode layer (layer_kernel.hpp).
+#include <hip/hip_runtime.h>
+
+#include "api.hpp"
+#include "layer_kernel.hpp"
+
+namespace moe {
+
+static int codes_of(int bits) { return bits == 4 ? 32 : 16; }
+
+static int lr_shift_for(int cpr) {
+    int s = 0;
+    while (s < 6 && (1 << s) < cpr) ++s;
+    return s;
+}
+
+struct LayerPlan {
+    LayerArgs a;
+    int grid;
+    size_t lds;
+    size_t ws_bytes;
+    size_t off_logits, off_act, off_partial;
+};
+
+static moe_status plan_layer(const moe_layer_weights *w, int d_in_check, LayerPlan &p) {
+    if (!w || !w->w_router) return MOE_EINVAL;
+    moe_status st;
+    for (const moe_qmat *m : {&w->gate, &w->up, &w->down})
+        if ((st = check_qmat(m)) != MOE_OK) return st;
+    const int d_in = w->gate.cols, d_ff = w->gate.rows, E = w->gate.n_experts;
+    if (w->up.rows != d_ff || w->up.cols != d_in || w->down.rows != d_in || w->down.cols != d_ff)
+        return MOE_EINVAL;
+    if (w->up.n_experts != E || w->down.n_experts != E || w->n_experts != E) return MOE_EINVAL;
+    if (w->up.bits != w->gate.bits) return MOE_EUNSUPPORTED;
+    if (w->up.sb_dtype != w->gate.sb_dtype || w->down.sb_dtype != w->gate.sb_dtype) return MOE_EUNSUPPORTED;
+    if (d_in_check >= 0 && d_in_check != d_in) return MOE_EINVAL;
+    if (w->top_k < 1 || w->top_k > MOE_MAX_TOP_K || w->top_k > E) return MOE_EINVAL;
+    if (w->n_shared < 0 || w->n_shared > MOE_MAX_SHARED) return MOE_EINVAL;
+    if (!valid_dtype(w->w_router_dtype)) return MOE_EUNSUPPORTED;
+    if (!aligned16(w->w_router)) return MOE_EINVAL;
+    int d_ffs = 0;
+    if (w->n_shared > 0) {
+        for (const moe_qmat *m : {&w->shared_gate, &w->shared_up, &w->shared_down})
+            if ((st = check_qmat(m)) != MOE_OK) return st;
+        d_ffs = w->shared_gate.rows;
+        if (w->shared_gate.cols != d_in || w->shared_up.cols != d_in || w->shared_up.rows != d_ffs ||
+            w->shared_down.rows != d_in || w->shared_down.cols != d_ffs)
+            return MOE_EINVAL;
+        if (w->shared_gate.n_experts != w->n_shared || w->shared_up.n_experts != w->n_shared ||
+            w->shared_down.n_experts != w->n_shared)
+            return MOE_EINVAL;
+        if (w->shared_gate.bits != w->gate.bits || w->shared_up.bits != w->gate.bits ||
+            w->shared_down.bits != w->down.bits)
+            return MOE_EUNSUPPORTED;
+        if (w->shared_gate.sb_dtype != w->gate.sb_dtype || w->shared_up.sb_dtype != w->gate.sb_dtype ||
+            w->shared_down.sb_dtype != w->gate.sb_dtype)
+            return MOE_EUNSUPPORTED;
+    } else if (w->w_shared_gate) {
+        return MOE_EINVAL;       // a shared gate needs shared experts
+    }
+    if (w->w_shared_gate && !aligned16(w->w_shared_gate)) return MOE_EINVAL;
+
+    LayerArgs &a = p.a;
+    a = LayerArgs{};
+    a.wr = w->w_router;
+    a.wg = w->w_shared_gate;
+    a.E = E; a.K = w->top_k; a.renorm = w->renormalize ? 1 : 0; a.S = w->n_shared;
+    a.d_in = d_in; a.d_ff = d_ff; a.d_ffs = d_ffs;
+    auto qm = [](const moe_qmat &m) {
+        QM q;
+        q.q = m.q;
+        q.s = reinterpret_cast<const uint16_t *>(m.scales);
+        q.b = reinterpret_cast<const uint16_t *>(m.biases);
+        q.rows = m.rows; q.cols = m.cols;
+        q.wpr = m.cols * m.bits / 32; q.gpr = m.cols / 64;
+        q.bits_ = m.bits; q.sb_ = m.sb_dtype;
+        return q;
+    };
+    a.gate = qm(w->gate); a.up = qm(w->up); a.down = qm(w->down);
+    if (a.S > 0) { a.sgate = qm(w->shared_gate); a.sup = qm(w->shared_up); a.sdown = qm(w->shared_down); }
+
+    const int slots = a.K + a.S;
+    a.n_route = (E + (a.wg ? 1 : 0) + 3) / 4;
+    a.a_lr_shift = lr_shift_for(d_in / codes_of(w->gate.bits));
+    a.a_tile = 4 * (64 >> a.a_lr_shift) * kLayerNRA;
+    a.a_tiles_r = (d_ff + a.a_tile - 1) / a.a_tile;
+    a.a_tiles_s = a.S > 0 ? (d_ffs + a.a_tile - 1) / a.a_tile : 0;
+    const int cb = codes_of(w->down.bits);
+    a.b_lr_shift_r = lr_shift_for(d_ff / cb);
+    a.b_lr_shift_s = a.S > 0 ? lr_shift_for(d_ffs / cb) : a.b_lr_shift_r;
+    a.b_tile = 4 * (64 >> a.b_lr_shift_r) * kLayerNRB;
+    a.b_tiles = (d_in + a.b_tile - 1) / a.b_tile;
+    const int dmax = d_ffs > d_ff ? d_ffs : d_ff;
+    a.act_stride = dmax;
+    p.grid = a.n_route + a.K * a.a_tiles_r + a.S * a.a_tiles_s + slots * a.b_tiles;
+    p.lds = (size_t)(dmax / cb) * (cb + 4) * sizeof(float);
+    if (p.lds > 64 * 1024) return MOE_EUNSUPPORTED;
+
+    size_t off = align_up((size_t)kCtrCount * kCtrStride * sizeof(uint32_t), 256);
+    p.off_logits = off;
+    off = align_up(off + (size_t)(E + 1) * sizeof(uint64_t), 256);
+    p.off_act = off;
+    off = align_up(off + (size_t)slots * dmax * sizeof(uint64_t), 256);
+    p.off_partial = off;
+    off = align_up(off + (size_t)slots * d_in * sizeof(uint64_t), 256);
+    p.ws_bytes = off;
+    return MOE_OK;
+}
+
+// Workgroups of `k` that can be resident at once on the current device (0 if
+// the runtime cannot tell).
+static int resident_capacity(LayerFn k, size_t lds) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(k), 256, lds) !=
+        hipSuccess)
+        return 0;
+    return cus * per_cu;
+}
+
+// Give each kernel-A unit enough row passes that the whole grid fits the
+// resident capacity when possible, so every kernel-B unit can issue its
+// weight loads from the start of the launch.
+static void fit_a_passes(LayerPlan &p, int capacity) {
+    LayerArgs &a = p.a;
+    const int slots = a.K + a.S;
+    const int n_b = slots * a.b_tiles;
+    const int base_tile = a.a_tile;
+    const int dff_s = a.S > 0 ? a.d_ffs : 0;
+    int passes = 1;
+    if (capacity > 0) {
+        const int room = capacity - a.n_route - n_b;
+        for (passes = 1; passes < 8; ++passes) {
+            const int t = base_tile * passes;
+            const int n_a = a.K * ((a.d_ff + t - 1) / t) + a.S * ((dff_s + t - 1) / t);
+            if (room > 0 && n_a <= room) break;
+        }
+    }
+    a.a_tile = base_tile * passes;
+    a.a_tiles_r = (a.d_ff + a.a_tile - 1) / a.a_tile;
+    a.a_tiles_s = a.S > 0 ? (dff_s + a.a_tile - 1) / a.a_tile : 0;
+    p.grid = a.n_route + a.K * a.a_tiles_r + a.S * a.a_tiles_s + n_b;
+}
+
+static LayerFn pick_layer(int ba, int bb, int sb, int xt) {
+    switch (ba) {
+    case 4: return layer_kernel_a4(bb, sb, xt);
+    case 6: return layer_kernel_a6(bb, sb, xt);
+    case 8: return layer_kernel_a8(bb, sb, xt);
+    }
+    return nullptr;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_decode_layer_workspace_bytes(const moe_layer_weights *weights) {
+    LayerPlan p;
+    return plan_layer(weights, -1, p) == MOE_OK ? p.ws_bytes : 0;
+}
+
+extern "C" moe_status moe_decode_layer(const moe_layer_weights *weights, const void *x, moe_dtype x_dtype,
+                                       const void *residual, moe_dtype residual_dtype, float *out,
+                                       int32_t *expert_ids, float *scores, float *shared_gate,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+    if (!x || !residual || !out || !workspace) return MOE_EINVAL;
+    if (!valid_dtype(x_dtype) || !valid_dtype(residual_dtype)) return MOE_EUNSUPPORTED;
+    if (!aligned16(x) || !aligned16(workspace)) return MOE_EINVAL;
+    LayerPlan p;
+    const moe_status st = plan_layer(weights, -1, p);
+    if (st != MOE_OK) return st;
+    if (weights->w_router_dtype != x_dtype) return MOE_EUNSUPPORTED;
+    if (workspace_bytes < p.ws_bytes) return MOE_EINVAL;
+    LayerFn k = pick_layer(weights->gate.bits, weights->down.bits, weights->gate.sb_dtype, x_dtype);
+    if (!k) return MOE_EUNSUPPORTED;
+    fit_a_passes(p, resident_capacity(k, p.lds));
+    LayerArgs &a = p.a;
+    a.x = x; a.resid = residual; a.resid_dt = residual_dtype; a.out = out;
+    a.ids_out = expert_ids; a.scores_out = scores; a.gate_out = shared_gate;
+    char *ws = reinterpret_cast<char *>(workspace);
+    a.ctr = reinterpret_cast<uint32_t *>(ws);
+    a.logits = reinterpret_cast<uint64_t *>(ws + p.off_logits);
+    a.act = reinterpret_cast<uint64_t *>(ws + p.off_act);
+    a.partial = reinterpret_cast<uint64_t *>(ws + p.off_partial);
+    hipLaunchKernelGGL(k, dim3(p.grid), dim3(256), p.lds, reinterpret_cast<hipStream_t>(stream), a);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}

@@ -12,8 +12,9 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (QuantStack, expert_ffn_workspace_bytes, moe_decode_expert_ffn, moe_decode_route,
-               moe_decode_tail, route_workspace_bytes)
+from . import (QuantStack, expert_ffn_workspace_bytes, layer_weights, layer_workspace_bytes,
+               moe_decode_expert_ffn, moe_decode_layer, moe_decode_route, moe_decode_tail,
+               route_workspace_bytes)
 
 _TORCH_16 = {"f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -69,6 +70,11 @@ class DecodeLayer:
             self.shared_ws = torch.zeros(max(nb, 1), device=dev, dtype=torch.uint8) if nb else None
         else:
             self.n_shared = 0
+        # fused single-launch path (one token per launch)
+        self.cweights = layer_weights(router, top_k, renormalize, gate, up, down, self.shared,
+                                      shared_gate_w)
+        nb = layer_workspace_bytes(self.cweights)
+        self.fused_ws = torch.zeros(nb, device=dev, dtype=torch.uint8) if nb else None
 
     def route(self, x: torch.Tensor, stream=None) -> None:
         moe_decode_route(x, self.router, self.top_k, self.renormalize, self.ids, self.scores,
@@ -92,6 +98,19 @@ class DecodeLayer:
         self.route(x, stream)
         self.experts(x, stream)
         self.tail(resid, out, stream)
+
+    def forward_fused(self, x: torch.Tensor, resid: torch.Tensor, out: torch.Tensor, stream=None,
+                      record: bool = True) -> None:
+        """The same layer in one launch (x [1, d_in] or [d_in]); fills ids/scores/gate if record."""
+        if self.fused_ws is None:
+            raise ValueError("layer not supported by the fused launch")
+        moe_decode_layer(self.cweights, x, resid, out, self.fused_ws,
+                         self.ids if record else None, self.scores if record else None,
+                         self.shared_gate if record else None, stream)
+
+    def fused_error_word(self) -> int:
+        """Nonzero if a wait inside a fused launch ever timed out (reads device memory)."""
+        return int(self.fused_ws[:4].view(torch.int32).item())
 
     def expert_bytes_per_step(self) -> int:
         """Bytes of expert weight one step reads when its K selections are distinct (T = 1)."""

@@ -28,30 +28,38 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_gpu_layer(cfg, w, x, resid, graph: bool = False, layer=None):
-    """Route + experts + tail for the tokens in x on the GPU; returns host copies."""
+def run_gpu_layer(cfg, w, x, resid, graph: bool = False, layer=None, fused: bool = False):
+    """The layer for the tokens in x on the GPU; returns host copies.
+
+    fused=False: route + expert FFN + tail (three calls); fused=True: the
+    single-launch moe_decode_layer (one token; act and partial are not exposed).
+    """
     if layer is None:
         layer = layer_from_host(cfg, w, DEV, n_tokens=x.shape[0])
     xd = tensor_from_encoded(x, cfg.x_dtype, DEV)
     rd = tensor_from_encoded(resid, cfg.resid_dtype, DEV)
     out = torch.empty(x.shape[0], cfg.d_in, device=DEV, dtype=torch.float32)
+    fwd = layer.forward_fused if fused else layer.forward
     if graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            layer.forward(xd, rd, out)          # warm-up outside the capture
+            fwd(xd, rd, out)          # warm-up outside the capture
         torch.cuda.current_stream().wait_stream(s)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            layer.forward(xd, rd, out)
+            fwd(xd, rd, out)
         out.zero_()
         g.replay()
     else:
-        layer.forward(xd, rd, out)
+        fwd(xd, rd, out)
     torch.cuda.synchronize()
     res = dict(ids=layer.ids.cpu().numpy(), scores=layer.scores.cpu().numpy(),
-               act=layer.act.cpu().numpy(), partial=layer.partial.cpu().numpy(),
+               act=None if fused else layer.act.cpu().numpy(),
+               partial=None if fused else layer.partial.cpu().numpy(),
                out=out.cpu().numpy())
+    if fused:
+        res["error_word"] = layer.fused_error_word()
     if layer.shared_gate is not None:
         res["gate"] = layer.shared_gate.cpu().numpy()
     if layer.n_shared:
@@ -66,12 +74,14 @@ def compare_layer(cfg, w, x, resid, gpu, label=""):
     assert np.array_equal(gpu["ids"], ids_ref), f"{label}: ids {gpu['ids']} vs {ids_ref}"
     ds = float(np.max(np.abs(gpu["scores"] - ref["route"]["scores"])))
     assert ds <= SCORE_TOL, f"{label}: scores off by {ds}"
+    if gpu.get("error_word"):
+        raise AssertionError(f"{label}: fused launch reported a wait time-out")
     if cfg.shared_gate:
         dg = float(np.max(np.abs(gpu["gate"] - ref["route"]["gate"])))
         assert dg <= SCORE_TOL, f"{label}: shared gate off by {dg}"
     errs = {}
     T = x.shape[0]
-    for t in range(T):
+    for t in range(T if gpu["act"] is not None else 0):
         for k in range(cfg.top_k):
             errs.setdefault("act", []).append(rel_err(gpu["act"][t, k], ref["ffn"]["act"][t, k]))
             errs.setdefault("partial", []).append(

@@ -178,6 +178,57 @@ def test_down_rejects(case, want):
     assert _down(**case) == want
 
 
+def _lw(**kw):
+    a = dict(wr=P, wr_dt=MOE_BF16, E=128, K=8, renorm=1, gate=_qm(), up=_qm(),
+             down=_qm(rows=2048, cols=768), S=0, sg=qmd.CQMat(), su=qmd.CQMat(), sd=qmd.CQMat(),
+             wg=None)
+    a.update(kw)
+    return qmd.CLayerWeights(a["wr"], a["wr_dt"], a["E"], a["K"], a["renorm"], a["gate"], a["up"],
+                             a["down"], a["S"], a["sg"], a["su"], a["sd"], a["wg"])
+
+
+def _layer(w=None, **kw):
+    a = dict(x=P, x_dt=MOE_BF16, resid=P, rdt=MOE_BF16, out=P, ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    w = w or _lw()
+    return lib.moe_decode_layer(ctypes.byref(w), a["x"], a["x_dt"], a["resid"], a["rdt"], a["out"],
+                                None, None, None, a["ws"], a["ws_bytes"], None)
+
+
+def test_layer_workspace_bytes():
+    n = qmd.layer_workspace_bytes(_lw())
+    assert n >= (8 * 768 + 8 * 2048 + 129) * 4
+    assert qmd.layer_workspace_bytes(_lw(K=0)) == 0
+    shared = dict(S=1, sg=_qm(E=1, rows=5632), su=_qm(E=1, rows=5632), sd=_qm(E=1, rows=2048, cols=5632))
+    assert qmd.layer_workspace_bytes(_lw(**shared)) > n
+
+
+@pytest.mark.parametrize("case,want", [
+    (dict(x=None), MOE_EINVAL),
+    (dict(out=None), MOE_EINVAL),
+    (dict(ws=None), MOE_EINVAL),
+    (dict(ws_bytes=64), MOE_EINVAL),
+    (dict(x=MIS), MOE_EINVAL),
+    (dict(x_dt=6), MOE_EUNSUPPORTED),
+    (dict(x_dt=MOE_F32), MOE_EUNSUPPORTED),                   # router dtype must match x
+    (dict(w=_lw(wr=None)), MOE_EINVAL),
+    (dict(w=_lw(K=0)), MOE_EINVAL),
+    (dict(w=_lw(K=33)), MOE_EINVAL),
+    (dict(w=_lw(E=64)), MOE_EINVAL),                          # n_experts must match the stacks
+    (dict(w=_lw(up=_qm(bits=8))), MOE_EUNSUPPORTED),
+    (dict(w=_lw(down=_qm(rows=2048, cols=768, dt=MOE_F16))), MOE_EUNSUPPORTED),
+    (dict(w=_lw(wg=P)), MOE_EINVAL),                          # shared gate without shared experts
+    (dict(w=_lw(S=9)), MOE_EINVAL),
+    (dict(w=_lw(S=1, sg=_qm(E=1, rows=512), su=_qm(E=1, rows=512), sd=_qm(E=1, rows=2048, cols=768))),
+     MOE_EINVAL),                                             # shared d_ff inconsistent
+    (dict(w=_lw(S=1, sg=_qm(E=1, bits=8), su=_qm(E=1, bits=8), sd=_qm(E=1, rows=2048, cols=768))),
+     MOE_EUNSUPPORTED),                                       # shared bits differ from routed
+    (dict(w=_lw(S=2, sg=_qm(E=1), su=_qm(E=1), sd=_qm(E=1, rows=2048, cols=768))), MOE_EINVAL),
+])
+def test_layer_rejects(case, want):
+    assert _layer(**case) == want
+
+
 def _tail(**kw):
     a = dict(partial=P, T=1, K=8, D=2048, shared=None, S=0, gate=None, resid=P, rdt=MOE_BF16, out=P)
     a.update(kw)

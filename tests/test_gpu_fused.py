@@ -1,0 +1,120 @@
+"""GPU parity of the fused single-launch layer (moe_decode_layer) against the oracle,
+and against the three-call path.  Every case prints its name before it runs."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from gpu_cases import DEV, compare_layer, margin_tokens, run_gpu_layer, say, small_cfg
+from helpers import rel_err
+from test_gpu_parity import SMALL
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_moe_decode_amd  # noqa: F401
+    yield
+
+
+@pytest.mark.parametrize("kw", SMALL + [dict(n_shared=1, d_ff_shared=256, shared_gate=True),
+                                        dict(n_shared=2, d_ff_shared=128, bits_down=6),
+                                        dict(n_shared=1, d_ff_shared=1152, shared_gate=True,
+                                             bits_gate_up=8, bits_down=8)],
+                         ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()) or "base")
+def test_fused_small_layers(kw):
+    cfg = small_cfg(**kw)
+    say(f"case fused small {kw}")
+    w = mi.gen_layer_weights(cfg, 0, threads=4)
+    x, resid = margin_tokens(cfg, 0, w, 2)
+    for t in range(2):
+        gpu, layer = run_gpu_layer(cfg, w, x[t:t + 1], resid[t:t + 1], fused=True)
+        compare_layer(cfg, w, x[t:t + 1], resid[t:t + 1], gpu, f"fused small {kw} t{t}")
+        ws = layer.fused_ws.cpu().numpy()
+        assert not np.any(ws[:4]), "error word set"
+
+
+def test_fused_jittered_bias():
+    for bits in ((4, 4), (8, 8), (4, 6)):
+        cfg = small_cfg(bits_gate_up=bits[0], bits_down=bits[1])
+        say(f"case fused jitter {bits}")
+        w = mi.gen_layer_weights(cfg, 2, jitter_bias=True, threads=4)
+        x, resid = margin_tokens(cfg, 2, w, 1)
+        gpu, _ = run_gpu_layer(cfg, w, x, resid, fused=True)
+        compare_layer(cfg, w, x, resid, gpu, f"fused jitter {bits}")
+
+
+@pytest.mark.parametrize("name,layers,T", [
+    ("tiny_e8_top2", (0,), 3),
+    ("qwen3_30b_a3b_moe", (0, 31), 2),
+    ("qwen1.5_moe_a2.7b", (0,), 2),
+    ("dots_llm1_mixed_bit", (0,), 1),
+])
+def test_fused_full_size_layers(name, layers, T):
+    cfg = mi.CONFIGS[name]
+    for li in layers:
+        say(f"case fused {name} layer {li}")
+        w = mi.gen_layer_weights(cfg, li)
+        x, resid = margin_tokens(cfg, li, w, T)
+        for t in range(T):
+            gpu, layer = run_gpu_layer(cfg, w, x[t:t + 1], resid[t:t + 1], graph=True, fused=True)
+            compare_layer(cfg, w, x[t:t + 1], resid[t:t + 1], gpu, f"fused {name} L{li} t{t}")
+            three, _ = run_gpu_layer(cfg, w, x[t:t + 1], resid[t:t + 1], layer=layer)
+            assert np.array_equal(three["ids"], gpu["ids"])
+            assert rel_err(gpu["out"], three["out"]) <= 1e-5
+
+
+def test_fused_determinism_graph_replays_and_clean_workspace():
+    cfg = mi.QWEN3
+    say("case fused determinism + graph replays")
+    w = mi.gen_layer_weights(cfg, 3)
+    x, resid = margin_tokens(cfg, 3, w, 1)
+    a, layer = run_gpu_layer(cfg, w, x, resid, fused=True)
+    for rep in range(3):
+        b, _ = run_gpu_layer(cfg, w, x, resid, layer=layer, fused=True)
+        assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["ids"], b["ids"])
+    from quantized_moe_decode_amd.layer import tensor_from_encoded
+    xd = tensor_from_encoded(x, cfg.x_dtype, DEV)
+    rd = tensor_from_encoded(resid, cfg.resid_dtype, DEV)
+    out = torch.zeros(1, cfg.d_in, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward_fused(xd, rd, out)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward_fused(xd, rd, out)
+    for rep in range(5):
+        out.fill_(-1.0)
+        layer.forward(xd, rd, torch.empty_like(out))       # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), a["out"]), rep
+    # every counter is back at zero and no wait timed out
+    ws = layer.fused_ws.view(torch.int32).cpu().numpy()
+    # control words 64 apart: error word, launch epoch, finished-tile counter
+    launches = 1 + 3 + 1 + 5
+    assert ws[0] == 0, "a wait timed out"
+    assert ws[64] == launches, f"epoch {ws[64]} after {launches} launches"
+    assert ws[128] == 0, "finished-tile counter not reset"
+
+
+def test_fused_tie_prefers_lower_index():
+    """Duplicate router rows tie exactly; the fused selection takes the lower id first."""
+    cfg = small_cfg(n_experts=8, top_k=3, x_dtype=mi.F32, router_dtype=mi.F32, resid_dtype=mi.F32)
+    say("case fused router tie")
+    w = mi.gen_layer_weights(cfg, 4, threads=4)
+    x, resid = mi.gen_tokens(cfg, 4, 1)
+    wr = np.zeros_like(w["router"])
+    r = x[0].astype(np.float32)
+    wr[6] = wr[2] = r * 0.05
+    wr[5] = r * 0.04
+    wr[1] = r * 0.01
+    w["router"] = wr
+    gpu, _ = run_gpu_layer(cfg, w, x, resid, fused=True)
+    assert gpu["ids"].tolist() == [[2, 6, 5]]
+    assert gpu["scores"][0, 0] == gpu["scores"][0, 1]
