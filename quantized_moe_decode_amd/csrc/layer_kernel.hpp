@@ -255,14 +255,11 @@ __device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     const int64_t erow0 = (int64_t)e * dff;
     const int cpr = a.d_in / F::kCodes;
     const int lr = 1 << a.a_lr_shift, j = lane & (lr - 1), rsub = lane >> a.a_lr_shift, rpw = kWave >> a.a_lr_shift;
-    // stages = (row pass, chunk position); the loads of stage s+1 are in
-    // flight while stage s is computed
+    // stages = (row pass, chunk position), each loaded and then consumed
     const int rb0 = row0 + wave * rpw * NR, pass_rows = 4 * rpw * NR;
     const int n_pass = rb0 < row_end ? (row_end - rb0 + pass_rows - 1) / pass_rows : 0;
     const int n_chunk = (cpr + lr - 1) / lr;
     const int n_stage = n_pass * n_chunk;
-    BlockRegs<BA, 2, NR> cur, nxt;
-    if (n_stage > 0) load_block<BA, 2, NR>(cur, mats, erow0, rb0 + rsub, rpw, row_end, j, cpr);
     float acc[2][NR];
     for (int st = 0; st < n_stage; ++st) {
         const int ps = st / n_chunk, ch = st - ps * n_chunk;
@@ -273,14 +270,11 @@ __device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int til
 #pragma unroll
                 for (int n = 0; n < NR; ++n) acc[m][n] = 0.f;
         }
-        if (st + 1 < n_stage) {
-            const int ps1 = (st + 1) / n_chunk, ch1 = (st + 1) - ps1 * n_chunk;
-            load_block<BA, 2, NR>(nxt, mats, erow0, rb0 + ps1 * pass_rows + rsub, rpw, row_end, ch1 * lr + j, cpr);
-        }
+        BlockRegs<BA, 2, NR> cur;
+        load_block<BA, 2, NR>(cur, mats, erow0, r0, rpw, row_end, ch * lr + j, cpr);
         float xv[F::kCodes];
         load_x_chunk<XT, F::kCodes>(a.x, (int64_t)cur.cc * F::kCodes, xv);
         dot_block<BA, SB, 2, NR>(cur, xv, sum_n<F::kCodes>(xv), acc);
-        cur = nxt;
         if (ch == n_chunk - 1) {
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
@@ -346,7 +340,7 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     const int n_pass = (valid && rb0 < row_end) ? (row_end - rb0 + pass_rows - 1) / pass_rows : 0;
     const int n_chunk = (cpr + lr - 1) / lr;
     const int n_stage = n_pass * n_chunk;
-    BlockRegs<BB, 1, NR> cur, nxt;
+    BlockRegs<BB, 1, NR> cur;
     if (n_stage > 0) load_block<BB, 1, NR>(cur, mats, erow0, rb0 + rsub, rpw, row_end, j, cpr);
 
     if (valid) {
@@ -364,15 +358,10 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
 #pragma unroll
                 for (int n = 0; n < NR; ++n) acc[0][n] = 0.f;
             }
-            if (st + 1 < n_stage) {
-                const int ps1 = (st + 1) / n_chunk, ch1 = (st + 1) - ps1 * n_chunk;
-                load_block<BB, 1, NR>(nxt, mats, erow0, rb0 + ps1 * pass_rows + rsub, rpw, row_end, ch1 * lr + j,
-                                      cpr);
-            }
+            if (st > 0) load_block<BB, 1, NR>(cur, mats, erow0, r0, rpw, row_end, ch * lr + j, cpr);
             float xv[CODES];
             read_staged<CODES>(staged_chunk<CODES>(xs, 0, cpr, cur.cc), xv);
             dot_block<BB, SB, 1, NR>(cur, xv, sum_n<CODES>(xv), acc);
-            cur = nxt;
             if (ch == n_chunk - 1) {
 #pragma unroll
                 for (int n = 0; n < NR; ++n) acc[0][n] = group_sum(acc[0][n], lr);
@@ -432,7 +421,7 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
 }
 
 template <int BA, int BB, int SB, int XT>
-__global__ __launch_bounds__(256, 2) void layer_kernel(LayerArgs a) {
+__global__ __launch_bounds__(256, 3) void layer_kernel(LayerArgs a) {
     __shared__ float s_logits[MOE_MAX_EXPERTS];
     __shared__ Selection sel;
     extern __shared__ float xs[];
