@@ -44,7 +44,7 @@
 namespace moe {
 
 constexpr int kLayerNRA = 4;        // rows per lane group, kernel A units
-constexpr int kLayerNRB = 8;        // rows per lane group, kernel B units
+constexpr int kLayerNRB = 4;        // rows per lane group, kernel B units
 constexpr int kCtrStride = 64;      // uint32 words between control words (256 bytes)
 constexpr uint32_t kSpinLimit = 1u << 19;
 
@@ -158,71 +158,114 @@ struct Selection {
     float gate;
 };
 
-// Top-k in one wave, PER logits per lane (expert lane + 64*i in l[i]): K
-// rounds of "largest untaken logit" (a DPP wave maximum), each taking the
-// lowest expert id that holds that value (a ballot), i.e. descending logit
-// with ties to the lower id.  Lane k ends with the k-th id and logit.
+// Top-k in one wave, PER logits per lane (expert lane + 64*i in l[i]): rounds
+// of "largest untaken logit" (a DPP wave maximum), each taking the lowest
+// expert id that holds that value (a ballot), i.e. descending logit with ties
+// to the lower id.  Lane k ends with the k-th id and logit.  Rounds [k0, k1)
+// run per call, so a caller can stop at the rank it needs and resume later.
 template <int PER>
-__device__ __forceinline__ void topk_wave(const float *s_logits, int E, int K, int lane, int &my_id,
-                                          float &my_logit, float &mx, float &z) {
+struct TopK {
     float l[PER];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int e = lane + i * kWave;
-        l[i] = e < E ? s_logits[e] : -INFINITY;
-        if (e >= E) taken |= 1u << i;
-    }
-    my_id = -1;
-    my_logit = 0.f;
-    for (int k = 0; k < K; ++k) {
-        float best = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) best = ((taken >> i) & 1u) ? best : fmaxf(best, l[i]);
-        const float m = wave_max(best);
-        int e = -1;
+    uint32_t taken;
+    int my_id;
+    float my_logit, mx;
+
+    __device__ __forceinline__ void init(const float *s_logits, int E, int lane) {
+        taken = 0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const uint64_t hit = __ballot(!((taken >> i) & 1u) && l[i] == m);
-            if (e < 0 && hit) e = i * kWave + (int)__ffsll((unsigned long long)hit) - 1;
+            const int e = lane + i * kWave;
+            l[i] = e < E ? s_logits[e] : -INFINITY;
+            if (e >= E) taken |= 1u << i;
         }
-        if (k == 0) mx = m;
-        if (lane == k) {
-            my_id = e;
-            my_logit = m;
-        }
-        if ((e & (kWave - 1)) == lane) taken |= 1u << ((e / kWave) & 31);
+        my_id = -1;
+        my_logit = 0.f;
+        mx = 0.f;
     }
-    float zz = 0.f;
+
+    __device__ __forceinline__ void rounds(int k0, int k1, int lane) {
+        for (int k = k0; k < k1; ++k) {
+            float best = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) zz += (lane + i * kWave < E) ? __expf(l[i] - mx) : 0.f;
-    z = wave_sum(zz);
+            for (int i = 0; i < PER; ++i) best = ((taken >> i) & 1u) ? best : fmaxf(best, l[i]);
+            const float m = wave_max(best);
+            int e = -1;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const uint64_t hit = __ballot(!((taken >> i) & 1u) && l[i] == m);
+                if (e < 0 && hit) e = i * kWave + (int)__ffsll((unsigned long long)hit) - 1;
+            }
+            if (k == 0) mx = m;
+            if (lane == k) {
+                my_id = e;
+                my_logit = m;
+            }
+            if ((e & (kWave - 1)) == lane) taken |= 1u << ((e / kWave) & 31);
+        }
+    }
+
+    // softmax over all E logits; lanes < K get their selection's score
+    __device__ __forceinline__ float score(int E, int K, bool renorm, int lane) const {
+        float zz = 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) zz += (lane + i * kWave < E) ? __expf(l[i] - mx) : 0.f;
+        const float z = wave_sum(zz);
+        const float p = lane < K ? __expf(my_logit - mx) / z : 0.f;
+        const float psum = wave_sum(p);
+        return renorm ? p / psum : p;
+    }
+};
+
+// Wave 0 runs the selection; the other waves wait at the barriers.  With
+// need_scores == false only the ids of ranks [0, upto] are produced; a later
+// finish_selection() completes the ranks and the scores.
+template <int PER>
+__device__ void select_impl(const LayerArgs &a, const float *s_logits, Selection *sel, int upto, bool all,
+                            TopK<PER> &tk) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    if (wave == 0) {
+        tk.init(s_logits, a.E, lane);
+        const int k1 = all ? a.K : upto + 1;
+        tk.rounds(0, k1, lane);
+        if (lane < k1) sel->ids[lane] = tk.my_id;
+        if (all) {
+            const float sc = tk.score(a.E, a.K, a.renorm, lane);
+            if (lane < a.K) sel->scores[lane] = sc;
+        }
+    }
+    __syncthreads();
 }
 
-// Wait for every router logit, then select in wave 0; softmax over all
-// experts (max-subtracted), renormalised over the selection when asked.
-__device__ void select_experts(const LayerArgs &a, uint32_t tag, float *s_logits, Selection *sel) {
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-    gather_tagged(a, a.logits, a.E, tag, [&](int e, float v) { s_logits[e] = v; });
-    if (tid == 0) sel->gate = a.wg ? sigmoidf_(wait_tagged(a, a.logits + a.E, tag)) : 1.0f;
-    __syncthreads();
+template <int PER>
+__device__ void finish_impl(const LayerArgs &a, Selection *sel, int done, TopK<PER> &tk) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
     if (wave == 0) {
-        int my_id;
-        float my_logit, mx = 0.f, z;
-        const int per = (a.E + kWave - 1) / kWave;
-        if (per <= 1) topk_wave<1>(s_logits, a.E, a.K, lane, my_id, my_logit, mx, z);
-        else if (per <= 2) topk_wave<2>(s_logits, a.E, a.K, lane, my_id, my_logit, mx, z);
-        else if (per <= 4) topk_wave<4>(s_logits, a.E, a.K, lane, my_id, my_logit, mx, z);
-        else if (per <= 8) topk_wave<8>(s_logits, a.E, a.K, lane, my_id, my_logit, mx, z);
-        else topk_wave<16>(s_logits, a.E, a.K, lane, my_id, my_logit, mx, z);
-        const float p = lane < a.K ? __expf(my_logit - mx) / z : 0.f;
-        const float psum = wave_sum(p);
+        tk.rounds(done, a.K, lane);
+        const float sc = tk.score(a.E, a.K, a.renorm, lane);
         if (lane < a.K) {
-            sel->ids[lane] = my_id;
-            sel->scores[lane] = a.renorm ? p / psum : p;
+            sel->ids[lane] = tk.my_id;
+            sel->scores[lane] = sc;
         }
     }
     __syncthreads();
+}
+
+// Wait for every router logit and stage them in LDS (plus the shared gate).
+__device__ void gather_logits(const LayerArgs &a, uint32_t tag, float *s_logits, Selection *sel) {
+    gather_tagged(a, a.logits, a.E, tag, [&](int e, float v) { s_logits[e] = v; });
+    if (threadIdx.x == 0) sel->gate = a.wg ? sigmoidf_(wait_tagged(a, a.logits + a.E, tag)) : 1.0f;
+    __syncthreads();
+}
+
+// Dispatch on the number of logits per lane of the selection wave.
+template <typename Fn>
+__device__ __forceinline__ void with_per(int E, Fn fn) {
+    const int per = (E + kWave - 1) / kWave;
+    if (per <= 1) fn(TopK<1>{});
+    else if (per <= 2) fn(TopK<2>{});
+    else if (per <= 4) fn(TopK<4>{});
+    else if (per <= 8) fn(TopK<8>{});
+    else fn(TopK<16>{});
 }
 
 __device__ __forceinline__ int n_slots(const LayerArgs &a) { return a.K + a.S; }
@@ -237,7 +280,8 @@ __device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     const bool routed = slot < a.K;
     int e;
     if (routed) {
-        select_experts(a, tag, s_logits, sel);
+        gather_logits(a, tag, s_logits, sel);
+        with_per(a.E, [&](auto tk) { select_impl(a, s_logits, sel, slot, false, tk); });
         e = sel->ids[slot];
     } else {
         e = slot - a.K;
@@ -272,9 +316,27 @@ __device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int til
         }
         BlockRegs<BA, 2, NR> cur;
         load_block<BA, 2, NR>(cur, mats, erow0, r0, rpw, row_end, ch * lr + j, cpr);
-        float xv[F::kCodes];
-        load_x_chunk<XT, F::kCodes>(a.x, (int64_t)cur.cc * F::kCodes, xv);
-        dot_block<BA, SB, 2, NR>(cur, xv, sum_n<F::kCodes>(xv), acc);
+        if constexpr (BA == 4 && XT == MOE_BF16) {
+            // raw bf16 inputs for the packed-dot path
+            const u32x4 *xp = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.x) +
+                                                               (int64_t)cur.cc * F::kCodes);
+            uint32_t xw[16];
+            float xsum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 v = xp[i];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    xw[4 * i + k] = v[k];
+                    xsum += __uint_as_float(v[k] << 16) + __uint_as_float(v[k] & 0xFFFF0000u);
+                }
+            }
+            dot_block_q4_bf16<SB, 2, NR>(cur, xw, xsum, acc);
+        } else {
+            float xv[F::kCodes];
+            load_x_chunk<XT, F::kCodes>(a.x, (int64_t)cur.cc * F::kCodes, xv);
+            dot_block<BA, SB, 2, NR>(cur, xv, sum_n<F::kCodes>(xv), acc);
+        }
         if (ch == n_chunk - 1) {
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
@@ -307,17 +369,10 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     const bool routed = slot < a.K;
     int e;
     float score = 1.0f;
-    if (routed) {
-        select_experts(a, tag, s_logits, sel);
+    if (routed) {            // ranks up to this slot first: enough to start loading weights
+        gather_logits(a, tag, s_logits, sel);
+        with_per(a.E, [&](auto tk) { select_impl(a, s_logits, sel, slot, false, tk); });
         e = sel->ids[slot];
-        score = sel->scores[slot];
-        if (slot == 0 && tile == 0) {            // publish the routing result once
-            if (tid < a.K) {
-                if (a.ids_out) a.ids_out[tid] = sel->ids[tid];
-                if (a.scores_out) a.scores_out[tid] = sel->scores[tid];
-            }
-            if (tid == 0 && a.gate_out && a.wg) a.gate_out[0] = sel->gate;
-        }
     } else {
         e = slot - a.K;
     }
@@ -342,6 +397,18 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     const int n_stage = n_pass * n_chunk;
     BlockRegs<BB, 1, NR> cur;
     if (n_stage > 0) load_block<BB, 1, NR>(cur, mats, erow0, rb0 + rsub, rpw, row_end, j, cpr);
+
+    if (routed) {            // full selection and scores while the weights and act are in flight
+        with_per(a.E, [&](auto tk) { select_impl(a, s_logits, sel, 0, true, tk); });
+        score = sel->scores[slot];
+        if (slot == 0 && tile == 0) {            // publish the routing result once
+            if (tid < a.K) {
+                if (a.ids_out) a.ids_out[tid] = sel->ids[tid];
+                if (a.scores_out) a.scores_out[tid] = sel->scores[tid];
+            }
+            if (tid == 0 && a.gate_out && a.wg) a.gate_out[0] = sel->gate;
+        }
+    }
 
     if (valid) {
         const uint64_t *act = a.act + (int64_t)slot * a.act_stride;

@@ -56,23 +56,119 @@ __device__ __forceinline__ void load_block(BlockRegs<BITS, NM, NR> &R, const QM 
         }
 }
 
+// The codes of word k of a 4- or 8-bit chunk as floats.
+template <int BITS>
+__device__ __forceinline__ void unpack_word(uint32_t w, float *q) {
+    if constexpr (BITS == 4) {
+        const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            q[2 * b] = (float)((lo >> (8 * b)) & 0xFFu);
+            q[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu);
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) q[b] = (float)((w >> (8 * b)) & 0xFFu);
+    }
+}
+
 // acc[m][n] += s * (q . xv) + b * xsum for the loaded chunk of every row.
+// For 4- and 8-bit codes the loop walks the chunk word by word across all
+// rows, so the NM*NR dot products form independent FMA chains that hide each
+// other's latency; 6-bit chunks (codes straddle words) are unpacked whole.
 template <int BITS, int SB, int NM, int NR>
 __device__ __forceinline__ void dot_block(const BlockRegs<BITS, NM, NR> &R, const float *xv, float xsum,
                                           float (&acc)[NM][NR]) {
     constexpr int CODES = Fmt<BITS>::kCodes;
+    float d[NM][NR];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int n = 0; n < NR; ++n) d[m][n] = 0.f;
+    if constexpr (BITS == 6) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int n = 0; n < NR; ++n) {
+                float q[CODES];
+                unpack<BITS>(R.w[m][n], q);
+#pragma unroll
+                for (int i = 0; i < CODES; ++i) d[m][n] += q[i] * xv[i];
+            }
+    } else {
+        constexpr int PER_WORD = 32 / BITS;
+#pragma unroll
+        for (int k = 0; k < Fmt<BITS>::kWords; ++k)
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int n = 0; n < NR; ++n) {
+                    float q[PER_WORD];
+                    unpack_word<BITS>(R.w[m][n].w[k], q);
+#pragma unroll
+                    for (int i = 0; i < PER_WORD; ++i) d[m][n] += q[i] * xv[k * PER_WORD + i];
+                }
+    }
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int n = 0; n < NR; ++n) {
-            float q[CODES];
-            unpack<BITS>(R.w[m][n], q);
-            float d = 0.f;
-#pragma unroll
-            for (int i = 0; i < CODES; ++i) d += q[i] * xv[i];
             const float s = R.live[n] ? sb_to_float<SB>(R.sr[m][n]) : 0.f;
             const float b = R.live[n] ? sb_to_float<SB>(R.br[m][n]) : 0.f;
-            acc[m][n] += s * d + b * xsum;
+            acc[m][n] += s * d[m][n] + b * xsum;
+        }
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// 4-bit codes against bf16 inputs with the packed dot instruction.  Each
+// code q is turned into the bf16 number 128 + q (exact: 0x4300 | q) with one
+// and-or per pair of codes, and v_dot2 multiplies two such numbers by two
+// bf16 inputs and adds both products (exact in fp32) to the accumulator:
+//     sum_i (s q_i + b) x_i = s * sum_i (128 + q_i) x_i + (b - 128 s) * sum_i x_i.
+// Pair p of word k holds codes (8k+p, 8k+p+4) (nibbles p and p+4), so the
+// inputs are paired the same way, once per chunk, with byte permutes.
+// xw: the chunk's 32 bf16 inputs as 16 words (element 2i in the low half of
+// word i).
+template <int SB, int NM, int NR>
+__device__ __forceinline__ void dot_block_q4_bf16(const BlockRegs<4, NM, NR> &R, const uint32_t *xw,
+                                                  float xsum, float (&acc)[NM][NR]) {
+    uint32_t xp[4][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t x0 = xw[4 * k], x1 = xw[4 * k + 1], x2 = xw[4 * k + 2], x3 = xw[4 * k + 3];
+        xp[k][0] = __builtin_amdgcn_perm(x2, x0, 0x05040100u);   // (x[8k],   x[8k+4])
+        xp[k][1] = __builtin_amdgcn_perm(x2, x0, 0x07060302u);   // (x[8k+1], x[8k+5])
+        xp[k][2] = __builtin_amdgcn_perm(x3, x1, 0x05040100u);   // (x[8k+2], x[8k+6])
+        xp[k][3] = __builtin_amdgcn_perm(x3, x1, 0x07060302u);   // (x[8k+3], x[8k+7])
+    }
+    float d[NM][NR];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int n = 0; n < NR; ++n) d[m][n] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int n = 0; n < NR; ++n) {
+                const uint32_t w = R.w[m][n].w[k];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t qp = ((w >> (4 * p)) & 0x000F000Fu) | 0x43004300u;
+                    d[m][n] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp),
+                                                              __builtin_bit_cast(bf16x2_t, xp[k][p]),
+                                                              d[m][n], false);
+                }
+            }
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int n = 0; n < NR; ++n) {
+            const float s = R.live[n] ? sb_to_float<SB>(R.sr[m][n]) : 0.f;
+            const float b = R.live[n] ? sb_to_float<SB>(R.br[m][n]) : 0.f;
+            acc[m][n] += s * d[m][n] + (b - 128.0f * s) * xsum;
         }
 }
 
