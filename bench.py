@@ -59,6 +59,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="for counter collection: skip the comparison path and the CPU baseline, "
+                         "and end with a plain copy kernel of --copy-mib MiB (the counters' calibration)")
+    ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--path", choices=("fused", "three-call"), default=None,
                     help="fused single-launch layer (default for one token per step) or "
                          "route + expert FFN + tail (default for several tokens per step)")
@@ -91,6 +95,8 @@ def main():
     # ---- weights and inputs, resident in HBM
     t0 = time.time()
     layers, host_keep = [], {}
+    if args.profile_run:
+        args.no_cpu_baseline = True
     keep_for_cpu = 0 if args.no_cpu_baseline else min(L, 4)
     for li in range(L):
         w = mi.gen_layer_weights(cfg, li)
@@ -236,7 +242,7 @@ def main():
 
     # ---- the other path on the same tokens, for comparison (not the headline)
     other = None
-    if T == 1:
+    if T == 1 and not args.profile_run:
         which = "three-call" if path == "fused" else "fused"
         og = []
         for r in range(R):
@@ -282,6 +288,19 @@ def main():
                "sample": f"{done_layers} layer evaluations of the first {keep_for_cpu} layers "
                          f"(token 0), {csecs:.1f}s, fp64, OpenMP over output rows"}
 
+    copy = None
+    if args.profile_run:
+        # a plain copy of known size: reads and writes copy-mib MiB each, so the
+        # HBM counters of a profiler run can be scaled to bytes
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        copy = {"kernel": "elementwise mul by 1 (torch)", "bytes_read": n * 4, "bytes_written": n * 4,
+                "launches": 3}
+
     line = {
         "metric": "expert-weight HBM GB/s (% of ~8 TB/s) and MoE-layer decode tokens/s",
         "value": round(gbps, 2),
@@ -310,6 +329,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if copy is not None:
+        line["calibration_copy"] = copy
     print(json.dumps(line), flush=True)
 
 

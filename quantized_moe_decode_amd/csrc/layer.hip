@@ -19,7 +19,7 @@ struct LayerPlan {
     int grid;
     size_t lds;
     size_t ws_bytes;
-    size_t off_logits, off_act, off_partial;
+    size_t off_logits, off_act, off_act_sent, off_partial;
 };
 
 static moe_status plan_layer(const moe_layer_weights *w, int d_in_check, LayerPlan &p) {
@@ -98,9 +98,12 @@ static moe_status plan_layer(const moe_layer_weights *w, int d_in_check, LayerPl
 
     size_t off = align_up((size_t)kCtrCount * kCtrStride * sizeof(uint32_t), 256);
     p.off_logits = off;
-    off = align_up(off + (size_t)(E + 1) * sizeof(uint64_t), 256);
+    a.logit_stride = (int)(align_up((size_t)(E + 1) * sizeof(uint64_t), 4096) / sizeof(uint64_t));
+    off += (size_t)kLogitCopies * a.logit_stride * sizeof(uint64_t);
     p.off_act = off;
     off = align_up(off + (size_t)slots * dmax * sizeof(uint64_t), 256);
+    p.off_act_sent = off;
+    off = align_up(off + (size_t)slots * kActCopies * kSentStride * sizeof(uint64_t), 256);
     p.off_partial = off;
     off = align_up(off + (size_t)slots * d_in * sizeof(uint64_t), 256);
     p.ws_bytes = off;
@@ -183,6 +186,7 @@ extern "C" moe_status moe_decode_layer(const moe_layer_weights *weights, const v
     a.ctr = reinterpret_cast<uint32_t *>(ws);
     a.logits = reinterpret_cast<uint64_t *>(ws + p.off_logits);
     a.act = reinterpret_cast<uint64_t *>(ws + p.off_act);
+    a.act_sent = reinterpret_cast<uint64_t *>(ws + p.off_act_sent);
     a.partial = reinterpret_cast<uint64_t *>(ws + p.off_partial);
     hipLaunchKernelGGL(k, dim3(p.grid), dim3(256), p.lds, reinterpret_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;

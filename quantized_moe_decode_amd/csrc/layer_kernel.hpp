@@ -47,6 +47,11 @@ constexpr int kLayerNRA = 4;        // rows per lane group, kernel A units
 constexpr int kLayerNRB = 4;        // rows per lane group, kernel B units
 constexpr int kCtrStride = 64;      // uint32 words between control words (256 bytes)
 constexpr uint32_t kSpinLimit = 1u << 19;
+constexpr int kLogitCopies = 16;    // copies of the router logits, each polled by 1/16 of the workgroups
+constexpr int kActCopies = 8;       // copies of each slot's last act row (the kernel-B units' sentinel)
+constexpr int kSentStride = 32;     // words between sentinel copies (256 bytes)
+constexpr int kSentinelSleep = 16;  // s_sleep between sentinel polls (~0.45 us): fewer polls, faster hand-off
+constexpr int kRetrySleep = 8;      // s_sleep between polls of words still missing after a batch read
 
 // control words (in units of kCtrStride)
 constexpr int kCtrErr = 0;
@@ -68,8 +73,10 @@ struct LayerArgs {
     int32_t *ids_out;
     float *scores_out;
     float *gate_out;
-    uint64_t *logits;               // [E + 1] tagged
+    uint64_t *logits;               // [kLogitCopies][logit_stride] tagged, E + 1 used per copy
+    int logit_stride;               // words between copies (a multiple of 512: 4 KiB)
     uint64_t *act;                  // [K + S][act_stride] tagged
+    uint64_t *act_sent;             // [K + S][kActCopies][kSentStride] tagged copies of each slot's last act row
     int act_stride;
     uint64_t *partial;              // [K + S][d_in] tagged
     uint32_t *ctr;                  // control words
@@ -85,27 +92,79 @@ __device__ __forceinline__ void st_tagged(uint64_t *p, float v, uint32_t tag) {
     __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ uint64_t ld_tagged(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void raise_error(const LayerArgs &a) {
+    __hip_atomic_fetch_or(ctr_at(a, kCtrErr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Poll one tagged word until it carries `tag`; returns its value (0 and the
-// error word raised on time-out).
+// error word raised on time-out).  Polls are spaced out: with hundreds of
+// workgroups polling, the polls themselves slow down the memory round trip
+// that delivers the value.
 __device__ __forceinline__ float wait_tagged(const LayerArgs &a, const uint64_t *p, uint32_t tag) {
     for (uint32_t i = 0; i < kSpinLimit; ++i) {
-        const uint64_t w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t w = ld_tagged(p);
         if ((uint32_t)(w >> 32) == tag) return __uint_as_float((uint32_t)w);
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(kSentinelSleep);
     }
-    __hip_atomic_fetch_or(ctr_at(a, kCtrErr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    raise_error(a);
     return 0.f;
 }
 
-// Gather n tagged words p[0..n): thread 0 first polls the last one (producers
-// finish at about the same time), then every thread reads its words, and only
-// words not yet tagged are polled again.  f(i, value) consumes word i.  This
-// keeps the polling traffic of a workgroup to one address instead of n.
-template <typename Fn>
-__device__ __forceinline__ void gather_tagged(const LayerArgs &a, const uint64_t *p, int n, uint32_t tag, Fn f) {
-    if (threadIdx.x == 0) (void)wait_tagged(a, p + n - 1, tag);
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) f(i, wait_tagged(a, p + i, tag));
+// Per thread: read the tagged words addr(0), .., addr(cnt - 1) (cnt <= N) with
+// all loads in flight together, then poll again only the ones not yet tagged,
+// so a batch costs one round trip once its producers are done.  v[u] gets the
+// values (0, and the error word raised, on time-out).
+template <int N, int SLEEP = kRetrySleep, typename Addr>
+__device__ __forceinline__ void poll_batch(const LayerArgs &a, uint32_t tag, int cnt, Addr addr, float *v) {
+    uint64_t w[N];
+    const uint64_t ready = (uint64_t)tag << 32;
+#pragma unroll
+    for (int u = 0; u < N; ++u) w[u] = u < cnt ? ld_tagged(addr(u)) : ready;
+    for (uint32_t spin = 0;; ++spin) {
+        bool all = true;
+#pragma unroll
+        for (int u = 0; u < N; ++u) all = all && (uint32_t)(w[u] >> 32) == tag;
+        if (all) break;
+        if (spin == kSpinLimit) {
+            raise_error(a);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(SLEEP);
+#pragma unroll
+        for (int u = 0; u < N; ++u)
+            if ((uint32_t)(w[u] >> 32) != tag) w[u] = ld_tagged(addr(u));
+    }
+#pragma unroll
+    for (int u = 0; u < N; ++u) v[u] = (uint32_t)(w[u] >> 32) == tag ? __uint_as_float((uint32_t)w[u]) : 0.f;
+}
+
+constexpr int kGatherPer = 4;       // words per thread per gather batch
+
+// Gather n tagged words addr(0..n) into f(i, value), in batches of
+// kGatherPer words per thread.  With a sentinel, thread 0 first waits for that
+// one word (written when the producers are about done), so that while the
+// producers run a workgroup polls one address rather than all n.
+template <typename Addr, typename Fn>
+__device__ __forceinline__ void gather_tagged(const LayerArgs &a, int n, const uint64_t *sentinel, uint32_t tag,
+                                              Addr addr, Fn f) {
+    const int nt = blockDim.x, t = threadIdx.x;
+    if (sentinel) {
+        if (t == 0) (void)wait_tagged(a, sentinel, tag);
+        __syncthreads();
+    }
+    for (int base = 0; base < n; base += kGatherPer * nt) {
+        const int left = n - base - t;
+        const int cnt = left <= 0 ? 0 : min(kGatherPer, (left + nt - 1) / nt);
+        float v[kGatherPer];
+        poll_batch<kGatherPer>(a, tag, cnt, [&](int u) { return addr(base + u * nt + t); }, v);
+#pragma unroll
+        for (int u = 0; u < kGatherPer; ++u)
+            if (u < cnt) f(base + u * nt + t, v[u]);
+    }
 }
 
 __device__ __forceinline__ uint32_t launch_tag(const LayerArgs &a) {
@@ -156,119 +215,156 @@ struct Selection {
     int ids[MOE_MAX_TOP_K];
     float scores[MOE_MAX_TOP_K];
     float gate;
+    uint32_t n_hit, hit_mask;       // rank-count bookkeeping, zeroed before the logits arrive
 };
 
-// Top-k in one wave, PER logits per lane (expert lane + 64*i in l[i]): rounds
-// of "largest untaken logit" (a DPP wave maximum), each taking the lowest
-// expert id that holds that value (a ballot), i.e. descending logit with ties
-// to the lower id.  Lane k ends with the k-th id and logit.  Rounds [k0, k1)
-// run per call, so a caller can stop at the rank it needs and resume later.
-template <int PER>
-struct TopK {
-    float l[PER];
-    uint32_t taken;
-    int my_id;
-    float my_logit, mx;
-
-    __device__ __forceinline__ void init(const float *s_logits, int E, int lane) {
-        taken = 0;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = lane + i * kWave;
-            l[i] = e < E ? s_logits[e] : -INFINITY;
-            if (e >= E) taken |= 1u << i;
-        }
-        my_id = -1;
-        my_logit = 0.f;
-        mx = 0.f;
-    }
-
-    __device__ __forceinline__ void rounds(int k0, int k1, int lane) {
-        for (int k = k0; k < k1; ++k) {
-            float best = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < PER; ++i) best = ((taken >> i) & 1u) ? best : fmaxf(best, l[i]);
-            const float m = wave_max(best);
-            int e = -1;
-#pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const uint64_t hit = __ballot(!((taken >> i) & 1u) && l[i] == m);
-                if (e < 0 && hit) e = i * kWave + (int)__ffsll((unsigned long long)hit) - 1;
-            }
-            if (k == 0) mx = m;
-            if (lane == k) {
-                my_id = e;
-                my_logit = m;
-            }
-            if ((e & (kWave - 1)) == lane) taken |= 1u << ((e / kWave) & 31);
-        }
-    }
-
-    // softmax over all E logits; lanes < K get their selection's score
-    __device__ __forceinline__ float score(int E, int K, bool renorm, int lane) const {
-        float zz = 0.f;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) zz += (lane + i * kWave < E) ? __expf(l[i] - mx) : 0.f;
-        const float z = wave_sum(zz);
-        const float p = lane < K ? __expf(my_logit - mx) / z : 0.f;
-        const float psum = wave_sum(p);
-        return renorm ? p / psum : p;
-    }
+template <int N>
+struct IntC {
+    static constexpr int value = N;
 };
 
-// Wave 0 runs the selection; the other waves wait at the barriers.  With
-// need_scores == false only the ids of ranks [0, upto] are produced; a later
-// finish_selection() completes the ranks and the scores.
-template <int PER>
-__device__ void select_impl(const LayerArgs &a, const float *s_logits, Selection *sel, int upto, bool all,
-                            TopK<PER> &tk) {
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-    if (wave == 0) {
-        tk.init(s_logits, a.E, lane);
-        const int k1 = all ? a.K : upto + 1;
-        tk.rounds(0, k1, lane);
-        if (lane < k1) sel->ids[lane] = tk.my_id;
-        if (all) {
-            const float sc = tk.score(a.E, a.K, a.renorm, lane);
-            if (lane < a.K) sel->scores[lane] = sc;
-        }
-    }
-    __syncthreads();
-}
-
-template <int PER>
-__device__ void finish_impl(const LayerArgs &a, Selection *sel, int done, TopK<PER> &tk) {
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-    if (wave == 0) {
-        tk.rounds(done, a.K, lane);
-        const float sc = tk.score(a.E, a.K, a.renorm, lane);
-        if (lane < a.K) {
-            sel->ids[lane] = tk.my_id;
-            sel->scores[lane] = sc;
-        }
-    }
-    __syncthreads();
-}
-
-// Wait for every router logit and stage them in LDS (plus the shared gate).
-__device__ void gather_logits(const LayerArgs &a, uint32_t tag, float *s_logits, Selection *sel) {
-    gather_tagged(a, a.logits, a.E, tag, [&](int e, float v) { s_logits[e] = v; });
-    if (threadIdx.x == 0) sel->gate = a.wg ? sigmoidf_(wait_tagged(a, a.logits + a.E, tag)) : 1.0f;
-    __syncthreads();
-}
-
-// Dispatch on the number of logits per lane of the selection wave.
+// Dispatch on the number of logits per lane of a one-wave pass over E logits.
 template <typename Fn>
 __device__ __forceinline__ void with_per(int E, Fn fn) {
     const int per = (E + kWave - 1) / kWave;
-    if (per <= 1) fn(TopK<1>{});
-    else if (per <= 2) fn(TopK<2>{});
-    else if (per <= 4) fn(TopK<4>{});
-    else if (per <= 8) fn(TopK<8>{});
-    else fn(TopK<16>{});
+    if (per <= 1) fn(IntC<1>{});
+    else if (per <= 2) fn(IntC<2>{});
+    else if (per <= 4) fn(IntC<4>{});
+    else if (per <= 8) fn(IntC<8>{});
+    else fn(IntC<16>{});
+}
+
+// Exact top-k in one wave, PER logits per lane (expert lane + 64*i in l[i]):
+// K rounds of "largest untaken logit" (a DPP wave maximum), each taking the
+// lowest expert id that holds that value, i.e. descending logit with ties to
+// the lower id.  Lane k writes the k-th id.
+template <int PER>
+__device__ void topk_rounds(const float *s_logits, int E, int K, int lane, Selection *sel) {
+    float l[PER];
+    uint32_t taken = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + i * kWave;
+        l[i] = e < E ? s_logits[e] : -INFINITY;
+        if (e >= E) taken |= 1u << i;
+    }
+    int my_id = -1;
+    for (int k = 0; k < K; ++k) {
+        float best = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) best = ((taken >> i) & 1u) ? best : fmaxf(best, l[i]);
+        const float m = wave_max(best);
+        int e = -1;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const uint64_t hit = __ballot(!((taken >> i) & 1u) && l[i] == m);
+            if (e < 0 && hit) e = i * kWave + (int)__ffsll((unsigned long long)hit) - 1;
+        }
+        if (lane == k) my_id = e;
+        if ((e & (kWave - 1)) == lane) taken |= 1u << ((e / kWave) & 31);
+    }
+    if (lane < K) sel->ids[lane] = my_id;
+}
+
+// Softmax over all E logits in one wave, then the selected ranks'
+// probabilities, renormalised over the K when asked; lane k writes scores[k].
+template <int PER>
+__device__ void softmax_scores(const LayerArgs &a, const float *s_logits, int lane, Selection *sel) {
+    const float mx = s_logits[sel->ids[0]];
+    float zz = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + i * kWave;
+        zz += e < a.E ? __expf(s_logits[e] - mx) : 0.f;
+    }
+    const float z = wave_sum(zz);
+    const float p = lane < a.K ? __expf(s_logits[sel->ids[lane]] - mx) / z : 0.f;
+    const float psum = wave_sum(p);
+    if (lane < a.K) sel->scores[lane] = a.renorm ? p / psum : p;
+}
+
+constexpr int kRankMaxE = 128;      // the block-wide rank count handles E up to this
+
+// All K ids at once.  For E <= kRankMaxE every thread of the block takes
+// part: thread t holds logit i = t / 2 and counts the larger logits in its
+// half of the list, and the two halves meet with a lane swap, so the count is
+// i's rank under "descending logit".  Rank r < K stores id i in ids[r].
+// Equal logits would share a rank, which shows as stored ranks other than
+// exactly 0..K-1; then (and for larger E) the exact wave rounds decide.
+// s_logits must be padded with -inf to a multiple of 8 entries and
+// n_hit/hit_mask zeroed before the preceding barrier.
+__device__ void select_all(const LayerArgs &a, const float *s_logits, Selection *sel) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    bool exact = false;
+    if (a.E <= kRankMaxE) {
+        const int i = tid >> 1, h = tid & 1;
+        const int half = ((a.E + 7) >> 3) << 2;
+        const bool live = i < a.E;
+        const float li = live ? s_logits[i] : 0.f;
+        const f32x4 *row = reinterpret_cast<const f32x4 *>(s_logits + h * half);
+        const int nq = half >> 2;
+        int cnt = 0;
+        for (int q0 = 0; q0 < nq; q0 += 8) {        // eight LDS reads in flight per step
+            f32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = row[min(q0 + u, nq - 1)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int c = (v[u].x > li ? 1 : 0) + (v[u].y > li ? 1 : 0) + (v[u].z > li ? 1 : 0) +
+                              (v[u].w > li ? 1 : 0);
+                cnt += q0 + u < nq ? c : 0;
+            }
+        }
+        cnt += __builtin_amdgcn_mov_dpp(cnt, 0xB1, 0xf, 0xf, false);    // quad_perm [1,0,3,2]
+        if (h == 0 && live && cnt < a.K) {
+            sel->ids[cnt] = i;
+            atomicAdd(&sel->n_hit, 1u);
+            atomicOr(&sel->hit_mask, 1u << cnt);
+        }
+        __syncthreads();
+        const uint32_t full = a.K >= 32 ? 0xffffffffu : (1u << a.K) - 1u;
+        exact = sel->n_hit == (uint32_t)a.K && sel->hit_mask == full;
+    }
+    if (!exact) {
+        if (wave == 0)
+            with_per(a.E, [&](auto per) { topk_rounds<decltype(per)::value>(s_logits, a.E, a.K, lane, sel); });
+        __syncthreads();
+    }
+}
+
+// This workgroup's copy of the router logits.
+__device__ __forceinline__ const uint64_t *my_logits(const LayerArgs &a) {
+    return a.logits + (int64_t)(blockIdx.x % kLogitCopies) * a.logit_stride;
+}
+
+// Wait for every router logit (and the shared-gate logit) and stage them in
+// LDS, padded with -inf for the rank count.  The last word written by the
+// last router workgroup is the sentinel.
+__device__ void gather_logits(const LayerArgs &a, uint32_t tag, float *s_logits, Selection *sel) {
+    const int n = a.E + (a.wg ? 1 : 0);
+    if (threadIdx.x == 0) {
+        if (!a.wg) sel->gate = 1.0f;
+        sel->n_hit = 0;
+        sel->hit_mask = 0;
+    }
+    for (int e = a.E + threadIdx.x; e < ((a.E + 7) & ~7); e += blockDim.x) s_logits[e] = -INFINITY;
+    const uint64_t *lg = my_logits(a);
+    gather_tagged(a, n, lg + n - 1, tag, [&](int i) { return lg + i; }, [&](int e, float v) {
+        if (e < a.E) s_logits[e] = v;
+        else sel->gate = sigmoidf_(v);
+    });
+    __syncthreads();
 }
 
 __device__ __forceinline__ int n_slots(const LayerArgs &a) { return a.K + a.S; }
+
+// Copies of a slot's last act row: the word its kernel-B units wait on
+// before they read the whole vector.
+__device__ __forceinline__ void store_act_sentinel(const LayerArgs &a, int slot, float v, uint32_t tag) {
+    uint64_t *p = a.act_sent + (int64_t)slot * kActCopies * kSentStride;
+#pragma unroll
+    for (int c = 0; c < kActCopies; ++c) st_tagged(p + c * kSentStride, v, tag);
+}
 
 // Kernel A unit: rows [row0, row0 + a_tile) of slot `slot`.
 template <int BA, int SB, int XT>
@@ -281,7 +377,7 @@ __device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     int e;
     if (routed) {
         gather_logits(a, tag, s_logits, sel);
-        with_per(a.E, [&](auto tk) { select_impl(a, s_logits, sel, slot, false, tk); });
+        select_all(a, s_logits, sel);
         e = sel->ids[slot];
     } else {
         e = slot - a.K;
@@ -292,7 +388,10 @@ __device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     const int row_end = min(row0 + a.a_tile, dff);
     uint64_t *act = a.act + (int64_t)slot * a.act_stride;
     if (e < 0 || e >= E) {
-        for (int r = row0 + tid; r < row_end; r += blockDim.x) st_tagged(act + r, 0.f, tag);
+        for (int r = row0 + tid; r < row_end; r += blockDim.x) {
+            st_tagged(act + r, 0.f, tag);
+            if (r == dff - 1) store_act_sentinel(a, slot, 0.f, tag);
+        }
         return;
     }
     const QM mats[2] = {routed ? a.gate : a.sgate, routed ? a.up : a.sup};
@@ -349,7 +448,9 @@ __device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int til
                     const int r = r0 + n * rpw;
                     if (r < row_end) {
                         const float g = acc[0][n], u = acc[1][n];
-                        st_tagged(act + r, g * sigmoidf_(g) * u, tag);
+                        const float v = g * sigmoidf_(g) * u;
+                        st_tagged(act + r, v, tag);
+                        if (r == dff - 1) store_act_sentinel(a, slot, v, tag);
                     }
                 }
             }
@@ -369,9 +470,9 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     const bool routed = slot < a.K;
     int e;
     float score = 1.0f;
-    if (routed) {            // ranks up to this slot first: enough to start loading weights
+    if (routed) {            // every unit ranks the logits itself: no extra hand-off
         gather_logits(a, tag, s_logits, sel);
-        with_per(a.E, [&](auto tk) { select_impl(a, s_logits, sel, slot, false, tk); });
+        select_all(a, s_logits, sel);
         e = sel->ids[slot];
     } else {
         e = slot - a.K;
@@ -398,25 +499,27 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     BlockRegs<BB, 1, NR> cur;
     if (n_stage > 0) load_block<BB, 1, NR>(cur, mats, erow0, rb0 + rsub, rpw, row_end, j, cpr);
 
-    if (routed) {            // full selection and scores while the weights and act are in flight
-        with_per(a.E, [&](auto tk) { select_impl(a, s_logits, sel, 0, true, tk); });
-        score = sel->scores[slot];
+    if (routed && wave == 0) {   // scores while the weights and act are in flight
+        with_per(a.E, [&](auto per) { softmax_scores<decltype(per)::value>(a, s_logits, lane, sel); });
         if (slot == 0 && tile == 0) {            // publish the routing result once
-            if (tid < a.K) {
-                if (a.ids_out) a.ids_out[tid] = sel->ids[tid];
-                if (a.scores_out) a.scores_out[tid] = sel->scores[tid];
+            if (lane < a.K) {
+                if (a.ids_out) a.ids_out[lane] = sel->ids[lane];
+                if (a.scores_out) a.scores_out[lane] = sel->scores[lane];
             }
-            if (tid == 0 && a.gate_out && a.wg) a.gate_out[0] = sel->gate;
+            if (lane == 0 && a.gate_out && a.wg) a.gate_out[0] = sel->gate;
         }
     }
 
     if (valid) {
         const uint64_t *act = a.act + (int64_t)slot * a.act_stride;
-        gather_tagged(a, act, cpr * CODES, tag, [&](int i, float v) {
+        const int n_act = cpr * CODES;
+        const uint64_t *sent = a.act_sent + ((int64_t)slot * kActCopies + blockIdx.x % kActCopies) * kSentStride;
+        gather_tagged(a, n_act, sent, tag, [&](int i) { return act + i; }, [&](int i, float v) {
             const int c = i / CODES;
             xs[c * (CODES + 4) + (i - c * CODES)] = v;
         });
         __syncthreads();
+        if (routed) score = sel->scores[slot];
         float acc[1][NR];
         for (int st = 0; st < n_stage; ++st) {
             const int ps = st / n_chunk, ch = st - ps * n_chunk;
@@ -458,20 +561,27 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     __syncthreads();
     __shared__ float s_gate;
     if (tid == 0)
-        s_gate = a.wg ? sigmoidf_(wait_tagged(a, a.logits + a.E, tag)) : 1.0f;
+        s_gate = a.wg ? sigmoidf_(wait_tagged(a, my_logits(a) + a.E, tag)) : 1.0f;
     __syncthreads();
     const float g = s_gate;
     const int ns = n_slots(a);
+    constexpr int kTailPer = 8;             // slots read together per batch
     for (int r = row0 + tid; r < row_end; r += blockDim.x) {
-        auto pv = [&](int s2) {
-            return s2 == ns - 1 ? s_own[r - row0] : wait_tagged(a, a.partial + (int64_t)s2 * a.d_in + r, tag);
-        };
-        float routed_sum = pv(0);
-        for (int k = 1; k < a.K; ++k) routed_sum += pv(k);
-        float sh = 0.f;
-        if (a.S > 0) {
-            sh = pv(a.K);
-            for (int s2 = a.K + 1; s2 < ns; ++s2) sh += pv(s2);
+        float routed_sum = 0.f, sh = 0.f;   // 0 + x == x: the sums start at slot 0 and slot K
+        for (int s0 = 0; s0 < ns; s0 += kTailPer) {
+            float v[kTailPer];
+            const int cnt = min(kTailPer, ns - 1 - s0);     // the last slot's rows are in s_own
+            poll_batch<kTailPer>(a, tag, cnt, [&](int u) { return a.partial + (int64_t)(s0 + u) * a.d_in + r; },
+                                 v);
+#pragma unroll
+            for (int u = 0; u < kTailPer; ++u) {
+                const int s2 = s0 + u;
+                if (s2 < ns) {
+                    const float pv = s2 == ns - 1 ? s_own[r - row0] : v[u];
+                    if (s2 < a.K) routed_sum += pv;
+                    else sh += pv;
+                }
+            }
         }
         a.out[r] = load_act(a.resid, a.resid_dt, r) + (routed_sum + sh * g);
     }
@@ -489,7 +599,7 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
 
 template <int BA, int BB, int SB, int XT>
 __global__ __launch_bounds__(256, 3) void layer_kernel(LayerArgs a) {
-    __shared__ float s_logits[MOE_MAX_EXPERTS];
+    __shared__ __align__(16) float s_logits[MOE_MAX_EXPERTS];
     __shared__ Selection sel;
     extern __shared__ float xs[];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
@@ -503,8 +613,9 @@ __global__ __launch_bounds__(256, 3) void layer_kernel(LayerArgs a) {
         if (row < n_log)
             v = row < a.E ? layer_row_dot<XT>(a.wr, row, a.x, a.d_in, lane)
                           : layer_row_dot<XT>(a.wg, 0, a.x, a.d_in, lane);
+        v = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));   // one value for every copy
         __syncthreads();
-        if (row < n_log && lane == 0) st_tagged(a.logits + row, v, s_tag);
+        if (row < n_log && lane < kLogitCopies) st_tagged(a.logits + (int64_t)lane * a.logit_stride + row, v, s_tag);
         return;
     }
     __syncthreads();

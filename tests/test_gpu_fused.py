@@ -103,18 +103,42 @@ def test_fused_determinism_graph_replays_and_clean_workspace():
     assert ws[128] == 0, "finished-tile counter not reset"
 
 
-def test_fused_tie_prefers_lower_index():
-    """Duplicate router rows tie exactly; the fused selection takes the lower id first."""
-    cfg = small_cfg(n_experts=8, top_k=3, x_dtype=mi.F32, router_dtype=mi.F32, resid_dtype=mi.F32)
-    say("case fused router tie")
+@pytest.mark.parametrize("top_k,rows,want", [
+    # exact tie inside the top-k: the lower id takes the higher rank
+    (3, {6: 0.05, 2: 0.05, 5: 0.04, 1: 0.01}, [2, 6, 5]),
+    # ties only below the top-k (four zero logits)
+    (4, {6: 0.05, 2: 0.04, 5: 0.03, 1: 0.02}, [6, 2, 5, 1]),
+    # the k-th place is a tie of four zero logits: the lowest id wins it
+    (5, {6: 0.05, 2: 0.04, 5: 0.03, 1: 0.02}, [6, 2, 5, 1, 0]),
+    # tie across the k-th place between two positive logits
+    (2, {3: 0.05, 5: 0.04, 1: 0.04}, [3, 1]),
+], ids=["inside", "below", "at-k-zeros", "at-k"])
+def test_fused_tie_prefers_lower_index(top_k, rows, want):
+    """Router rows that tie exactly: descending logit, ties to the lower id, as the oracle."""
+    cfg = small_cfg(n_experts=8, top_k=top_k, x_dtype=mi.F32, router_dtype=mi.F32, resid_dtype=mi.F32)
+    say(f"case fused router tie k={top_k} {rows}")
     w = mi.gen_layer_weights(cfg, 4, threads=4)
     x, resid = mi.gen_tokens(cfg, 4, 1)
     wr = np.zeros_like(w["router"])
     r = x[0].astype(np.float32)
-    wr[6] = wr[2] = r * 0.05
-    wr[5] = r * 0.04
-    wr[1] = r * 0.01
+    for e, c in rows.items():
+        wr[e] = r * np.float32(c)
     w["router"] = wr
     gpu, _ = run_gpu_layer(cfg, w, x, resid, fused=True)
-    assert gpu["ids"].tolist() == [[2, 6, 5]]
-    assert gpu["scores"][0, 0] == gpu["scores"][0, 1]
+    assert gpu["ids"].tolist() == [want]
+    import oracle
+    ref = oracle.route(x, cfg.x_dtype, w["router"], cfg.router_dtype, top_k, cfg.renormalize)
+    assert ref["ids"].tolist() == [want]
+    np.testing.assert_allclose(gpu["scores"], ref["scores"], rtol=1e-5, atol=1e-7)
+
+
+@pytest.mark.parametrize("n_experts,top_k", [(160, 6), (1000, 8), (64, 32)])
+def test_fused_expert_counts(n_experts, top_k):
+    """Expert counts on both sides of the block-wide rank count's limit, and k = 32."""
+    cfg = small_cfg(n_experts=n_experts, top_k=top_k)
+    say(f"case fused E={n_experts} K={top_k}")
+    w = mi.gen_layer_weights(cfg, 5, threads=8)
+    x, resid = margin_tokens(cfg, 5, w, 1)
+    gpu, layer = run_gpu_layer(cfg, w, x, resid, fused=True)
+    compare_layer(cfg, w, x, resid, gpu, f"fused E={n_experts} K={top_k}")
+    assert not np.any(layer.fused_ws.cpu().numpy()[:4]), "error word set"
