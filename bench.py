@@ -42,6 +42,71 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+COUNTERS = os.path.join(ROOT, "profiles", "layer_kernel_qwen3_30b_a3b_48L_counters.json")
+FUSED_KERNEL = "moe::layer_kernel"
+COPY_KERNEL = "MulFunctor"
+
+
+def kernel_sources_sha256() -> str:
+    """Hash of every HIP source and public header the library is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (os.path.join(ROOT, "quantized_moe_decode_amd", "csrc"), os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(d)):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, command: str) -> dict:
+    """Per-launch HBM bytes of the fused layer kernel from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for the calibration copy kernel of known size."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        layer, copy = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if FUSED_KERNEL in r["Kernel_Name"]:
+                layer.append(v)
+            elif COPY_KERNEL in r["Kernel_Name"]:
+                copy.append(v)
+        if not layer or not copy:
+            raise SystemExit(f"{path}: no {counter} rows for the layer kernel or the copy kernel")
+        return statistics.mean(layer), len(layer), statistics.mean(copy)
+
+    known_kib = copy_mib * 1024.0
+    f_layer, n_f, f_copy = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_layer, n_w, w_copy = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale, w_scale = known_kib / f_copy, known_kib / w_copy
+    return {
+        "kernel": FUSED_KERNEL, "workload": "qwen3_30b_a3b_moe",
+        "command": command,
+        "sources_sha256": kernel_sources_sha256(),
+        "fetch_kib_per_launch_raw": round(f_layer, 2), "write_kib_per_launch_raw": round(w_layer, 2),
+        "launches": [n_f, n_w],
+        "copy_mib": copy_mib, "copy_fetch_kib_raw": round(f_copy, 2), "copy_write_kib_raw": round(w_copy, 2),
+        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+        "hbm_bytes_per_launch": int(round((f_layer * f_scale + w_layer * w_scale) * 1024)),
+    }
+
+
+def traffic_per_launch():
+    """HBM bytes per fused launch from the committed counter record, or None
+    when the record is missing or the kernel sources changed since it was taken."""
+    import json as _json
+    try:
+        rec = _json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    return rec["hbm_bytes_per_launch"]
 
 
 def log(*a):
@@ -59,10 +124,16 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling measurement")
     ap.add_argument("--profile-run", action="store_true",
                     help="for counter collection: skip the comparison path and the CPU baseline, "
                          "and end with a plain copy kernel of --copy-mib MiB (the counters' calibration)")
     ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the counter record from two rocprofv3 --pmc counter_collection.csv "
+                         "files (FETCH_SIZE, WRITE_SIZE of a --profile-run) and exit")
+    ap.add_argument("--counters-command", default="", help="the profiler command, for the record")
     ap.add_argument("--path", choices=("fused", "three-call"), default=None,
                     help="fused single-launch layer (default for one token per step) or "
                          "route + expert FFN + tail (default for several tokens per step)")
@@ -71,6 +142,13 @@ def parse():
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        rec = summarize_counters(*args.summarize_counters, args.copy_mib, args.counters_command)
+        with open(COUNTERS, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the MoE decode layer here runs on a single MI355X "
@@ -204,7 +282,8 @@ def main():
                     "bound": "hbm", "achieved": round(alg / (avg_us * 1e-6) / 1e9, 1),
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(alg / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-                    "traffic": None, "avg_launch_us": round(avg_us, 3),
+                    "traffic": traffic_per_launch(), "traffic_unit": "HBM bytes per launch",
+                    "avg_launch_us": round(avg_us, 3),
                     "bytes_per_launch": int(alg)}
     else:
         # kernel A alone, from graphs holding only its launches for the same tokens
@@ -264,6 +343,47 @@ def main():
         o_secs = ev0.elapsed_time(ev1) / 1000.0
         other = {"path": which, "GBps": round(sum(step_bytes[i % R] for i in range(n_o)) / o_secs / 1e9, 2),
                  "ms_per_step": round(o_secs / n_o * 1e3, 4)}
+
+    # ---- practical ceiling: the library's streaming-read probe on cold data, one
+    # layer's worth of expert bytes per launch and 1 GiB per launch, each launch
+    # on a different slice of a 4 GiB buffer (well beyond the 256 MB last-level
+    # cache); launches captured in a graph and timed with HIP events.
+    ceiling = None
+    if not args.no_ceiling and not args.profile_run:
+        big = torch.ones((4 << 30) // 4, device=dev)
+        ceiling = {"kernel": "read_probe_kernel (moe_decode_read_probe: 16-byte loads, read once)"}
+        for label, nbytes in (("per_layer_expert_bytes", int(np.mean(step_bytes)) // L // 16 * 16),
+                              ("1GiB", 1 << 30)):
+            nel = nbytes // 4
+            nsl = big.numel() // nel
+            reps = min(64, nsl)
+            sl = [big[(i % nsl) * nel:(i % nsl + 1) * nel] for i in range(reps)]
+            part = torch.zeros(qmd.read_probe_blocks(nbytes), device=dev)
+            ss = torch.cuda.Stream()
+            ss.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(ss):
+                for i in range(reps):
+                    qmd.moe_decode_read_probe(sl[i], part)
+            torch.cuda.current_stream().wait_stream(ss)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(reps):
+                    qmd.moe_decode_read_probe(sl[i], part)
+            g.replay()
+            torch.cuda.synchronize()
+            assert float(part.sum().item()) == float(nel), "read probe did not read every byte once"
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            g.replay()
+            g.replay()
+            ev1.record()
+            torch.cuda.synchronize()
+            t = ev0.elapsed_time(ev1) / 1000.0 / (2 * reps)
+            ceiling[label] = {"bytes": nbytes, "us_per_launch": round(t * 1e6, 3),
+                              "GBps": round(nbytes / t / 1e9, 1)}
+        del big
+        torch.cuda.synchronize()
 
     # ---- CPU oracle baseline on a bounded sample
     cpu = None
@@ -328,6 +448,7 @@ def main():
         "other_path": other,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "ceiling": ceiling,
     }
     if copy is not None:
         line["calibration_copy"] = copy

@@ -237,6 +237,21 @@ moe_status moe_decode_layer(const moe_layer_weights *weights, const void *x, moe
 /* 0 when the weights are invalid or unsupported. */
 size_t moe_decode_layer_workspace_bytes(const moe_layer_weights *weights);
 
+/*
+ * Streaming-read probe: a measurement aid, not part of the layer.  Reads
+ * `bytes` bytes at `data` (device memory, 16-byte aligned, bytes a nonzero
+ * multiple of 16) exactly once with 16-byte loads and writes one fp32 partial
+ * sum of the buffer's fp32 values per workgroup to partial_sums[0..n) (device
+ * memory), n = moe_decode_read_probe_blocks(bytes); n_partial must be at least
+ * n (MOE_EINVAL otherwise).  Its launch time gives the machine's practical
+ * HBM read rate for a read of that size, the ceiling the decode kernels are
+ * compared with (meTile PR #30: decode GEMVs measured against streaming).
+ * Asynchronous on `stream`; allocates nothing.
+ */
+moe_status moe_decode_read_probe(const void *data, size_t bytes, float *partial_sums, int32_t n_partial,
+                                 void *stream);
+int32_t moe_decode_read_probe_blocks(size_t bytes);
+
 /* Human-readable name of a status code (static storage). */
 const char *moe_decode_status_string(moe_status s);
 

@@ -78,6 +78,10 @@ def _load_library():
     L.moe_decode_layer_workspace_bytes.restype = sz
     L.moe_decode_tail.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp]
     L.moe_decode_tail.restype = i32
+    L.moe_decode_read_probe.argtypes = [vp, sz, vp, i32, vp]
+    L.moe_decode_read_probe.restype = i32
+    L.moe_decode_read_probe_blocks.argtypes = [sz]
+    L.moe_decode_read_probe_blocks.restype = i32
     L.moe_decode_status_string.argtypes = [i32]
     L.moe_decode_status_string.restype = ctypes.c_char_p
     L.moe_decode_abi_version.restype = i32
@@ -250,10 +254,24 @@ def moe_decode_tail(partial: torch.Tensor, residual: torch.Tensor, out: torch.Te
     _check(st, "moe_decode_tail")
 
 
+def read_probe_blocks(nbytes: int) -> int:
+    """Number of fp32 partial sums moe_decode_read_probe writes for nbytes."""
+    return int(lib.moe_decode_read_probe_blocks(nbytes))
+
+
+def moe_decode_read_probe(data: torch.Tensor, partial_sums: torch.Tensor, stream=None) -> None:
+    """Read data (contiguous device tensor) once; one fp32 sum per workgroup into partial_sums."""
+    nbytes = data.numel() * data.element_size()
+    st = lib.moe_decode_read_probe(_ptr(data), nbytes, _ptr(partial_sums), partial_sums.numel(),
+                                   _stream(stream))
+    _check(st, "moe_decode_read_probe")
+
+
 from .layer import DecodeLayer  # noqa: E402  (needs the functions above)
 
 __all__ = ["QuantStack", "DecodeLayer", "moe_decode_route", "moe_decode_expert_ffn",
            "moe_decode_layer", "layer_weights", "layer_workspace_bytes",
            "moe_decode_gate_up", "moe_decode_down",
            "moe_decode_tail", "route_workspace_bytes", "expert_ffn_workspace_bytes",
+           "moe_decode_read_probe", "read_probe_blocks",
            "MoeError", "status_string", "abi_version", "lib"]

@@ -251,6 +251,24 @@ def test_tail_rejects(kw, want):
     assert _tail(**kw) == want
 
 
+@pytest.mark.parametrize("data,nbytes,out,n,want", [
+    (None, 4096, P, 64, MOE_EINVAL),
+    (P, 4096, None, 64, MOE_EINVAL),
+    (P, 0, P, 64, MOE_EINVAL),
+    (P, 4100, P, 64, MOE_EINVAL),           # not a multiple of 16 bytes
+    (P + 8, 4096, P, 64, MOE_EINVAL),       # not 16-byte aligned
+    (P, 1 << 30, P, 1, MOE_EINVAL),         # too few partial sums for the grid
+])
+def test_read_probe_rejects(data, nbytes, out, n, want):
+    assert lib.moe_decode_read_probe(data, nbytes, out, n, None) == want
+
+
+def test_read_probe_blocks():
+    assert lib.moe_decode_read_probe_blocks(0) == 0
+    assert lib.moe_decode_read_probe_blocks(16) == 1
+    assert 1 <= lib.moe_decode_read_probe_blocks(1 << 30) <= 4096
+
+
 def test_binding_raises_on_error():
     """The Python layer turns a status into MoeError (host-side rejection, no launch)."""
     import torch
