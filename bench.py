@@ -48,14 +48,20 @@ FUSED_KERNEL = "moe::layer_kernel"
 COPY_KERNEL = "MulFunctor"
 
 
+# the files the fused layer kernel is built from (sources, public header, flags)
+LAYER_KERNEL_FILES = ["quantized_moe_decode_amd/csrc/" + f for f in
+                      ("api.hpp", "common.hpp", "qgemv.hpp", "layer_kernel.hpp", "layer.hip",
+                       "layer_a4.hip", "layer_a6.hip", "layer_a8.hip")] + \
+                     ["include/moe_decode.h", "quantized_moe_decode_amd/build.py"]
+
+
 def kernel_sources_sha256() -> str:
-    """Hash of every HIP source and public header the library is built from."""
+    """Hash of the files the fused layer kernel is built from."""
     import hashlib
     h = hashlib.sha256()
-    for d in (os.path.join(ROOT, "quantized_moe_decode_amd", "csrc"), os.path.join(ROOT, "include")):
-        for name in sorted(os.listdir(d)):
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for rel in LAYER_KERNEL_FILES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
