@@ -93,7 +93,13 @@ static moe_status plan_layer(const moe_layer_weights *w, int d_in_check, LayerPl
     const int dmax = d_ffs > d_ff ? d_ffs : d_ff;
     a.act_stride = dmax;
     p.grid = a.n_route + a.K * a.a_tiles_r + a.S * a.a_tiles_s + slots * a.b_tiles;
-    p.lds = (size_t)(dmax / cb) * (cb + 4) * sizeof(float);
+    // dynamic LDS: kernel-B units stage act as fp32 chunks (+4 floats each),
+    // kernel-A units stage x raw (+16 bytes per chunk)
+    const int ca = codes_of(w->gate.bits);
+    const size_t x_elem = w->w_router_dtype == MOE_F32 ? 4 : 2;     // x has the router's dtype
+    const size_t lds_b = (size_t)(dmax / cb) * (cb + 4) * sizeof(float);
+    const size_t lds_a = (size_t)(d_in / ca) * ((size_t)ca * x_elem + 16);
+    p.lds = lds_b > lds_a ? lds_b : lds_a;
     if (p.lds > 64 * 1024) return MOE_EUNSUPPORTED;
 
     size_t off = align_up((size_t)kCtrCount * kCtrStride * sizeof(uint32_t), 256);

@@ -369,11 +369,14 @@ __device__ __forceinline__ void store_act_sentinel(const LayerArgs &a, int slot,
 // Kernel A unit: rows [row0, row0 + a_tile) of slot `slot`.
 template <int BA, int SB, int XT>
 __device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int tile, float *s_logits,
-                             Selection *sel) {
+                             Selection *sel, void *xs) {
     constexpr int NR = kLayerNRA;
     using F = Fmt<BA>;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const bool routed = slot < a.K;
+    // x into LDS while the logits are on their way: the weight stream then
+    // shares the memory pipeline with nothing else
+    stage_x_raw<XT, F::kCodes>(a.x, a.d_in / F::kCodes, xs);
     int e;
     if (routed) {
         gather_logits(a, tag, s_logits, sel);
@@ -381,6 +384,7 @@ __device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int til
         e = sel->ids[slot];
     } else {
         e = slot - a.K;
+        __syncthreads();
     }
     const int dff = routed ? a.d_ff : a.d_ffs;
     const int E = routed ? a.E : a.S;
@@ -413,27 +417,27 @@ __device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int til
 #pragma unroll
                 for (int n = 0; n < NR; ++n) acc[m][n] = 0.f;
         }
+        const int cpos = ch * lr + j;
+        XRaw<XT, F::kCodes> xr;
+        read_x_raw<XT, F::kCodes>(xs, cpos < cpr ? cpos : 0, xr);
         BlockRegs<BA, 2, NR> cur;
-        load_block<BA, 2, NR>(cur, mats, erow0, r0, rpw, row_end, ch * lr + j, cpr);
+        load_block<BA, 2, NR>(cur, mats, erow0, r0, rpw, row_end, cpos, cpr);
         if constexpr (BA == 4 && XT == MOE_BF16) {
             // raw bf16 inputs for the packed-dot path
-            const u32x4 *xp = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.x) +
-                                                               (int64_t)cur.cc * F::kCodes);
             uint32_t xw[16];
             float xsum = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4 v = xp[i];
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    xw[4 * i + k] = v[k];
-                    xsum += __uint_as_float(v[k] << 16) + __uint_as_float(v[k] & 0xFFFF0000u);
+                    const uint32_t v = xr.v[i][k];
+                    xw[4 * i + k] = v;
+                    xsum += __uint_as_float(v << 16) + __uint_as_float(v & 0xFFFF0000u);
                 }
-            }
             dot_block_q4_bf16<SB, 2, NR>(cur, xw, xsum, acc);
         } else {
             float xv[F::kCodes];
-            load_x_chunk<XT, F::kCodes>(a.x, (int64_t)cur.cc * F::kCodes, xv);
+            convert_x<XT, F::kCodes>(xr, xv);
             dot_block<BA, SB, 2, NR>(cur, xv, sum_n<F::kCodes>(xv), acc);
         }
         if (ch == n_chunk - 1) {
@@ -632,7 +636,7 @@ __global__ __launch_bounds__(256, 3) void layer_kernel(LayerArgs a) {
             slot = a.K + bs / a.a_tiles_s;
             tile = bs % a.a_tiles_s;
         }
-        layer_a_unit<BA, SB, XT>(a, tag, slot, tile, s_logits, &sel);
+        layer_a_unit<BA, SB, XT>(a, tag, slot, tile, s_logits, &sel, xs);
     } else {
         b -= n_a;
         layer_b_unit<BB, SB>(a, tag, b / a.b_tiles, b % a.b_tiles, s_logits, &sel, xs);

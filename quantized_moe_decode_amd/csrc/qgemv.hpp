@@ -54,6 +54,10 @@ __device__ __forceinline__ void load_block(BlockRegs<BITS, NM, NR> &R, const QM 
             R.sr[m][n] = mats[m].s[gi];
             R.br[m][n] = mats[m].b[gi];
         }
+    // Keep every load of the block here: left alone, the compiler sinks the
+    // scale/bias loads down to their first use, after the codes have arrived,
+    // which costs a second memory round trip per block.
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // The codes of word k of a 4- or 8-bit chunk as floats.
@@ -173,20 +177,35 @@ __device__ __forceinline__ void dot_block_q4_bf16(const BlockRegs<4, NM, NR> &R,
 }
 
 // Input chunk of CODES consecutive values, read straight from global memory.
+// Raw words of one input chunk: CODES elements of dtype XT (4 or 2 bytes).
 template <int XT, int CODES>
-__device__ __forceinline__ void load_x_chunk(const void *x, int64_t off, float *xv) {
-    if constexpr (XT == MOE_F32) {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(x) + off);
+struct XRaw {
+    static constexpr int kVecs = CODES * (XT == MOE_F32 ? 4 : 2) / 16;
+    u32x4 v[kVecs];
+};
+
+// Issue the loads of an input chunk (elements off .. off+CODES of x); the
+// values are converted later by convert_x, so the loads can be issued ahead
+// of the weight loads without waiting on them.
+template <int XT, int CODES>
+__device__ __forceinline__ void load_x_raw(const void *x, int64_t off, XRaw<XT, CODES> &r) {
+    constexpr int kElem = XT == MOE_F32 ? 4 : 2;
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(x) + off * kElem);
 #pragma unroll
-        for (int i = 0; i < CODES / 4; ++i) {
-            const f32x4 v = p[i];
-            xv[4 * i] = v.x; xv[4 * i + 1] = v.y; xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
-        }
+    for (int i = 0; i < XRaw<XT, CODES>::kVecs; ++i) r.v[i] = p[i];
+}
+
+template <int XT, int CODES>
+__device__ __forceinline__ void convert_x(const XRaw<XT, CODES> &r, float *xv) {
+    if constexpr (XT == MOE_F32) {
+#pragma unroll
+        for (int i = 0; i < CODES / 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) xv[4 * i + k] = __uint_as_float(r.v[i][k]);
     } else {
-        const u32x4 *p = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(x) + off);
 #pragma unroll
         for (int i = 0; i < CODES / 8; ++i) {
-            const u32x4 v = p[i];
+            const u32x4 v = r.v[i];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 if constexpr (XT == MOE_BF16) {
@@ -203,6 +222,42 @@ __device__ __forceinline__ void load_x_chunk(const void *x, int64_t off, float *
             }
         }
     }
+}
+
+// Input chunks staged raw in LDS: chunk c at byte c * xraw_stride (16 bytes of
+// padding per chunk keep 16-byte reads of consecutive chunks by consecutive
+// lanes free of bank conflicts).
+template <int XT, int CODES>
+constexpr int xraw_stride() {
+    return XRaw<XT, CODES>::kVecs * 16 + 16;
+}
+
+// Copy the cpr chunks of x (16-byte aligned) into that layout, all threads of
+// the block; the caller's next barrier makes them visible.
+template <int XT, int CODES>
+__device__ __forceinline__ void stage_x_raw(const void *x, int cpr, void *lds) {
+    constexpr int V = XRaw<XT, CODES>::kVecs;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(x);
+    char *dst = reinterpret_cast<char *>(lds);
+    for (int i = threadIdx.x; i < cpr * V; i += blockDim.x) {
+        const int c = i / V, v = i - c * V;
+        *reinterpret_cast<u32x4 *>(dst + c * xraw_stride<XT, CODES>() + v * 16) = src[i];
+    }
+}
+
+template <int XT, int CODES>
+__device__ __forceinline__ void read_x_raw(const void *lds, int c, XRaw<XT, CODES> &r) {
+    const u32x4 *p =
+        reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(lds) + c * xraw_stride<XT, CODES>());
+#pragma unroll
+    for (int i = 0; i < XRaw<XT, CODES>::kVecs; ++i) r.v[i] = p[i];
+}
+
+template <int XT, int CODES>
+__device__ __forceinline__ void load_x_chunk(const void *x, int64_t off, float *xv) {
+    XRaw<XT, CODES> r;
+    load_x_raw<XT, CODES>(x, off, r);
+    convert_x<XT, CODES>(r, xv);
 }
 
 template <int N>
