@@ -130,6 +130,45 @@ __device__ __forceinline__ float group_sum(float v, int width) {
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum(v, kWave); }
 
+// v + (value of DPP control CTRL) in the rows of ROW_MASK; other rows add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add_rows(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Sum over aligned groups of W lanes (a power of two <= 64) with DPP only:
+// within a row of 16 every lane gets the sum (quad permutations, half-mirror,
+// mirror); across rows the row broadcasts carry it forward, so for W >= 32
+// only the group's last lane holds the total.  Read the result there.
+template <int W>
+__device__ __forceinline__ float group_sum_last(float v) {
+    if constexpr (W >= 2) v += dpp_f<0xB1>(v);     // quad_perm [1,0,3,2]
+    if constexpr (W >= 4) v += dpp_f<0x4E>(v);     // quad_perm [2,3,0,1]
+    if constexpr (W >= 8) v += dpp_f<0x141>(v);    // row_half_mirror
+    if constexpr (W >= 16) v += dpp_f<0x140>(v);   // row_mirror
+    if constexpr (W >= 32) v = dpp_add_rows<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    if constexpr (W >= 64) v = dpp_add_rows<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+// fn(IntC-like tag with ::value = 1 << shift) for a wave-uniform shift in 0..6.
+template <int N>
+struct WidthC {
+    static constexpr int value = N;
+};
+template <typename Fn>
+__device__ __forceinline__ void with_width(int shift, Fn fn) {
+    switch (shift) {
+    case 0: fn(WidthC<1>{}); break;
+    case 1: fn(WidthC<2>{}); break;
+    case 2: fn(WidthC<4>{}); break;
+    case 3: fn(WidthC<8>{}); break;
+    case 4: fn(WidthC<16>{}); break;
+    case 5: fn(WidthC<32>{}); break;
+    default: fn(WidthC<64>{}); break;
+    }
+}
+
 // Maximum over the wave with DPP row shifts and row broadcasts; every lane
 // gets the result.
 template <int CTRL, int ROW_MASK>

@@ -441,12 +441,14 @@ __device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int til
             dot_block<BA, SB, 2, NR>(cur, xv, sum_n<F::kCodes>(xv), acc);
         }
         if (ch == n_chunk - 1) {
+            with_width(a.a_lr_shift, [&](auto w) {
 #pragma unroll
-            for (int n = 0; n < NR; ++n) {
-                acc[0][n] = group_sum(acc[0][n], lr);
-                acc[1][n] = group_sum(acc[1][n], lr);
-            }
-            if (j == 0) {
+                for (int n = 0; n < NR; ++n) {
+                    acc[0][n] = group_sum_last<decltype(w)::value>(acc[0][n]);
+                    acc[1][n] = group_sum_last<decltype(w)::value>(acc[1][n]);
+                }
+            });
+            if (j == lr - 1) {
 #pragma unroll
                 for (int n = 0; n < NR; ++n) {
                     const int r = r0 + n * rpw;
@@ -518,9 +520,16 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
         const uint64_t *act = a.act + (int64_t)slot * a.act_stride;
         const int n_act = cpr * CODES;
         const uint64_t *sent = a.act_sent + ((int64_t)slot * kActCopies + blockIdx.x % kActCopies) * kSentStride;
+        // 4-bit down projections take act as fp16 pairs (packed dot); the
+        // others as fp32 chunks
+        constexpr bool kF16 = BB == 4;
         gather_tagged(a, n_act, sent, tag, [&](int i) { return act + i; }, [&](int i, float v) {
             const int c = i / CODES;
-            xs[c * (CODES + 4) + (i - c * CODES)] = v;
+            if constexpr (kF16)
+                *reinterpret_cast<_Float16 *>(reinterpret_cast<char *>(xs) + c * kF16ChunkBytes +
+                                              f16_pair_offset(i - c * CODES)) = (_Float16)v;
+            else
+                xs[c * (CODES + 4) + (i - c * CODES)] = v;
         });
         __syncthreads();
         if (routed) score = sel->scores[slot];
@@ -533,13 +542,28 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
                 for (int n = 0; n < NR; ++n) acc[0][n] = 0.f;
             }
             if (st > 0) load_block<BB, 1, NR>(cur, mats, erow0, r0, rpw, row_end, ch * lr + j, cpr);
-            float xv[CODES];
-            read_staged<CODES>(staged_chunk<CODES>(xs, 0, cpr, cur.cc), xv);
-            dot_block<BB, SB, 1, NR>(cur, xv, sum_n<CODES>(xv), acc);
-            if (ch == n_chunk - 1) {
+            if constexpr (kF16) {
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(xs) +
+                                                                   cur.cc * kF16ChunkBytes);
+                uint32_t ap[16];
 #pragma unroll
-                for (int n = 0; n < NR; ++n) acc[0][n] = group_sum(acc[0][n], lr);
-                if (j == 0) {
+                for (int i = 0; i < 4; ++i) {
+                    const u32x4 v = src[i];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) ap[4 * i + k] = v[k];
+                }
+                if constexpr (BB == 4) dot_block_q4_f16<SB, 1, NR>(cur, ap, f16_pairs_sum(ap), acc);
+            } else {
+                float xv[CODES];
+                read_staged<CODES>(staged_chunk<CODES>(xs, 0, cpr, cur.cc), xv);
+                dot_block<BB, SB, 1, NR>(cur, xv, sum_n<CODES>(xv), acc);
+            }
+            if (ch == n_chunk - 1) {
+                with_width(lrs, [&](auto w) {
+#pragma unroll
+                    for (int n = 0; n < NR; ++n) acc[0][n] = group_sum_last<decltype(w)::value>(acc[0][n]);
+                });
+                if (j == lr - 1) {
 #pragma unroll
                     for (int n = 0; n < NR; ++n) {
                         const int r = r0 + n * rpw;

@@ -224,6 +224,67 @@ __device__ __forceinline__ void convert_x(const XRaw<XT, CODES> &r, float *xv) {
     }
 }
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// fp16 inputs of one 4-bit chunk staged for dot_block_q4_f16: 16 pairs, pair
+// 4k + p = (input 8k+p, input 8k+p+4) (the codes a nibble pair of word k
+// holds), then 16 bytes of padding.
+constexpr int kF16ChunkBytes = 16 * 4 + 16;
+
+// LDS byte offset (within a chunk) of input i of the chunk, in that order.
+__device__ __forceinline__ int f16_pair_offset(int i) {
+    const int k = i >> 3, r = i & 7;
+    return (4 * k + (r & 3)) * 4 + (r >> 2) * 2;
+}
+
+// 4-bit codes against fp16 inputs with the packed fp16 dot instruction.  A
+// pair of codes becomes the fp16 pair (1024 + q, 1024 + q') with one and-or
+// (0x6400 | q is 1024 + q exactly) and then (q, q') with one packed fp16
+// subtraction (exact), so no large offset has to cancel later; v_dot2
+// multiplies it by two fp16 inputs (products exact in fp32) and adds both to
+// the fp32 accumulator.  ap: the chunk's 16 staged pairs; asum: their sum.
+template <int SB, int NM, int NR>
+__device__ __forceinline__ void dot_block_q4_f16(const BlockRegs<4, NM, NR> &R, const uint32_t *ap, float asum,
+                                                 float (&acc)[NM][NR]) {
+    const f16x2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
+    float d[NM][NR];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int n = 0; n < NR; ++n) d[m][n] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int n = 0; n < NR; ++n) {
+                const uint32_t w = R.w[m][n].w[k];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t qp = ((w >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
+                    const f16x2_t q = __builtin_bit_cast(f16x2_t, qp) - off;
+                    d[m][n] = __builtin_amdgcn_fdot2(q, __builtin_bit_cast(f16x2_t, ap[4 * k + p]), d[m][n], false);
+                }
+            }
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int n = 0; n < NR; ++n) {
+            const float s = R.live[n] ? sb_to_float<SB>(R.sr[m][n]) : 0.f;
+            const float b = R.live[n] ? sb_to_float<SB>(R.br[m][n]) : 0.f;
+            acc[m][n] += s * d[m][n] + b * asum;
+        }
+}
+
+// Sum of a chunk's 16 staged fp16 pairs, in fp32.
+__device__ __forceinline__ float f16_pairs_sum(const uint32_t *ap) {
+    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, ap[i]), one, s, false);
+    return s;
+}
+
 // Input chunks staged raw in LDS: chunk c at byte c * xraw_stride (16 bytes of
 // padding per chunk keep 16-byte reads of consecutive chunks by consecutive
 // lanes free of bank conflicts).

@@ -64,7 +64,10 @@ def test_fused_full_size_layers(name, layers, T):
             compare_layer(cfg, w, x[t:t + 1], resid[t:t + 1], gpu, f"fused {name} L{li} t{t}")
             three, _ = run_gpu_layer(cfg, w, x[t:t + 1], resid[t:t + 1], layer=layer)
             assert np.array_equal(three["ids"], gpu["ids"])
-            assert rel_err(gpu["out"], three["out"]) <= 1e-5
+            # the fused launch rounds act to fp16 before 4-bit down projections
+            # (relative 2^-11 per element; about 2.3e-4 of |out|_inf measured on these
+            # layers), the three-call path keeps fp32: both sit within the oracle's bar
+            assert rel_err(gpu["out"], three["out"]) <= 1e-3
 
 
 def test_fused_determinism_graph_replays_and_clean_workspace():
