@@ -113,23 +113,6 @@ __device__ __forceinline__ float dpp_f(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
-// Sum over aligned groups of `width` lanes (a power of two <= 64); every lane
-// of the group ends with the same bits.  Distances 1 and 2 use quad
-// permutations, 4 and 8 the row half-mirror and row mirror (DPP, no LDS
-// traffic); 16 and 32 use lane shuffles.  Each step adds a value that is
-// uniform over the partner set, so all lanes of a group compute the same sum.
-__device__ __forceinline__ float group_sum(float v, int width) {
-    if (width >= 2) v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
-    if (width >= 4) v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
-    if (width >= 8) v += dpp_f<0x141>(v);   // row_half_mirror
-    if (width >= 16) v += dpp_f<0x140>(v);  // row_mirror
-    if (width >= 32) v += __shfl_xor(v, 16, kWave);
-    if (width >= 64) v += __shfl_xor(v, 32, kWave);
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) { return group_sum(v, kWave); }
-
 // v + (value of DPP control CTRL) in the rows of ROW_MASK; other rows add 0.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_add_rows(float v) {
@@ -149,6 +132,12 @@ __device__ __forceinline__ float group_sum_last(float v) {
     if constexpr (W >= 32) v = dpp_add_rows<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
     if constexpr (W >= 64) v = dpp_add_rows<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
     return v;
+}
+
+// Sum over the whole wave, the same value in every lane (DPP reduction into
+// lane 63, then a broadcast of that lane).
+__device__ __forceinline__ float wave_sum(float v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_sum_last<kWave>(v)), kWave - 1));
 }
 
 // fn(IntC-like tag with ::value = 1 << shift) for a wave-uniform shift in 0..6.

@@ -169,14 +169,16 @@ __global__ __launch_bounds__(256) void gate_up_kernel(FfnArgs a) {
             const int r0 = rb + rsub;
             float acc[2][kNR][MAXT];
             row_block<BITS, SB, XT, 2, MAXT>(mats, erow0, r0, rpw, row_end, j, lr, cpr, a.x, x_off, lds, nt, acc);
+            with_width(__builtin_ctz(lr), [&](auto w) {
 #pragma unroll
-            for (int n = 0; n < kNR; ++n)
+                for (int n = 0; n < kNR; ++n)
 #pragma unroll
-                for (int t = 0; t < MAXT; ++t) {
-                    acc[0][n][t] = group_sum(acc[0][n][t], lr);
-                    acc[1][n][t] = group_sum(acc[1][n][t], lr);
-                }
-            if (j == 0) {
+                    for (int t = 0; t < MAXT; ++t) {
+                        acc[0][n][t] = group_sum_last<decltype(w)::value>(acc[0][n][t]);
+                        acc[1][n][t] = group_sum_last<decltype(w)::value>(acc[1][n][t]);
+                    }
+            });
+            if (j == lr - 1) {
 #pragma unroll
                 for (int n = 0; n < kNR; ++n) {
                     const int r = r0 + n * rpw;
@@ -231,11 +233,13 @@ __global__ __launch_bounds__(256) void down_kernel(FfnArgs a) {
             const int r0 = rb + rsub;
             float acc[1][kNR][MAXT];
             row_block<BITS, SB, MOE_F32, 1, MAXT>(mats, erow0, r0, rpw, row_end, j, lr, cpr, a.act, x_off, lds, nt, acc);
+            with_width(__builtin_ctz(lr), [&](auto w) {
 #pragma unroll
-            for (int n = 0; n < kNR; ++n)
+                for (int n = 0; n < kNR; ++n)
 #pragma unroll
-                for (int t = 0; t < MAXT; ++t) acc[0][n][t] = group_sum(acc[0][n][t], lr);
-            if (j == 0) {
+                    for (int t = 0; t < MAXT; ++t) acc[0][n][t] = group_sum_last<decltype(w)::value>(acc[0][n][t]);
+            });
+            if (j == lr - 1) {
 #pragma unroll
                 for (int n = 0; n < kNR; ++n) {
                     const int r = r0 + n * rpw;
