@@ -50,8 +50,12 @@ constexpr uint32_t kSpinLimit = 1u << 19;
 constexpr int kLogitCopies = 16;    // copies of the router logits, each polled by 1/16 of the workgroups
 constexpr int kActCopies = 8;       // copies of each slot's last act row (the kernel-B units' sentinel)
 constexpr int kSentStride = 32;     // words between sentinel copies (256 bytes)
-constexpr int kSentinelSleep = 16;  // s_sleep between sentinel polls (~0.45 us): fewer polls, faster hand-off
-constexpr int kRetrySleep = 8;      // s_sleep between polls of words still missing after a batch read
+// s_sleep arguments (units of 64 cycles) between polls: with hundreds of
+// pollers, sparse polls make the hand-off faster, not slower
+constexpr int kLogitSleep = 24;     // the router-logit sentinel (~900 pollers over 16 copies)
+constexpr int kActSleep = 2;        // a slot's act sentinel (64 pollers over 8 copies)
+constexpr int kRetrySleep = 2;      // words still missing after a batch read
+constexpr int kTailSleep = 2;       // the tail's reads of the other slots' partial rows
 
 // control words (in units of kCtrStride)
 constexpr int kCtrErr = 0;
@@ -104,11 +108,12 @@ __device__ __forceinline__ void raise_error(const LayerArgs &a) {
 // error word raised on time-out).  Polls are spaced out: with hundreds of
 // workgroups polling, the polls themselves slow down the memory round trip
 // that delivers the value.
+template <int SLEEP>
 __device__ __forceinline__ float wait_tagged(const LayerArgs &a, const uint64_t *p, uint32_t tag) {
     for (uint32_t i = 0; i < kSpinLimit; ++i) {
         const uint64_t w = ld_tagged(p);
         if ((uint32_t)(w >> 32) == tag) return __uint_as_float((uint32_t)w);
-        __builtin_amdgcn_s_sleep(kSentinelSleep);
+        __builtin_amdgcn_s_sleep(SLEEP);
     }
     raise_error(a);
     return 0.f;
@@ -148,12 +153,12 @@ constexpr int kGatherPer = 4;       // words per thread per gather batch
 // kGatherPer words per thread.  With a sentinel, thread 0 first waits for that
 // one word (written when the producers are about done), so that while the
 // producers run a workgroup polls one address rather than all n.
-template <typename Addr, typename Fn>
+template <int SLEEP, typename Addr, typename Fn>
 __device__ __forceinline__ void gather_tagged(const LayerArgs &a, int n, const uint64_t *sentinel, uint32_t tag,
                                               Addr addr, Fn f) {
     const int nt = blockDim.x, t = threadIdx.x;
     if (sentinel) {
-        if (t == 0) (void)wait_tagged(a, sentinel, tag);
+        if (t == 0) (void)wait_tagged<SLEEP>(a, sentinel, tag);
         __syncthreads();
     }
     for (int base = 0; base < n; base += kGatherPer * nt) {
@@ -349,7 +354,7 @@ __device__ void gather_logits(const LayerArgs &a, uint32_t tag, float *s_logits,
     }
     for (int e = a.E + threadIdx.x; e < ((a.E + 7) & ~7); e += blockDim.x) s_logits[e] = -INFINITY;
     const uint64_t *lg = my_logits(a);
-    gather_tagged(a, n, lg + n - 1, tag, [&](int i) { return lg + i; }, [&](int e, float v) {
+    gather_tagged<kLogitSleep>(a, n, lg + n - 1, tag, [&](int i) { return lg + i; }, [&](int e, float v) {
         if (e < a.E) s_logits[e] = v;
         else sel->gate = sigmoidf_(v);
     });
@@ -523,7 +528,7 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
         // 4-bit down projections take act as fp16 pairs (packed dot); the
         // others as fp32 chunks
         constexpr bool kF16 = BB == 4;
-        gather_tagged(a, n_act, sent, tag, [&](int i) { return act + i; }, [&](int i, float v) {
+        gather_tagged<kActSleep>(a, n_act, sent, tag, [&](int i) { return act + i; }, [&](int i, float v) {
             const int c = i / CODES;
             if constexpr (kF16)
                 *reinterpret_cast<_Float16 *>(reinterpret_cast<char *>(xs) + c * kF16ChunkBytes +
@@ -589,7 +594,7 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     __syncthreads();
     __shared__ float s_gate;
     if (tid == 0)
-        s_gate = a.wg ? sigmoidf_(wait_tagged(a, my_logits(a) + a.E, tag)) : 1.0f;
+        s_gate = a.wg ? sigmoidf_(wait_tagged<kLogitSleep>(a, my_logits(a) + a.E, tag)) : 1.0f;
     __syncthreads();
     const float g = s_gate;
     const int ns = n_slots(a);
@@ -599,8 +604,8 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
         for (int s0 = 0; s0 < ns; s0 += kTailPer) {
             float v[kTailPer];
             const int cnt = min(kTailPer, ns - 1 - s0);     // the last slot's rows are in s_own
-            poll_batch<kTailPer>(a, tag, cnt, [&](int u) { return a.partial + (int64_t)(s0 + u) * a.d_in + r; },
-                                 v);
+            poll_batch<kTailPer, kTailSleep>(
+                a, tag, cnt, [&](int u) { return a.partial + (int64_t)(s0 + u) * a.d_in + r; }, v);
 #pragma unroll
             for (int u = 0; u < kTailPer; ++u) {
                 const int s2 = s0 + u;
