@@ -1,0 +1,326 @@
+// Small-batch decode (several tokens per step) with 4-bit weights: each work
+// item is one expert and at most kBatchTok of its tokens (mlxcel PR #276, "What
+// changed" step 2, applied to every token routed to the expert), so each
+// touched expert's rows are streamed once per work item and applied to all
+// of its tokens.
+//
+// A workgroup first stages its tokens' inputs in LDS, paired the way the
+// packed dot instructions consume them (see dot_block_q4_bf16 and
+// dot_block_q4_f16): record (t, c) holds chunk c of token t as 16 pairs,
+// pair 4k + p = (v[8k+p], v[8k+p+4]), then the fp32 sum of the chunk.  The
+// codes of a word are turned into a 16-bit pair once and multiplied into
+// every token's accumulator:
+//   kernel A: bf16 x, codes as bf16 128 + q, bias folded as b - 128 s;
+//   kernel B: act rounded to fp16, codes as exact fp16 q.
+#include <hip/hip_runtime.h>
+
+#include "api.hpp"
+#include "common.hpp"
+#include "ffn.hpp"
+#include "qgemv.hpp"
+
+namespace moe {
+
+constexpr int kRec = 80;         // bytes per staged chunk: 64 of pairs, the chunk sum, padding
+
+size_t batch_lds_bytes(int cols) { return (size_t)kBatchTok * (cols / 32) * kRec; }
+
+// Quad sum (lanes 4i..4i+3 end with the same value).
+__device__ __forceinline__ float quad_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    return v + dpp_f<0x4E>(v);
+}
+
+// Stage nt tokens' inputs.  Thread i handles token t, chunk c, word k (8
+// inputs); the four k of a chunk are consecutive lanes.  Src(t, c, k, v)
+// fills v with 4 pair words and returns the inputs' sum.
+template <typename Src>
+__device__ __forceinline__ void stage_pairs(char *lds, int nt, int cpr, Src src) {
+    const int n = nt * cpr * 4;
+    for (int i0 = 0; i0 < n; i0 += blockDim.x) {       // uniform trip count: the quad sum needs whole quads
+        const int i = i0 + threadIdx.x;
+        const bool ok = i < n;
+        const int k = i & 3, tc = i >> 2;
+        const int t = ok ? tc / cpr : 0, c = ok ? tc - t * cpr : 0;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        float sum = 0.f;
+        if (ok) sum = src(t, c, k, v);
+        sum = quad_sum(sum);
+        if (ok) {
+            char *rec = lds + (t * cpr + c) * kRec;
+            *reinterpret_cast<u32x4 *>(rec + k * 16) = v;
+            if (k == 0) *reinterpret_cast<float *>(rec + 64) = sum;
+        }
+    }
+}
+
+// fn(tag with ::value == nt) for a workgroup-uniform nt in 1..kBatchTok: the
+// compute loops then see a compile-time token count (no per-token guards).
+template <int N>
+struct TokC {
+    static constexpr int value = N;
+};
+template <typename Fn>
+__device__ __forceinline__ void with_tokens(int nt, Fn fn) {
+    static_assert(kBatchTok == 4, "token dispatch covers 1..4");
+    switch (nt) {
+    case 1: fn(TokC<1>{}); break;
+    case 2: fn(TokC<2>{}); break;
+    case 3: fn(TokC<3>{}); break;
+    default: fn(TokC<4>{}); break;
+    }
+}
+
+// Pairs (v[8k+p], v[8k+p+4]) of 8 consecutive 16-bit inputs held as 4 words.
+__device__ __forceinline__ u32x4 pair_words(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+    u32x4 v;
+    v[0] = __builtin_amdgcn_perm(w2, w0, 0x05040100u);
+    v[1] = __builtin_amdgcn_perm(w2, w0, 0x07060302u);
+    v[2] = __builtin_amdgcn_perm(w3, w1, 0x05040100u);
+    v[3] = __builtin_amdgcn_perm(w3, w1, 0x07060302u);
+    return v;
+}
+
+// Kernel A: gate and up projections of one work item over a tile of rows, then SwiGLU.
+template <int SB>
+__global__ __launch_bounds__(256) void gate_up_batch_q4(FfnArgs a) {
+    constexpr int NR = kBatchNRA;
+    extern __shared__ __align__(16) char lds[];
+    Work wk;
+    if (!get_work(a, blockIdx.y, wk)) return;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int row0 = blockIdx.x * a.rows_per_wg;
+    const int row_end = min(row0 + a.rows_per_wg, a.d_ff);
+    const int nt = wk.npairs;
+    if (wk.e < 0 || wk.e >= a.E) {
+        for (int i = 0; i < nt; ++i) {
+            const int64_t p = pair_at(wk, i);
+            for (int r = row0 + tid; r < row_end; r += blockDim.x) a.act[p * a.d_ff + r] = 0.f;
+        }
+        return;
+    }
+    const int cpr = a.d_in / 32;
+    const uint16_t *x = reinterpret_cast<const uint16_t *>(a.x);
+    stage_pairs(lds, nt, cpr, [&](int t, int c, int k, u32x4 &v) {
+        const int64_t tok = pair_at(wk, t) / a.K;
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(x + tok * a.d_in + c * 32 + k * 8);
+        v = pair_words(w[0], w[1], w[2], w[3]);
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s += __uint_as_float(w[i] << 16) + __uint_as_float(w[i] & 0xFFFF0000u);
+        return s;
+    });
+    __syncthreads();
+
+    const int lr = 1 << a.lr_shift, j = lane & (lr - 1), rsub = lane >> a.lr_shift, rpw = kWave >> a.lr_shift;
+    const QM mats[2] = {a.gate, a.up};
+    const int64_t erow0 = (int64_t)wk.e * a.d_ff;
+    with_tokens(nt, [&](auto ntc) {
+        constexpr int NT = decltype(ntc)::value;
+        for (int rb = row0 + wave * rpw * NR; rb < row_end; rb += 4 * rpw * NR) {
+            const int r0 = rb + rsub;
+            float acc[2][NR][NT];
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int n = 0; n < NR; ++n)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) acc[m][n][t] = 0.f;
+            for (int c0 = 0; c0 < cpr; c0 += lr) {
+                BlockRegs<4, 2, NR> R;
+                load_block<4, 2, NR>(R, mats, erow0, r0, rpw, row_end, c0 + j, cpr);
+                float d[2][NR][NT];
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int n = 0; n < NR; ++n)
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) d[m][n][t] = 0.f;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    uint32_t xk[NT][4];     // plain words: bit casts of vector elements are not used
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + (t * cpr + R.cc) * kRec + k * 16);
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) xk[t][p] = v[p];
+                    }
+#pragma unroll
+                    for (int m = 0; m < 2; ++m)
+#pragma unroll
+                        for (int n = 0; n < NR; ++n) {
+                            const uint32_t w = R.w[m][n].w[k];
+#pragma unroll
+                            for (int p = 0; p < 4; ++p) {
+                                const bf16x2_t q =
+                                    __builtin_bit_cast(bf16x2_t, ((w >> (4 * p)) & 0x000F000Fu) | 0x43004300u);
+#pragma unroll
+                                for (int t = 0; t < NT; ++t)
+                                    d[m][n][t] = __builtin_amdgcn_fdot2_f32_bf16(
+                                        q, __builtin_bit_cast(bf16x2_t, xk[t][p]), d[m][n][t], false);
+                            }
+                        }
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const float xsum = *reinterpret_cast<const float *>(lds + (t * cpr + R.cc) * kRec + 64);
+#pragma unroll
+                    for (int m = 0; m < 2; ++m)
+#pragma unroll
+                        for (int n = 0; n < NR; ++n) {
+                            const float s = R.live[n] ? sb_to_float<SB>(R.sr[m][n]) : 0.f;
+                            const float b = R.live[n] ? sb_to_float<SB>(R.br[m][n]) : 0.f;
+                            acc[m][n][t] += s * d[m][n][t] + (b - 128.0f * s) * xsum;
+                        }
+                }
+            }
+            with_width(a.lr_shift, [&](auto wd) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int n = 0; n < NR; ++n)
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) acc[m][n][t] = group_sum_last<decltype(wd)::value>(acc[m][n][t]);
+            });
+            if (j == lr - 1) {
+#pragma unroll
+                for (int n = 0; n < NR; ++n) {
+                    const int r = r0 + n * rpw;
+                    if (r < row_end) {
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) {
+                            const float g = acc[0][n][t], u = acc[1][n][t];
+                            a.act[(int64_t)pair_at(wk, t) * a.d_ff + r] = g * sigmoidf_(g) * u;
+                        }
+                    }
+                }
+            }
+        }
+    });
+}
+
+// Kernel B: down projection of one work item over a tile of output rows, times each pair's score.
+template <int SB>
+__global__ __launch_bounds__(256) void down_batch_q4(FfnArgs a) {
+    constexpr int NR = kBatchNRB;
+    extern __shared__ __align__(16) char lds[];
+    Work wk;
+    if (!get_work(a, blockIdx.y, wk)) return;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int row0 = blockIdx.x * a.rows_per_wg;
+    const int row_end = min(row0 + a.rows_per_wg, a.d_in);
+    const int nt = wk.npairs;
+    if (wk.e < 0 || wk.e >= a.E) {
+        for (int i = 0; i < nt; ++i) {
+            const int64_t p = pair_at(wk, i);
+            for (int r = row0 + tid; r < row_end; r += blockDim.x) a.partial[p * a.d_in + r] = 0.f;
+        }
+        return;
+    }
+    const int cpr = a.d_ff / 32;
+    stage_pairs(lds, nt, cpr, [&](int t, int c, int k, u32x4 &v) {
+        const int64_t p = pair_at(wk, t);
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(a.act + p * a.d_ff + c * 32 + k * 8);
+        const f32x4 lo = src[0], hi = src[1];
+        const float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        uint32_t h[8];
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const _Float16 q = (_Float16)f[i];
+            s += (float)q;
+            h[i] = __builtin_bit_cast(uint16_t, q);
+        }
+        v = pair_words(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+        return s;
+    });
+    __syncthreads();
+
+    const int lr = 1 << a.lr_shift, j = lane & (lr - 1), rsub = lane >> a.lr_shift, rpw = kWave >> a.lr_shift;
+    const QM mats[1] = {a.down};
+    const int64_t erow0 = (int64_t)wk.e * a.d_in;
+    const f16x2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
+    with_tokens(nt, [&](auto ntc) {
+        constexpr int NT = decltype(ntc)::value;
+        for (int rb = row0 + wave * rpw * NR; rb < row_end; rb += 4 * rpw * NR) {
+            const int r0 = rb + rsub;
+            float acc[NR][NT];
+#pragma unroll
+            for (int n = 0; n < NR; ++n)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[n][t] = 0.f;
+            for (int c0 = 0; c0 < cpr; c0 += lr) {
+                BlockRegs<4, 1, NR> R;
+                load_block<4, 1, NR>(R, mats, erow0, r0, rpw, row_end, c0 + j, cpr);
+                float d[NR][NT];
+#pragma unroll
+                for (int n = 0; n < NR; ++n)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) d[n][t] = 0.f;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    uint32_t xk[NT][4];     // plain words: bit casts of vector elements are not used
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + (t * cpr + R.cc) * kRec + k * 16);
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) xk[t][p] = v[p];
+                    }
+#pragma unroll
+                    for (int n = 0; n < NR; ++n) {
+                        const uint32_t w = R.w[0][n].w[k];
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) {
+                            const f16x2_t q =
+                                __builtin_bit_cast(f16x2_t, ((w >> (4 * p)) & 0x000F000Fu) | 0x64006400u) - off;
+#pragma unroll
+                            for (int t = 0; t < NT; ++t)
+                                d[n][t] = __builtin_amdgcn_fdot2(q, __builtin_bit_cast(f16x2_t, xk[t][p]), d[n][t],
+                                                                 false);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const float asum = *reinterpret_cast<const float *>(lds + (t * cpr + R.cc) * kRec + 64);
+#pragma unroll
+                    for (int n = 0; n < NR; ++n) {
+                        const float s = R.live[n] ? sb_to_float<SB>(R.sr[0][n]) : 0.f;
+                        const float b = R.live[n] ? sb_to_float<SB>(R.br[0][n]) : 0.f;
+                        acc[n][t] += s * d[n][t] + b * asum;
+                    }
+                }
+            }
+            with_width(a.lr_shift, [&](auto wd) {
+#pragma unroll
+                for (int n = 0; n < NR; ++n)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) acc[n][t] = group_sum_last<decltype(wd)::value>(acc[n][t]);
+            });
+            if (j == lr - 1) {
+#pragma unroll
+                for (int n = 0; n < NR; ++n) {
+                    const int r = r0 + n * rpw;
+                    if (r < row_end) {
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) {
+                            const int64_t p = pair_at(wk, t);
+                            const float sc = a.scores ? a.scores[p] : 1.0f;
+                            a.partial[p * a.d_in + r] = sc * acc[n][t];
+                        }
+                    }
+                }
+            }
+        }
+    });
+}
+
+KernelFn batch_gate_up_q4(int sb) {
+    return sb == MOE_BF16 ? gate_up_batch_q4<MOE_BF16> : sb == MOE_F16 ? gate_up_batch_q4<MOE_F16> : nullptr;
+}
+
+KernelFn batch_down_q4(int sb) {
+    return sb == MOE_BF16 ? down_batch_q4<MOE_BF16> : sb == MOE_F16 ? down_batch_q4<MOE_F16> : nullptr;
+}
+
+}  // namespace moe

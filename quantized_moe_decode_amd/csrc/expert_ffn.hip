@@ -26,56 +26,9 @@
 #include "api.hpp"
 #include "common.hpp"
 #include "qgemv.hpp"
+#include "ffn.hpp"
 
 namespace moe {
-
-struct FfnArgs {
-    const void *x;
-    int x_dt;
-    int T, K, E, d_in, d_ff;
-    QM gate, up, down;
-    const int32_t *ids;
-    const float *scores;
-    float *act;
-    float *partial;
-    // multi-token work list, built by bucket_kernel (all null when T == 1)
-    const int32_t *work_expert;   // [max_work] expert id, or -1 for the out-of-range ids
-    const int32_t *work_begin;    // [max_work + 1] offsets into pair_list
-    const int32_t *pair_list;     // [T*K] pair index t*K + k, grouped by expert
-    const int32_t *n_work;        // number of work items
-    int lr_shift;                 // log2(lanes per row)
-    int rows_per_wg;
-    int tpp;                      // tokens per LDS pass
-};
-
-struct Work {
-    int e, npairs, single;
-    const int32_t *pairs;
-};
-
-__device__ __forceinline__ bool get_work(const FfnArgs &a, int w, Work &wk) {
-    if (!a.pair_list) {
-        wk.e = a.ids[w];
-        wk.npairs = 1;
-        wk.single = w;
-        wk.pairs = nullptr;
-        return true;
-    }
-    if (w >= *a.n_work) return false;
-    wk.e = a.work_expert[w];
-    const int b = a.work_begin[w];
-    wk.npairs = a.work_begin[w + 1] - b;
-    wk.pairs = a.pair_list + b;
-    wk.single = 0;
-    return true;
-}
-
-__device__ __forceinline__ int pair_at(const Work &wk, int i) { return wk.pairs ? wk.pairs[i] : wk.single; }
-
-// Rows of one lane group processed together: the loads of all of them are
-// issued before any is consumed, so each lane keeps several 16-byte loads in
-// flight.
-constexpr int kNR = 4;
 
 // Dot products of kNR rows (r0, r0+rstep, ...) of NM matrices of the expert
 // whose first row is erow0, accumulated per lane (the caller combines the
@@ -260,45 +213,79 @@ __global__ __launch_bounds__(256) void down_kernel(FfnArgs a) {
 
 // Small-batch bucketing: groups the (token, slot) pairs by expert with a
 // stable counting sort (pairs stay in ascending t*K + k order inside an
-// expert).  Work items list the touched experts in ascending id order, then
-// one item (expert -1) collecting every out-of-range id.  One workgroup.
-__global__ __launch_bounds__(256) void bucket_kernel(const int32_t *ids, int n_pairs, int E,
-                                                     int32_t *work_expert, int32_t *work_begin,
-                                                     int32_t *pair_list, int32_t *n_work) {
-    __shared__ int cnt[MOE_MAX_EXPERTS + 1];
-    __shared__ int cur[MOE_MAX_EXPERTS + 1];
+// expert) and cuts each expert's list into work items of at most max_tok
+// pairs.  Work items list the touched experts in ascending id order, then
+// the items (expert -1) collecting every out-of-range id.  One workgroup:
+// histogram by LDS atomics, block scans, and each pair's rank among the
+// earlier pairs of its bucket.
+constexpr int kBucketThreads = 1024;
+constexpr int kScanMax = 2048;      // entries a block scan handles (E + 2 <= 1026)
+
+// Exclusive prefix sums of v[0..n) in place (n <= kScanMax), using tmp
+// (kScanMax entries) as the other half of a ping-pong Hillis-Steele scan.
+// All threads of the block call it; it ends with a barrier.
+__device__ void block_exclusive_scan(int *v, int *tmp, int n) {
     const int tid = threadIdx.x;
-    for (int i = tid; i <= E; i += blockDim.x) cnt[i] = 0;
+    for (int i = tid; i < kScanMax; i += blockDim.x) tmp[i] = (i >= 1 && i <= n) ? v[i - 1] : 0;
+    __syncthreads();
+    int *src = tmp, *dst = v;
+    for (int d = 1; d < kScanMax; d <<= 1) {
+        for (int i = tid; i < kScanMax; i += blockDim.x) dst[i] = src[i] + (i >= d ? src[i - d] : 0);
+        __syncthreads();
+        int *t = src;
+        src = dst;
+        dst = t;
+    }
+    if (src != v)
+        for (int i = tid; i < kScanMax; i += blockDim.x) v[i] = src[i];
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t *ids, int n_pairs, int E, int max_tok,
+                                                                int32_t *work_expert, int32_t *work_begin,
+                                                                int32_t *pair_list, int32_t *n_work) {
+    __shared__ int off[kScanMax];       // pairs, then first pair, per bucket (bucket E: out-of-range ids)
+    __shared__ int ioff[kScanMax];      // work items, then first work item, per bucket
+    __shared__ int tmp[kScanMax];
+    __shared__ int cnt[MOE_MAX_EXPERTS + 1];
+    __shared__ int bucket[MOE_MAX_TOKENS * MOE_MAX_TOP_K];
+    const int tid = threadIdx.x, nb = E + 1;
+    for (int i = tid; i < nb; i += blockDim.x) cnt[i] = 0;
     __syncthreads();
     for (int p = tid; p < n_pairs; p += blockDim.x) {
         const int e = ids[p];
-        atomicAdd(&cnt[(e >= 0 && e < E) ? e : E], 1);
+        const int b = (e >= 0 && e < E) ? e : E;
+        bucket[p] = b;
+        atomicAdd(&cnt[b], 1);
     }
     __syncthreads();
+    for (int i = tid; i < nb; i += blockDim.x) {
+        off[i] = cnt[i];
+        ioff[i] = (cnt[i] + max_tok - 1) / max_tok;
+    }
+    __syncthreads();
+    block_exclusive_scan(off, tmp, nb);     // off[nb] = n_pairs
+    block_exclusive_scan(ioff, tmp, nb);    // ioff[nb] = number of work items
+    for (int p = tid; p < n_pairs; p += blockDim.x) {
+        const int b = bucket[p];
+        int r = 0;
+        for (int q = 0; q < p; ++q) r += bucket[q] == b ? 1 : 0;
+        pair_list[off[b] + r] = p;
+    }
+    for (int b = tid; b < nb; b += blockDim.x) {
+        const int items = ioff[b + 1] - ioff[b];
+        for (int i = 0; i < items; ++i) {
+            work_expert[ioff[b] + i] = b < E ? b : -1;
+            work_begin[ioff[b] + i] = off[b] + i * max_tok;
+        }
+    }
     if (tid == 0) {
-        int off = 0, w = 0;
-        for (int e = 0; e <= E; ++e) {
-            cur[e] = off;
-            if (cnt[e]) {
-                work_expert[w] = (e < E) ? e : -1;
-                work_begin[w] = off;
-                ++w;
-                off += cnt[e];
-            }
-        }
-        work_begin[w] = off;
-        *n_work = w;
-        for (int p = 0; p < n_pairs; ++p) {
-            const int e = ids[p];
-            const int b = (e >= 0 && e < E) ? e : E;
-            pair_list[cur[b]++] = p;
-        }
+        work_begin[ioff[nb]] = n_pairs;
+        *n_work = ioff[nb];
     }
 }
 
 // ------------------------------------------------------------------ host side
-
-using KernelFn = void (*)(FfnArgs);
 
 // Kernel A instantiations: bits x scale dtype x (single-token input dtype, or
 // staged multi-token inputs).
@@ -361,7 +348,12 @@ static QM to_qm(const moe_qmat *m) {
 
 static constexpr size_t kLdsBudget = 64 * 1024;
 
-static int max_work_items(int T, int K, int E) { return (T * K < E ? T * K : E) + 1; }
+// Work items after bucketing: at most ceil(n/kBatchTok) + (non-empty buckets).
+static int max_work_items(int T, int K, int E) {
+    const int n = T * K;
+    const int buckets = n < E + 1 ? n : E + 1;
+    return (n + kBatchTok - 1) / kBatchTok + buckets;
+}
 
 }  // namespace moe
 
@@ -419,8 +411,8 @@ static moe_status plan_common(Plan &p, int n_tokens, int top_k, int E, const int
 
 static void launch_bucket(const Plan &p) {
     if (!p.a.pair_list) return;
-    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(256), 0, p.s, p.a.ids, p.a.T * p.a.K, p.a.E,
-                       const_cast<int32_t *>(p.a.work_expert), const_cast<int32_t *>(p.a.work_begin),
+    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, p.s, p.a.ids, p.a.T * p.a.K, p.a.E,
+                       kBatchTok, const_cast<int32_t *>(p.a.work_expert), const_cast<int32_t *>(p.a.work_begin),
                        const_cast<int32_t *>(p.a.pair_list), const_cast<int32_t *>(p.a.n_work));
 }
 
@@ -444,23 +436,44 @@ static moe_status geometry(FfnArgs &a, int maxt, int cols, int bits, size_t &lds
     return MOE_OK;
 }
 
+// The 4-bit multi-token kernels (batch.hip), when their LDS fits; rows_per_wg
+// covers `passes` row passes of a workgroup.
+static KernelFn batch_geometry(FfnArgs &a, int cols, int bits, int nr, int passes, KernelFn k, size_t &lds) {
+    if (bits != 4 || !k) return nullptr;
+    lds = batch_lds_bytes(cols);
+    if (lds > kLdsBudget) return nullptr;
+    a.lr_shift = pick_lr_shift(cols / 32);
+    a.rows_per_wg = passes * 4 * (kWave >> a.lr_shift) * nr;
+    a.tpp = kBatchTok;
+    return k;
+}
+
 static moe_status launch_a(Plan &p) {
-    KernelFn k = select_gate_up(p.a.gate.bits_, p.a.gate.sb_, p.a.x_dt, p.maxt > 1);
-    if (!k) return MOE_EUNSUPPORTED;
-    size_t lds;
-    const moe_status st = geometry(p.a, p.maxt, p.a.d_in, p.a.gate.bits_, lds);
-    if (st != MOE_OK) return st;
+    size_t lds = 0;
+    KernelFn k = nullptr;
+    if (p.maxt > 1 && p.a.x_dt == MOE_BF16)
+        k = batch_geometry(p.a, p.a.d_in, p.a.gate.bits_, kBatchNRA, 2, batch_gate_up_q4(p.a.gate.sb_), lds);
+    if (!k) {
+        k = select_gate_up(p.a.gate.bits_, p.a.gate.sb_, p.a.x_dt, p.maxt > 1);
+        if (!k) return MOE_EUNSUPPORTED;
+        const moe_status st = geometry(p.a, p.maxt, p.a.d_in, p.a.gate.bits_, lds);
+        if (st != MOE_OK) return st;
+    }
     dim3 grid((p.a.d_ff + p.a.rows_per_wg - 1) / p.a.rows_per_wg, p.n_items);
     hipLaunchKernelGGL(k, grid, dim3(256), lds, p.s, p.a);
     return MOE_OK;
 }
 
 static moe_status launch_b(Plan &p) {
-    KernelFn k = select_down(p.a.down.bits_, p.a.down.sb_, p.maxt > 1);
-    if (!k) return MOE_EUNSUPPORTED;
-    size_t lds;
-    const moe_status st = geometry(p.a, p.maxt, p.a.d_ff, p.a.down.bits_, lds);
-    if (st != MOE_OK) return st;
+    size_t lds = 0;
+    KernelFn k = nullptr;
+    if (p.maxt > 1) k = batch_geometry(p.a, p.a.d_ff, p.a.down.bits_, kBatchNRB, 1, batch_down_q4(p.a.down.sb_), lds);
+    if (!k) {
+        k = select_down(p.a.down.bits_, p.a.down.sb_, p.maxt > 1);
+        if (!k) return MOE_EUNSUPPORTED;
+        const moe_status st = geometry(p.a, p.maxt, p.a.d_ff, p.a.down.bits_, lds);
+        if (st != MOE_OK) return st;
+    }
     dim3 grid((p.a.d_in + p.a.rows_per_wg - 1) / p.a.rows_per_wg, p.n_items);
     hipLaunchKernelGGL(k, grid, dim3(256), lds, p.s, p.a);
     return MOE_OK;

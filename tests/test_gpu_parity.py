@@ -103,6 +103,20 @@ def test_full_size_layers(name, layers, T):
             compare_layer(cfg, w, x, resid, gpu, f"{name} L{li} T={T}")
 
 
+@pytest.mark.parametrize("kw", [dict(), dict(bits_gate_up=8, bits_down=8),
+                                dict(x_dtype=mi.F16, router_dtype=mi.F16, resid_dtype=mi.F16),
+                                dict(d_in=4096, d_ff=1408)],
+                         ids=["q4-bf16", "q8", "q4-f16x", "wide"])
+def test_many_tokens_per_expert(kw):
+    """32 tokens over 4 experts: each expert's token list is cut into several work items."""
+    cfg = small_cfg(n_experts=4, top_k=2, **kw)
+    say(f"case 32 tokens over 4 experts {kw}")
+    w = mi.gen_layer_weights(cfg, 6, threads=8)
+    x, resid = margin_tokens(cfg, 6, w, 32)
+    gpu, _ = run_gpu_layer(cfg, w, x, resid, graph=True)
+    compare_layer(cfg, w, x, resid, gpu, f"32 tokens over 4 experts {kw}")
+
+
 # ------------------------------------------------------------- edge cases
 def test_out_of_range_ids_give_zero_rows():
     from quantized_moe_decode_amd.layer import layer_from_host, tensor_from_encoded
