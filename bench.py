@@ -140,6 +140,8 @@ def parse():
                     help="write the counter record from two rocprofv3 --pmc counter_collection.csv "
                          "files (FETCH_SIZE, WRITE_SIZE of a --profile-run) and exit")
     ap.add_argument("--counters-command", default="", help="the profiler command, for the record")
+    ap.add_argument("--ws", choices=("shared", "per-layer"), default="shared",
+                    help="fused path: one workspace for all layers of a step (default) or one per layer")
     ap.add_argument("--path", choices=("fused", "three-call"), default=None,
                     help="fused single-launch layer (default for one token per step) or "
                          "route + expert FFN + tail (default for several tokens per step)")
@@ -165,7 +167,7 @@ def main():
     import torch
     import moe_inputs as mi
     import quantized_moe_decode_amd as qmd
-    from quantized_moe_decode_amd.layer import layer_from_host, tensor_from_encoded
+    from quantized_moe_decode_amd.layer import layer_from_host, share_fused_workspace, tensor_from_encoded
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -202,6 +204,8 @@ def main():
             xs[r][li] = tensor_from_encoded(x, cfg.x_dtype, dev)
             rs[r][li] = tensor_from_encoded(rd, cfg.resid_dtype, dev)
     outs = [torch.zeros(T, cfg.d_in, device=dev) for _ in range(L)]
+    if args.ws == "shared":
+        share_fused_workspace(layers)
     torch.cuda.synchronize()
 
     path = args.path or ("fused" if T == 1 else "three-call")

@@ -15,9 +15,9 @@
 //   [.., + B units)           one (slot, row tile of d_in) of kernel B each
 // A and B units of routed slots wait for every router logit and then rank
 // them themselves, so each knows the selected experts without another round
-// trip.  B units issue the loads of their first weight chunks before they
-// wait for their slot's act vector, so the down-projection weights stream
-// while kernel A runs.  The B unit of the last slot of each row tile (the
+// trip.  B units issue the loads of their weights before they wait for their
+// slot's act vector, so the down-projection weights stream while kernel A
+// runs.  The B unit of the last slot of each row tile (the
 // highest block index of that tile) keeps its own partial rows in LDS, waits
 // for the other slots' rows and runs the tail: it sums them in slot order
 // and writes the output.
@@ -220,7 +220,10 @@ struct Selection {
     int ids[MOE_MAX_TOP_K];
     float scores[MOE_MAX_TOP_K];
     float gate;
-    uint32_t n_hit, hit_mask;       // rank-count bookkeeping, zeroed before the logits arrive
+    uint32_t n_over;                                  // a first-round wave had too many candidates
+    __align__(16) uint64_t cand[kWave / 2];           // their (logit, id) keys, zero-padded
+    __align__(16) uint32_t cand_key[MOE_MAX_TOP_K];   // the one-wave path's selected keys and ids
+    int cand_id[MOE_MAX_TOP_K];                       // in id order, before ranking
 };
 
 template <int N>
@@ -228,47 +231,114 @@ struct IntC {
     static constexpr int value = N;
 };
 
-// Dispatch on the number of logits per lane of a one-wave pass over E logits.
+// Dispatch on the number of logit words per lane of a one-wave pass over E
+// logits: two for up to 128 experts, else sixteen (the largest count); words
+// past E hold nothing.  Two instantiations keep the kernel's code small.
 template <typename Fn>
 __device__ __forceinline__ void with_per(int E, Fn fn) {
-    const int per = (E + kWave - 1) / kWave;
-    if (per <= 1) fn(IntC<1>{});
-    else if (per <= 2) fn(IntC<2>{});
-    else if (per <= 4) fn(IntC<4>{});
-    else if (per <= 8) fn(IntC<8>{});
-    else fn(IntC<16>{});
+    if (E <= 2 * kWave) fn(IntC<2>{});
+    else fn(IntC<MOE_MAX_EXPERTS / kWave>{});
 }
 
-// Exact top-k in one wave, PER logits per lane (expert lane + 64*i in l[i]):
-// K rounds of "largest untaken logit" (a DPP wave maximum), each taking the
-// lowest expert id that holds that value, i.e. descending logit with ties to
-// the lower id.  Lane k writes the k-th id.
+// Order-preserving image of an fp32 logit as an unsigned key (larger logit,
+// larger key); -0 maps to the key of +0 so that equal values tie.
+__device__ __forceinline__ uint32_t logit_key(float v) {
+    const uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Number of keys >= c over the wave's PER key words (one ballot per word).
 template <int PER>
-__device__ void topk_rounds(const float *s_logits, int E, int K, int lane, Selection *sel) {
-    float l[PER];
-    uint32_t taken = 0;
+__device__ __forceinline__ int count_ge(const uint32_t *key, uint32_t c) {
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) n += __popcll(__ballot(key[i] >= c));
+    return n;
+}
+
+// Exact top-k in one wave, PER logits per lane (expert lane + 64*i in key i):
+// descending logit, ties to the lower expert id.  It serves ties and large
+// expert counts; its cost is one wave's serial instruction stream.
+//  1. A threshold t with at least K keys >= t, raised two bits at a time from
+//     the top: of the three candidates that set the next two bits, the largest
+//     one that still has K keys at or above it is kept (three independent
+//     ballot counts per step).  The search stops as soon as exactly K keys are
+//     >= t, which the gap between the K-th and (K+1)-th logit usually allows
+//     after a dozen bits; otherwise it ends with t equal to the K-th key.
+//  2. The selection: every key above t, plus the lowest-id keys equal to t
+//     until there are K.
+//  3. The K selected (key, id) pairs are packed in id order into LDS, and the
+//     first K lanes rank one pair each against all of them: larger keys, and
+//     equal keys of lower id, come first.  Rank r stores its id in ids[r].
+template <int PER>
+__device__ __forceinline__ void topk_radix(const float *s_logits, int E, int K, int lane, Selection *sel) {
+    uint32_t key[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = lane + i * kWave;
-        l[i] = e < E ? s_logits[e] : -INFINITY;
-        if (e >= E) taken |= 1u << i;
+        key[i] = e < E ? logit_key(s_logits[e]) : 0u;    // 0 is below every finite logit's key
     }
-    int my_id = -1;
-    for (int k = 0; k < K; ++k) {
-        float best = -INFINITY;
+    uint32_t t = 0;
+    for (int b = 30; b >= 0; b -= 2) {
+        const uint32_t c1 = t | (1u << b), c2 = t | (2u << b), c3 = t | (3u << b);
+        const int n1 = count_ge<PER>(key, c1), n2 = count_ge<PER>(key, c2), n3 = count_ge<PER>(key, c3);
+        int n;
+        if (n3 >= K) { t = c3; n = n3; }
+        else if (n2 >= K) { t = c2; n = n2; }
+        else if (n1 >= K) { t = c1; n = n1; }
+        else n = K + 1;
+        if (n == K) break;
+    }
+    int need = K;
+    uint64_t selm[PER];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) best = ((taken >> i) & 1u) ? best : fmaxf(best, l[i]);
-        const float m = wave_max(best);
-        int e = -1;
+    for (int i = 0; i < PER; ++i) {
+        selm[i] = __ballot(key[i] > t);
+        need -= __popcll(selm[i]);
+    }
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const uint64_t hit = __ballot(!((taken >> i) & 1u) && l[i] == m);
-            if (e < 0 && hit) e = i * kWave + (int)__ffsll((unsigned long long)hit) - 1;
+    for (int i = 0; i < PER; ++i) {             // keys equal to t: lowest ids first
+        uint64_t eq = __ballot(key[i] == t);
+        const int c = __popcll(eq);
+        if (c <= need) {
+            selm[i] |= eq;
+            need -= c;
+        } else {
+            for (; need > 0; --need) {
+                selm[i] |= eq & (~eq + 1);      // lowest remaining set bit
+                eq &= eq - 1;
+            }
         }
-        if (lane == k) my_id = e;
-        if ((e & (kWave - 1)) == lane) taken |= 1u << ((e / kWave) & 31);
     }
-    if (lane < K) sel->ids[lane] = my_id;
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        if ((selm[i] >> lane) & 1u) {
+            const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(selm[i] >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)selm[i], 0u));
+            sel->cand_key[pos] = key[i];
+            sel->cand_id[pos] = lane + i * kWave;
+        }
+        base += __popcll(selm[i]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < K) {
+        const uint32_t kt = sel->cand_key[lane];
+        const uint4 *ck = reinterpret_cast<const uint4 *>(sel->cand_key);
+        int rank = 0;
+        for (int u0 = 0; u0 < K; u0 += 4) {
+            const uint4 v = ck[u0 >> 2];
+            const uint32_t kv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int u = u0 + q;
+                rank += (u < K && (kv[q] > kt || (kv[q] == kt && u < lane))) ? 1 : 0;
+            }
+        }
+        sel->ids[rank] = sel->cand_id[lane];
+    }
 }
 
 // Softmax over all E logits in one wave, then the selected ranks'
@@ -288,51 +358,73 @@ __device__ void softmax_scores(const LayerArgs &a, const float *s_logits, int la
     if (lane < a.K) sel->scores[lane] = a.renorm ? p / psum : p;
 }
 
-constexpr int kRankMaxE = 128;      // the block-wide rank count handles E up to this
+constexpr int kRankMaxE = 2 * kWave;    // the two-round selection handles E up to this
+constexpr int kCandMax = kWave / 2;     // candidates the second round ranks
+constexpr int kCandPerWave = kCandMax / 4;
 
-// All K ids at once.  For E <= kRankMaxE every thread of the block takes
-// part: thread t holds logit i = t / 2 and counts the larger logits in its
-// half of the list, and the two halves meet with a lane swap, so the count is
-// i's rank under "descending logit".  Rank r < K stores id i in ids[r].
-// Equal logits would share a rank, which shows as stored ranks other than
-// exactly 0..K-1; then (and for larger E) the exact wave rounds decide.
-// s_logits must be padded with -inf to a multiple of 8 entries and
-// n_hit/hit_mask zeroed before the preceding barrier.
-__device__ void select_all(const LayerArgs &a, const float *s_logits, Selection *sel) {
+// All K ids, in rank order, in sel->ids.  The vector work of one selection
+// is shared by every workgroup on the CU that selects at the same moment, so
+// the fast path keeps it small and spread over all four waves:
+//  1. wave w ranks logits 32w..32w+31 among themselves (two lanes per logit,
+//     sixteen comparisons each: the sign of l_i - l_j, exact for finite
+//     values once -0 is stored as +0).  A logit with fewer than K larger ones
+//     in its group is a candidate; every true top-K logit is one.
+//  2. if no group has more than 8 candidates (K <= 8 without ties at a
+//     group's cut), wave 0 ranks the (at most 32) candidates by the key
+//     (logit, then lower id first), unique per expert, and rank r < K stores
+//     its id in ids[r].
+// Otherwise (more experts, larger K, ties at the cut), the exact one-wave
+// selection decides.  s_logits must hold -0 as +0 and be padded with -inf to
+// kRankMaxE entries; n_over and cand[] must be zeroed before the preceding
+// barrier.
+__device__ __forceinline__ void select_all(const LayerArgs &a, const float *s_logits, Selection *sel) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     bool exact = false;
     if (a.E <= kRankMaxE) {
-        const int i = tid >> 1, h = tid & 1;
-        const int half = ((a.E + 7) >> 3) << 2;
-        const bool live = i < a.E;
-        const float li = live ? s_logits[i] : 0.f;
-        const f32x4 *row = reinterpret_cast<const f32x4 *>(s_logits + h * half);
-        const int nq = half >> 2;
-        int cnt = 0;
-        for (int q0 = 0; q0 < nq; q0 += 8) {        // eight LDS reads in flight per step
-            f32x4 v[8];
+        const int i = 32 * wave + (lane >> 1), h = lane & 1;
+        const float li = s_logits[i];
+        const f32x4 *row = reinterpret_cast<const f32x4 *>(s_logits + 32 * wave + 16 * h);
+        f32x4 v[4];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = row[min(q0 + u, nq - 1)];
+        for (int u = 0; u < 4; ++u) v[u] = row[u];
+        uint32_t c4[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int c = (v[u].x > li ? 1 : 0) + (v[u].y > li ? 1 : 0) + (v[u].z > li ? 1 : 0) +
-                              (v[u].w > li ? 1 : 0);
-                cnt += q0 + u < nq ? c : 0;
-            }
+        for (int u = 0; u < 4; ++u) {                   // l_j > l_i  <=>  l_i - l_j < 0
+            c4[0] += __float_as_uint(li - v[u].x) >> 31;
+            c4[1] += __float_as_uint(li - v[u].y) >> 31;
+            c4[2] += __float_as_uint(li - v[u].z) >> 31;
+            c4[3] += __float_as_uint(li - v[u].w) >> 31;
         }
+        int cnt = (int)(c4[0] + c4[1] + c4[2] + c4[3]);
         cnt += __builtin_amdgcn_mov_dpp(cnt, 0xB1, 0xf, 0xf, false);    // quad_perm [1,0,3,2]
-        if (h == 0 && live && cnt < a.K) {
-            sel->ids[cnt] = i;
-            atomicAdd(&sel->n_hit, 1u);
-            atomicOr(&sel->hit_mask, 1u << cnt);
-        }
+        const bool is_cand = h == 0 && i < a.E && cnt < a.K;
+        const uint64_t bal = __ballot(is_cand);
+        // wave w owns candidate places 8w..8w+7; a wave with more candidates
+        // (K > 8, or ties) sends the selection to the exact path
+        const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        if (is_cand && pos < kCandPerWave)
+            sel->cand[kCandPerWave * wave + pos] = ((uint64_t)logit_key(li) << 32) | (0xFFFFFFFFu - (uint32_t)i);
+        if (lane == 0 && __popcll(bal) > kCandPerWave) sel->n_over = 1;
         __syncthreads();
-        const uint32_t full = a.K >= 32 ? 0xffffffffu : (1u << a.K) - 1u;
-        exact = sel->n_hit == (uint32_t)a.K && sel->hit_mask == full;
+        if (sel->n_over == 0) {
+            if (wave == 0) {
+                const int c = lane >> 1, hh = lane & 1;
+                const uint64_t kc = sel->cand[c];           // 0 past the last candidate
+                const uint64_t *cr = sel->cand + 16 * hh;
+                int r = 0;
+#pragma unroll
+                for (int u = 0; u < 16; ++u) r += cr[u] > kc ? 1 : 0;
+                r += __builtin_amdgcn_mov_dpp(r, 0xB1, 0xf, 0xf, false);
+                if (hh == 0 && kc != 0 && r < a.K) sel->ids[r] = (int)(0xFFFFFFFFu - (uint32_t)kc);
+            }
+            __syncthreads();
+            exact = true;
+        }
     }
     if (!exact) {
         if (wave == 0)
-            with_per(a.E, [&](auto per) { topk_rounds<decltype(per)::value>(s_logits, a.E, a.K, lane, sel); });
+            with_per(a.E, [&](auto per) { topk_radix<decltype(per)::value>(s_logits, a.E, a.K, lane, sel); });
         __syncthreads();
     }
 }
@@ -349,13 +441,13 @@ __device__ void gather_logits(const LayerArgs &a, uint32_t tag, float *s_logits,
     const int n = a.E + (a.wg ? 1 : 0);
     if (threadIdx.x == 0) {
         if (!a.wg) sel->gate = 1.0f;
-        sel->n_hit = 0;
-        sel->hit_mask = 0;
+        sel->n_over = 0;
     }
-    for (int e = a.E + threadIdx.x; e < ((a.E + 7) & ~7); e += blockDim.x) s_logits[e] = -INFINITY;
+    if (threadIdx.x < kCandMax) sel->cand[threadIdx.x] = 0;
+    for (int e = a.E + threadIdx.x; e < kRankMaxE; e += blockDim.x) s_logits[e] = -INFINITY;
     const uint64_t *lg = my_logits(a);
     gather_tagged<kLogitSleep>(a, n, lg + n - 1, tag, [&](int i) { return lg + i; }, [&](int e, float v) {
-        if (e < a.E) s_logits[e] = v;
+        if (e < a.E) s_logits[e] = v == 0.f ? 0.f : v;      // -0 as +0
         else sel->gate = sigmoidf_(v);
     });
     __syncthreads();
@@ -371,26 +463,14 @@ __device__ __forceinline__ void store_act_sentinel(const LayerArgs &a, int slot,
     for (int c = 0; c < kActCopies; ++c) st_tagged(p + c * kSentStride, v, tag);
 }
 
-// Kernel A unit: rows [row0, row0 + a_tile) of slot `slot`.
+// Kernel A unit: rows [row0, row0 + a_tile) of slot `slot`, expert e (x
+// already staged in LDS).
 template <int BA, int SB, int XT>
-__device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int tile, float *s_logits,
-                             Selection *sel, void *xs) {
+__device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int tile, int e, void *xs) {
     constexpr int NR = kLayerNRA;
     using F = Fmt<BA>;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const bool routed = slot < a.K;
-    // x into LDS while the logits are on their way: the weight stream then
-    // shares the memory pipeline with nothing else
-    stage_x_raw<XT, F::kCodes>(a.x, a.d_in / F::kCodes, xs);
-    int e;
-    if (routed) {
-        gather_logits(a, tag, s_logits, sel);
-        select_all(a, s_logits, sel);
-        e = sel->ids[slot];
-    } else {
-        e = slot - a.K;
-        __syncthreads();
-    }
     const int dff = routed ? a.d_ff : a.d_ffs;
     const int E = routed ? a.E : a.S;
     const int row0 = tile * a.a_tile;
@@ -472,22 +552,14 @@ __device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int til
 // Kernel B unit: rows [row0, row0 + b_tile) of d_in for slot `slot`.  The
 // unit of the last slot also runs the tail for those rows.
 template <int BB, int SB>
-__device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int tile, float *s_logits,
+__device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int tile, int e, float *s_logits,
                              Selection *sel, float *xs) {
     constexpr int NR = kLayerNRB;
     using F = Fmt<BB>;
     constexpr int CODES = F::kCodes;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const bool routed = slot < a.K;
-    int e;
     float score = 1.0f;
-    if (routed) {            // every unit ranks the logits itself: no extra hand-off
-        gather_logits(a, tag, s_logits, sel);
-        select_all(a, s_logits, sel);
-        e = sel->ids[slot];
-    } else {
-        e = slot - a.K;
-    }
     const int dff = routed ? a.d_ff : a.d_ffs;
     const int E = routed ? a.E : a.S;
     const int row0 = tile * a.b_tile;
@@ -655,21 +727,35 @@ __global__ __launch_bounds__(256, 3) void layer_kernel(LayerArgs a) {
     const uint32_t tag = s_tag;
     b -= a.n_route;
     const int n_a = a.K * a.a_tiles_r + a.S * a.a_tiles_s;
-    if (b < n_a) {
-        int slot, tile;
-        if (b < a.K * a.a_tiles_r) {
-            slot = b / a.a_tiles_r;
-            tile = b % a.a_tiles_r;
-        } else {
-            const int bs = b - a.K * a.a_tiles_r;
-            slot = a.K + bs / a.a_tiles_s;
-            tile = bs % a.a_tiles_s;
-        }
-        layer_a_unit<BA, SB, XT>(a, tag, slot, tile, s_logits, &sel, xs);
-    } else {
+    const bool is_a = b < n_a;
+    int slot, tile;
+    if (!is_a) {
         b -= n_a;
-        layer_b_unit<BB, SB>(a, tag, b / a.b_tiles, b % a.b_tiles, s_logits, &sel, xs);
+        slot = b / a.b_tiles;
+        tile = b % a.b_tiles;
+    } else if (b < a.K * a.a_tiles_r) {
+        slot = b / a.a_tiles_r;
+        tile = b % a.a_tiles_r;
+    } else {
+        const int bs = b - a.K * a.a_tiles_r;
+        slot = a.K + bs / a.a_tiles_s;
+        tile = bs % a.a_tiles_s;
     }
+    // kernel-A units stage x in LDS while the logits are on their way: the
+    // weight stream then shares the memory pipeline with nothing else
+    if (is_a) stage_x_raw<XT, Fmt<BA>::kCodes>(a.x, a.d_in / Fmt<BA>::kCodes, xs);
+    // routed units rank the logits themselves (one copy of this code for both
+    // roles): no extra hand-off
+    int e = slot - a.K;
+    if (slot < a.K) {
+        gather_logits(a, tag, s_logits, &sel);
+        select_all(a, s_logits, &sel);
+        e = sel.ids[slot];
+    } else {
+        __syncthreads();
+    }
+    if (is_a) layer_a_unit<BA, SB, XT>(a, tag, slot, tile, e, xs);
+    else layer_b_unit<BB, SB>(a, tag, slot, tile, e, s_logits, &sel, xs);
 }
 
 using LayerFn = void (*)(LayerArgs);

@@ -120,6 +120,22 @@ class DecodeLayer:
         return n
 
 
+def share_fused_workspace(layers: Sequence[DecodeLayer]) -> Optional[torch.Tensor]:
+    """Give every layer the same fused-launch workspace (one zeroed buffer of the
+    largest size).  Valid for layers whose launches run in order on one stream,
+    as the layers of a decode step do: each launch leaves the workspace ready
+    for the next.  A workspace that stays the same buffer stays cache-resident
+    from one layer to the next."""
+    sizes = [l.fused_ws.numel() for l in layers if l.fused_ws is not None]
+    if not sizes:
+        return None
+    ws = torch.zeros(max(sizes), device=layers[0].router.device, dtype=torch.uint8)
+    for l in layers:
+        if l.fused_ws is not None:
+            l.fused_ws = ws
+    return ws
+
+
 def layer_from_host(cfg, weights: dict, device, n_tokens: Optional[int] = None) -> DecodeLayer:
     """Build a DecodeLayer from host weights in the generator's layout."""
     router = tensor_from_encoded(weights["router"], cfg.router_dtype, device)

@@ -135,9 +135,40 @@ def test_fused_tie_prefers_lower_index(top_k, rows, want):
     np.testing.assert_allclose(gpu["scores"], ref["scores"], rtol=1e-5, atol=1e-7)
 
 
+@pytest.mark.parametrize("n_experts,top_k,rows,want", [
+    # ties between ids held in different lane words of the selecting wave (ids 64 apart)
+    (200, 6, {150: 0.05, 3: 0.04, 70: 0.04, 199: 0.03, 66: 0.03, 130: 0.03, 10: 0.02},
+     [150, 3, 70, 66, 130, 199]),
+    # the k-th place split inside a three-way tie spread over three lane words
+    (200, 5, {150: 0.05, 3: 0.04, 70: 0.04, 199: 0.03, 66: 0.03, 130: 0.03, 10: 0.02},
+     [150, 3, 70, 66, 130]),
+    # every logit zero: the lowest ids, in id order
+    (200, 8, {}, list(range(8))),
+    # a negative-only router: the zero logits outrank the negative ones
+    (130, 4, {5: -0.02, 129: -0.01}, [0, 1, 2, 3]),
+], ids=["across-words", "split-at-k", "all-zero", "negatives"])
+def test_fused_ties_many_experts(n_experts, top_k, rows, want):
+    """Exact ties with more experts than one wave has lanes: descending logit, ties to the lower id."""
+    cfg = small_cfg(n_experts=n_experts, top_k=top_k, x_dtype=mi.F32, router_dtype=mi.F32, resid_dtype=mi.F32)
+    say(f"case fused router ties E={n_experts} k={top_k}")
+    w = mi.gen_layer_weights(cfg, 6, threads=8)
+    x, resid = mi.gen_tokens(cfg, 6, 1)
+    wr = np.zeros_like(w["router"])
+    r = x[0].astype(np.float32)
+    for e, c in rows.items():
+        wr[e] = r * np.float32(c)
+    w["router"] = wr
+    gpu, _ = run_gpu_layer(cfg, w, x, resid, fused=True)
+    import oracle
+    ref = oracle.route(x, cfg.x_dtype, w["router"], cfg.router_dtype, top_k, cfg.renormalize)
+    assert ref["ids"].tolist() == [want]
+    assert gpu["ids"].tolist() == [want]
+    np.testing.assert_allclose(gpu["scores"], ref["scores"], rtol=1e-5, atol=1e-7)
+
+
 @pytest.mark.parametrize("n_experts,top_k", [(160, 6), (1000, 8), (64, 32)])
 def test_fused_expert_counts(n_experts, top_k):
-    """Expert counts on both sides of the block-wide rank count's limit, and k = 32."""
+    """Expert counts from one lane word to sixteen in the selecting wave, and k = 32."""
     cfg = small_cfg(n_experts=n_experts, top_k=top_k)
     say(f"case fused E={n_experts} K={top_k}")
     w = mi.gen_layer_weights(cfg, 5, threads=8)
