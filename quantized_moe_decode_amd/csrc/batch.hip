@@ -149,11 +149,11 @@ __global__ __launch_bounds__(256) void gate_up_batch_q4(FfnArgs a) {
                     for (int m = 0; m < 2; ++m)
 #pragma unroll
                         for (int n = 0; n < NR; ++n) {
-                            const uint32_t w = R.w[m][n].w[k];
+                            uint32_t qw[4];
+                            nibble_pairs<0x43u>(R.w[m][n].w[k], qw);
 #pragma unroll
                             for (int p = 0; p < 4; ++p) {
-                                const bf16x2_t q =
-                                    __builtin_bit_cast(bf16x2_t, ((w >> (4 * p)) & 0x000F000Fu) | 0x43004300u);
+                                const bf16x2_t q = __builtin_bit_cast(bf16x2_t, qw[p]);
 #pragma unroll
                                 for (int t = 0; t < NT; ++t)
                                     d[m][n][t] = __builtin_amdgcn_fdot2_f32_bf16(
@@ -268,11 +268,11 @@ __global__ __launch_bounds__(256) void down_batch_q4(FfnArgs a) {
                     }
 #pragma unroll
                     for (int n = 0; n < NR; ++n) {
-                        const uint32_t w = R.w[0][n].w[k];
+                        uint32_t qw[4];
+                        nibble_pairs<0x64u>(R.w[0][n].w[k], qw);
 #pragma unroll
                         for (int p = 0; p < 4; ++p) {
-                            const f16x2_t q =
-                                __builtin_bit_cast(f16x2_t, ((w >> (4 * p)) & 0x000F000Fu) | 0x64006400u) - off;
+                            const f16x2_t q = __builtin_bit_cast(f16x2_t, qw[p]) - off;
 #pragma unroll
                             for (int t = 0; t < NT; ++t)
                                 d[n][t] = __builtin_amdgcn_fdot2(q, __builtin_bit_cast(f16x2_t, xk[t][p]), d[n][t],

@@ -125,9 +125,27 @@ __device__ __forceinline__ void dot_block(const BlockRegs<BITS, NM, NR> &R, cons
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// The four code pairs of a 4-bit word for the packed dot instructions: pair p
+// holds codes p and p + 4 (the nibbles at bits 4p and 16 + 4p) as the low and
+// high 16-bit halves, each MAGIC << 8 | q.  With MAGIC = 0x43 that is the bf16
+// 128 + q, with MAGIC = 0x64 the fp16 1024 + q (both exact).  Masking the even
+// and the odd nibbles once and placing bytes with v_perm costs seven
+// instructions per word, where shift-mask-or per pair costs eleven (this
+// target has no literal operand for a three-input and-or).
+template <uint32_t MAGIC>
+__device__ __forceinline__ void nibble_pairs(uint32_t w, uint32_t (&q)[4]) {
+    constexpr uint32_t kMagic4 = MAGIC * 0x01010101u;
+    const uint32_t lo = w & 0x0F0F0F0Fu;            // byte b: nibble 2b
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;     // byte b: nibble 2b + 1
+    q[0] = __builtin_amdgcn_perm(kMagic4, lo, 0x04020400u);     // nibbles 0, 4
+    q[1] = __builtin_amdgcn_perm(kMagic4, hi, 0x04020400u);     // nibbles 1, 5
+    q[2] = __builtin_amdgcn_perm(kMagic4, lo, 0x04030401u);     // nibbles 2, 6
+    q[3] = __builtin_amdgcn_perm(kMagic4, hi, 0x04030401u);     // nibbles 3, 7
+}
+
 // 4-bit codes against bf16 inputs with the packed dot instruction.  Each
-// code q is turned into the bf16 number 128 + q (exact: 0x4300 | q) with one
-// and-or per pair of codes, and v_dot2 multiplies two such numbers by two
+// code q is turned into the bf16 number 128 + q (exact: 0x4300 | q, by
+// nibble_pairs), and v_dot2 multiplies two such numbers by two
 // bf16 inputs and adds both products (exact in fp32) to the accumulator:
 //     sum_i (s q_i + b) x_i = s * sum_i (128 + q_i) x_i + (b - 128 s) * sum_i x_i.
 // Pair p of word k holds codes (8k+p, 8k+p+4) (nibbles p and p+4), so the
@@ -157,10 +175,11 @@ __device__ __forceinline__ void dot_block_q4_bf16(const BlockRegs<4, NM, NR> &R,
         for (int m = 0; m < NM; ++m)
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
-                const uint32_t w = R.w[m][n].w[k];
+                uint32_t qw[4];
+                nibble_pairs<0x43u>(R.w[m][n].w[k], qw);
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    const uint32_t qp = ((w >> (4 * p)) & 0x000F000Fu) | 0x43004300u;
+                    const uint32_t qp = qw[p];
                     d[m][n] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp),
                                                               __builtin_bit_cast(bf16x2_t, xp[k][p]),
                                                               d[m][n], false);
@@ -238,8 +257,8 @@ __device__ __forceinline__ int f16_pair_offset(int i) {
 }
 
 // 4-bit codes against fp16 inputs with the packed fp16 dot instruction.  A
-// pair of codes becomes the fp16 pair (1024 + q, 1024 + q') with one and-or
-// (0x6400 | q is 1024 + q exactly) and then (q, q') with one packed fp16
+// pair of codes becomes the fp16 pair (1024 + q, 1024 + q') (nibble_pairs:
+// 0x6400 | q is 1024 + q exactly) and then (q, q') with one packed fp16
 // subtraction (exact), so no large offset has to cancel later; v_dot2
 // multiplies it by two fp16 inputs (products exact in fp32) and adds both to
 // the fp32 accumulator.  ap: the chunk's 16 staged pairs; asum: their sum.
@@ -258,11 +277,11 @@ __device__ __forceinline__ void dot_block_q4_f16(const BlockRegs<4, NM, NR> &R, 
         for (int m = 0; m < NM; ++m)
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
-                const uint32_t w = R.w[m][n].w[k];
+                uint32_t qw[4];
+                nibble_pairs<0x64u>(R.w[m][n].w[k], qw);
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    const uint32_t qp = ((w >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
-                    const f16x2_t q = __builtin_bit_cast(f16x2_t, qp) - off;
+                    const f16x2_t q = __builtin_bit_cast(f16x2_t, qw[p]) - off;
                     d[m][n] = __builtin_amdgcn_fdot2(q, __builtin_bit_cast(f16x2_t, ap[4 * k + p]), d[m][n], false);
                 }
             }
