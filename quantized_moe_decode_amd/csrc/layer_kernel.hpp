@@ -600,6 +600,11 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
         // 4-bit down projections take act as fp16 pairs (packed dot); the
         // others as fp32 chunks
         constexpr bool kF16 = BB == 4;
+        // the first stage's codes unpacked while act is on its way: after it
+        // arrives only the dot products remain
+        [[maybe_unused]] uint32_t pre[1][NR][16];
+        if constexpr (kF16)
+            if (n_stage > 0) unpack_q4_f16<1, NR>(cur, pre);
         gather_tagged<kActSleep>(a, n_act, sent, tag, [&](int i) { return act + i; }, [&](int i, float v) {
             const int c = i / CODES;
             if constexpr (kF16)
@@ -629,7 +634,10 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
 #pragma unroll
                     for (int k = 0; k < 4; ++k) ap[4 * i + k] = v[k];
                 }
-                if constexpr (BB == 4) dot_block_q4_f16<SB, 1, NR>(cur, ap, f16_pairs_sum(ap), acc);
+                if constexpr (BB == 4) {
+                    if (st == 0) dot_pre_q4_f16<SB, 1, NR>(cur, pre, ap, f16_pairs_sum(ap), acc);
+                    else dot_block_q4_f16<SB, 1, NR>(cur, ap, f16_pairs_sum(ap), acc);
+                }
             } else {
                 float xv[CODES];
                 read_staged<CODES>(staged_chunk<CODES>(xs, 0, cpr, cur.cc), xv);

@@ -295,6 +295,54 @@ __device__ __forceinline__ void dot_block_q4_f16(const BlockRegs<4, NM, NR> &R, 
         }
 }
 
+// The codes of a 4-bit block as the exact fp16 pairs dot_block_q4_f16 forms,
+// unpacked ahead of their inputs (while those are still on their way):
+// pre[m][n][4k + p] is pair p of word k.
+template <int NM, int NR>
+__device__ __forceinline__ void unpack_q4_f16(const BlockRegs<4, NM, NR> &R, uint32_t (&pre)[NM][NR][16]) {
+    const f16x2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int n = 0; n < NR; ++n)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                uint32_t qw[4];
+                nibble_pairs<0x64u>(R.w[m][n].w[k], qw);
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    pre[m][n][4 * k + p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, qw[p]) - off);
+            }
+}
+
+// dot_block_q4_f16 on codes already unpacked by unpack_q4_f16 (R supplies the
+// scales, biases and row validity).
+template <int SB, int NM, int NR>
+__device__ __forceinline__ void dot_pre_q4_f16(const BlockRegs<4, NM, NR> &R, const uint32_t (&pre)[NM][NR][16],
+                                               const uint32_t *ap, float asum, float (&acc)[NM][NR]) {
+    float d[NM][NR];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int n = 0; n < NR; ++n) d[m][n] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int n = 0; n < NR; ++n)
+                d[m][n] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pre[m][n][i]),
+                                                 __builtin_bit_cast(f16x2_t, ap[i]), d[m][n], false);
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int n = 0; n < NR; ++n) {
+            const float s = R.live[n] ? sb_to_float<SB>(R.sr[m][n]) : 0.f;
+            const float b = R.live[n] ? sb_to_float<SB>(R.br[m][n]) : 0.f;
+            acc[m][n] += s * d[m][n] + b * asum;
+        }
+}
+
 // Sum of a chunk's 16 staged fp16 pairs, in fp32.
 __device__ __forceinline__ float f16_pairs_sum(const uint32_t *ap) {
     const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
