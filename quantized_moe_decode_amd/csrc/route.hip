@@ -6,9 +6,9 @@
 // (one wave per router row, fp32 accumulation over the contraction with a
 // wave64 butterfly reduction).  The router matrix is read once, spread over
 // many CUs.  Logits are published with device-coherent stores and a
-// device-scope counter per token; the last workgroup to arrive selects the
-// top-k from that token's logits (read with device-coherent loads) and
-// computes its scores.  No cache-wide fence is needed: only the logits and
+// device-scope counter per token; the last workgroup to arrive stages that
+// token's logits (device-coherent loads) in LDS, selects the top-k with the
+// whole block (topk.hpp) and computes the scores.  No cache-wide fence is needed: only the logits and
 // the counter cross workgroups.  The last workgroup resets the counter, so
 // the workspace is ready for the next call (and for graph replays).
 #include <hip/hip_runtime.h>
@@ -16,6 +16,7 @@
 
 #include "api.hpp"
 #include "common.hpp"
+#include "topk.hpp"
 
 namespace moe {
 
@@ -115,62 +116,22 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
         s_last = (prev == gridDim.x - 1);
     }
     __syncthreads();
-    if (!s_last || wave != 0) return;
+    if (!s_last) return;
 
-    // Last workgroup of token t: top-k over the E logits in one wave.  Each
-    // lane owns experts lane, lane+64, ... (at most 16 of them).
-    constexpr int kPer = MOE_MAX_EXPERTS / kWave;
-    float mine[kPer];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int e = lane + i * kWave;
-        mine[i] = (e < a.E) ? __hip_atomic_load(logits + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                            : -INFINITY;
-    }
-    int my_id = -1;           // lane k keeps the k-th selection
-    float my_logit = 0.f, mx = 0.f;
-    for (int k = 0; k < a.K; ++k) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int e = lane + i * kWave;
-            if (e < a.E && !((taken >> i) & 1u) && (mine[i] > bv || (mine[i] == bv && e < bi))) {
-                bv = mine[i];
-                bi = e;
-            }
-        }
-        // wave argmax: larger logit wins, ties go to the lower index
-#pragma unroll
-        for (int m = 32; m > 0; m >>= 1) {
-            const float ov = __shfl_xor(bv, m, kWave);
-            const int oi = __shfl_xor(bi, m, kWave);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if (k == 0) mx = bv;
-        if (lane == k) {
-            my_id = bi;
-            my_logit = bv;
-        }
-        if ((bi & (kWave - 1)) == lane) taken |= 1u << ((bi / kWave) & 31);
-    }
-    // softmax over all experts, max-subtracted (the maximum is the first selection)
-    float z = 0.f;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int e = lane + i * kWave;
-        if (e < a.E) z += expf(mine[i] - mx);
-    }
-    z = wave_sum(z);
-    const float p = (lane < a.K) ? expf(my_logit - mx) / z : 0.f;
-    const float psum = wave_sum(p);
+    // Last workgroup of token t: its logits into LDS (device-coherent loads),
+    // then the block-wide top-k and, in one wave, the softmax scores.
+    __shared__ __align__(16) float s_logits[MOE_MAX_EXPERTS];
+    __shared__ Selection sel;
+    stage_logits(a.E, s_logits, &sel, [&](int e) {
+        return __hip_atomic_load(logits + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    });
+    __syncthreads();
+    select_all(a.E, a.K, s_logits, &sel);
+    if (wave != 0) return;
+    with_per(a.E, [&](auto per) { softmax_scores<decltype(per)::value>(a.E, a.K, a.renorm, s_logits, lane, &sel); });
     if (lane < a.K) {
-        a.ids[t * a.K + lane] = my_id;
-        a.scores[t * a.K + lane] = a.renorm ? p / psum : p;
+        a.ids[t * a.K + lane] = sel.ids[lane];
+        a.scores[t * a.K + lane] = sel.scores[lane];
     }
     if (lane == 0) {
         if (a.wg) {
