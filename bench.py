@@ -50,8 +50,9 @@ COPY_KERNEL = "MulFunctor"
 
 # the files the fused layer kernel is built from (sources, public header, flags)
 LAYER_KERNEL_FILES = ["quantized_moe_decode_amd/csrc/" + f for f in
-                      ("api.hpp", "common.hpp", "qgemv.hpp", "layer_kernel.hpp", "layer.hip",
-                       "layer_a4.hip", "layer_a6.hip", "layer_a8.hip")] + \
+                      ("api.hpp", "common.hpp", "qgemv.hpp", "topk.hpp", "layer_kernel.hpp", "layer.hip",
+                       "layer_a4.hip", "layer_a6.hip", "layer_a8.hip",
+                       "layer_a4p.hip", "layer_a6p.hip", "layer_a8p.hip")] + \
                      ["include/moe_decode.h", "quantized_moe_decode_amd/build.py"]
 
 

@@ -16,6 +16,7 @@ static int lr_shift_for(int cpr) {
 
 struct LayerPlan {
     LayerArgs a;
+    int a_nr;                       // kLayerNRA: kernel-A units of one stage; kLayerNRA2: pipelined stages
     int grid;
     size_t lds;
     size_t ws_bytes;
@@ -128,22 +129,35 @@ static int resident_capacity(LayerFn k, size_t lds) {
     return cus * per_cu;
 }
 
-// Give each kernel-A unit enough row passes that the whole grid fits the
-// resident capacity when possible, so every kernel-B unit can issue its
-// weight loads from the start of the launch.
-static void fit_a_passes(LayerPlan &p, int capacity) {
+// Size the kernel-A units.  A unit is one stage (kLayerNRA rows per lane
+// group at one chunk position) when its rows' inputs fit the lane group and
+// the grid then fits the resident capacity; otherwise units take several
+// row passes of kLayerNRA2 rows, pipelined two stages deep, with enough
+// passes that the grid fits the resident capacity when possible, so every
+// kernel-B unit can issue its weight loads from the start of the launch.
+// cap1, cap2: resident capacity with single-stage and with pipelined units
+// (0 if unknown).
+static void fit_a_passes(LayerPlan &p, int cap1, int cap2) {
     LayerArgs &a = p.a;
     const int slots = a.K + a.S;
     const int n_b = slots * a.b_tiles;
-    const int base_tile = a.a_tile;
     const int dff_s = a.S > 0 ? a.d_ffs : 0;
-    int passes = 1;
-    if (capacity > 0) {
-        const int room = capacity - a.n_route - n_b;
-        for (passes = 1; passes < 8; ++passes) {
-            const int t = base_tile * passes;
-            const int n_a = a.K * ((a.d_ff + t - 1) / t) + a.S * ((dff_s + t - 1) / t);
-            if (room > 0 && n_a <= room) break;
+    const int rpw = 64 >> a.a_lr_shift;
+    auto n_a_for = [&](int t) { return a.K * ((a.d_ff + t - 1) / t) + a.S * ((dff_s + t - 1) / t); };
+    const int cpr = a.d_in / (a.gate.bits_ == 4 ? 32 : 16);
+    const int single = 4 * rpw * kLayerNRA;
+    const int room1 = cap1 - a.n_route - n_b;
+    p.a_nr = kLayerNRA;
+    int base_tile = single, passes = 1;
+    if (cpr > (1 << a.a_lr_shift) || (cap1 > 0 && (room1 <= 0 || n_a_for(single) > room1))) {
+        // several stages per unit: up to 8 row passes, fewer when the grid
+        // then fits the resident capacity (more units stream in parallel)
+        p.a_nr = kLayerNRA2;
+        base_tile = 4 * rpw * kLayerNRA2;
+        const int room2 = cap2 - a.n_route - n_b;
+        if (cap2 > 0) {
+            for (passes = 1; passes < 8; ++passes)
+                if (room2 > 0 && n_a_for(base_tile * passes) <= room2) break;
         }
     }
     a.a_tile = base_tile * passes;
@@ -152,11 +166,12 @@ static void fit_a_passes(LayerPlan &p, int capacity) {
     p.grid = a.n_route + a.K * a.a_tiles_r + a.S * a.a_tiles_s + n_b;
 }
 
-static LayerFn pick_layer(int ba, int bb, int sb, int xt) {
+static LayerFn pick_layer(int ba, int bb, int sb, int xt, int anr) {
+    const bool single = anr == kLayerNRA;
     switch (ba) {
-    case 4: return layer_kernel_a4(bb, sb, xt);
-    case 6: return layer_kernel_a6(bb, sb, xt);
-    case 8: return layer_kernel_a8(bb, sb, xt);
+    case 4: return single ? layer_kernel_a4(bb, sb, xt) : layer_kernel_a4p(bb, sb, xt);
+    case 6: return single ? layer_kernel_a6(bb, sb, xt) : layer_kernel_a6p(bb, sb, xt);
+    case 8: return single ? layer_kernel_a8(bb, sb, xt) : layer_kernel_a8p(bb, sb, xt);
     }
     return nullptr;
 }
@@ -182,9 +197,11 @@ extern "C" moe_status moe_decode_layer(const moe_layer_weights *weights, const v
     if (st != MOE_OK) return st;
     if (weights->w_router_dtype != x_dtype) return MOE_EUNSUPPORTED;
     if (workspace_bytes < p.ws_bytes) return MOE_EINVAL;
-    LayerFn k = pick_layer(weights->gate.bits, weights->down.bits, weights->gate.sb_dtype, x_dtype);
-    if (!k) return MOE_EUNSUPPORTED;
-    fit_a_passes(p, resident_capacity(k, p.lds));
+    LayerFn k1 = pick_layer(weights->gate.bits, weights->down.bits, weights->gate.sb_dtype, x_dtype, kLayerNRA);
+    LayerFn k2 = pick_layer(weights->gate.bits, weights->down.bits, weights->gate.sb_dtype, x_dtype, kLayerNRA2);
+    if (!k1 || !k2) return MOE_EUNSUPPORTED;
+    fit_a_passes(p, resident_capacity(k1, p.lds), resident_capacity(k2, p.lds));
+    LayerFn k = p.a_nr == kLayerNRA ? k1 : k2;
     LayerArgs &a = p.a;
     a.x = x; a.resid = residual; a.resid_dt = residual_dtype; a.out = out;
     a.ids_out = expert_ids; a.scores_out = scores; a.gate_out = shared_gate;

@@ -1,0 +1,6 @@
+// Instantiations of the fused layer kernel (pipelined kernel-A units) with 4-bit gate/up weights.
+#include "layer_kernel.hpp"
+
+namespace moe {
+LayerFn layer_kernel_a4p(int bb, int sb, int xt) { return layer_kernel_pick<4, kLayerNRA2>(bb, sb, xt); }
+}  // namespace moe

@@ -2,5 +2,5 @@
 #include "layer_kernel.hpp"
 
 namespace moe {
-LayerFn layer_kernel_a6(int bb, int sb, int xt) { return layer_kernel_pick<6>(bb, sb, xt); }
+LayerFn layer_kernel_a6(int bb, int sb, int xt) { return layer_kernel_pick<6, kLayerNRA>(bb, sb, xt); }
 }  // namespace moe

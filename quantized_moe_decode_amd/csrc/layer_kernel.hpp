@@ -44,7 +44,8 @@
 
 namespace moe {
 
-constexpr int kLayerNRA = 4;        // rows per lane group, kernel A units
+constexpr int kLayerNRA = 4;        // rows per lane group, kernel A units with a single stage
+constexpr int kLayerNRA2 = 2;       // rows per lane group and stage, kernel A units with several (two in flight)
 constexpr int kLayerNRB = 4;        // rows per lane group, kernel B units
 constexpr int kCtrStride = 64;      // uint32 words between control words (256 bytes)
 constexpr uint32_t kSpinLimit = 1u << 19;
@@ -254,7 +255,7 @@ __device__ __forceinline__ void store_act_sentinel(const LayerArgs &a, int slot,
 // Kernel A unit: rows [row0, row0 + a_tile) of slot `slot`, expert e (x
 // already staged in LDS).
 template <int BA, int SB, int XT>
-__device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int tile, int e, void *xs) {
+__device__ void layer_a_unit_single(const LayerArgs &a, uint32_t tag, int slot, int tile, int e, void *xs) {
     constexpr int NR = kLayerNRA;
     using F = Fmt<BA>;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
@@ -275,7 +276,8 @@ __device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     const int64_t erow0 = (int64_t)e * dff;
     const int cpr = a.d_in / F::kCodes;
     const int lr = 1 << a.a_lr_shift, j = lane & (lr - 1), rsub = lane >> a.a_lr_shift, rpw = kWave >> a.a_lr_shift;
-    // stages = (row pass, chunk position), each loaded and then consumed
+    // stages = (row pass, chunk position), each loaded and then consumed (a
+    // unit of one stage is the common case: nothing to overlap)
     const int rb0 = row0 + wave * rpw * NR, pass_rows = 4 * rpw * NR;
     const int n_pass = rb0 < row_end ? (row_end - rb0 + pass_rows - 1) / pass_rows : 0;
     const int n_chunk = (cpr + lr - 1) / lr;
@@ -333,6 +335,111 @@ __device__ void layer_a_unit(const LayerArgs &a, uint32_t tag, int slot, int til
                     }
                 }
             }
+        }
+    }
+}
+
+// Kernel A unit of several stages, pipelined two deep (same work as
+// layer_a_unit_single, kLayerNRA2 rows per lane group and stage).
+template <int BA, int SB, int XT>
+__device__ void layer_a_unit_pipelined(const LayerArgs &a, uint32_t tag, int slot, int tile, int e, void *xs) {
+    using F = Fmt<BA>;
+    constexpr int NR = kLayerNRA2;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const bool routed = slot < a.K;
+    const int dff = routed ? a.d_ff : a.d_ffs;
+    const int E = routed ? a.E : a.S;
+    const int row0 = tile * a.a_tile;
+    const int row_end = min(row0 + a.a_tile, dff);
+    uint64_t *act = a.act + (int64_t)slot * a.act_stride;
+    if (e < 0 || e >= E) {
+        for (int r = row0 + tid; r < row_end; r += blockDim.x) {
+            st_tagged(act + r, 0.f, tag);
+            if (r == dff - 1) store_act_sentinel(a, slot, 0.f, tag);
+        }
+        return;
+    }
+    const QM mats[2] = {routed ? a.gate : a.sgate, routed ? a.up : a.sup};
+    const int64_t erow0 = (int64_t)e * dff;
+    const int cpr = a.d_in / F::kCodes;
+    const int lr = 1 << a.a_lr_shift, j = lane & (lr - 1), rsub = lane >> a.a_lr_shift, rpw = kWave >> a.a_lr_shift;
+    // stages = (row pass, chunk position).  Two of them live in registers:
+    // the loads of stage st + 1 are in flight while stage st is consumed, so
+    // a unit of several stages streams without a round trip per stage.
+    const int rb0 = row0 + wave * rpw * NR, pass_rows = 4 * rpw * NR;
+    const int n_pass = rb0 < row_end ? (row_end - rb0 + pass_rows - 1) / pass_rows : 0;
+    const int n_chunk = (cpr + lr - 1) / lr;
+    const int n_stage = n_pass * n_chunk;
+    auto stage_row = [&](int st) { return rb0 + (st / n_chunk) * pass_rows + rsub; };
+    auto load = [&](BlockRegs<BA, 2, NR> &R, int st) {
+        load_block<BA, 2, NR>(R, mats, erow0, stage_row(st), rpw, row_end, (st % n_chunk) * lr + j, cpr);
+    };
+    float acc[2][NR];
+    // a stage's inputs: chunk position c of x, staged in LDS
+    auto read_x = [&](XRaw<XT, F::kCodes> &xr, int st) {
+        const int c = (st % n_chunk) * lr + j;
+        read_x_raw<XT, F::kCodes>(xs, c < cpr ? c : 0, xr);
+    };
+    auto consume = [&](const BlockRegs<BA, 2, NR> &cur, const XRaw<XT, F::kCodes> &xr, int st) {
+        const int ch = st % n_chunk;
+        if (ch == 0) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int n = 0; n < NR; ++n) acc[m][n] = 0.f;
+        }
+        if constexpr (BA == 4 && XT == MOE_BF16) {
+            // raw bf16 inputs for the packed-dot path
+            uint32_t xw[16];
+            float xsum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t v = xr.v[i][k];
+                    xw[4 * i + k] = v;
+                    xsum += __uint_as_float(v << 16) + __uint_as_float(v & 0xFFFF0000u);
+                }
+            dot_block_q4_bf16<SB, 2, NR>(cur, xw, xsum, acc);
+        } else {
+            float xv[F::kCodes];
+            convert_x<XT, F::kCodes>(xr, xv);
+            dot_block<BA, SB, 2, NR>(cur, xv, sum_n<F::kCodes>(xv), acc);
+        }
+        if (ch == n_chunk - 1) {
+            with_width(a.a_lr_shift, [&](auto w) {
+#pragma unroll
+                for (int n = 0; n < NR; ++n) {
+                    acc[0][n] = group_sum_last<decltype(w)::value>(acc[0][n]);
+                    acc[1][n] = group_sum_last<decltype(w)::value>(acc[1][n]);
+                }
+            });
+            if (j == lr - 1) {
+                const int r0 = stage_row(st);
+#pragma unroll
+                for (int n = 0; n < NR; ++n) {
+                    const int r = r0 + n * rpw;
+                    if (r < row_end) {
+                        const float g = acc[0][n], u = acc[1][n];
+                        const float v = g * sigmoidf_(g) * u;
+                        st_tagged(act + r, v, tag);
+                        if (r == dff - 1) store_act_sentinel(a, slot, v, tag);
+                    }
+                }
+            }
+        }
+    };
+    BlockRegs<BA, 2, NR> ra, rb;
+    if (n_stage > 0) load(ra, 0);
+    for (int st = 0; st < n_stage; st += 2) {
+        if (st + 1 < n_stage) load(rb, st + 1);
+        XRaw<XT, F::kCodes> xr;
+        read_x(xr, st);
+        consume(ra, xr, st);
+        if (st + 1 < n_stage) {
+            if (st + 2 < n_stage) load(ra, st + 2);
+            read_x(xr, st + 1);
+            consume(rb, xr, st + 1);
         }
     }
 }
@@ -498,7 +605,8 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     }
 }
 
-template <int BA, int BB, int SB, int XT>
+// ANR: kLayerNRA (kernel-A units of one stage) or kLayerNRA2 (pipelined stages).
+template <int BA, int BB, int SB, int XT, int ANR>
 __global__ __launch_bounds__(256, 3) void layer_kernel(LayerArgs a) {
     __shared__ __align__(16) float s_logits[MOE_MAX_EXPERTS];
     __shared__ Selection sel;
@@ -550,21 +658,28 @@ __global__ __launch_bounds__(256, 3) void layer_kernel(LayerArgs a) {
     } else {
         __syncthreads();
     }
-    if (is_a) layer_a_unit<BA, SB, XT>(a, tag, slot, tile, e, xs);
+    if (is_a) {
+        if constexpr (ANR == kLayerNRA) layer_a_unit_single<BA, SB, XT>(a, tag, slot, tile, e, xs);
+        else layer_a_unit_pipelined<BA, SB, XT>(a, tag, slot, tile, e, xs);
+    }
     else layer_b_unit<BB, SB>(a, tag, slot, tile, e, s_logits, &sel, xs);
 }
 
 using LayerFn = void (*)(LayerArgs);
 
-// Instantiation tables, one translation unit per gate/up bit width.
+// Instantiation tables, one translation unit per gate/up bit width and
+// kernel-A unit kind (single stage, pipelined).
 LayerFn layer_kernel_a4(int bb, int sb, int xt);
 LayerFn layer_kernel_a6(int bb, int sb, int xt);
 LayerFn layer_kernel_a8(int bb, int sb, int xt);
+LayerFn layer_kernel_a4p(int bb, int sb, int xt);
+LayerFn layer_kernel_a6p(int bb, int sb, int xt);
+LayerFn layer_kernel_a8p(int bb, int sb, int xt);
 
-template <int BA>
+template <int BA, int ANR>
 LayerFn layer_kernel_pick(int bb, int sb, int xt) {
 #define MOE_L(BB, S, X) \
-    if (bb == BB && sb == S && xt == X) return layer_kernel<BA, BB, S, X>;
+    if (bb == BB && sb == S && xt == X) return layer_kernel<BA, BB, S, X, ANR>;
 #define MOE_LX(BB, S) MOE_L(BB, S, MOE_F32) MOE_L(BB, S, MOE_F16) MOE_L(BB, S, MOE_BF16)
     MOE_LX(4, MOE_BF16) MOE_LX(4, MOE_F16)
     MOE_LX(6, MOE_BF16) MOE_LX(6, MOE_F16)
