@@ -99,10 +99,10 @@ typedef struct {
  *   expert_ids  out int32 [n_tokens][top_k]
  *   scores      out float [n_tokens][top_k]
  *   shared_gate out float [n_tokens]; must be NULL iff w_shared_gate is NULL
- *   workspace   device scratch of at least moe_decode_route_workspace_bytes();
- *               must be zero-filled before its first use and not written by
- *               the caller afterwards: each call leaves it in the state the
- *               next call expects (its per-token completion counters back at
+ *   workspace   device scratch of at least moe_decode_route_workspace_bytes(),
+ *               16-byte aligned; zero-filled before its first use and not
+ *               written by the caller afterwards: each call leaves it in the
+ *               state the next call expects (its flagged logit words back at
  *               zero).  Calls that may run concurrently need separate
  *               workspaces.
  * Limits: 1 <= n_tokens <= 32, 1 <= top_k <= min(n_experts, 32),

@@ -216,47 +216,78 @@ __global__ __launch_bounds__(256) void down_kernel(FfnArgs a) {
 // expert) and cuts each expert's list into work items of at most max_tok
 // pairs.  Work items list the touched experts in ascending id order, then
 // the items (expert -1) collecting every out-of-range id.  One workgroup:
-// histogram by LDS atomics, block scans, and each pair's rank among the
-// earlier pairs of its bucket.
+// histogram by LDS atomics, a block scan, and each pair's rank among the
+// earlier pairs of its bucket.  A token selects an expert at most once, so
+// for in-range buckets that rank is the number of earlier tokens in the
+// bucket's token mask; ids that repeat within a token, and the out-of-range
+// bucket, take the direct count instead.
 constexpr int kBucketThreads = 1024;
 constexpr int kScanMax = 2048;      // entries a block scan handles (E + 2 <= 1026)
 
-// Exclusive prefix sums of v[0..n) in place (n <= kScanMax), using tmp
-// (kScanMax entries) as the other half of a ping-pong Hillis-Steele scan.
-// All threads of the block call it; it ends with a barrier.
-__device__ void block_exclusive_scan(int *v, int *tmp, int n) {
+// Exclusive prefix sums of a[0..n] and b[0..n] together, in place (entry n
+// receives the total; n < kScanMax), by a Hillis-Steele scan over the next
+// power of two above n, ping-ponging with ta/tb (kScanMax entries each).  All
+// threads of the block call it; it ends with a barrier.
+__device__ void block_exclusive_scan2(int *a, int *b, int *ta, int *tb, int n) {
     const int tid = threadIdx.x;
-    for (int i = tid; i < kScanMax; i += blockDim.x) tmp[i] = (i >= 1 && i <= n) ? v[i - 1] : 0;
-    __syncthreads();
-    int *src = tmp, *dst = v;
-    for (int d = 1; d < kScanMax; d <<= 1) {
-        for (int i = tid; i < kScanMax; i += blockDim.x) dst[i] = src[i] + (i >= d ? src[i - d] : 0);
-        __syncthreads();
-        int *t = src;
-        src = dst;
-        dst = t;
+    int m = 1;
+    while (m < n + 1) m <<= 1;
+    for (int i = tid; i < m; i += blockDim.x) {
+        const bool in = i >= 1 && i <= n;
+        ta[i] = in ? a[i - 1] : 0;
+        tb[i] = in ? b[i - 1] : 0;
     }
-    if (src != v)
-        for (int i = tid; i < kScanMax; i += blockDim.x) v[i] = src[i];
+    __syncthreads();
+    int *sa = ta, *sb = tb, *da = a, *db = b;
+    for (int d = 1; d < m; d <<= 1) {
+        for (int i = tid; i < m; i += blockDim.x) {
+            da[i] = sa[i] + (i >= d ? sa[i - d] : 0);
+            db[i] = sb[i] + (i >= d ? sb[i - d] : 0);
+        }
+        __syncthreads();
+        int *t = sa;
+        sa = da;
+        da = t;
+        t = sb;
+        sb = db;
+        db = t;
+    }
+    if (sa != a)
+        for (int i = tid; i < m; i += blockDim.x) {
+            a[i] = sa[i];
+            b[i] = sb[i];
+        }
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t *ids, int n_pairs, int E, int max_tok,
-                                                                int32_t *work_expert, int32_t *work_begin,
-                                                                int32_t *pair_list, int32_t *n_work) {
+__global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t *ids, int n_pairs, int top_k, int E,
+                                                                int max_tok, int32_t *work_expert,
+                                                                int32_t *work_begin, int32_t *pair_list,
+                                                                int32_t *n_work) {
     __shared__ int off[kScanMax];       // pairs, then first pair, per bucket (bucket E: out-of-range ids)
     __shared__ int ioff[kScanMax];      // work items, then first work item, per bucket
-    __shared__ int tmp[kScanMax];
+    __shared__ int tmp[kScanMax], tmp2[kScanMax];
     __shared__ int cnt[MOE_MAX_EXPERTS + 1];
-    __shared__ int bucket[MOE_MAX_TOKENS * MOE_MAX_TOP_K];
+    __shared__ uint32_t tmask[MOE_MAX_EXPERTS + 1];     // tokens with a pair in the bucket
+    __shared__ __align__(16) int bucket[MOE_MAX_TOKENS * MOE_MAX_TOP_K];
+    __shared__ int s_repeat;
+    static_assert(MOE_MAX_TOKENS <= 32, "one mask bit per token");
     const int tid = threadIdx.x, nb = E + 1;
-    for (int i = tid; i < nb; i += blockDim.x) cnt[i] = 0;
+    for (int i = tid; i < nb; i += blockDim.x) {
+        cnt[i] = 0;
+        tmask[i] = 0;
+    }
+    if (tid == 0) s_repeat = 0;
     __syncthreads();
     for (int p = tid; p < n_pairs; p += blockDim.x) {
         const int e = ids[p];
         const int b = (e >= 0 && e < E) ? e : E;
         bucket[p] = b;
         atomicAdd(&cnt[b], 1);
+        if (b < E) {
+            const uint32_t bit = 1u << (p / top_k);
+            if (atomicOr(&tmask[b], bit) & bit) s_repeat = 1;
+        }
     }
     __syncthreads();
     for (int i = tid; i < nb; i += blockDim.x) {
@@ -264,12 +295,23 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t *i
         ioff[i] = (cnt[i] + max_tok - 1) / max_tok;
     }
     __syncthreads();
-    block_exclusive_scan(off, tmp, nb);     // off[nb] = n_pairs
-    block_exclusive_scan(ioff, tmp, nb);    // ioff[nb] = number of work items
+    block_exclusive_scan2(off, ioff, tmp, tmp2, nb);    // off[nb] = n_pairs, ioff[nb] = work items
+    // a pair's rank among the earlier pairs of its bucket
+    const int4 *b4 = reinterpret_cast<const int4 *>(bucket);
+    const bool repeat = s_repeat != 0;
     for (int p = tid; p < n_pairs; p += blockDim.x) {
         const int b = bucket[p];
         int r = 0;
-        for (int q = 0; q < p; ++q) r += bucket[q] == b ? 1 : 0;
+        if (b < E && !repeat) {
+            r = __popc(tmask[b] & ((1u << (p / top_k)) - 1u));
+        } else {    // direct count, 16-byte LDS reads
+            int q = 0;
+            for (; q + 4 <= p; q += 4) {
+                const int4 v = b4[q >> 2];
+                r += (v.x == b ? 1 : 0) + (v.y == b ? 1 : 0) + (v.z == b ? 1 : 0) + (v.w == b ? 1 : 0);
+            }
+            for (; q < p; ++q) r += bucket[q] == b ? 1 : 0;
+        }
         pair_list[off[b] + r] = p;
     }
     for (int b = tid; b < nb; b += blockDim.x) {
@@ -411,7 +453,7 @@ static moe_status plan_common(Plan &p, int n_tokens, int top_k, int E, const int
 
 static void launch_bucket(const Plan &p) {
     if (!p.a.pair_list) return;
-    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, p.s, p.a.ids, p.a.T * p.a.K, p.a.E,
+    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, p.s, p.a.ids, p.a.T * p.a.K, p.a.K, p.a.E,
                        kBatchTok, const_cast<int32_t *>(p.a.work_expert), const_cast<int32_t *>(p.a.work_begin),
                        const_cast<int32_t *>(p.a.pair_list), const_cast<int32_t *>(p.a.n_work));
 }

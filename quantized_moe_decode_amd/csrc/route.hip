@@ -2,15 +2,17 @@
 // optional shared-expert gate (Red Lite dev39, "Change": the layer is
 // GPU-routed; the shared expert's output is scaled by a scalar gate).
 //
-// One launch.  Workgroups of four waves each compute four router logits
-// (one wave per router row, fp32 accumulation over the contraction with a
-// wave64 butterfly reduction).  The router matrix is read once, spread over
-// many CUs.  Logits are published with device-coherent stores and a
-// device-scope counter per token; the last workgroup to arrive stages that
-// token's logits (device-coherent loads) in LDS, selects the top-k with the
-// whole block (topk.hpp) and computes the scores.  No cache-wide fence is needed: only the logits and
-// the counter cross workgroups.  The last workgroup resets the counter, so
-// the workspace is ready for the next call (and for graph replays).
+// One launch.  Workgroups of four waves each compute four router logits of
+// one token (one wave per router row, fp32 accumulation over the contraction
+// with a wave64 butterfly reduction).  The router matrix is read once, spread
+// over many CUs.  Each logit is published as one 64-bit word, the fp32 value
+// and a nonzero flag, written with one device-scope store.  The last
+// workgroup of each token's row of the grid (every other one has a lower
+// index, so in-order dispatch cannot deadlock) polls that token's words until
+// all are flagged, stages the logits in LDS, selects the top-k with the whole
+// block (topk.hpp), computes the scores and clears the words, so the
+// workspace is ready for the next call (and for graph replays).  No counter,
+// atomic read-modify-write or cache-wide fence is involved.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -31,8 +33,7 @@ struct RouteArgs {
     int32_t *ids;
     float *scores;
     float *gate;
-    float *logits;           // workspace [T][E + 1]
-    uint32_t *counters;      // workspace [T]
+    uint64_t *logits;        // workspace [T][E + 1] flagged words, zero between calls
 };
 
 // Eight consecutive elements of a row as floats (one 16-byte load for 16-bit
@@ -91,41 +92,48 @@ __device__ float row_dot(const void *w, int64_t row, const void *x, int64_t xrow
     return wave_sum(acc);
 }
 
+constexpr uint64_t kLogitFlag = 1ull << 32;
+constexpr uint32_t kRouteSpinLimit = 1u << 22;
+
+// Wait for one flagged logit word and return its value (0 if the wait ever
+// ran out, which in-order dispatch rules out).
+__device__ __forceinline__ float wait_logit(const uint64_t *w) {
+    for (uint32_t i = 0; i < kRouteSpinLimit; ++i) {
+        const uint64_t v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v & kLogitFlag) return __uint_as_float((uint32_t)v);
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return 0.f;
+}
+
 template <int XT, int WT, int GT>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
-    __shared__ int s_last;
     const int t = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int n_rows = a.E + (a.wg ? 1 : 0);
-    float *logits = a.logits + (int64_t)t * (a.E + 1);
+    uint64_t *logits = a.logits + (int64_t)t * (a.E + 1);
 
     const int row = blockIdx.x * kRouteWaves + wave;
     if (row < n_rows) {
         const float v = (row < a.E) ? row_dot<XT, WT>(a.wr, row, a.x, t, a.d_in, lane)
                                     : row_dot<XT, GT>(a.wg, 0, a.x, t, a.d_in, lane);
-        if (lane == 0) {
-            // device-coherent store, completed before this workgroup signals
-            __hip_atomic_store(logits + row, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __builtin_amdgcn_s_waitcnt(0);
-        }
+        if (lane == 0)
+            __hip_atomic_store(logits + row, kLogitFlag | __float_as_uint(v), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(&a.counters[t], 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == gridDim.x - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
+    if (blockIdx.x != gridDim.x - 1) return;
 
-    // Last workgroup of token t: its logits into LDS (device-coherent loads),
-    // then the block-wide top-k and, in one wave, the softmax scores.
+    // The token's selector: its logits into LDS as they are flagged, then the
+    // block-wide top-k and, in one wave, the softmax scores.
     __shared__ __align__(16) float s_logits[MOE_MAX_EXPERTS];
     __shared__ Selection sel;
-    stage_logits(a.E, s_logits, &sel, [&](int e) {
-        return __hip_atomic_load(logits + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    });
+    __shared__ float s_gate_logit;
+    stage_logits(a.E, s_logits, &sel, [&](int e) { return wait_logit(logits + e); });
+    if (tid == 0 && a.wg) s_gate_logit = wait_logit(logits + a.E);
     __syncthreads();
+    // every word of the token has been read: clear them for the next call
+    for (int e = tid; e < n_rows; e += blockDim.x)
+        __hip_atomic_store(logits + e, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     select_all(a.E, a.K, s_logits, &sel);
     if (wave != 0) return;
     with_per(a.E, [&](auto per) { softmax_scores<decltype(per)::value>(a.E, a.K, a.renorm, s_logits, lane, &sel); });
@@ -133,14 +141,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
         a.ids[t * a.K + lane] = sel.ids[lane];
         a.scores[t * a.K + lane] = sel.scores[lane];
     }
-    if (lane == 0) {
-        if (a.wg) {
-            const float gl = __hip_atomic_load(logits + a.E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            a.gate[t] = 1.0f / (1.0f + expf(-gl));
-        }
-        // leave the counter at zero for the next call
-        __hip_atomic_store(&a.counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (lane == 0 && a.wg) a.gate[t] = 1.0f / (1.0f + expf(-s_gate_logit));
 }
 
 using RouteFn = void (*)(RouteArgs);
@@ -177,8 +178,7 @@ using namespace moe;
 
 extern "C" size_t moe_decode_route_workspace_bytes(int32_t n_tokens, int32_t n_experts) {
     if (n_tokens < 1 || n_experts < 1) return 0;
-    const size_t logits = (size_t)n_tokens * (n_experts + 1) * sizeof(float);
-    return align_up(logits, 256) + align_up((size_t)n_tokens * sizeof(uint32_t), 256);
+    return align_up((size_t)n_tokens * (n_experts + 1) * sizeof(uint64_t), 256);
 }
 
 extern "C" moe_status moe_decode_route(const void *x, moe_dtype x_dtype, int32_t n_tokens, int32_t d_in,
@@ -196,7 +196,8 @@ extern "C" moe_status moe_decode_route(const void *x, moe_dtype x_dtype, int32_t
     if (!valid_dtype(x_dtype) || !valid_dtype(w_router_dtype) ||
         (w_shared_gate && !valid_dtype(w_shared_gate_dtype)))
         return MOE_EUNSUPPORTED;
-    if (!aligned16(x) || !aligned16(w_router) || (w_shared_gate && !aligned16(w_shared_gate)))
+    if (!aligned16(x) || !aligned16(w_router) || (w_shared_gate && !aligned16(w_shared_gate)) ||
+        !aligned16(workspace))
         return MOE_EINVAL;
     if (workspace_bytes < moe_decode_route_workspace_bytes(n_tokens, n_experts)) return MOE_EINVAL;
 
@@ -205,10 +206,7 @@ extern "C" moe_status moe_decode_route(const void *x, moe_dtype x_dtype, int32_t
     a.x_dt = x_dtype; a.wr_dt = w_router_dtype; a.wg_dt = w_shared_gate_dtype;
     a.T = n_tokens; a.d_in = d_in; a.E = n_experts; a.K = top_k; a.renorm = renormalize ? 1 : 0;
     a.ids = expert_ids; a.scores = scores; a.gate = shared_gate;
-    char *ws = reinterpret_cast<char *>(workspace);
-    a.logits = reinterpret_cast<float *>(ws);
-    a.counters = reinterpret_cast<uint32_t *>(
-        ws + align_up((size_t)n_tokens * (n_experts + 1) * sizeof(float), 256));
+    a.logits = reinterpret_cast<uint64_t *>(workspace);
 
     const int n_rows = n_experts + (w_shared_gate ? 1 : 0);
     dim3 grid((n_rows + kRouteWaves - 1) / kRouteWaves, n_tokens);

@@ -47,8 +47,8 @@ def test_abi_version_and_status_strings():
 
 
 def test_workspace_sizes():
-    assert qmd.route_workspace_bytes(1, 128) >= (128 + 1) * 4 + 4
-    assert qmd.route_workspace_bytes(32, 1024) >= 32 * 1025 * 4 + 32 * 4
+    assert qmd.route_workspace_bytes(1, 128) >= (128 + 1) * 8          # one flagged 64-bit word per logit
+    assert qmd.route_workspace_bytes(32, 1024) >= 32 * 1025 * 8
     assert qmd.route_workspace_bytes(0, 8) == 0
     assert qmd.expert_ffn_workspace_bytes(1, 8, 128) == 0
     mw = min(32 * 8, 128) + 1

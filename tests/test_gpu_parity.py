@@ -143,6 +143,48 @@ def test_out_of_range_ids_give_zero_rows():
             assert np.max(np.abs(part[t, 0] - ref["partial"][t, 0])) <= 2e-3 * np.max(np.abs(ref["partial"][t, 0]))
 
 
+@pytest.mark.parametrize("ids_rows", [
+    # an expert repeated inside a token (the ranks then come from the direct count)
+    [[5, 5, 2, 9], [2, 5, 5, 5], [9, 1, 1, 0]],
+    # distinct per token, shared across tokens, plus out-of-range ids twice in one token
+    [[5, 2, -1, 9], [2, 5, 7, 40], [-3, 9, 5, 99]],
+    # more than four tokens on one expert (several work items for it)
+    [[3, 0, 1, 2], [3, 4, 5, 6], [3, 7, 0, 1], [3, 2, 4, 5], [3, 6, 7, 0], [3, 1, 2, 4]],
+], ids=["repeat-in-token", "shared-and-out-of-range", "six-tokens-one-expert"])
+def test_multi_token_ids_outside_topk(ids_rows):
+    """The multi-token expert FFN with id patterns routing never produces: every
+    (token, slot) row matches the oracle's, in its own place."""
+    from quantized_moe_decode_amd.layer import layer_from_host, tensor_from_encoded
+    import quantized_moe_decode_amd as q
+    ids = np.array(ids_rows, np.int32)
+    T, K = ids.shape
+    cfg = small_cfg(top_k=K, n_experts=10)
+    say(f"case multi-token ids {ids.tolist()}")
+    w = mi.gen_layer_weights(cfg, 8, threads=4)
+    layer = layer_from_host(cfg, w, DEV, n_tokens=T)
+    x, _ = mi.gen_tokens(cfg, 8, T)
+    xd = tensor_from_encoded(x, cfg.x_dtype, DEV)
+    sc = np.random.default_rng([8, T]).uniform(0.1, 1.0, (T, K))
+    layer.ids.copy_(torch.from_numpy(ids))
+    layer.scores.copy_(torch.from_numpy(sc.astype(np.float32)))
+    layer.act.fill_(7.0)
+    layer.partial.fill_(7.0)
+    q.moe_decode_expert_ffn(xd, layer.gate, layer.up, layer.down, layer.ids, layer.scores,
+                            layer.act, layer.partial, layer.ffn_ws)
+    torch.cuda.synchronize()
+    act, part = layer.act.cpu().numpy(), layer.partial.cpu().numpy()
+    ref = oracle.expert_ffn(x, cfg.x_dtype, w["gate"], w["up"], w["down"], ids,
+                            sc.astype(np.float32).astype(np.float64))
+    for t in range(T):
+        for k in range(K):
+            if not 0 <= ids[t, k] < cfg.n_experts:
+                assert np.all(act[t, k] == 0) and np.all(part[t, k] == 0)
+                continue
+            ra, rp = ref["act"][t, k], ref["partial"][t, k]
+            assert np.max(np.abs(act[t, k] - ra)) <= 2e-3 * np.max(np.abs(ra)), (t, k)
+            assert np.max(np.abs(part[t, k] - rp)) <= 2e-3 * np.max(np.abs(rp)), (t, k)
+
+
 def test_exact_tie_prefers_lower_index():
     """Duplicate router rows give bit-identical fp32 logits; the lower expert id wins."""
     import quantized_moe_decode_amd as q
@@ -164,11 +206,14 @@ def test_exact_tie_prefers_lower_index():
     assert ids.cpu().numpy().tolist() == [[4, 11, 9, 2]]
     s = sc.cpu().numpy()[0]
     assert s[0] == s[1]
-    # the same workspace serves the next call unchanged (its counters were reset)
+    # each call leaves the workspace all zero (its flagged logit words cleared),
+    # so the same workspace serves the next call unchanged
+    assert not np.any(ws.cpu().numpy()), "route workspace not cleared"
     ids2 = torch.full_like(ids, -7)
     q.moe_decode_route(xd, wd, 4, True, ids2, sc, ws)
     torch.cuda.synchronize()
     assert ids2.cpu().numpy().tolist() == [[4, 11, 9, 2]]
+    assert not np.any(ws.cpu().numpy()), "route workspace not cleared"
 
 
 def test_many_experts_top32():
