@@ -175,26 +175,53 @@ __global__ __launch_bounds__(256) void gate_up_batch_q4(FfnArgs a) {
                 }
             }
             with_width(a.lr_shift, [&](auto wd) {
+                constexpr int W = decltype(wd)::value;
+                if constexpr (W >= 16) {
+                    // every (projection, row, token) sum of the lane group at once:
+                    // value m * V/2 + n * NTP + t ends in the lanes of index
+                    // (that value) << SH, where the gate sum (m = 0) meets the up
+                    // sum from across the group's top lane bit
+                    constexpr int NTP = NT == 3 ? 4 : NT;
+                    constexpr int V = 2 * NR * NTP, SH = ilog2(W) - ilog2(V);
+                    float sv[V];
 #pragma unroll
-                for (int m = 0; m < 2; ++m)
+                    for (int m = 0; m < 2; ++m)
 #pragma unroll
-                    for (int n = 0; n < NR; ++n)
+                        for (int n = 0; n < NR; ++n)
 #pragma unroll
-                        for (int t = 0; t < NT; ++t) acc[m][n][t] = group_sum_last<decltype(wd)::value>(acc[m][n][t]);
-            });
-            if (j == lr - 1) {
+                            for (int t = 0; t < NTP; ++t)
+                                sv[m * (V / 2) + n * NTP + t] = t < NT ? acc[m][n][t] : 0.f;
+                    group_multi_sum<W, V>(sv);
+                    const float u = group_partner<W>(sv[0]);
+                    const int li = lane & (W - 1), idx = li >> SH;
+                    if ((li & ((1 << SH) - 1)) == 0 && idx < V / 2) {
+                        const int n = idx / NTP, t = idx - n * NTP;
+                        const int r = r0 + n * rpw;
+                        const float g = sv[0];
+                        if (t < NT && r < row_end) a.act[(int64_t)pair_at(wk, t) * a.d_ff + r] = g * sigmoidf_(g) * u;
+                    }
+                } else {
 #pragma unroll
-                for (int n = 0; n < NR; ++n) {
-                    const int r = r0 + n * rpw;
-                    if (r < row_end) {
+                    for (int m = 0; m < 2; ++m)
 #pragma unroll
-                        for (int t = 0; t < NT; ++t) {
-                            const float g = acc[0][n][t], u = acc[1][n][t];
-                            a.act[(int64_t)pair_at(wk, t) * a.d_ff + r] = g * sigmoidf_(g) * u;
+                        for (int n = 0; n < NR; ++n)
+#pragma unroll
+                            for (int t = 0; t < NT; ++t) acc[m][n][t] = group_sum_last<W>(acc[m][n][t]);
+                    if (j == lr - 1) {
+#pragma unroll
+                        for (int n = 0; n < NR; ++n) {
+                            const int r = r0 + n * rpw;
+                            if (r < row_end) {
+#pragma unroll
+                                for (int t = 0; t < NT; ++t) {
+                                    const float g = acc[0][n][t], u = acc[1][n][t];
+                                    a.act[(int64_t)pair_at(wk, t) * a.d_ff + r] = g * sigmoidf_(g) * u;
+                                }
+                            }
                         }
                     }
                 }
-            }
+            });
         }
     });
 }
@@ -292,25 +319,49 @@ __global__ __launch_bounds__(256) void down_batch_q4(FfnArgs a) {
                 }
             }
             with_width(a.lr_shift, [&](auto wd) {
+                constexpr int W = decltype(wd)::value;
+                if constexpr (W >= 16) {
+                    // every (row, token) sum of the lane group at once: value
+                    // n * NTP + t ends in the lanes of index (that value) << SH
+                    constexpr int NTP = NT == 3 ? 4 : NT;
+                    constexpr int V = NR * NTP, SH = ilog2(W) - ilog2(V);
+                    float sv[V];
 #pragma unroll
-                for (int n = 0; n < NR; ++n)
+                    for (int n = 0; n < NR; ++n)
 #pragma unroll
-                    for (int t = 0; t < NT; ++t) acc[n][t] = group_sum_last<decltype(wd)::value>(acc[n][t]);
-            });
-            if (j == lr - 1) {
-#pragma unroll
-                for (int n = 0; n < NR; ++n) {
-                    const int r = r0 + n * rpw;
-                    if (r < row_end) {
-#pragma unroll
-                        for (int t = 0; t < NT; ++t) {
+                        for (int t = 0; t < NTP; ++t) sv[n * NTP + t] = t < NT ? acc[n][t] : 0.f;
+                    group_multi_sum<W, V>(sv);
+                    const int li = lane & (W - 1), idx = li >> SH;
+                    if ((li & ((1 << SH) - 1)) == 0) {
+                        const int n = idx / NTP, t = idx - n * NTP;
+                        const int r = r0 + n * rpw;
+                        if (t < NT && r < row_end) {
                             const int64_t p = pair_at(wk, t);
                             const float sc = a.scores ? a.scores[p] : 1.0f;
-                            a.partial[p * a.d_in + r] = sc * acc[n][t];
+                            a.partial[p * a.d_in + r] = sc * sv[0];
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int n = 0; n < NR; ++n)
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) acc[n][t] = group_sum_last<W>(acc[n][t]);
+                    if (j == lr - 1) {
+#pragma unroll
+                        for (int n = 0; n < NR; ++n) {
+                            const int r = r0 + n * rpw;
+                            if (r < row_end) {
+#pragma unroll
+                                for (int t = 0; t < NT; ++t) {
+                                    const int64_t p = pair_at(wk, t);
+                                    const float sc = a.scores ? a.scores[p] : 1.0f;
+                                    a.partial[p * a.d_in + r] = sc * acc[n][t];
+                                }
+                            }
                         }
                     }
                 }
-            }
+            });
         }
     });
 }

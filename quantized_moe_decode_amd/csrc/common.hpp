@@ -134,6 +134,95 @@ __device__ __forceinline__ float group_sum_last(float v) {
     return v;
 }
 
+// DPP control that pairs every lane with the lane across bit B (B <= 3) of
+// its index within a row: row_ror:8 for bit 3, row_half_mirror (lanes r and
+// 7 - r, which differ in bit 2) for bit 2, quad permutations for bits 1, 0.
+template <int B>
+constexpr int dpp_across_bit() {
+    return B == 3 ? 0x128 : B == 2 ? 0x141 : B == 1 ? 0x4E : 0xB1;
+}
+
+// The gfx950 permlane swap across lane bit B (5: lanes l and l ^ 32; 4: l
+// and l ^ 16) of two registers a, b.  In the lower lane of each pair, r0 is
+// its own a and r1 its partner's a; in the upper lane, r0 is its partner's b
+// and r1 its own b.  So r0 + r1 is a's pair sum in lower lanes and b's in
+// upper lanes, and with a = b = x the partner's x is r1 (lower) or r0 (upper).
+template <int B>
+__device__ __forceinline__ void swap_across(float a, float b, float &r0, float &r1) {
+    static_assert(B == 4 || B == 5, "permlane swaps cover lane bits 4 and 5");
+    if constexpr (B == 5) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        r0 = __uint_as_float(r[0]);
+        r1 = __uint_as_float(r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        r0 = __uint_as_float(r[0]);
+        r1 = __uint_as_float(r[1]);
+    }
+}
+
+template <int K, int LW, int LV, int V>
+__device__ __forceinline__ void multi_sum_step(float (&v)[V], int lane) {
+    if constexpr (K < LW) {
+        constexpr int B = LW - 1 - K;
+        if constexpr (K < LV) {               // halve: keep one half, add the partner's
+            constexpr int H = (V >> K) / 2;
+#pragma unroll
+            for (int j = 0; j < H; ++j) {
+                if constexpr (B >= 4) {
+                    float r0, r1;
+                    swap_across<B>(v[j], v[j + H], r0, r1);
+                    v[j] = r0 + r1;
+                } else {
+                    const bool hi = (lane >> B) & 1;
+                    const float keep = hi ? v[j + H] : v[j], send = hi ? v[j] : v[j + H];
+                    v[j] = keep + dpp_f<dpp_across_bit<B>()>(send);
+                }
+            }
+        } else {                              // add across the bit
+            if constexpr (B >= 4) {
+                float r0, r1;
+                swap_across<B>(v[0], v[0], r0, r1);
+                v[0] = r0 + r1;
+            } else {
+                v[0] += dpp_f<dpp_across_bit<B>()>(v[0]);
+            }
+        }
+        multi_sum_step<K + 1, LW, LV, V>(v, lane);
+    }
+}
+
+constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
+
+// Sums of V values over aligned groups of W lanes at once (W and V powers of
+// two, V <= W, W <= 64): lane l ends with, in v[0], the group sum of value
+// (l mod W) >> (log2 W - log2 V), so each value's sum sits in W / V
+// consecutive lanes.  Each of the first log2 V steps halves the values a
+// lane holds (a lane and its partner across one lane bit each keep one half
+// and add the other's half), the remaining steps add across the remaining
+// bits: V - 1 + log2 W additions in all, against V log2 W for V separate
+// reductions.  The partners are the gfx950 permlane swaps for bits 5 and 4
+// and DPP for bits 3..0.
+template <int W, int V>
+__device__ __forceinline__ void group_multi_sum(float (&v)[V]) {
+    static_assert(ilog2(V) <= ilog2(W) && W <= 64, "at most one value per lane of the group");
+    multi_sum_step<0, ilog2(W), ilog2(V), V>(v, threadIdx.x & (kWave - 1));
+}
+
+// x of the lane across the top bit of its W-lane group (W >= 16).
+template <int W>
+__device__ __forceinline__ float group_partner(float x) {
+    static_assert(W >= 16 && W <= 64, "partner across lane bit 3, 4 or 5");
+    constexpr int B = ilog2(W) - 1;
+    if constexpr (B == 3) {
+        return dpp_f<dpp_across_bit<3>()>(x);
+    } else {
+        float r0, r1;
+        swap_across<B>(x, x, r0, r1);
+        return ((threadIdx.x >> B) & 1) ? r0 : r1;
+    }
+}
+
 // Sum over the whole wave, the same value in every lane (DPP reduction into
 // lane 63, then a broadcast of that lane).
 __device__ __forceinline__ float wave_sum(float v) {
