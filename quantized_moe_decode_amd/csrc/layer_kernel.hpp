@@ -252,6 +252,60 @@ __device__ __forceinline__ void store_act_sentinel(const LayerArgs &a, int slot,
     for (int c = 0; c < kActCopies; ++c) st_tagged(p + c * kSentStride, v, tag);
 }
 
+// Kernel-A epilogue: reduce the gate and up sums of NR rows over each lane
+// group of width 1 << lrs and store the rows' SwiGLU values, rows r0 +
+// n * rpw (r0 is the lane group's first row).  Wide groups reduce all 2 NR
+// sums at once, and lane (n << SH) of a group stores row n with the up sum
+// from the lane across the group's top bit; narrow groups reduce each sum
+// on its own and the group's last lane stores every row.
+template <int NR>
+__device__ __forceinline__ void a_epilogue(const LayerArgs &a, int lrs, float (&acc)[2][NR], int r0, int rpw,
+                                           int row_end, int dff, uint64_t *act, int slot, uint32_t tag) {
+    const int lane = threadIdx.x & (kWave - 1);
+    with_width(lrs, [&](auto w) {
+        constexpr int W = decltype(w)::value;
+        constexpr int V = 2 * NR;
+        if constexpr (W >= 16 && W >= V) {
+            float sv[V];
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int n = 0; n < NR; ++n) sv[m * NR + n] = acc[m][n];
+            group_multi_sum<W, V>(sv);
+            const float u = group_partner<W>(sv[0]);
+            constexpr int SH = ilog2(W) - ilog2(V);
+            const int li = lane & (W - 1), n = li >> SH;
+            if ((li & ((1 << SH) - 1)) == 0 && n < NR) {
+                const int r = r0 + n * rpw;
+                if (r < row_end) {
+                    const float g = sv[0];
+                    const float v = g * sigmoidf_(g) * u;
+                    st_tagged(act + r, v, tag);
+                    if (r == dff - 1) store_act_sentinel(a, slot, v, tag);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < NR; ++n) {
+                acc[0][n] = group_sum_last<W>(acc[0][n]);
+                acc[1][n] = group_sum_last<W>(acc[1][n]);
+            }
+            if ((lane & (W - 1)) == W - 1) {
+#pragma unroll
+                for (int n = 0; n < NR; ++n) {
+                    const int r = r0 + n * rpw;
+                    if (r < row_end) {
+                        const float g = acc[0][n], u = acc[1][n];
+                        const float v = g * sigmoidf_(g) * u;
+                        st_tagged(act + r, v, tag);
+                        if (r == dff - 1) store_act_sentinel(a, slot, v, tag);
+                    }
+                }
+            }
+        }
+    });
+}
+
 // Kernel A unit: rows [row0, row0 + a_tile) of slot `slot`, expert e (x
 // already staged in LDS).
 template <int BA, int SB, int XT>
@@ -315,27 +369,7 @@ __device__ void layer_a_unit_single(const LayerArgs &a, uint32_t tag, int slot, 
             convert_x<XT, F::kCodes>(xr, xv);
             dot_block<BA, SB, 2, NR>(cur, xv, sum_n<F::kCodes>(xv), acc);
         }
-        if (ch == n_chunk - 1) {
-            with_width(a.a_lr_shift, [&](auto w) {
-#pragma unroll
-                for (int n = 0; n < NR; ++n) {
-                    acc[0][n] = group_sum_last<decltype(w)::value>(acc[0][n]);
-                    acc[1][n] = group_sum_last<decltype(w)::value>(acc[1][n]);
-                }
-            });
-            if (j == lr - 1) {
-#pragma unroll
-                for (int n = 0; n < NR; ++n) {
-                    const int r = r0 + n * rpw;
-                    if (r < row_end) {
-                        const float g = acc[0][n], u = acc[1][n];
-                        const float v = g * sigmoidf_(g) * u;
-                        st_tagged(act + r, v, tag);
-                        if (r == dff - 1) store_act_sentinel(a, slot, v, tag);
-                    }
-                }
-            }
-        }
+        if (ch == n_chunk - 1) a_epilogue<NR>(a, a.a_lr_shift, acc, r0, rpw, row_end, dff, act, slot, tag);
     }
 }
 
@@ -406,28 +440,7 @@ __device__ void layer_a_unit_pipelined(const LayerArgs &a, uint32_t tag, int slo
             convert_x<XT, F::kCodes>(xr, xv);
             dot_block<BA, SB, 2, NR>(cur, xv, sum_n<F::kCodes>(xv), acc);
         }
-        if (ch == n_chunk - 1) {
-            with_width(a.a_lr_shift, [&](auto w) {
-#pragma unroll
-                for (int n = 0; n < NR; ++n) {
-                    acc[0][n] = group_sum_last<decltype(w)::value>(acc[0][n]);
-                    acc[1][n] = group_sum_last<decltype(w)::value>(acc[1][n]);
-                }
-            });
-            if (j == lr - 1) {
-                const int r0 = stage_row(st);
-#pragma unroll
-                for (int n = 0; n < NR; ++n) {
-                    const int r = r0 + n * rpw;
-                    if (r < row_end) {
-                        const float g = acc[0][n], u = acc[1][n];
-                        const float v = g * sigmoidf_(g) * u;
-                        st_tagged(act + r, v, tag);
-                        if (r == dff - 1) store_act_sentinel(a, slot, v, tag);
-                    }
-                }
-            }
-        }
+        if (ch == n_chunk - 1) a_epilogue<NR>(a, a.a_lr_shift, acc, stage_row(st), rpw, row_end, dff, act, slot, tag);
     };
     BlockRegs<BA, 2, NR> ra, rb;
     if (n_stage > 0) load(ra, 0);
@@ -539,21 +552,32 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
                 dot_block<BB, SB, 1, NR>(cur, xv, sum_n<CODES>(xv), acc);
             }
             if (ch == n_chunk - 1) {
+                auto put = [&](int r, float v) {
+                    if (r < row_end) {
+                        if (last_slot) s_own[r - row0] = score * v;
+                        else st_tagged(part + r, score * v, tag);
+                    }
+                };
                 with_width(lrs, [&](auto w) {
+                    constexpr int W = decltype(w)::value;
+                    if constexpr (W >= 16 && W >= NR) {
+                        // all NR sums at once; lane (n << SH) of the group holds row n
+                        float sv[NR];
 #pragma unroll
-                    for (int n = 0; n < NR; ++n) acc[0][n] = group_sum_last<decltype(w)::value>(acc[0][n]);
-                });
-                if (j == lr - 1) {
+                        for (int n = 0; n < NR; ++n) sv[n] = acc[0][n];
+                        group_multi_sum<W, NR>(sv);
+                        constexpr int SH = ilog2(W) - ilog2(NR);
+                        const int li = lane & (W - 1);
+                        if ((li & ((1 << SH) - 1)) == 0) put(r0 + (li >> SH) * rpw, sv[0]);
+                    } else {
 #pragma unroll
-                    for (int n = 0; n < NR; ++n) {
-                        const int r = r0 + n * rpw;
-                        if (r < row_end) {
-                            const float v = score * acc[0][n];
-                            if (last_slot) s_own[r - row0] = v;
-                            else st_tagged(part + r, v, tag);
+                        for (int n = 0; n < NR; ++n) acc[0][n] = group_sum_last<W>(acc[0][n]);
+                        if (j == lr - 1) {
+#pragma unroll
+                            for (int n = 0; n < NR; ++n) put(r0 + n * rpw, acc[0][n]);
                         }
                     }
-                }
+                });
             }
         }
     } else {
