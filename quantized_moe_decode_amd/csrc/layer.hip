@@ -164,6 +164,7 @@ static void fit_a_passes(LayerPlan &p, int cap1, int cap2) {
     a.a_tiles_r = (a.d_ff + a.a_tile - 1) / a.a_tile;
     a.a_tiles_s = a.S > 0 ? (dff_s + a.a_tile - 1) / a.a_tile : 0;
     p.grid = a.n_route + a.K * a.a_tiles_r + a.S * a.a_tiles_s + n_b;
+    a.by_xcd = slots == 8 && a.n_route % 8 == 0 && (a.S == 0 || a.a_tiles_s == a.a_tiles_r) ? 1 : 0;
 }
 
 static LayerFn pick_layer(int ba, int bb, int sb, int xt, int anr) {

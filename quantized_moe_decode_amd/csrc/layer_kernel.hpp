@@ -87,6 +87,7 @@ struct LayerArgs {
     uint64_t *partial;              // [K + S][d_in] tagged
     uint32_t *ctr;                  // control words
     int n_route;
+    int by_xcd;                     // units in slot-interleaved order: slot s's units on XCD s (8 slots)
     int a_lr_shift, a_tile, a_tiles_r, a_tiles_s;
     int b_lr_shift_r, b_lr_shift_s, b_tile, b_tiles;
 };
@@ -504,7 +505,7 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     if (valid) {
         const uint64_t *act = a.act + (int64_t)slot * a.act_stride;
         const int n_act = cpr * CODES;
-        const uint64_t *sent = a.act_sent + ((int64_t)slot * kActCopies + blockIdx.x % kActCopies) * kSentStride;
+        const uint64_t *sent = a.act_sent + ((int64_t)slot * kActCopies + tile % kActCopies) * kSentStride;
         // 4-bit down projections take act as fp16 pairs (packed dot); the
         // others as fp32 chunks
         constexpr bool kF16 = BB == 4;
@@ -655,9 +656,22 @@ __global__ __launch_bounds__(256, 3) void layer_kernel(LayerArgs a) {
     const uint32_t tag = s_tag;
     b -= a.n_route;
     const int n_a = a.K * a.a_tiles_r + a.S * a.a_tiles_s;
-    const bool is_a = b < n_a;
+    bool is_a = b < n_a;
     int slot, tile;
-    if (!is_a) {
+    if (a.by_xcd) {
+        // Workgroups go to the 8 XCDs round robin (block i to XCD i mod 8), and
+        // the router blocks are a multiple of 8: in this order every unit of
+        // slot s lands on XCD s, so the act hand-off between the slot's A and
+        // B units stays within one XCD and its L2 (a round trip between two
+        // workgroups measures ~1.0 us within an XCD, ~1.5 us across).  Every
+        // slot has the same tile counts; the order still waits only on lower
+        // block indices (A tiles of a slot, then its B tiles; the tail's slot
+        // is the last of each group of 8).
+        slot = b % 8;
+        const int q = b / 8;
+        is_a = q < a.a_tiles_r;
+        tile = is_a ? q : q - a.a_tiles_r;
+    } else if (!is_a) {
         b -= n_a;
         slot = b / a.b_tiles;
         tile = b % a.b_tiles;

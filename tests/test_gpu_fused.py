@@ -37,6 +37,29 @@ def test_fused_small_layers(kw):
         assert not np.any(ws[:4]), "error word set"
 
 
+# Eight slots at d_in = 2048 (units in the XCD-aligned slot order; top-8
+# routed, or top-6 plus two shared experts), a ragged d_ff (704 = 44 x 16),
+# each input dtype's dot path and 6-bit down projections.
+@pytest.mark.parametrize("kw", [
+    dict(d_ff=704, n_experts=12, top_k=8),
+    dict(d_ff=768, n_experts=10, top_k=8, x_dtype=mi.F16, router_dtype=mi.F16, resid_dtype=mi.F16),
+    dict(d_ff=768, n_experts=9, top_k=8, x_dtype=mi.F32, router_dtype=mi.F32, resid_dtype=mi.F32,
+         sb_dtype=mi.F16),
+    dict(d_ff=768, n_experts=11, top_k=8, bits_down=6),
+    dict(d_ff=768, n_experts=10, top_k=6, n_shared=2, d_ff_shared=704),
+], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_fused_eight_slots(kw):
+    cfg = small_cfg(d_in=2048, **kw)
+    say(f"case fused eight slots {kw}")
+    w = mi.gen_layer_weights(cfg, 5, threads=4)
+    x, resid = margin_tokens(cfg, 5, w, 2)
+    for t in range(2):
+        gpu, layer = run_gpu_layer(cfg, w, x[t:t + 1], resid[t:t + 1], fused=True)
+        compare_layer(cfg, w, x[t:t + 1], resid[t:t + 1], gpu, f"fused eight slots {kw} t{t}")
+        ws = layer.fused_ws.cpu().numpy()
+        assert not np.any(ws[:4]), "error word set"
+
+
 def test_fused_jittered_bias():
     for bits in ((4, 4), (8, 8), (4, 6)):
         cfg = small_cfg(bits_gate_up=bits[0], bits_down=bits[1])
