@@ -54,7 +54,7 @@ constexpr int kActCopies = 8;       // copies of each slot's last act row (the k
 constexpr int kSentStride = 32;     // words between sentinel copies (256 bytes)
 // s_sleep arguments (units of 64 cycles) between polls: with hundreds of
 // pollers, sparse polls make the hand-off faster, not slower
-constexpr int kLogitSleep = 24;     // the router-logit sentinel (~900 pollers over 16 copies)
+constexpr int kLogitSleep = 24;     // the router logits (~900 polling workgroups over 16 copies)
 constexpr int kActSleep = 2;        // a slot's act sentinel (64 pollers over 8 copies)
 constexpr int kRetrySleep = 2;      // words still missing after a batch read
 constexpr int kTailSleep = 2;       // the tail's reads of the other slots' partial rows
@@ -153,9 +153,10 @@ __device__ __forceinline__ void poll_batch(const LayerArgs &a, uint32_t tag, int
 constexpr int kGatherPer = 4;       // words per thread per gather batch
 
 // Gather n tagged words addr(0..n) into f(i, value), in batches of
-// kGatherPer words per thread.  With a sentinel, thread 0 first waits for that
-// one word (written when the producers are about done), so that while the
-// producers run a workgroup polls one address rather than all n.
+// kGatherPer words per thread, SLEEP between polls of missing words.  With a
+// sentinel, thread 0 first waits for that one word (written when the
+// producers are about done), so that while the producers run a workgroup
+// polls one address rather than all n.
 template <int SLEEP, typename Addr, typename Fn>
 __device__ __forceinline__ void gather_tagged(const LayerArgs &a, int n, const uint64_t *sentinel, uint32_t tag,
                                               Addr addr, Fn f) {
@@ -168,7 +169,7 @@ __device__ __forceinline__ void gather_tagged(const LayerArgs &a, int n, const u
         const int left = n - base - t;
         const int cnt = left <= 0 ? 0 : min(kGatherPer, (left + nt - 1) / nt);
         float v[kGatherPer];
-        poll_batch<kGatherPer>(a, tag, cnt, [&](int u) { return addr(base + u * nt + t); }, v);
+        poll_batch<kGatherPer, SLEEP>(a, tag, cnt, [&](int u) { return addr(base + u * nt + t); }, v);
 #pragma unroll
         for (int u = 0; u < kGatherPer; ++u)
             if (u < cnt) f(base + u * nt + t, v[u]);
@@ -225,8 +226,10 @@ __device__ __forceinline__ const uint64_t *my_logits(const LayerArgs &a) {
 }
 
 // Wait for every router logit (and the shared-gate logit) and stage them in
-// LDS, padded with -inf for the rank count.  The last word written by the
-// last router workgroup is the sentinel.
+// LDS, padded with -inf for the rank count.  Each thread polls its words
+// directly, with no sentinel first: the router rows all finish within about
+// a memory round trip of each other, and one round trip fewer measured 0.3 us
+// less per launch than a sentinel wait followed by the gather.
 __device__ void gather_logits(const LayerArgs &a, uint32_t tag, float *s_logits, Selection *sel) {
     const int n = a.E + (a.wg ? 1 : 0);
     if (threadIdx.x == 0) {
@@ -236,7 +239,7 @@ __device__ void gather_logits(const LayerArgs &a, uint32_t tag, float *s_logits,
     if (threadIdx.x < kCandMax) sel->cand[threadIdx.x] = 0;
     for (int e = a.E + threadIdx.x; e < kRankMaxE; e += blockDim.x) s_logits[e] = -INFINITY;
     const uint64_t *lg = my_logits(a);
-    gather_tagged<kLogitSleep>(a, n, lg + n - 1, tag, [&](int i) { return lg + i; }, [&](int e, float v) {
+    gather_tagged<kLogitSleep>(a, n, nullptr, tag, [&](int i) { return lg + i; }, [&](int e, float v) {
         if (e < a.E) s_logits[e] = v == 0.f ? 0.f : v;      // -0 as +0
         else sel->gate = sigmoidf_(v);
     });
