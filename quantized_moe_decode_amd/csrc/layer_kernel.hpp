@@ -484,7 +484,9 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     const QM mats[1] = {routed ? a.down : a.sdown};
     const int64_t erow0 = (int64_t)(valid ? e : 0) * a.d_in;
     const bool last_slot = slot == n_slots(a) - 1;
-    __shared__ float s_own[MOE_MAX_DIM / 4];      // own partial rows, kept for the tail
+    // own partial rows, kept for the tail: a tile is at most 4 waves x 64 lane
+    // groups of one lane x kLayerNRB rows
+    __shared__ float s_own[4 * kWave * kLayerNRB];
 
     // stages = (row pass, chunk position); stage 0 is loaded before act is ready
     const int rb0 = row0 + wave * rpw * NR, pass_rows = 4 * rpw * NR;
