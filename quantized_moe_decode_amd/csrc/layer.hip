@@ -1,6 +1,8 @@
 // moe_decode_layer: the fused single-launch decode layer (layer_kernel.hpp).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "api.hpp"
 #include "layer_kernel.hpp"
 
@@ -129,41 +131,62 @@ static int resident_capacity(LayerFn k, size_t lds) {
     return cus * per_cu;
 }
 
-// Size the kernel-A units.  A unit is one stage (kLayerNRA rows per lane
-// group at one chunk position) when its rows' inputs fit the lane group and
-// the grid then fits the resident capacity; otherwise units take several
-// row passes of kLayerNRA2 rows, pipelined two stages deep, with enough
-// passes that the grid fits the resident capacity when possible, so every
-// kernel-B unit can issue its weight loads from the start of the launch.
+// Size the kernel-A and kernel-B units.  A kernel-A unit is either one stage
+// (kLayerNRA rows per lane group at one chunk position; only when the rows'
+// inputs fit the lane group) or several, pipelined two deep (kLayerNRA2 rows
+// per lane group and stage, `passes` row passes of every chunk position).  A
+// kernel-B unit covers `bp` row passes of kLayerNRB rows per lane group at
+// every chunk position; only its first stage is loaded before act arrives.
+// Among the layouts whose grid fits the resident capacity (every unit
+// issues its loads from the start of the launch, and no unit waits for a
+// slot to free up), take the one with the fewest serial stages: a kernel-A
+// unit's stages plus a kernel-B unit's stages after act (measured: the
+// dots.llm1-shaped layer 50.7 us with single-pass B units that do not all fit,
+// 37.8 us with 4-pass B units and 2-pass A units; the Qwen1.5-shaped layer is
+// best with single-pass B units).  Ties go to single-stage A units, then to
+// fewer B passes; if nothing fits, the smallest grid.
 // cap1, cap2: resident capacity with single-stage and with pipelined units
 // (0 if unknown).
 static void fit_a_passes(LayerPlan &p, int cap1, int cap2) {
     LayerArgs &a = p.a;
     const int slots = a.K + a.S;
-    const int n_b = slots * a.b_tiles;
     const int dff_s = a.S > 0 ? a.d_ffs : 0;
     const int rpw = 64 >> a.a_lr_shift;
     auto n_a_for = [&](int t) { return a.K * ((a.d_ff + t - 1) / t) + a.S * ((dff_s + t - 1) / t); };
     const int cpr = a.d_in / (a.gate.bits_ == 4 ? 32 : 16);
-    const int single = 4 * rpw * kLayerNRA;
-    const int room1 = cap1 - a.n_route - n_b;
-    p.a_nr = kLayerNRA;
-    int base_tile = single, passes = 1;
-    if (cpr > (1 << a.a_lr_shift) || (cap1 > 0 && (room1 <= 0 || n_a_for(single) > room1))) {
-        // several stages per unit: up to 8 row passes, fewer when the grid
-        // then fits the resident capacity (more units stream in parallel)
-        p.a_nr = kLayerNRA2;
-        base_tile = 4 * rpw * kLayerNRA2;
-        const int room2 = cap2 - a.n_route - n_b;
-        if (cap2 > 0) {
-            for (passes = 1; passes < 8; ++passes)
-                if (room2 > 0 && n_a_for(base_tile * passes) <= room2) break;
-        }
+    const int n_chunk_a = (cpr + (1 << a.a_lr_shift) - 1) >> a.a_lr_shift;
+    const int single = 4 * rpw * kLayerNRA, piped = 4 * rpw * kLayerNRA2;
+    const int cb = a.down.bits_ == 4 ? 32 : 16;
+    auto chunks_b = [&](int dff, int lrs) { return (dff / cb + (1 << lrs) - 1) >> lrs; };
+    int n_chunk_b = chunks_b(a.d_ff, a.b_lr_shift_r);
+    if (a.S > 0) n_chunk_b = std::max(n_chunk_b, chunks_b(a.d_ffs, a.b_lr_shift_s));
+    const int b_pass = a.b_tile;                     // one pass of a kernel-B unit
+    struct Layout { int a_nr, a_tile, bp, grid, cost; };
+    Layout best{0, 0, 0, 0, 0}, smallest{0, 0, 0, 0, 0};
+    bool have = false, have_small = false;
+    auto consider = [&](int a_nr, int a_tile, int bp, int stages_a, int cap) {
+        const int n_b = slots * ((a.d_in + b_pass * bp - 1) / (b_pass * bp));
+        const int grid = a.n_route + n_a_for(a_tile) + n_b;
+        const Layout l{a_nr, a_tile, bp, grid, stages_a + bp * n_chunk_b - 1};
+        if (!have_small || grid < smallest.grid) { smallest = l; have_small = true; }
+        if (cap > 0 && grid > cap) return false;
+        if (!have || l.cost < best.cost) { best = l; have = true; }
+        return true;
+    };
+    for (int bp = 1; bp <= 16 && b_pass * bp <= 4 * kWave * kLayerNRB; bp *= 2) {
+        if (bp > 1 && b_pass * (bp / 2) >= a.d_in) break;     // one tile already covers d_in
+        if (cpr <= (1 << a.a_lr_shift)) consider(kLayerNRA, single, bp, 1, cap1);
+        for (int passes = 1; passes <= 8; ++passes)
+            if (consider(kLayerNRA2, piped * passes, bp, passes * n_chunk_a, cap2)) break;
     }
-    a.a_tile = base_tile * passes;
+    const Layout &l = have ? best : smallest;
+    p.a_nr = l.a_nr;
+    a.a_tile = l.a_tile;
     a.a_tiles_r = (a.d_ff + a.a_tile - 1) / a.a_tile;
     a.a_tiles_s = a.S > 0 ? (dff_s + a.a_tile - 1) / a.a_tile : 0;
-    p.grid = a.n_route + a.K * a.a_tiles_r + a.S * a.a_tiles_s + n_b;
+    a.b_tile = b_pass * l.bp;
+    a.b_tiles = (a.d_in + a.b_tile - 1) / a.b_tile;
+    p.grid = a.n_route + a.K * a.a_tiles_r + a.S * a.a_tiles_s + slots * a.b_tiles;
     a.by_xcd = slots == 8 && a.n_route % 8 == 0 && (a.S == 0 || a.a_tiles_s == a.a_tiles_r) ? 1 : 0;
 }
 
