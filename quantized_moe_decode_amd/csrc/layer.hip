@@ -139,12 +139,13 @@ static int resident_capacity(LayerFn k, size_t lds) {
 // every chunk position; only its first stage is loaded before act arrives.
 // Among the layouts whose grid fits the resident capacity (every unit
 // issues its loads from the start of the launch, and no unit waits for a
-// slot to free up), take the one with the fewest serial stages: a kernel-A
-// unit's stages plus a kernel-B unit's stages after act (measured: the
-// dots.llm1-shaped layer 50.7 us with single-pass B units that do not all fit,
-// 37.8 us with 4-pass B units and 2-pass A units; the Qwen1.5-shaped layer is
-// best with single-pass B units).  Ties go to single-stage A units, then to
-// fewer B passes; if nothing fits, the smallest grid.
+// slot to free up; the router workgroups' slots count, as they free up
+// early), take the one with the fewest serial stages: a kernel-A unit's
+// stages plus a kernel-B unit's stages after act (measured: the
+// dots.llm1-shaped layer 50.7 us with single-pass B units that do not all
+// fit, 37.8 us with 4-pass B units and 2-pass A units; the Qwen1.5-shaped
+// layer is best with single-pass B units).  Ties go to single-stage A
+// units, then to fewer B passes; if nothing fits, the smallest grid.
 // cap1, cap2: resident capacity with single-stage and with pipelined units
 // (0 if unknown).
 static void fit_a_passes(LayerPlan &p, int cap1, int cap2) {
@@ -169,7 +170,9 @@ static void fit_a_passes(LayerPlan &p, int cap1, int cap2) {
         const int grid = a.n_route + n_a_for(a_tile) + n_b;
         const Layout l{a_nr, a_tile, bp, grid, stages_a + bp * n_chunk_b - 1};
         if (!have_small || grid < smallest.grid) { smallest = l; have_small = true; }
-        if (cap > 0 && grid > cap) return false;
+        // the router workgroups exit within ~2 us, long before routing is
+        // done, so up to n_route units past the capacity start in their place
+        if (cap > 0 && grid > cap + a.n_route) return false;
         if (!have || l.cost < best.cost) { best = l; have = true; }
         return true;
     };

@@ -44,7 +44,9 @@
 
 namespace moe {
 
-constexpr int kLayerNRA = 4;        // rows per lane group, kernel A units with a single stage
+constexpr int kLayerNRA = 3;        // rows per lane group, kernel A units with a single stage: 12-row
+                                    // units put exactly two on each CU at the Qwen3-30B-A3B shape
+                                    // (16-row units put two on half of them, which finished last)
 constexpr int kLayerNRA2 = 2;       // rows per lane group and stage, kernel A units with several (two in flight)
 constexpr int kLayerNRB = 4;        // rows per lane group, kernel B units
 constexpr int kCtrStride = 64;      // uint32 words between control words (256 bytes)
@@ -268,13 +270,14 @@ __device__ __forceinline__ void a_epilogue(const LayerArgs &a, int lrs, float (&
     const int lane = threadIdx.x & (kWave - 1);
     with_width(lrs, [&](auto w) {
         constexpr int W = decltype(w)::value;
-        constexpr int V = 2 * NR;
+        constexpr int NRP = NR <= 1 ? 1 : NR <= 2 ? 2 : NR <= 4 ? 4 : 8;    // NR rounded up to a power of two
+        constexpr int V = 2 * NRP;
         if constexpr (W >= 16 && W >= V) {
             float sv[V];
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int n = 0; n < NR; ++n) sv[m * NR + n] = acc[m][n];
+                for (int n = 0; n < NRP; ++n) sv[m * NRP + n] = n < NR ? acc[m][n] : 0.f;
             group_multi_sum<W, V>(sv);
             const float u = group_partner<W>(sv[0]);
             constexpr int SH = ilog2(W) - ilog2(V);
