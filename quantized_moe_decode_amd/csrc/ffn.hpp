@@ -53,7 +53,8 @@ __device__ __forceinline__ int pair_at(const Work &wk, int i) { return wk.pairs 
 // Rows of one lane group processed together: the loads of all of them are
 // issued before any is consumed, so each lane keeps several 16-byte loads in
 // flight.
-constexpr int kNR = 4;
+constexpr int kNR = 3;          // rows per lane group, single- and multi-token kernels (12-row workgroups:
+                                // two per CU for the Qwen3-shaped gate/up)
 
 // Small-batch decode: the bucketing splits an expert's token list into work
 // items of at most kBatchTok tokens, so a workgroup stages its tokens' inputs
