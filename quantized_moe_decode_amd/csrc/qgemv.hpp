@@ -34,26 +34,57 @@ struct BlockRegs {
 
 // Loads of NR rows x NM matrices at chunk position c.  Rows past row_end and
 // chunks past the row read an in-bounds neighbour (the same cache lines) and
-// are masked out in dot_block, so the loads need no branches.
-template <int BITS, int NM, int NR>
+// are masked out in dot_block, so the loads need no branches.  With SBASE,
+// erow0 (the expert's first row, the same for the whole wave) gives the
+// expert's base addresses once in scalar registers and each lane adds a
+// 32-bit offset (24-bit multiplies: rows and row lengths are at most 8192),
+// so a load costs a couple of vector instructions instead of a 64-bit
+// address computation; without it every address is formed per lane in 64
+// bits, which schedules better in some kernels.
+template <int BITS, int NM, int NR, bool SBASE = true>
 __device__ __forceinline__ void load_block(BlockRegs<BITS, NM, NR> &R, const QM *mats, int64_t erow0,
                                            int r0, int rstep, int row_end, int c, int cpr) {
     using F = Fmt<BITS>;
     const bool okc = c < cpr;
     R.cc = okc ? c : 0;
+    if constexpr (!SBASE) {
 #pragma unroll
-    for (int n = 0; n < NR; ++n) R.live[n] = okc && (r0 + n * rstep < row_end);
+        for (int n = 0; n < NR; ++n) R.live[n] = okc && (r0 + n * rstep < row_end);
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int n = 0; n < NR; ++n) {
+                const int64_t row = erow0 + min(r0 + n * rstep, row_end - 1);
+                R.w[m][n] = load_chunk<BITS>(mats[m].q + row * mats[m].wpr + R.cc * F::kWords);
+                const int64_t gi = row * mats[m].gpr + R.cc / F::kChunksPerGroup;
+                R.sr[m][n] = mats[m].s[gi];
+                R.br[m][n] = mats[m].b[gi];
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        return;
+    }
+    const uint32_t e_lo = __builtin_amdgcn_readfirstlane((uint32_t)erow0);
+    const uint32_t e_hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)erow0 >> 32));
+    const int64_t er = (int64_t)(((uint64_t)e_hi << 32) | e_lo);
+    uint32_t rr[NR];
+#pragma unroll
+    for (int n = 0; n < NR; ++n) {
+        R.live[n] = okc && (r0 + n * rstep < row_end);
+        rr[n] = (uint32_t)min(r0 + n * rstep, row_end - 1);
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        const uint32_t *qb = mats[m].q + er * mats[m].wpr;
+        const uint16_t *sb = mats[m].s + er * mats[m].gpr;
+        const uint16_t *bb = mats[m].b + er * mats[m].gpr;
 #pragma unroll
         for (int n = 0; n < NR; ++n) {
-            const int r = min(r0 + n * rstep, row_end - 1);
-            const int64_t row = erow0 + r;
-            R.w[m][n] = load_chunk<BITS>(mats[m].q + row * mats[m].wpr + R.cc * F::kWords);
-            const int64_t gi = row * mats[m].gpr + R.cc / F::kChunksPerGroup;
-            R.sr[m][n] = mats[m].s[gi];
-            R.br[m][n] = mats[m].b[gi];
+            R.w[m][n] = load_chunk<BITS>(qb + (__umul24(rr[n], (uint32_t)mats[m].wpr) + (uint32_t)R.cc * F::kWords));
+            const uint32_t gi = __umul24(rr[n], (uint32_t)mats[m].gpr) + (uint32_t)R.cc / F::kChunksPerGroup;
+            R.sr[m][n] = sb[gi];
+            R.br[m][n] = bb[gi];
         }
+    }
     // Keep every load of the block here: left alone, the compiler sinks the
     // scale/bias loads down to their first use, after the codes have arrived,
     // which costs a second memory round trip per block.
