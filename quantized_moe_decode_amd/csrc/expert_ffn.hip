@@ -374,6 +374,19 @@ static int pick_lr_shift(int cpr) {
     return s;
 }
 
+// Lanes per row for the multi-token kernels: the power of two (8 to 64) that
+// leaves the fewest idle lanes over a row's chunks, the larger on a tie
+// (768 inputs, 24 chunks: 8 lanes looping three times rather than 32 lanes
+// of which 8 idle).
+static int pick_lr_shift_dense(int cpr) {
+    int best = 6, best_slots = ((cpr + 63) >> 6) << 6;
+    for (int s = 5; s >= 3; --s) {
+        const int slots = ((cpr + (1 << s) - 1) >> s) << s;
+        if (slots < best_slots) best = s, best_slots = slots;
+    }
+    return best;
+}
+
 static QM to_qm(const moe_qmat *m) {
     QM q;
     q.q = m->q;
@@ -482,15 +495,16 @@ static moe_status geometry(FfnArgs &a, int maxt, int cols, int bits, size_t &lds
 // covers `passes` row passes of a workgroup.  More passes amortise a
 // workgroup's staging of its tokens' inputs; measured on the 32-token
 // Qwen3-shaped step (per-launch averages): gate/up 68.8 / 61.5 / 59.3 /
-// 63.1 us at 1 / 2 / 4 / 8 passes, down 44.9 / 42.4 / 43.5 / 47.4 us at
-// 1 / 2 / 4 / 8.
+// 63.1 us at 1 / 2 / 4 / 8 passes.  Down (768 inputs: 8 lanes per row, 2
+// rows per lane group) is fastest with a single pass: its workgroups are
+// small and many, six per CU.
 constexpr int kBatchPassesA = 4;
-constexpr int kBatchPassesB = 2;
+constexpr int kBatchPassesB = 1;
 static KernelFn batch_geometry(FfnArgs &a, int cols, int bits, int nr, int passes, KernelFn k, size_t &lds) {
     if (bits != 4 || !k) return nullptr;
     lds = batch_lds_bytes(cols);
     if (lds > kLdsBudget) return nullptr;
-    a.lr_shift = pick_lr_shift(cols / 32);
+    a.lr_shift = pick_lr_shift_dense(cols / 32);
     a.rows_per_wg = passes * 4 * (kWave >> a.lr_shift) * nr;
     a.tpp = kBatchTok;
     return k;

@@ -69,6 +69,6 @@ KernelFn batch_gate_up_q4(int sb);
 KernelFn batch_down_q4(int sb);
 size_t batch_lds_bytes(int cols);
 constexpr int kBatchNRA = 2;     // rows per lane group, kernel A (2 matrices x 4 tokens of accumulators)
-constexpr int kBatchNRB = 4;     // rows per lane group, kernel B
+constexpr int kBatchNRB = 2;     // rows per lane group, kernel B
 
 }  // namespace moe

@@ -34,6 +34,7 @@ SMALL = [
     dict(x_dtype=mi.F16, router_dtype=mi.F16, resid_dtype=mi.F16, renormalize=False),
     dict(d_in=64, d_ff=64, n_experts=3, top_k=1),             # smallest legal shapes
     dict(d_in=1088, d_ff=704, n_experts=9, top_k=4, bits_down=6),  # odd group counts
+    dict(d_in=1088, d_ff=704, n_experts=9, top_k=4),          # 4-bit, rows of 34 and 22 chunks
 ]
 
 
