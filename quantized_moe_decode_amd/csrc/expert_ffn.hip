@@ -221,42 +221,58 @@ __global__ __launch_bounds__(256) void down_kernel(FfnArgs a) {
 // for in-range buckets that rank is the number of earlier tokens in the
 // bucket's token mask; ids that repeat within a token, and the out-of-range
 // bucket, take the direct count instead.
-constexpr int kBucketThreads = 1024;
-constexpr int kScanMax = 2048;      // entries a block scan handles (E + 2 <= 1026)
+constexpr int kBucketThreads = 256;
+constexpr int kScanMax = MOE_MAX_EXPERTS + 2;   // bucket entries (E + 1 buckets and the total)
 
-// Exclusive prefix sums of a[0..n] and b[0..n] together, in place (entry n
-// receives the total; n < kScanMax), by a Hillis-Steele scan over the next
-// power of two above n, ping-ponging with ta/tb (kScanMax entries each).  All
-// threads of the block call it; it ends with a barrier.
-__device__ void block_exclusive_scan2(int *a, int *b, int *ta, int *tb, int n) {
-    const int tid = threadIdx.x;
-    int m = 1;
-    while (m < n + 1) m <<= 1;
-    for (int i = tid; i < m; i += blockDim.x) {
-        const bool in = i >= 1 && i <= n;
-        ta[i] = in ? a[i - 1] : 0;
-        tb[i] = in ? b[i - 1] : 0;
+// Exclusive prefix sums of a[0..n) and b[0..n) together, in place; a[n] and
+// b[n] receive the totals.  Thread t owns a run of consecutive entries: the
+// runs' sums are scanned across each wave with lane shuffles and across the
+// waves through LDS, then every thread rewrites its own run, so the whole
+// scan takes two barriers.  All threads of the block call it.
+__device__ void block_exclusive_scan2(int *a, int *b, int n) {
+    __shared__ int wsum_a[kBucketThreads / kWave], wsum_b[kBucketThreads / kWave];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, nw = blockDim.x / kWave;
+    const int per = (n + blockDim.x - 1) / blockDim.x;
+    const int i0 = min(tid * per, n), i1 = min(i0 + per, n);
+    int ra = 0, rb = 0;
+    for (int i = i0; i < i1; ++i) {
+        ra += a[i];
+        rb += b[i];
+    }
+    int xa = ra, xb = rb;     // inclusive scan of the run sums over the wave
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int ya = __shfl_up(xa, d), yb = __shfl_up(xb, d);
+        if (lane >= d) {
+            xa += ya;
+            xb += yb;
+        }
+    }
+    if (lane == kWave - 1) {
+        wsum_a[wave] = xa;
+        wsum_b[wave] = xb;
     }
     __syncthreads();
-    int *sa = ta, *sb = tb, *da = a, *db = b;
-    for (int d = 1; d < m; d <<= 1) {
-        for (int i = tid; i < m; i += blockDim.x) {
-            da[i] = sa[i] + (i >= d ? sa[i - d] : 0);
-            db[i] = sb[i] + (i >= d ? sb[i - d] : 0);
+    int pa = xa - ra, pb = xb - rb, ta = 0, tb = 0;
+    for (int w = 0; w < nw; ++w) {
+        if (w < wave) {
+            pa += wsum_a[w];
+            pb += wsum_b[w];
         }
-        __syncthreads();
-        int *t = sa;
-        sa = da;
-        da = t;
-        t = sb;
-        sb = db;
-        db = t;
+        ta += wsum_a[w];
+        tb += wsum_b[w];
     }
-    if (sa != a)
-        for (int i = tid; i < m; i += blockDim.x) {
-            a[i] = sa[i];
-            b[i] = sb[i];
-        }
+    for (int i = i0; i < i1; ++i) {
+        const int va = a[i], vb = b[i];
+        a[i] = pa;
+        b[i] = pb;
+        pa += va;
+        pb += vb;
+    }
+    if (tid == 0) {
+        a[n] = ta;
+        b[n] = tb;
+    }
     __syncthreads();
 }
 
@@ -266,7 +282,6 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t *i
                                                                 int32_t *n_work) {
     __shared__ int off[kScanMax];       // pairs, then first pair, per bucket (bucket E: out-of-range ids)
     __shared__ int ioff[kScanMax];      // work items, then first work item, per bucket
-    __shared__ int tmp[kScanMax], tmp2[kScanMax];
     __shared__ int cnt[MOE_MAX_EXPERTS + 1];
     __shared__ uint32_t tmask[MOE_MAX_EXPERTS + 1];     // tokens with a pair in the bucket
     __shared__ __align__(16) int bucket[MOE_MAX_TOKENS * MOE_MAX_TOP_K];
@@ -295,7 +310,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t *i
         ioff[i] = (cnt[i] + max_tok - 1) / max_tok;
     }
     __syncthreads();
-    block_exclusive_scan2(off, ioff, tmp, tmp2, nb);    // off[nb] = n_pairs, ioff[nb] = work items
+    block_exclusive_scan2(off, ioff, nb);    // off[nb] = n_pairs, ioff[nb] = work items
     // a pair's rank among the earlier pairs of its bucket
     const int4 *b4 = reinterpret_cast<const int4 *>(bucket);
     const bool repeat = s_repeat != 0;
