@@ -295,3 +295,34 @@ def test_repeated_runs_are_bit_identical_and_graph_replays_match():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), a["out"]), rep
+
+
+def test_batch_graph_replays_match_eager():
+    """32 tokens (routing, bucketing, the multi-token kernels, tail) captured
+    once and replayed four times with eager work on the same buffers between
+    the replays: every replay equals the eager result bit for bit."""
+    cfg = mi.QWEN3_B32
+    say("case graph replays, 32 tokens (qwen3 layer 0)")
+    w = mi.gen_layer_weights(cfg, 0)
+    x, resid = margin_tokens(cfg, 0, w, 32)
+    a, layer = run_gpu_layer(cfg, w, x, resid)
+    from quantized_moe_decode_amd.layer import tensor_from_encoded
+    xd = tensor_from_encoded(x, cfg.x_dtype, DEV)
+    rd = tensor_from_encoded(resid, cfg.resid_dtype, DEV)
+    out = torch.zeros(32, cfg.d_in, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(xd, rd, out)
+    torch.cuda.current_stream().wait_stream(s)
+    assert np.array_equal(out.cpu().numpy(), a["out"])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(xd, rd, out)
+    for rep in range(4):
+        out.fill_(-1.0)
+        layer.partial.fill_(3.0)          # eager work between replays
+        layer.act.fill_(-2.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), a["out"]), rep
