@@ -19,20 +19,28 @@ struct TailArgs {
     int resid_dt, T, K, D, S;
 };
 
+// p[0] + p[D] + ... + p[(n-1) D], added in that order; the loads are issued
+// eight at a time so that they are in flight together.
+__device__ __forceinline__ float sum_rows(const float *p, int n, int D) {
+    float sum = 0.f;
+    for (int k0 = 0; k0 < n; k0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = k0 + u < n ? p[(int64_t)(k0 + u) * D] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (k0 + u < n) sum = k0 + u == 0 ? v[u] : sum + v[u];
+    }
+    return sum;
+}
+
 __global__ __launch_bounds__(256) void tail_kernel(TailArgs a) {
     const int64_t n = (int64_t)a.T * a.D;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= n) return;
     const int t = (int)(idx / a.D), i = (int)(idx % a.D);
-    const float *p = a.partial + (int64_t)t * a.K * a.D + i;
-    float routed = p[0];
-    for (int k = 1; k < a.K; ++k) routed += p[(int64_t)k * a.D];
-    float sh = 0.f;
-    if (a.S > 0) {
-        const float *s = a.shared + (int64_t)t * a.S * a.D + i;
-        sh = s[0];
-        for (int k = 1; k < a.S; ++k) sh += s[(int64_t)k * a.D];
-    }
+    const float routed = sum_rows(a.partial + (int64_t)t * a.K * a.D + i, a.K, a.D);
+    const float sh = a.S > 0 ? sum_rows(a.shared + (int64_t)t * a.S * a.D + i, a.S, a.D) : 0.f;
     const float g = a.gate ? a.gate[t] : 1.0f;
     a.out[idx] = load_act(a.resid, a.resid_dt, idx) + (routed + sh * g);
 }
