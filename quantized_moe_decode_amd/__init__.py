@@ -9,7 +9,7 @@ mirror the C ABI in ``include/moe_decode.h``:
                            (down * score -> partial) for the selected experts
     moe_decode_tail        out = resid + (sum_k partial_k + shared * gate)
 
-The library must be built (``python -m quantized_moe_decode_amd.build``);
+The library must be built (``python quantized_moe_decode_amd/build.py``);
 importing this module without it raises ImportError -- there is no fallback.
 """
 from __future__ import annotations
@@ -53,7 +53,7 @@ class CLayerWeights(ctypes.Structure):
 
 def _load_library():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_moe_decode_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python quantized_moe_decode_amd/build.py`")
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     L.moe_decode_route.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, i32, vp, i32,

@@ -1,6 +1,6 @@
 """Build libmoe_decode.so for gfx950 in-tree with hipcc.
 
-    python -m quantized_moe_decode_amd.build
+    python quantized_moe_decode_amd/build.py
 
 Each HIP source is compiled to an object under ``_build/`` (in parallel) and
 linked into ``quantized_moe_decode_amd/lib/libmoe_decode.so``.  Packed FP32
