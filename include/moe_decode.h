@@ -41,13 +41,14 @@
 extern "C" {
 #endif
 
-#define MOE_DECODE_ABI_VERSION 1
+#define MOE_DECODE_ABI_VERSION 2
 
 typedef enum {
     MOE_OK = 0,
     MOE_EINVAL = 1,        /* null pointer, inconsistent shape, out-of-range size, misalignment */
     MOE_EUNSUPPORTED = 2,  /* bit width, group size or dtype combination that is not built */
-    MOE_EHIP = 3           /* the HIP runtime reported an error when launching */
+    MOE_EHIP = 3,          /* the HIP runtime reported an error when launching */
+    MOE_ETIMEOUT = 4       /* recorded in a workspace: a wait inside a launch ran out (moe_decode_workspace_status) */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
@@ -101,10 +102,16 @@ typedef struct {
  *   shared_gate out float [n_tokens]; must be NULL iff w_shared_gate is NULL
  *   workspace   device scratch of at least moe_decode_route_workspace_bytes(),
  *               16-byte aligned; zero-filled before its first use and not
- *               written by the caller afterwards: each call leaves it in the
- *               state the next call expects (its flagged logit words back at
- *               zero).  Calls that may run concurrently need separate
- *               workspaces.
+ *               written by the caller afterwards: it carries a launch epoch
+ *               from call to call, and each call leaves it in the state the
+ *               next call expects.  The router logits travel between the
+ *               launch's workgroups as words tagged with that epoch, so no
+ *               word of an earlier call can be taken for one of this call.
+ *               Every internal wait is bounded; if one runs out (possible only
+ *               when other work starves the launch for a long time) the
+ *               workspace's error word is raised, stays raised, and
+ *               moe_decode_workspace_status reports MOE_ETIMEOUT.  Calls that
+ *               may run concurrently need separate workspaces.
  * Limits: 1 <= n_tokens <= 32, 1 <= top_k <= min(n_experts, 32),
  *         n_experts <= 1024, d_in a multiple of 64 and <= 8192.
  */
@@ -116,6 +123,19 @@ moe_status moe_decode_route(const void *x, moe_dtype x_dtype, int32_t n_tokens, 
                             void *workspace, size_t workspace_bytes, void *stream);
 
 size_t moe_decode_route_workspace_bytes(int32_t n_tokens, int32_t n_experts);
+
+/*
+ * Status recorded in the workspace of moe_decode_route or moe_decode_layer.
+ * `head` is a host copy of the first MOE_WORKSPACE_HEAD_BYTES bytes of the
+ * workspace, taken after the stream has passed the calls of interest (the
+ * library itself never copies device memory).  Returns MOE_OK, or
+ * MOE_ETIMEOUT when a wait inside some launch that used the workspace ran out
+ * since the workspace was last zero-filled (that launch's results are
+ * invalid); MOE_EINVAL for a null `head` or head_bytes <
+ * MOE_WORKSPACE_HEAD_BYTES.  Host-only; no device access.
+ */
+#define MOE_WORKSPACE_HEAD_BYTES 4
+moe_status moe_decode_workspace_status(const void *head, size_t head_bytes);
 
 /*
  * Expert FFN (mlxcel PR #276, "What changed" step 2).  For every token t and
@@ -211,9 +231,11 @@ moe_status moe_decode_tail(const float *partial, int32_t n_tokens, int32_t top_k
  * aligned, zero-filled before its first use and not written by the caller
  * afterwards (each launch leaves it ready for the next).  Its first 4 bytes
  * become nonzero, and stay so, if an internal wait ever timed out (results of
- * that launch invalid); this cannot happen unless the device is shared with
- * work that starves the launch for a long time.  Launches that may run
- * concurrently need separate workspaces.
+ * that launch invalid; moe_decode_workspace_status reports MOE_ETIMEOUT); this
+ * cannot happen unless the device is shared with work that starves the launch
+ * for a long time.  Launches that may run concurrently need separate
+ * workspaces; launches in order on one stream may share one workspace, also
+ * across layers of different shapes, if it has the largest layer's size.
  */
 #define MOE_MAX_SHARED 8
 

@@ -258,6 +258,20 @@ def gen_tokens(cfg: LayerConfig, layer: int, n_tokens: int, attempts: Optional[S
     return np.stack(xs), np.stack(rs)
 
 
+def gen_layer_weights_for(cfg: LayerConfig, layer: int, experts: Sequence[int],
+                          threads: int = 8) -> dict:
+    """A layer's weights with the routed stacks holding only the listed experts
+    (stack entry i is expert experts[i]); router and shared tensors complete."""
+    out = {p: gen_proj_stack(cfg, layer, p, experts=experts, threads=threads)
+           for p in ("gate", "up", "down")}
+    out["router"] = gen_router(cfg, layer)
+    if cfg.n_shared:
+        for p in ("shared_gate_proj", "shared_up", "shared_down"):
+            out[p] = gen_proj_stack(cfg, layer, p, threads=threads)
+    out["shared_gate_w"] = gen_shared_gate_w(cfg, layer) if cfg.shared_gate else None
+    return out
+
+
 def gen_layer_weights(cfg: LayerConfig, layer: int, jitter_bias: bool = False,
                       threads: int = 8) -> dict:
     """Every weight tensor of one layer: routed stacks, router, and shared stacks if any."""

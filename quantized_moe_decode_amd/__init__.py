@@ -24,7 +24,8 @@ import torch  # first: the library then binds to torch's HIP runtime
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "lib", "libmoe_decode.so")
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, 1, 2, 3
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ETIMEOUT = 0, 1, 2, 3, 4
+MOE_WORKSPACE_HEAD_BYTES = 4
 MOE_F32, MOE_F16, MOE_BF16 = 0, 1, 2
 TORCH_DTYPE_CODE = {torch.float32: MOE_F32, torch.float16: MOE_F16, torch.bfloat16: MOE_BF16}
 
@@ -82,6 +83,8 @@ def _load_library():
     L.moe_decode_read_probe.restype = i32
     L.moe_decode_read_probe_blocks.argtypes = [sz]
     L.moe_decode_read_probe_blocks.restype = i32
+    L.moe_decode_workspace_status.argtypes = [vp, sz]
+    L.moe_decode_workspace_status.restype = i32
     L.moe_decode_status_string.argtypes = [i32]
     L.moe_decode_status_string.restype = ctypes.c_char_p
     L.moe_decode_abi_version.restype = i32
@@ -146,6 +149,13 @@ class QuantStack:
         """Weight bytes of `experts` experts (codes + scales + biases)."""
         per = (self.q[0].numel() * 4 + self.scales[0].numel() * 2 + self.biases[0].numel() * 2)
         return per * experts
+
+
+def workspace_status(workspace: torch.Tensor) -> int:
+    """MOE_OK or MOE_ETIMEOUT for the workspace of moe_decode_route or
+    moe_decode_layer (copies its first bytes to the host; synchronises)."""
+    head = workspace.view(torch.uint8)[:MOE_WORKSPACE_HEAD_BYTES].cpu().numpy()
+    return int(lib.moe_decode_workspace_status(head.ctypes.data_as(ctypes.c_void_p), head.nbytes))
 
 
 def route_workspace_bytes(n_tokens: int, n_experts: int) -> int:
@@ -273,5 +283,5 @@ __all__ = ["QuantStack", "DecodeLayer", "moe_decode_route", "moe_decode_expert_f
            "moe_decode_layer", "layer_weights", "layer_workspace_bytes",
            "moe_decode_gate_up", "moe_decode_down",
            "moe_decode_tail", "route_workspace_bytes", "expert_ffn_workspace_bytes",
-           "moe_decode_read_probe", "read_probe_blocks",
+           "moe_decode_read_probe", "read_probe_blocks", "workspace_status",
            "MoeError", "status_string", "abi_version", "lib"]

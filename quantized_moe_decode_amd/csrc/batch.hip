@@ -11,7 +11,11 @@
 // codes of a word are turned into a 16-bit pair once and multiplied into
 // every token's accumulator:
 //   kernel A: bf16 x, codes as bf16 128 + q, bias folded as b - 128 s;
-//   kernel B: act rounded to fp16, codes as exact fp16 q.
+//   kernel B: act rounded to fp16 after a power-of-two scaling per chunk
+//             (f16_stage_scale: the chunk's largest value lands in
+//             [2^14, 2^15), so nothing overflows and nothing becomes an fp16
+//             subnormal), codes as exact fp16 q, the chunk's contribution
+//             scaled back.
 #include <hip/hip_runtime.h>
 
 #include "api.hpp"
@@ -21,14 +25,32 @@
 
 namespace moe {
 
-constexpr int kRec = 80;         // bytes per staged chunk: 64 of pairs, the chunk sum, padding
+constexpr int kRec = 80;         // bytes per staged chunk: 64 of pairs, the chunk sum, its staging scale, padding
+constexpr int kRecSum = 64;
+constexpr int kRecScale = 68;
 
 size_t batch_lds_bytes(int cols) { return (size_t)kBatchTok * (cols / 32) * kRec; }
+
+// Pairs (v[8k+p], v[8k+p+4]) of 8 consecutive 16-bit inputs held as 4 words.
+__device__ __forceinline__ u32x4 pair_words(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+    u32x4 v;
+    v[0] = __builtin_amdgcn_perm(w2, w0, 0x05040100u);
+    v[1] = __builtin_amdgcn_perm(w2, w0, 0x07060302u);
+    v[2] = __builtin_amdgcn_perm(w3, w1, 0x05040100u);
+    v[3] = __builtin_amdgcn_perm(w3, w1, 0x07060302u);
+    return v;
+}
 
 // Quad sum (lanes 4i..4i+3 end with the same value).
 __device__ __forceinline__ float quad_sum(float v) {
     v += dpp_f<0xB1>(v);
     return v + dpp_f<0x4E>(v);
+}
+
+// Quad maximum of unsigned values (lanes 4i..4i+3 end with the same value).
+__device__ __forceinline__ uint32_t quad_max_u(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xf, 0xf, false));
+    return max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xf, 0xf, false));
 }
 
 // Stage nt tokens' inputs.  Thread i handles token t, chunk c, word k (8
@@ -49,7 +71,52 @@ __device__ __forceinline__ void stage_pairs(char *lds, int nt, int cpr, Src src)
         if (ok) {
             char *rec = lds + (t * cpr + c) * kRec;
             *reinterpret_cast<u32x4 *>(rec + k * 16) = v;
-            if (k == 0) *reinterpret_cast<float *>(rec + 64) = sum;
+            if (k == 0) *reinterpret_cast<float *>(rec + kRecSum) = sum;
+        }
+    }
+}
+
+// Stage nt act vectors (fp32 [.., cpr*32]) as fp16 pairs, every chunk of 32
+// scaled by its power-of-two staging factor (stored at kRecScale).  Thread i
+// handles act row t, chunk c, word k (8 values); the four k of a chunk are a
+// quad, whose maximum gives the chunk's factor.
+__device__ __forceinline__ void stage_act_f16(char *lds, int nt, int cpr, const Work &wk, const float *act,
+                                              int d_ff) {
+    const int n = nt * cpr * 4;
+    for (int i0 = 0; i0 < n; i0 += blockDim.x) {       // uniform trip count: whole quads
+        const int i = i0 + threadIdx.x;
+        const bool ok = i < n;
+        const int k = i & 3, tc = i >> 2;
+        const int t = ok ? tc / cpr : 0, c = ok ? tc - t * cpr : 0;
+        float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (ok) {
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(act + (int64_t)pair_at(wk, t) * d_ff + c * 32 + k * 8);
+            const f32x4 lo = src[0], hi = src[1];
+            f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+            f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+        }
+        uint32_t m = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = max(m, __float_as_uint(f[e]) & 0x7FFFFFFFu);
+        float inv;
+        const float cs = f16_stage_scale(quad_max_u(m), inv);
+        uint32_t h[8];
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const _Float16 q = (_Float16)(f[e] * inv);
+            sum += (float)q;
+            h[e] = __builtin_bit_cast(uint16_t, q);
+        }
+        sum = quad_sum(sum);
+        if (ok) {
+            char *rec = lds + (t * cpr + c) * kRec;
+            *reinterpret_cast<u32x4 *>(rec + k * 16) =
+                pair_words(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+            if (k == 0) {
+                *reinterpret_cast<float *>(rec + kRecSum) = sum;
+                *reinterpret_cast<float *>(rec + kRecScale) = cs;
+            }
         }
     }
 }
@@ -69,16 +136,6 @@ __device__ __forceinline__ void with_tokens(int nt, Fn fn) {
     static_assert(kBatchTok == 4, "token dispatch covers 1..4");
     if (nt <= 2) fn(TokC<2>{});
     else fn(TokC<4>{});
-}
-
-// Pairs (v[8k+p], v[8k+p+4]) of 8 consecutive 16-bit inputs held as 4 words.
-__device__ __forceinline__ u32x4 pair_words(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
-    u32x4 v;
-    v[0] = __builtin_amdgcn_perm(w2, w0, 0x05040100u);
-    v[1] = __builtin_amdgcn_perm(w2, w0, 0x07060302u);
-    v[2] = __builtin_amdgcn_perm(w3, w1, 0x05040100u);
-    v[3] = __builtin_amdgcn_perm(w3, w1, 0x07060302u);
-    return v;
 }
 
 // Kernel A: gate and up projections of one work item over a tile of rows, then SwiGLU.
@@ -163,7 +220,7 @@ __global__ __launch_bounds__(256) void gate_up_batch_q4(FfnArgs a) {
                 }
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const float xsum = *reinterpret_cast<const float *>(lds + (t * cpr + R.cc) * kRec + 64);
+                    const float xsum = *reinterpret_cast<const float *>(lds + (t * cpr + R.cc) * kRec + kRecSum);
 #pragma unroll
                     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -249,22 +306,7 @@ __global__ __launch_bounds__(256, 6) void down_batch_q4(FfnArgs a) {
         return;
     }
     const int cpr = a.d_ff / 32;
-    stage_pairs(lds, nt, cpr, [&](int t, int c, int k, u32x4 &v) {
-        const int64_t p = pair_at(wk, t);
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(a.act + p * a.d_ff + c * 32 + k * 8);
-        const f32x4 lo = src[0], hi = src[1];
-        const float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        uint32_t h[8];
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const _Float16 q = (_Float16)f[i];
-            s += (float)q;
-            h[i] = __builtin_bit_cast(uint16_t, q);
-        }
-        v = pair_words(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-        return s;
-    });
+    stage_act_f16(lds, nt, cpr, wk, a.act, a.d_ff);
     __syncthreads();
 
     const int lr = 1 << a.lr_shift, j = lane & (lr - 1), rsub = lane >> a.lr_shift, rpw = kWave >> a.lr_shift;
@@ -313,12 +355,14 @@ __global__ __launch_bounds__(256, 6) void down_batch_q4(FfnArgs a) {
                 }
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const float asum = *reinterpret_cast<const float *>(lds + (t * cpr + R.cc) * kRec + 64);
+                    const char *rec = lds + (t * cpr + R.cc) * kRec;
+                    const float asum = *reinterpret_cast<const float *>(rec + kRecSum);
+                    const float cs = *reinterpret_cast<const float *>(rec + kRecScale);
 #pragma unroll
                     for (int n = 0; n < NR; ++n) {
                         const float s = R.live[n] ? sb_to_float<SB>(R.sr[0][n]) : 0.f;
                         const float b = R.live[n] ? sb_to_float<SB>(R.br[0][n]) : 0.f;
-                        acc[n][t] += s * d[n][t] + b * asum;
+                        acc[n][t] += (s * d[n][t] + b * asum) * cs;
                     }
                 }
             }

@@ -182,6 +182,39 @@ __device__ __forceinline__ void gather_tagged(const LayerArgs &a, int n, const u
     }
 }
 
+// The act gather of a kernel-B unit with 4-bit down weights: act[0, n) (n a
+// multiple of 32) into LDS as fp16 pair chunks of 32 values (kF16ChunkBytes
+// each, pairs placed as dot_block_q4_f16 reads them), every chunk scaled by
+// its power-of-two staging factor, which is stored beside the chunk.  With a
+// block of 256 threads and batches of 256 consecutive elements, the 32
+// elements of a chunk are 32 consecutive lanes of one wave, so its largest
+// magnitude is a 32-lane reduction; all lanes take part (elements past n
+// read as 0).
+__device__ __forceinline__ void gather_act_f16(const LayerArgs &a, int n, const uint64_t *sentinel, uint32_t tag,
+                                               const uint64_t *act, char *lds) {
+    const int nt = blockDim.x, t = threadIdx.x;
+    if (t == 0) (void)wait_tagged<kActSleep>(a, sentinel, tag);
+    __syncthreads();
+    for (int base = 0; base < n; base += kGatherPer * nt) {
+        const int left = n - base - t;
+        const int cnt = left <= 0 ? 0 : min(kGatherPer, (left + nt - 1) / nt);
+        float v[kGatherPer];
+        poll_batch<kGatherPer, kActSleep>(a, tag, cnt, [&](int u) { return act + base + u * nt + t; }, v);
+#pragma unroll
+        for (int u = 0; u < kGatherPer; ++u) {
+            if (base + u * nt >= n) break;                  // the same for the whole block
+            float inv;
+            const float cs = f16_stage_scale(group_max32_u(__float_as_uint(v[u]) & 0x7FFFFFFFu), inv);
+            if (u < cnt) {
+                const int i = base + u * nt + t, c = i >> 5;
+                char *rec = lds + c * kF16ChunkBytes;
+                *reinterpret_cast<_Float16 *>(rec + f16_pair_offset(i & 31)) = (_Float16)(v[u] * inv);
+                if ((i & 31) == 0) *reinterpret_cast<float *>(rec + kF16ScaleOffset) = cs;
+            }
+        }
+    }
+}
+
 __device__ __forceinline__ uint32_t launch_tag(const LayerArgs &a) {
     return __hip_atomic_load(ctr_at(a, kCtrEpoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 }
@@ -518,22 +551,22 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
         const uint64_t *act = a.act + (int64_t)slot * a.act_stride;
         const int n_act = cpr * CODES;
         const uint64_t *sent = a.act_sent + ((int64_t)slot * kActCopies + tile % kActCopies) * kSentStride;
-        // 4-bit down projections take act as fp16 pairs (packed dot); the
-        // others as fp32 chunks
+        // 4-bit down projections take act as fp16 pairs (packed dot), each
+        // chunk scaled by a power of two into fp16's range (f16_stage_scale);
+        // the others take act as fp32 chunks
         constexpr bool kF16 = BB == 4;
         // the first stage's codes unpacked while act is on its way: after it
         // arrives only the dot products remain
         [[maybe_unused]] uint32_t pre[1][NR][16];
-        if constexpr (kF16)
+        if constexpr (kF16) {
             if (n_stage > 0) unpack_q4_f16<1, NR>(cur, pre);
-        gather_tagged<kActSleep>(a, n_act, sent, tag, [&](int i) { return act + i; }, [&](int i, float v) {
-            const int c = i / CODES;
-            if constexpr (kF16)
-                *reinterpret_cast<_Float16 *>(reinterpret_cast<char *>(xs) + c * kF16ChunkBytes +
-                                              f16_pair_offset(i - c * CODES)) = (_Float16)v;
-            else
+            gather_act_f16(a, n_act, sent, tag, act, reinterpret_cast<char *>(xs));
+        } else {
+            gather_tagged<kActSleep>(a, n_act, sent, tag, [&](int i) { return act + i; }, [&](int i, float v) {
+                const int c = i / CODES;
                 xs[c * (CODES + 4) + (i - c * CODES)] = v;
-        });
+            });
+        }
         __syncthreads();
         if (routed) score = sel->scores[slot];
         float acc[1][NR];
@@ -555,9 +588,11 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
 #pragma unroll
                     for (int k = 0; k < 4; ++k) ap[4 * i + k] = v[k];
                 }
+                const float cs = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(src) +
+                                                                  kF16ScaleOffset);
                 if constexpr (BB == 4) {
-                    if (st == 0) dot_pre_q4_f16<SB, 1, NR>(cur, pre, ap, f16_pairs_sum(ap), acc);
-                    else dot_block_q4_f16<SB, 1, NR>(cur, ap, f16_pairs_sum(ap), acc);
+                    if (st == 0) dot_pre_q4_f16<SB, 1, NR>(cur, pre, ap, f16_pairs_sum(ap), cs, acc);
+                    else dot_block_q4_f16<SB, 1, NR>(cur, ap, f16_pairs_sum(ap), cs, acc);
                 }
             } else {
                 float xv[CODES];

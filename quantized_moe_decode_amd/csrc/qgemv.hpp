@@ -278,8 +278,36 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // fp16 inputs of one 4-bit chunk staged for dot_block_q4_f16: 16 pairs, pair
 // 4k + p = (input 8k+p, input 8k+p+4) (the codes a nibble pair of word k
-// holds), then 16 bytes of padding.
+// holds), then the chunk's staging scale (fp32, at byte kF16ScaleOffset) and
+// padding.
 constexpr int kF16ChunkBytes = 16 * 4 + 16;
+constexpr int kF16ScaleOffset = 64;
+
+// Staging scale of a chunk of fp32 values that is rounded to fp16: the values
+// are multiplied by inv = 2^-k before rounding and the chunk's dot products by
+// the returned 2^k afterwards (both exact), with k chosen from the bit pattern
+// m of the chunk's largest magnitude so that the largest scaled value lies in
+// [2^14, 2^15).  Nothing overflows fp16 then, and every value within 2^-28 of
+// the chunk's largest keeps fp16's 11-bit precision (no fp16 subnormals).
+// m's biased exponent e gives |max| in [2^(e-127), 2^(e-126)); inv = 2^(141-e).
+// Exponents below 15 (|max| < 2^-112, zero included) take e = 15, so that
+// both factors are normal floats.
+__device__ __forceinline__ float f16_stage_scale(uint32_t max_abs_bits, float &inv) {
+    const int e = max((int)(max_abs_bits >> 23), 15);
+    inv = __uint_as_float((uint32_t)(268 - e) << 23);
+    return __uint_as_float((uint32_t)(e - 14) << 23);
+}
+
+// Unsigned maximum over aligned groups of 32 lanes; every lane gets its
+// group's.  All 64 lanes must be active.
+__device__ __forceinline__ uint32_t group_max32_u(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xf, 0xf, false));  // row_half_mirror
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xf, 0xf, false));  // row_mirror
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);               // across lane bit 4
+    return max(x, ((threadIdx.x >> 4) & 1) ? (uint32_t)r[0] : (uint32_t)r[1]);
+}
 
 // LDS byte offset (within a chunk) of input i of the chunk, in that order.
 __device__ __forceinline__ int f16_pair_offset(int i) {
@@ -292,10 +320,11 @@ __device__ __forceinline__ int f16_pair_offset(int i) {
 // 0x6400 | q is 1024 + q exactly) and then (q, q') with one packed fp16
 // subtraction (exact), so no large offset has to cancel later; v_dot2
 // multiplies it by two fp16 inputs (products exact in fp32) and adds both to
-// the fp32 accumulator.  ap: the chunk's 16 staged pairs; asum: their sum.
+// the fp32 accumulator.  ap: the chunk's 16 staged pairs; asum: their sum; cs:
+// the chunk's staging scale (f16_stage_scale), applied to its contribution.
 template <int SB, int NM, int NR>
 __device__ __forceinline__ void dot_block_q4_f16(const BlockRegs<4, NM, NR> &R, const uint32_t *ap, float asum,
-                                                 float (&acc)[NM][NR]) {
+                                                 float cs, float (&acc)[NM][NR]) {
     const f16x2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
     float d[NM][NR];
 #pragma unroll
@@ -322,7 +351,7 @@ __device__ __forceinline__ void dot_block_q4_f16(const BlockRegs<4, NM, NR> &R, 
         for (int n = 0; n < NR; ++n) {
             const float s = R.live[n] ? sb_to_float<SB>(R.sr[m][n]) : 0.f;
             const float b = R.live[n] ? sb_to_float<SB>(R.br[m][n]) : 0.f;
-            acc[m][n] += s * d[m][n] + b * asum;
+            acc[m][n] += (s * d[m][n] + b * asum) * cs;
         }
 }
 
@@ -350,7 +379,7 @@ __device__ __forceinline__ void unpack_q4_f16(const BlockRegs<4, NM, NR> &R, uin
 // scales, biases and row validity).
 template <int SB, int NM, int NR>
 __device__ __forceinline__ void dot_pre_q4_f16(const BlockRegs<4, NM, NR> &R, const uint32_t (&pre)[NM][NR][16],
-                                               const uint32_t *ap, float asum, float (&acc)[NM][NR]) {
+                                               const uint32_t *ap, float asum, float cs, float (&acc)[NM][NR]) {
     float d[NM][NR];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -370,7 +399,7 @@ __device__ __forceinline__ void dot_pre_q4_f16(const BlockRegs<4, NM, NR> &R, co
         for (int n = 0; n < NR; ++n) {
             const float s = R.live[n] ? sb_to_float<SB>(R.sr[m][n]) : 0.f;
             const float b = R.live[n] ? sb_to_float<SB>(R.br[m][n]) : 0.f;
-            acc[m][n] += s * d[m][n] + b * asum;
+            acc[m][n] += (s * d[m][n] + b * asum) * cs;
         }
 }
 

@@ -6,13 +6,17 @@
 // one token (one wave per router row, fp32 accumulation over the contraction
 // with a wave64 butterfly reduction).  The router matrix is read once, spread
 // over many CUs.  Each logit is published as one 64-bit word, the fp32 value
-// and a nonzero flag, written with one device-scope store.  The last
-// workgroup of each token's row of the grid (every other one has a lower
-// index, so in-order dispatch cannot deadlock) polls that token's words until
-// all are flagged, stages the logits in LDS, selects the top-k with the whole
-// block (topk.hpp), computes the scores and clears the words, so the
-// workspace is ready for the next call (and for graph replays).  No counter,
-// atomic read-modify-write or cache-wide fence is involved.
+// and above it the launch's tag (1 + the launch epoch kept in the workspace),
+// written with one device-scope store.  The last workgroup of each token's
+// row of the grid (every other one has a lower index, so in-order dispatch
+// cannot deadlock) polls that token's words until all carry the tag, stages
+// the logits in LDS, selects the top-k with the whole block (topk.hpp) and
+// computes the scores.  The last selector to finish moves the workspace to
+// the next epoch, once every workgroup of the launch has read the tag, so a
+// word left by an earlier launch (or written late by one whose wait ran out)
+// never matches a later launch's tag.  Every wait is bounded; on time-out the
+// workspace's error word is raised and stays raised.  No cache-wide fence is
+// involved.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -33,7 +37,8 @@ struct RouteArgs {
     int32_t *ids;
     float *scores;
     float *gate;
-    uint64_t *logits;        // workspace [T][E + 1] flagged words, zero between calls
+    uint64_t *logits;        // workspace [T][E + 1] tagged words
+    uint32_t *ctr;           // workspace control words, kRouteCtrStride apart: error, epoch, selectors done
 };
 
 // Eight consecutive elements of a row as floats (one 16-byte load for 16-bit
@@ -92,17 +97,20 @@ __device__ float row_dot(const void *w, int64_t row, const void *x, int64_t xrow
     return wave_sum(acc);
 }
 
-constexpr uint64_t kLogitFlag = 1ull << 32;
 constexpr uint32_t kRouteSpinLimit = 1u << 22;
+constexpr int kRouteCtrStride = 64;          // uint32 words between control words (256 bytes)
+constexpr int kRouteCtrErr = 0, kRouteCtrEpoch = 1, kRouteCtrDone = 2;
+constexpr size_t kRouteHeadBytes = 1024;     // control words, then the tagged logits
 
-// Wait for one flagged logit word and return its value (0 if the wait ever
-// ran out, which in-order dispatch rules out).
-__device__ __forceinline__ float wait_logit(const uint64_t *w) {
+// Wait for one tagged logit word and return its value (0, with the error word
+// raised, if the wait runs out).
+__device__ __forceinline__ float wait_logit(const RouteArgs &a, const uint64_t *w, uint32_t tag) {
     for (uint32_t i = 0; i < kRouteSpinLimit; ++i) {
         const uint64_t v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (v & kLogitFlag) return __uint_as_float((uint32_t)v);
+        if ((uint32_t)(v >> 32) == tag) return __uint_as_float((uint32_t)v);
         __builtin_amdgcn_s_sleep(1);
     }
+    __hip_atomic_fetch_or(a.ctr + kRouteCtrErr * kRouteCtrStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return 0.f;
 }
 
@@ -112,13 +120,19 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int n_rows = a.E + (a.wg ? 1 : 0);
     uint64_t *logits = a.logits + (int64_t)t * (a.E + 1);
+    __shared__ uint32_t s_tag;
+    if (tid == 0)
+        s_tag = __hip_atomic_load(a.ctr + kRouteCtrEpoch * kRouteCtrStride, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    __syncthreads();
+    const uint32_t tag = s_tag;
 
     const int row = blockIdx.x * kRouteWaves + wave;
     if (row < n_rows) {
         const float v = (row < a.E) ? row_dot<XT, WT>(a.wr, row, a.x, t, a.d_in, lane)
                                     : row_dot<XT, GT>(a.wg, 0, a.x, t, a.d_in, lane);
         if (lane == 0)
-            __hip_atomic_store(logits + row, kLogitFlag | __float_as_uint(v), __ATOMIC_RELAXED,
+            __hip_atomic_store(logits + row, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
     if (blockIdx.x != gridDim.x - 1) return;
@@ -128,12 +142,20 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     __shared__ __align__(16) float s_logits[MOE_MAX_EXPERTS];
     __shared__ Selection sel;
     __shared__ float s_gate_logit;
-    stage_logits(a.E, s_logits, &sel, [&](int e) { return wait_logit(logits + e); });
-    if (tid == 0 && a.wg) s_gate_logit = wait_logit(logits + a.E);
+    stage_logits(a.E, s_logits, &sel, [&](int e) { return wait_logit(a, logits + e, tag); });
+    if (tid == 0 && a.wg) s_gate_logit = wait_logit(a, logits + a.E, tag);
     __syncthreads();
-    // every word of the token has been read: clear them for the next call
-    for (int e = tid; e < n_rows; e += blockDim.x)
-        __hip_atomic_store(logits + e, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // every word of the token has been read, so every workgroup of this token
+    // has read the tag: the last token's selector moves the workspace to the
+    // next epoch
+    if (tid == 0) {
+        uint32_t *done = a.ctr + kRouteCtrDone * kRouteCtrStride;
+        if (__hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)a.T - 1) {
+            __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.ctr + kRouteCtrEpoch * kRouteCtrStride, tag, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
     select_all(a.E, a.K, s_logits, &sel);
     if (wave != 0) return;
     with_per(a.E, [&](auto per) { softmax_scores<decltype(per)::value>(a.E, a.K, a.renorm, s_logits, lane, &sel); });
@@ -178,7 +200,14 @@ using namespace moe;
 
 extern "C" size_t moe_decode_route_workspace_bytes(int32_t n_tokens, int32_t n_experts) {
     if (n_tokens < 1 || n_experts < 1) return 0;
-    return align_up((size_t)n_tokens * (n_experts + 1) * sizeof(uint64_t), 256);
+    return kRouteHeadBytes + align_up((size_t)n_tokens * (n_experts + 1) * sizeof(uint64_t), 256);
+}
+
+extern "C" moe_status moe_decode_workspace_status(const void *head, size_t head_bytes) {
+    if (!head || head_bytes < MOE_WORKSPACE_HEAD_BYTES) return MOE_EINVAL;
+    uint32_t err;
+    __builtin_memcpy(&err, head, sizeof err);
+    return err ? MOE_ETIMEOUT : MOE_OK;
 }
 
 extern "C" moe_status moe_decode_route(const void *x, moe_dtype x_dtype, int32_t n_tokens, int32_t d_in,
@@ -206,7 +235,8 @@ extern "C" moe_status moe_decode_route(const void *x, moe_dtype x_dtype, int32_t
     a.x_dt = x_dtype; a.wr_dt = w_router_dtype; a.wg_dt = w_shared_gate_dtype;
     a.T = n_tokens; a.d_in = d_in; a.E = n_experts; a.K = top_k; a.renorm = renormalize ? 1 : 0;
     a.ids = expert_ids; a.scores = scores; a.gate = shared_gate;
-    a.logits = reinterpret_cast<uint64_t *>(workspace);
+    a.ctr = reinterpret_cast<uint32_t *>(workspace);
+    a.logits = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(workspace) + kRouteHeadBytes);
 
     const int n_rows = n_experts + (w_shared_gate ? 1 : 0);
     dim3 grid((n_rows + kRouteWaves - 1) / kRouteWaves, n_tokens);

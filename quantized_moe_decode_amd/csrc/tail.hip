@@ -75,6 +75,7 @@ extern "C" const char *moe_decode_status_string(moe_status s) {
     case MOE_EINVAL: return "MOE_EINVAL: invalid argument (null pointer, shape, size or alignment)";
     case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: bit width, group size or dtype not built";
     case MOE_EHIP: return "MOE_EHIP: HIP launch error";
+    case MOE_ETIMEOUT: return "MOE_ETIMEOUT: a wait inside a launch ran out; its results are invalid";
     }
     return "unknown moe_status";
 }

@@ -136,6 +136,78 @@ def share_fused_workspace(layers: Sequence[DecodeLayer]) -> Optional[torch.Tenso
     return ws
 
 
+class DecodeStep:
+    """One decode step: every layer in order on one stream, each token's step
+    captured once into a HIP graph (torch.cuda.CUDAGraph over the library's
+    launches) and replayed.
+
+    path "fused": one moe_decode_layer launch per layer (one token per step),
+    all layers sharing one fused workspace; path "three-call": route, expert
+    FFN (routed, then shared) and tail per layer (any token count).  Inputs
+    are given per distinct token (or token batch) r and layer l as device
+    tensors xs[r][l], rs[r][l]; layer l writes outs[l] [T, d_in] fp32 and its
+    routing into layers[l].ids / .scores.  Layers run back to back: no work
+    of layer l + 1 starts before layer l has finished.
+    """
+
+    def __init__(self, layers: Sequence[DecodeLayer], xs, rs, path: str = "fused",
+                 share_workspace: bool = True):
+        if path not in ("fused", "three-call"):
+            raise ValueError(path)
+        if path == "fused" and any(l.n_tokens != 1 for l in layers):
+            raise ValueError("the fused launch takes one token per step")
+        self.layers, self.xs, self.rs, self.path = list(layers), xs, rs, path
+        dev = layers[0].router.device
+        self.outs = [torch.zeros(l.n_tokens, l.d_in, device=dev) for l in layers]
+        self.fused_ws = share_fused_workspace(self.layers) if (path == "fused" and share_workspace) else None
+        self.graphs = []
+
+    @property
+    def n_distinct(self) -> int:
+        return len(self.xs)
+
+    def eager(self, r: int, path: Optional[str] = None) -> None:
+        fused = (path or self.path) == "fused"
+        for li, lay in enumerate(self.layers):
+            if fused:
+                lay.forward_fused(self.xs[r][li], self.rs[r][li], self.outs[li])
+            else:
+                lay.forward(self.xs[r][li], self.rs[r][li], self.outs[li])
+
+    def capture(self, path: Optional[str] = None):
+        """One graph per distinct token; returns them (also kept as .graphs when
+        path is the step's own)."""
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):           # warm-up launches outside the capture
+            for r in range(self.n_distinct):
+                self.eager(r, path)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graphs = []
+        for r in range(self.n_distinct):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.eager(r, path)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        if path is None or path == self.path:
+            self.graphs = graphs
+        return graphs
+
+    def replay(self, r: int) -> None:
+        self.graphs[r].replay()
+
+    def error_words(self) -> int:
+        """Nonzero if a wait inside any launch of the step ever timed out: the
+        fused workspaces' error words, or the route workspaces' (reads device
+        memory)."""
+        from . import MOE_OK, workspace_status
+        if self.path == "fused":
+            return max((l.fused_error_word() for l in self.layers), default=0)
+        return int(any(workspace_status(l.route_ws) != MOE_OK for l in self.layers))
+
+
 def layer_from_host(cfg, weights: dict, device, n_tokens: Optional[int] = None) -> DecodeLayer:
     """Build a DecodeLayer from host weights in the generator's layout."""
     router = tensor_from_encoded(weights["router"], cfg.router_dtype, device)

@@ -15,7 +15,7 @@ import torch
 
 import moe_inputs as mi
 import oracle
-from helpers import np_decode, pick_tokens, rel_err
+from helpers import np_decode, oracle_layer_selected, pick_tokens, rel_err  # noqa: F401
 from quantized_moe_decode_amd.layer import layer_from_host, tensor_from_encoded
 
 DEV = torch.device("cuda:0")
@@ -60,6 +60,9 @@ def run_gpu_layer(cfg, w, x, resid, graph: bool = False, layer=None, fused: bool
                out=out.cpu().numpy())
     if fused:
         res["error_word"] = layer.fused_error_word()
+    else:
+        import quantized_moe_decode_amd as q
+        res["error_word"] = int(q.workspace_status(layer.route_ws) != q.MOE_OK)
     if layer.shared_gate is not None:
         res["gate"] = layer.shared_gate.cpu().numpy()
     if layer.n_shared:
@@ -67,15 +70,18 @@ def run_gpu_layer(cfg, w, x, resid, graph: bool = False, layer=None, fused: bool
     return res, layer
 
 
-def compare_layer(cfg, w, x, resid, gpu, label=""):
-    """Assert the GPU result matches the oracle on the same inputs; returns the errors."""
-    ref = oracle.layer(cfg, w, x, resid)
+def compare_layer(cfg, w, x, resid, gpu, label="", ref=None):
+    """Assert the GPU result matches the oracle on the same inputs; returns the
+    errors.  `ref` is the oracle's result when already computed (then `w` is
+    not used)."""
+    if ref is None:
+        ref = oracle.layer(cfg, w, x, resid)
     ids_ref = ref["route"]["ids"]
     assert np.array_equal(gpu["ids"], ids_ref), f"{label}: ids {gpu['ids']} vs {ids_ref}"
     ds = float(np.max(np.abs(gpu["scores"] - ref["route"]["scores"])))
     assert ds <= SCORE_TOL, f"{label}: scores off by {ds}"
     if gpu.get("error_word"):
-        raise AssertionError(f"{label}: fused launch reported a wait time-out")
+        raise AssertionError(f"{label}: a launch reported a wait time-out")
     if cfg.shared_gate:
         dg = float(np.max(np.abs(gpu["gate"] - ref["route"]["gate"])))
         assert dg <= SCORE_TOL, f"{label}: shared gate off by {dg}"

@@ -40,14 +40,28 @@ def test_library_exports_declared_symbol(name):
 
 
 def test_abi_version_and_status_strings():
-    assert qmd.abi_version() == 1
-    for code in (0, 1, 2, 3):
+    assert qmd.abi_version() == 2
+    for code in (0, 1, 2, 3, 4):
         assert qmd.status_string(code).startswith("MOE_")
     assert "unknown" in qmd.status_string(99)
 
 
+def test_workspace_status_reads_the_error_word():
+    """moe_decode_workspace_status interprets a host copy of a workspace's head:
+    a zero error word is MOE_OK, any nonzero one MOE_ETIMEOUT; too short or null
+    heads are rejected."""
+    f = lib.moe_decode_workspace_status
+    for word, want in ((0, MOE_OK), (1, qmd.MOE_ETIMEOUT), (0x80000000, qmd.MOE_ETIMEOUT)):
+        head = (ctypes.c_uint32 * 4)(word, 0, 0, 0)
+        assert f(ctypes.cast(head, ctypes.c_void_p), 16) == want
+        assert f(ctypes.cast(head, ctypes.c_void_p), qmd.MOE_WORKSPACE_HEAD_BYTES) == want
+    head = (ctypes.c_uint32 * 1)(0)
+    assert f(ctypes.cast(head, ctypes.c_void_p), qmd.MOE_WORKSPACE_HEAD_BYTES - 1) == MOE_EINVAL
+    assert f(None, 16) == MOE_EINVAL
+
+
 def test_workspace_sizes():
-    assert qmd.route_workspace_bytes(1, 128) >= (128 + 1) * 8          # one flagged 64-bit word per logit
+    assert qmd.route_workspace_bytes(1, 128) >= (128 + 1) * 8          # one tagged 64-bit word per logit
     assert qmd.route_workspace_bytes(32, 1024) >= 32 * 1025 * 8
     assert qmd.route_workspace_bytes(0, 8) == 0
     assert qmd.expert_ffn_workspace_bytes(1, 8, 128) == 0

@@ -1,0 +1,90 @@
+"""The decode step as the benchmark runs it, against the oracle: several
+full-size layers in order on one stream, each distinct token's step captured
+once into a HIP graph and replayed in rotated order, the fused launches of all
+layers sharing one workspace (quantized_moe_decode_amd.layer.DecodeStep, the
+class the benchmark uses).  Every layer's output and routing is compared with
+the oracle after every replay.  Every case prints its name before it runs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from gpu_cases import DEV, compare_layer, say
+from helpers import oracle_layer_selected, pick_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_moe_decode_amd  # noqa: F401
+    yield
+
+
+def build_step(specs, n_distinct, path, n_tokens=1):
+    """Layers (cfg, layer index) on the device, margin tokens per layer, and the
+    oracle's result for every (token, layer)."""
+    from quantized_moe_decode_amd.layer import DecodeStep, layer_from_host, tensor_from_encoded
+    layers, host_x, host_r = [], [], []
+    for cfg, li in specs:
+        w = mi.gen_layer_weights(cfg, li)
+        layers.append(layer_from_host(cfg, w, DEV, n_tokens=n_tokens))
+        x, r, _ = pick_tokens(cfg, li, n_distinct * n_tokens, w["router"])
+        host_x.append(x.reshape(n_distinct, n_tokens, -1))
+        host_r.append(r.reshape(n_distinct, n_tokens, -1))
+        del w
+    xs = [[tensor_from_encoded(host_x[l][t], specs[l][0].x_dtype, DEV) for l in range(len(specs))]
+          for t in range(n_distinct)]
+    rs = [[tensor_from_encoded(host_r[l][t], specs[l][0].resid_dtype, DEV) for l in range(len(specs))]
+          for t in range(n_distinct)]
+    step = DecodeStep(layers, xs, rs, path=path)
+    refs = {(t, l): oracle_layer_selected(specs[l][0], specs[l][1], host_x[l][t], host_r[l][t])
+            for t in range(n_distinct) for l in range(len(specs))}
+    return step, host_x, host_r, refs
+
+
+def check_replays(step, specs, host_x, host_r, refs, order, label):
+    step.capture()
+    for i, t in enumerate(order):
+        for o in step.outs:
+            o.fill_(-1.0)                  # eager work on the step's buffers between replays
+        for lay in step.layers:
+            lay.ids.fill_(-1)
+        step.replay(t)
+        torch.cuda.synchronize()
+        assert step.error_words() == 0, f"{label}: a fused wait timed out"
+        for l, (cfg, li) in enumerate(specs):
+            lay = step.layers[l]
+            gpu = dict(ids=lay.ids.cpu().numpy(), scores=lay.scores.cpu().numpy(),
+                       act=None, partial=None, out=step.outs[l].cpu().numpy())
+            if lay.shared_gate is not None:
+                gpu["gate"] = lay.shared_gate.cpu().numpy()
+            compare_layer(cfg, None, host_x[l][t], host_r[l][t], gpu,
+                          f"{label} replay {i} token {t} layer {l} ({cfg.name} L{li})", ref=refs[(t, l)])
+
+
+MIXED = [(mi.QWEN3, 0), (mi.QWEN3, 1), (mi.QWEN3, 2), (mi.QWEN3, 3), (mi.QWEN15, 0), (mi.QWEN15, 1)]
+
+
+def test_fused_step_shared_workspace():
+    say("case decode step: fused, 4 Qwen3 + 2 Qwen1.5 layers, one shared workspace, 3 tokens")
+    step, hx, hr, refs = build_step(MIXED, 3, "fused")
+    ptrs = {l.fused_ws.data_ptr() for l in step.layers}
+    assert len(ptrs) == 1 and step.fused_ws is not None, "layers do not share one fused workspace"
+    check_replays(step, MIXED, hx, hr, refs, [0, 1, 2, 1, 0, 2, 2], "fused step")
+
+
+def test_three_call_step():
+    say("case decode step: three-call, 4 Qwen3 + 2 Qwen1.5 layers, 2 tokens")
+    step, hx, hr, refs = build_step(MIXED, 2, "three-call")
+    check_replays(step, MIXED, hx, hr, refs, [0, 1, 1, 0], "three-call step")
+
+
+def test_batch32_step():
+    specs = [(mi.QWEN3_B32, 0), (mi.QWEN3_B32, 1), (mi.QWEN3_B32, 2)]
+    say("case decode step: 32 tokens per step, 3 Qwen3 layers, 2 token batches")
+    step, hx, hr, refs = build_step(specs, 2, "three-call", n_tokens=32)
+    check_replays(step, specs, hx, hr, refs, [0, 1, 0], "batch-32 step")

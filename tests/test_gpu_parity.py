@@ -207,14 +207,16 @@ def test_exact_tie_prefers_lower_index():
     assert ids.cpu().numpy().tolist() == [[4, 11, 9, 2]]
     s = sc.cpu().numpy()[0]
     assert s[0] == s[1]
-    # each call leaves the workspace all zero (its flagged logit words cleared),
-    # so the same workspace serves the next call unchanged
-    assert not np.any(ws.cpu().numpy()), "route workspace not cleared"
-    ids2 = torch.full_like(ids, -7)
-    q.moe_decode_route(xd, wd, 4, True, ids2, sc, ws)
-    torch.cuda.synchronize()
-    assert ids2.cpu().numpy().tolist() == [[4, 11, 9, 2]]
-    assert not np.any(ws.cpu().numpy()), "route workspace not cleared"
+    # the workspace carries the launch epoch from call to call: the same
+    # workspace serves the next calls unchanged, and no wait ran out
+    for call in range(3):
+        ids2 = torch.full_like(ids, -7)
+        q.moe_decode_route(xd, wd, 4, True, ids2, sc, ws)
+        torch.cuda.synchronize()
+        assert ids2.cpu().numpy().tolist() == [[4, 11, 9, 2]], call
+    assert q.workspace_status(ws) == q.MOE_OK
+    epoch = int(ws[256:260].view(torch.int32).item())
+    assert epoch == 4, f"route epoch {epoch} after 4 calls"
 
 
 def test_many_experts_top32():
