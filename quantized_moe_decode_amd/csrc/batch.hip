@@ -11,11 +11,9 @@
 // codes of a word are turned into a 16-bit pair once and multiplied into
 // every token's accumulator:
 //   kernel A: bf16 x, codes as bf16 128 + q, bias folded as b - 128 s;
-//   kernel B: act rounded to fp16 after a power-of-two scaling per chunk
-//             (f16_stage_scale: the chunk's largest value lands in
-//             [2^14, 2^15), so nothing overflows and nothing becomes an fp16
-//             subnormal), codes as exact fp16 q, the chunk's contribution
-//             scaled back.
+//   kernel B: act rounded to fp16 after a power-of-two factor (2^8, or one
+//             fitted to the token's vector if that would overflow fp16),
+//             codes as exact fp16 q, the token's sums scaled back when stored.
 #include <hip/hip_runtime.h>
 
 #include "api.hpp"
@@ -25,9 +23,9 @@
 
 namespace moe {
 
-constexpr int kRec = 80;         // bytes per staged chunk: 64 of pairs, the chunk sum, its staging scale, padding
+constexpr int kRec = 80;         // bytes per staged chunk: 64 of pairs, the chunk sum, padding
 constexpr int kRecSum = 64;
-constexpr int kRecScale = 68;
+constexpr int kBatchThreads = kFfnThreads;
 
 size_t batch_lds_bytes(int cols) { return (size_t)kBatchTok * (cols / 32) * kRec; }
 
@@ -76,49 +74,91 @@ __device__ __forceinline__ void stage_pairs(char *lds, int nt, int cpr, Src src)
     }
 }
 
-// Stage nt act vectors (fp32 [.., cpr*32]) as fp16 pairs, every chunk of 32
-// scaled by its power-of-two staging factor (stored at kRecScale).  Thread i
+// Stage nt act vectors (fp32 [.., cpr*32]) as fp16 pairs; s_cs[t] gets the
+// factor by which token t's dot products are to be multiplied.  Thread i
 // handles act row t, chunk c, word k (8 values); the four k of a chunk are a
-// quad, whose maximum gives the chunk's factor.
+// quad.  The values are staged times kActF16Prescale (s_cs = its inverse)
+// unless some value would overflow fp16 that way (one compare per value; the
+// waves' ballots meet in LDS over a barrier): then each token's largest
+// magnitude is found (LDS atomic maxima) and every token is staged again with
+// the factor fitted to it (f16_stage_scale).  Ends with a workgroup barrier.
 __device__ __forceinline__ void stage_act_f16(char *lds, int nt, int cpr, const Work &wk, const float *act,
-                                              int d_ff) {
+                                              int d_ff, float *s_cs) {
+    constexpr int kWaves = kBatchThreads / kWave;
+    static_assert(kWaves == 4, "one flag word per wave, read as one 16-byte word");
+    __shared__ __align__(16) uint32_t s_wave[kWaves];
+    __shared__ uint32_t s_max[kBatchTok];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
     const int n = nt * cpr * 4;
-    for (int i0 = 0; i0 < n; i0 += blockDim.x) {       // uniform trip count: whole quads
-        const int i = i0 + threadIdx.x;
-        const bool ok = i < n;
+    auto load = [&](int i, float (&f)[8], int &t) {
         const int k = i & 3, tc = i >> 2;
-        const int t = ok ? tc / cpr : 0, c = ok ? tc - t * cpr : 0;
-        float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (ok) {
-            const f32x4 *src = reinterpret_cast<const f32x4 *>(act + (int64_t)pair_at(wk, t) * d_ff + c * 32 + k * 8);
-            const f32x4 lo = src[0], hi = src[1];
-            f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
-            f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+        t = tc / cpr;
+        const int c = tc - t * cpr;
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(act + (int64_t)pair_at(wk, t) * d_ff + c * 32 + k * 8);
+        const f32x4 lo = src[0], hi = src[1];
+        f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+        f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+    };
+    // one pass: every value times its token's factor, rounded and placed;
+    // returns whether any value of this thread reaches kActF16Overflow
+    auto stage = [&](auto inv_of) {
+        bool over = false;
+        for (int i0 = 0; i0 < n; i0 += kBatchThreads) {       // uniform trip count: whole quads
+            const int i = i0 + threadIdx.x;
+            float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            int t = 0;
+            if (i < n) load(i, f, t);
+            const float inv = inv_of(t);
+            uint32_t h[8];
+            float sum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                over |= !(__builtin_fabsf(f[e]) < kActF16Overflow);      // NaN counts as over
+                const _Float16 q = (_Float16)(f[e] * inv);
+                sum += (float)q;
+                h[e] = __builtin_bit_cast(uint16_t, q);
+            }
+            sum = quad_sum(sum);
+            if (i < n) {
+                char *rec = lds + (i >> 2) * kRec;
+                *reinterpret_cast<u32x4 *>(rec + (i & 3) * 16) =
+                    pair_words(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+                if ((i & 3) == 0) *reinterpret_cast<float *>(rec + kRecSum) = sum;
+            }
         }
+        return over;
+    };
+    const bool over = stage([](int) { return kActF16Prescale; });
+    const uint64_t b_over = __builtin_amdgcn_ballot_w64(over);
+    if (lane == 0) s_wave[wave] = b_over ? 1u : 0u;
+    if (threadIdx.x < kBatchTok) {
+        s_cs[threadIdx.x] = kActF16Postscale;
+        s_max[threadIdx.x] = 0;
+    }
+    __syncthreads();
+    const u32x4 fl = *reinterpret_cast<const u32x4 *>(s_wave);
+    if (!(fl.x | fl.y | fl.z | fl.w)) return;
+    // a value past fp16's range at 2^8: per-token maxima, then all again, fitted
+    for (int i = threadIdx.x; i < n; i += kBatchThreads) {
+        float f[8];
+        int t;
+        load(i, f, t);
         uint32_t m = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) m = max(m, __float_as_uint(f[e]) & 0x7FFFFFFFu);
-        float inv;
-        const float cs = f16_stage_scale(quad_max_u(m), inv);
-        uint32_t h[8];
-        float sum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const _Float16 q = (_Float16)(f[e] * inv);
-            sum += (float)q;
-            h[e] = __builtin_bit_cast(uint16_t, q);
-        }
-        sum = quad_sum(sum);
-        if (ok) {
-            char *rec = lds + (t * cpr + c) * kRec;
-            *reinterpret_cast<u32x4 *>(rec + k * 16) =
-                pair_words(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-            if (k == 0) {
-                *reinterpret_cast<float *>(rec + kRecSum) = sum;
-                *reinterpret_cast<float *>(rec + kRecScale) = cs;
-            }
-        }
+        atomicMax(&s_max[t], m);
     }
+    __syncthreads();
+    (void)stage([&](int t) {
+        float inv;
+        (void)f16_stage_scale(s_max[t], inv);
+        return inv;
+    });
+    if (threadIdx.x < kBatchTok) {
+        float inv;
+        s_cs[threadIdx.x] = f16_stage_scale(s_max[threadIdx.x], inv);
+    }
+    __syncthreads();
 }
 
 // fn(tag) for a workgroup-uniform nt in 1..kBatchTok, with ::value = 2 for
@@ -140,7 +180,7 @@ __device__ __forceinline__ void with_tokens(int nt, Fn fn) {
 
 // Kernel A: gate and up projections of one work item over a tile of rows, then SwiGLU.
 template <int SB>
-__global__ __launch_bounds__(256) void gate_up_batch_q4(FfnArgs a) {
+__global__ __launch_bounds__(kBatchThreads) void gate_up_batch_q4(FfnArgs a) {
     constexpr int NR = kBatchNRA;
     extern __shared__ __align__(16) char lds[];
     Work wk;
@@ -289,7 +329,7 @@ __global__ __launch_bounds__(256) void gate_up_batch_q4(FfnArgs a) {
 // loop-invariant value, reloaded once per row pass) measured faster than five
 // without the spill.
 template <int SB>
-__global__ __launch_bounds__(256, 6) void down_batch_q4(FfnArgs a) {
+__global__ __launch_bounds__(kBatchThreads, 6) void down_batch_q4(FfnArgs a) {
     constexpr int NR = kBatchNRB;
     extern __shared__ __align__(16) char lds[];
     Work wk;
@@ -306,8 +346,8 @@ __global__ __launch_bounds__(256, 6) void down_batch_q4(FfnArgs a) {
         return;
     }
     const int cpr = a.d_ff / 32;
-    stage_act_f16(lds, nt, cpr, wk, a.act, a.d_ff);
-    __syncthreads();
+    __shared__ float s_cs[kBatchTok];
+    stage_act_f16(lds, nt, cpr, wk, a.act, a.d_ff, s_cs);
 
     const int lr = 1 << a.lr_shift, j = lane & (lr - 1), rsub = lane >> a.lr_shift, rpw = kWave >> a.lr_shift;
     const QM mats[1] = {a.down};
@@ -355,14 +395,12 @@ __global__ __launch_bounds__(256, 6) void down_batch_q4(FfnArgs a) {
                 }
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const char *rec = lds + (t * cpr + R.cc) * kRec;
-                    const float asum = *reinterpret_cast<const float *>(rec + kRecSum);
-                    const float cs = *reinterpret_cast<const float *>(rec + kRecScale);
+                    const float asum = *reinterpret_cast<const float *>(lds + (t * cpr + R.cc) * kRec + kRecSum);
 #pragma unroll
                     for (int n = 0; n < NR; ++n) {
                         const float s = R.live[n] ? sb_to_float<SB>(R.sr[0][n]) : 0.f;
                         const float b = R.live[n] ? sb_to_float<SB>(R.br[0][n]) : 0.f;
-                        acc[n][t] += (s * d[n][t] + b * asum) * cs;
+                        acc[n][t] += s * d[n][t] + b * asum;
                     }
                 }
             }
@@ -385,7 +423,7 @@ __global__ __launch_bounds__(256, 6) void down_batch_q4(FfnArgs a) {
                         const int r = r0 + n * rpw;
                         if (t < nt && r < row_end) {
                             const int64_t p = pair_at(wk, t);
-                            const float sc = a.scores ? a.scores[p] : 1.0f;
+                            const float sc = (a.scores ? a.scores[p] : 1.0f) * s_cs[t];   // exact: a power of two
                             a.partial[p * a.d_in + r] = sc * sv[0];
                         }
                     }
@@ -403,7 +441,7 @@ __global__ __launch_bounds__(256, 6) void down_batch_q4(FfnArgs a) {
                                 for (int t = 0; t < NT; ++t) {
                                     if (t >= nt) break;
                                     const int64_t p = pair_at(wk, t);
-                                    const float sc = a.scores ? a.scores[p] : 1.0f;
+                                    const float sc = (a.scores ? a.scores[p] : 1.0f) * s_cs[t];
                                     a.partial[p * a.d_in + r] = sc * acc[n][t];
                                 }
                             }

@@ -537,7 +537,7 @@ static moe_status launch_a(Plan &p) {
         if (st != MOE_OK) return st;
     }
     dim3 grid((p.a.d_ff + p.a.rows_per_wg - 1) / p.a.rows_per_wg, p.n_items);
-    hipLaunchKernelGGL(k, grid, dim3(256), lds, p.s, p.a);
+    hipLaunchKernelGGL(k, grid, dim3(kFfnThreads), lds, p.s, p.a);
     return MOE_OK;
 }
 
@@ -552,7 +552,7 @@ static moe_status launch_b(Plan &p) {
         if (st != MOE_OK) return st;
     }
     dim3 grid((p.a.d_in + p.a.rows_per_wg - 1) / p.a.rows_per_wg, p.n_items);
-    hipLaunchKernelGGL(k, grid, dim3(256), lds, p.s, p.a);
+    hipLaunchKernelGGL(k, grid, dim3(kFfnThreads), lds, p.s, p.a);
     return MOE_OK;
 }
 

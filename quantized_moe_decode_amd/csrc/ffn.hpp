@@ -63,6 +63,8 @@ constexpr int kBatchTok = 4;
 
 using KernelFn = void (*)(FfnArgs);
 
+constexpr int kFfnThreads = 256;     // threads per workgroup of every expert-FFN kernel
+
 // Multi-token kernels for 4-bit weights (batch.hip): kernel A with bf16 x,
 // kernel B with any act; scale dtype sb.  LDS bytes for `cols` inputs.
 KernelFn batch_gate_up_q4(int sb);

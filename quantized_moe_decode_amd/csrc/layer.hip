@@ -125,7 +125,7 @@ static int resident_capacity(LayerFn k, size_t lds) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(k), 256, lds) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(k), kLayerThreads, lds) !=
         hipSuccess)
         return 0;
     return cus * per_cu;
@@ -238,6 +238,6 @@ extern "C" moe_status moe_decode_layer(const moe_layer_weights *weights, const v
     a.act = reinterpret_cast<uint64_t *>(ws + p.off_act);
     a.act_sent = reinterpret_cast<uint64_t *>(ws + p.off_act_sent);
     a.partial = reinterpret_cast<uint64_t *>(ws + p.off_partial);
-    hipLaunchKernelGGL(k, dim3(p.grid), dim3(256), p.lds, reinterpret_cast<hipStream_t>(stream), a);
+    hipLaunchKernelGGL(k, dim3(p.grid), dim3(kLayerThreads), p.lds, reinterpret_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }

@@ -53,6 +53,8 @@ constexpr int kLayerNRA = 3;        // rows per lane group, kernel A units with 
                                     // (16-row units put two on half of them, which finished last)
 constexpr int kLayerNRA2 = 2;       // rows per lane group and stage, kernel A units with several (two in flight)
 constexpr int kLayerNRB = 4;        // rows per lane group, kernel B units
+constexpr int kLayerThreads = 256;  // threads per workgroup (the launch's block size)
+constexpr int kLayerWaves = kLayerThreads / kWave;
 constexpr int kCtrStride = 64;      // uint32 words between control words (256 bytes)
 constexpr uint32_t kSpinLimit = 1u << 19;
 constexpr int kLogitCopies = 16;    // copies of the router logits, each polled by 1/16 of the workgroups
@@ -184,35 +186,56 @@ __device__ __forceinline__ void gather_tagged(const LayerArgs &a, int n, const u
 
 // The act gather of a kernel-B unit with 4-bit down weights: act[0, n) (n a
 // multiple of 32) into LDS as fp16 pair chunks of 32 values (kF16ChunkBytes
-// each, pairs placed as dot_block_q4_f16 reads them), every chunk scaled by
-// its power-of-two staging factor, which is stored beside the chunk.  With a
-// block of 256 threads and batches of 256 consecutive elements, the 32
-// elements of a chunk are 32 consecutive lanes of one wave, so its largest
-// magnitude is a 32-lane reduction; all lanes take part (elements past n
-// read as 0).
-__device__ __forceinline__ void gather_act_f16(const LayerArgs &a, int n, const uint64_t *sentinel, uint32_t tag,
-                                               const uint64_t *act, char *lds) {
-    const int nt = blockDim.x, t = threadIdx.x;
+// each, placed as dot_block_q4_f16 reads them), each value times
+// kActF16Prescale.  Returns the factor by which the dot products of the
+// staged values are to be multiplied: kActF16Postscale, unless some value
+// would overflow fp16 that way (one compare per value; the waves' ballots
+// meet in LDS over the barrier that ends the gather).  Then every thread
+// reads its words again (all are present by then) and the vector is staged
+// with the factor fitted to its largest magnitude (f16_stage_scale).
+__device__ __forceinline__ float gather_act_f16(const LayerArgs &a, int n, const uint64_t *sentinel, uint32_t tag,
+                                                const uint64_t *act, char *lds) {
+    static_assert(kLayerWaves == 4, "one flag word per wave, read as one 16-byte word");
+    __shared__ __align__(16) uint32_t s_wave[2][kLayerWaves];   // per wave: overflow flag, largest magnitude
+    constexpr int nt = kLayerThreads;
+    const int t = threadIdx.x, lane = t & (kWave - 1), wave = t >> 6;
+    auto place = [&](int i, float v) {
+        *reinterpret_cast<_Float16 *>(lds + (i >> 5) * kF16ChunkBytes + f16_pair_offset(i & 31)) = (_Float16)v;
+    };
     if (t == 0) (void)wait_tagged<kActSleep>(a, sentinel, tag);
     __syncthreads();
+    bool over = false;
     for (int base = 0; base < n; base += kGatherPer * nt) {
         const int left = n - base - t;
         const int cnt = left <= 0 ? 0 : min(kGatherPer, (left + nt - 1) / nt);
         float v[kGatherPer];
         poll_batch<kGatherPer, kActSleep>(a, tag, cnt, [&](int u) { return act + base + u * nt + t; }, v);
 #pragma unroll
-        for (int u = 0; u < kGatherPer; ++u) {
-            if (base + u * nt >= n) break;                  // the same for the whole block
-            float inv;
-            const float cs = f16_stage_scale(group_max32_u(__float_as_uint(v[u]) & 0x7FFFFFFFu), inv);
+        for (int u = 0; u < kGatherPer; ++u)
             if (u < cnt) {
-                const int i = base + u * nt + t, c = i >> 5;
-                char *rec = lds + c * kF16ChunkBytes;
-                *reinterpret_cast<_Float16 *>(rec + f16_pair_offset(i & 31)) = (_Float16)(v[u] * inv);
-                if ((i & 31) == 0) *reinterpret_cast<float *>(rec + kF16ScaleOffset) = cs;
+                over |= !(__builtin_fabsf(v[u]) < kActF16Overflow);      // NaN counts as over
+                place(base + u * nt + t, v[u] * kActF16Prescale);
             }
-        }
     }
+    const uint64_t b_over = __builtin_amdgcn_ballot_w64(over);
+    if (lane == 0) s_wave[0][wave] = b_over ? 1u : 0u;
+    __syncthreads();
+    const u32x4 f = *reinterpret_cast<const u32x4 *>(s_wave[0]);
+    if (!(f.x | f.y | f.z | f.w)) return kActF16Postscale;
+    // the slot's largest magnitude, then the values again, scaled to fit
+    uint32_t mx = 0;
+    for (int i = t; i < n; i += nt) mx = max(mx, (uint32_t)ld_tagged(act + i) & 0x7FFFFFFFu);
+    const float wm = wave_max(__uint_as_float(mx));       // magnitudes as floats order like their bits
+    if (lane == 0) s_wave[1][wave] = __float_as_uint(wm);
+    __syncthreads();
+    uint32_t m = 0;
+#pragma unroll
+    for (int w = 0; w < kLayerWaves; ++w) m = max(m, s_wave[1][w]);
+    float inv;
+    const float cs = f16_stage_scale(m, inv);
+    for (int i = t; i < n; i += nt) place(i, __uint_as_float((uint32_t)ld_tagged(act + i)) * inv);
+    __syncthreads();
+    return cs;
 }
 
 __device__ __forceinline__ uint32_t launch_tag(const LayerArgs &a) {
@@ -551,24 +574,26 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
         const uint64_t *act = a.act + (int64_t)slot * a.act_stride;
         const int n_act = cpr * CODES;
         const uint64_t *sent = a.act_sent + ((int64_t)slot * kActCopies + tile % kActCopies) * kSentStride;
-        // 4-bit down projections take act as fp16 pairs (packed dot), each
-        // chunk scaled by a power of two into fp16's range (f16_stage_scale);
-        // the others take act as fp32 chunks
+        // 4-bit down projections take act as fp16 pairs (packed dot), staged
+        // with a power-of-two factor whose inverse joins the score
+        // (gather_act_f16); the others take act as fp32 chunks
         constexpr bool kF16 = BB == 4;
         // the first stage's codes unpacked while act is on its way: after it
         // arrives only the dot products remain
         [[maybe_unused]] uint32_t pre[1][NR][16];
+        float cs = 1.0f;
         if constexpr (kF16) {
             if (n_stage > 0) unpack_q4_f16<1, NR>(cur, pre);
-            gather_act_f16(a, n_act, sent, tag, act, reinterpret_cast<char *>(xs));
+            cs = gather_act_f16(a, n_act, sent, tag, act, reinterpret_cast<char *>(xs));
         } else {
             gather_tagged<kActSleep>(a, n_act, sent, tag, [&](int i) { return act + i; }, [&](int i, float v) {
                 const int c = i / CODES;
                 xs[c * (CODES + 4) + (i - c * CODES)] = v;
             });
+            __syncthreads();
         }
-        __syncthreads();
         if (routed) score = sel->scores[slot];
+        const float sc = score * cs;         // exact: cs is a power of two
         float acc[1][NR];
         for (int st = 0; st < n_stage; ++st) {
             const int ps = st / n_chunk, ch = st - ps * n_chunk;
@@ -588,11 +613,9 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
 #pragma unroll
                     for (int k = 0; k < 4; ++k) ap[4 * i + k] = v[k];
                 }
-                const float cs = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(src) +
-                                                                  kF16ScaleOffset);
                 if constexpr (BB == 4) {
-                    if (st == 0) dot_pre_q4_f16<SB, 1, NR>(cur, pre, ap, f16_pairs_sum(ap), cs, acc);
-                    else dot_block_q4_f16<SB, 1, NR>(cur, ap, f16_pairs_sum(ap), cs, acc);
+                    if (st == 0) dot_pre_q4_f16<SB, 1, NR>(cur, pre, ap, f16_pairs_sum(ap), acc);
+                    else dot_block_q4_f16<SB, 1, NR>(cur, ap, f16_pairs_sum(ap), acc);
                 }
             } else {
                 float xv[CODES];
@@ -602,8 +625,8 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
             if (ch == n_chunk - 1) {
                 auto put = [&](int r, float v) {
                     if (r < row_end) {
-                        if (last_slot) s_own[r - row0] = score * v;
-                        else st_tagged(part + r, score * v, tag);
+                        if (last_slot) s_own[r - row0] = sc * v;
+                        else st_tagged(part + r, sc * v, tag);
                     }
                 };
                 with_width(lrs, [&](auto w) {
@@ -679,7 +702,7 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
 
 // ANR: kLayerNRA (kernel-A units of one stage) or kLayerNRA2 (pipelined stages).
 template <int BA, int BB, int SB, int XT, int ANR>
-__global__ __launch_bounds__(256, 3) void layer_kernel(LayerArgs a) {
+__global__ __launch_bounds__(kLayerThreads, 3) void layer_kernel(LayerArgs a) {
     __shared__ __align__(16) float s_logits[MOE_MAX_EXPERTS];
     __shared__ Selection sel;
     extern __shared__ float xs[];

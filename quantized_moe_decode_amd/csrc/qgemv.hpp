@@ -278,35 +278,34 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // fp16 inputs of one 4-bit chunk staged for dot_block_q4_f16: 16 pairs, pair
 // 4k + p = (input 8k+p, input 8k+p+4) (the codes a nibble pair of word k
-// holds), then the chunk's staging scale (fp32, at byte kF16ScaleOffset) and
-// padding.
+// holds), then 16 bytes of padding.
 constexpr int kF16ChunkBytes = 16 * 4 + 16;
-constexpr int kF16ScaleOffset = 64;
 
-// Staging scale of a chunk of fp32 values that is rounded to fp16: the values
-// are multiplied by inv = 2^-k before rounding and the chunk's dot products by
-// the returned 2^k afterwards (both exact), with k chosen from the bit pattern
-// m of the chunk's largest magnitude so that the largest scaled value lies in
-// [2^14, 2^15).  Nothing overflows fp16 then, and every value within 2^-28 of
-// the chunk's largest keeps fp16's 11-bit precision (no fp16 subnormals).
-// m's biased exponent e gives |max| in [2^(e-127), 2^(e-126)); inv = 2^(141-e).
-// Exponents below 15 (|max| < 2^-112, zero included) take e = 15, so that
-// both factors are normal floats.
+// Staging of fp32 act as fp16 for the packed fp16 dot of a 4-bit down
+// projection.  Every value is multiplied by kActF16Prescale = 2^8 before it is
+// rounded (exact), and the dot products by 2^-8 afterwards (exact, folded into
+// the score).  fp16's normal range then holds |act| from 2^-22 to 255.9 with
+// 11-bit precision; a smaller value is an fp16 subnormal with an absolute
+// error of at most 2^-25 after scaling, 2^-33 before, so over a row of n <=
+// 8192 terms such errors stay below n 2^-33 |w|max.  A value of
+// kActF16Overflow = 65520 / 2^8 or more would round to fp16 infinity: the
+// stagers check for it and then stage the vector again with a factor fitted
+// to its largest magnitude m (f16_stage_scale).
+constexpr float kActF16Prescale = 256.0f;
+constexpr float kActF16Postscale = 1.0f / 256.0f;
+constexpr float kActF16Overflow = 255.9375f;
+
+// The power-of-two staging factor for a vector whose largest magnitude has
+// the bit pattern m: values are multiplied by inv = 2^-k before rounding and
+// the dot products by the returned 2^k afterwards (both exact), k chosen so
+// that m 2^-k lies in [2^14, 2^15): nothing overflows, and every value within
+// 2^-28 of m keeps fp16's 11-bit precision.  m's biased exponent e gives m in
+// [2^(e-127), 2^(e-126)), so inv = 2^(141-e); exponents below 15 (m < 2^-112,
+// zero included) take e = 15, keeping both factors normal floats.
 __device__ __forceinline__ float f16_stage_scale(uint32_t max_abs_bits, float &inv) {
     const int e = max((int)(max_abs_bits >> 23), 15);
     inv = __uint_as_float((uint32_t)(268 - e) << 23);
     return __uint_as_float((uint32_t)(e - 14) << 23);
-}
-
-// Unsigned maximum over aligned groups of 32 lanes; every lane gets its
-// group's.  All 64 lanes must be active.
-__device__ __forceinline__ uint32_t group_max32_u(uint32_t x) {
-    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
-    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
-    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xf, 0xf, false));  // row_half_mirror
-    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xf, 0xf, false));  // row_mirror
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);               // across lane bit 4
-    return max(x, ((threadIdx.x >> 4) & 1) ? (uint32_t)r[0] : (uint32_t)r[1]);
 }
 
 // LDS byte offset (within a chunk) of input i of the chunk, in that order.
@@ -320,11 +319,10 @@ __device__ __forceinline__ int f16_pair_offset(int i) {
 // 0x6400 | q is 1024 + q exactly) and then (q, q') with one packed fp16
 // subtraction (exact), so no large offset has to cancel later; v_dot2
 // multiplies it by two fp16 inputs (products exact in fp32) and adds both to
-// the fp32 accumulator.  ap: the chunk's 16 staged pairs; asum: their sum; cs:
-// the chunk's staging scale (f16_stage_scale), applied to its contribution.
+// the fp32 accumulator.  ap: the chunk's 16 staged pairs; asum: their sum.
 template <int SB, int NM, int NR>
 __device__ __forceinline__ void dot_block_q4_f16(const BlockRegs<4, NM, NR> &R, const uint32_t *ap, float asum,
-                                                 float cs, float (&acc)[NM][NR]) {
+                                                 float (&acc)[NM][NR]) {
     const f16x2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
     float d[NM][NR];
 #pragma unroll
@@ -351,7 +349,7 @@ __device__ __forceinline__ void dot_block_q4_f16(const BlockRegs<4, NM, NR> &R, 
         for (int n = 0; n < NR; ++n) {
             const float s = R.live[n] ? sb_to_float<SB>(R.sr[m][n]) : 0.f;
             const float b = R.live[n] ? sb_to_float<SB>(R.br[m][n]) : 0.f;
-            acc[m][n] += (s * d[m][n] + b * asum) * cs;
+            acc[m][n] += s * d[m][n] + b * asum;
         }
 }
 
@@ -379,7 +377,7 @@ __device__ __forceinline__ void unpack_q4_f16(const BlockRegs<4, NM, NR> &R, uin
 // scales, biases and row validity).
 template <int SB, int NM, int NR>
 __device__ __forceinline__ void dot_pre_q4_f16(const BlockRegs<4, NM, NR> &R, const uint32_t (&pre)[NM][NR][16],
-                                               const uint32_t *ap, float asum, float cs, float (&acc)[NM][NR]) {
+                                               const uint32_t *ap, float asum, float (&acc)[NM][NR]) {
     float d[NM][NR];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -399,7 +397,7 @@ __device__ __forceinline__ void dot_pre_q4_f16(const BlockRegs<4, NM, NR> &R, co
         for (int n = 0; n < NR; ++n) {
             const float s = R.live[n] ? sb_to_float<SB>(R.sr[m][n]) : 0.f;
             const float b = R.live[n] ? sb_to_float<SB>(R.br[m][n]) : 0.f;
-            acc[m][n] += (s * d[m][n] + b * asum) * cs;
+            acc[m][n] += s * d[m][n] + b * asum;
         }
 }
 
