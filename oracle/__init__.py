@@ -225,3 +225,27 @@ def layer(cfg, weights: dict, x, resid, ids=None, scores=None):
     gate = r["gate"] if cfg.shared_gate else None
     out = tail(f["partial"], resid, cfg.resid_dtype, shared, gate)
     return dict(route=r, ffn=f, shared=sf, out=out)
+
+
+def selected_weights(cfg, layer_idx, x):
+    """The weights layer() needs for the tokens in x on layer `layer_idx` of a
+    seeded workload, generating (with the shared input generator) only the
+    experts this oracle's routing selects, so that the routed stacks of a
+    full-size layer need not be on the host: returns (weights, ids, scores)
+    where the routed stacks' entry i is expert sel[i] and ids are positions
+    in that list, for layer(..., ids=ids, scores=scores)."""
+    import moe_inputs as mi
+    r = route(x, cfg.x_dtype, mi.gen_router(cfg, layer_idx), cfg.router_dtype, cfg.top_k,
+              cfg.renormalize)
+    sel = sorted(set(int(e) for e in r["ids"].reshape(-1)))
+    w = mi.gen_layer_weights_for(cfg, layer_idx, sel)
+    pos = {e: i for i, e in enumerate(sel)}
+    sub_ids = np.vectorize(pos.get)(r["ids"]).astype(np.int32)
+    return w, sub_ids, r["scores"]
+
+
+def layer_selected(cfg, layer_idx, x, resid):
+    """layer() for layer `layer_idx` of a seeded workload on the selected experts
+    only (selected_weights); the route result keeps the true expert ids."""
+    w, sub_ids, scores = selected_weights(cfg, layer_idx, x)
+    return layer(cfg, w, x, resid, ids=sub_ids, scores=scores)

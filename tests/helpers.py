@@ -124,19 +124,9 @@ def pick_tokens(cfg: mi.LayerConfig, layer: int, n_tokens: int, router, wg=None,
 
 
 def oracle_layer_selected(cfg, layer_idx, x, resid):
-    """oracle.layer for layer `layer_idx` of the seeded workload, generating only
-    the experts the oracle's own routing selects (the routed stacks of a
-    full-size layer need not be on the host)."""
+    """The oracle's layer result generating only the selected experts (oracle.layer_selected)."""
     import oracle
-    r = oracle.route(x, cfg.x_dtype, mi.gen_router(cfg, layer_idx), cfg.router_dtype, cfg.top_k,
-                     cfg.renormalize)
-    sel = sorted(set(int(e) for e in r["ids"].reshape(-1)))
-    w = mi.gen_layer_weights_for(cfg, layer_idx, sel)
-    pos = {e: i for i, e in enumerate(sel)}
-    sub_ids = np.vectorize(pos.get)(r["ids"]).astype(np.int32)
-    ref = oracle.layer(cfg, w, x, resid, ids=sub_ids, scores=r["scores"])
-    assert np.array_equal(ref["route"]["ids"], r["ids"])
-    return ref
+    return oracle.layer_selected(cfg, layer_idx, x, resid)
 
 
 def rel_err(got, ref) -> float:
