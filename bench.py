@@ -156,39 +156,74 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def gpu_state() -> dict:
-    """GPU busy percentage, clocks and the processes using the GPU, from amd-smi
-    (null fields when it cannot tell).  A contended GPU invalidates timings."""
+_SMI_HELPER = r"""
+import json, subprocess, sys
+for _ in sys.stdin:
     out = {}
     for key, args in (("metric", ["metric", "-g", "0", "--usage", "--clock", "--json"]),
                       ("process", ["process", "-g", "0", "--json"])):
         try:
             r = subprocess.run(["amd-smi", *args], capture_output=True, text=True, timeout=20)
             out[key] = json.loads(r.stdout) if r.returncode == 0 else None
-        except (OSError, subprocess.SubprocessError, ValueError):
+        except Exception:
             out[key] = None
-    state = {"gfx_busy_pct": None, "umc_busy_pct": None, "gfx_clk_mhz_max": None, "mem_clk_mhz": None,
-             "other_processes": None}
-    try:
-        m = out["metric"]
-        m = (m["gpu_data"] if isinstance(m, dict) else m)[0]
-        state["gfx_busy_pct"] = m["usage"]["gfx_activity"]["value"]
-        state["umc_busy_pct"] = m["usage"]["umc_activity"]["value"]
-        clk = m["clock"]
-        gfx = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_") and isinstance(v, dict)]
-        state["gfx_clk_mhz_max"] = max(x for x in gfx if isinstance(x, (int, float)))
-        mem = [v["clk"]["value"] for k, v in clk.items() if k.startswith("mem_") and isinstance(v, dict)]
-        state["mem_clk_mhz"] = mem[0] if mem else None
-    except (KeyError, TypeError, IndexError, ValueError):
-        pass
-    try:
-        p = out["process"]
-        p = (p["gpu_data"] if isinstance(p, dict) and "gpu_data" in p else p)[0]
-        procs = [q.get("process_info") for q in p.get("process_list", []) if isinstance(q, dict)]
-        state["other_processes"] = len([q for q in procs if isinstance(q, dict) and q.get("pid") != os.getpid()])
-    except (KeyError, TypeError, AttributeError, IndexError):
-        pass
-    return state
+    print(json.dumps(out), flush=True)
+"""
+
+
+class GpuStateSampler:
+    """amd-smi's view of GPU 0 (busy percentages, clocks, other processes),
+    sampled on request by a helper process started before this process
+    touches the GPU: a process that has initialised the GPU must not start
+    other programs itself.  A contended GPU invalidates timings."""
+
+    def __init__(self):
+        try:
+            self.proc = subprocess.Popen([sys.executable, "-c", _SMI_HELPER], stdin=subprocess.PIPE,
+                                         stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+        except OSError:
+            self.proc = None
+
+    def sample(self) -> dict:
+        state = {"gfx_busy_pct": None, "umc_busy_pct": None, "gfx_clk_mhz_max": None, "mem_clk_mhz": None,
+                 "other_processes": None}
+        if self.proc is None:
+            return state
+        try:
+            self.proc.stdin.write("s\n")
+            self.proc.stdin.flush()
+            out = json.loads(self.proc.stdout.readline())
+        except (OSError, ValueError):
+            return state
+        try:
+            m = out["metric"]
+            m = (m["gpu_data"] if isinstance(m, dict) else m)[0]
+            state["gfx_busy_pct"] = m["usage"]["gfx_activity"]["value"]
+            state["umc_busy_pct"] = m["usage"]["umc_activity"]["value"]
+            clk = m["clock"]
+            gfx = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_") and isinstance(v, dict)]
+            state["gfx_clk_mhz_max"] = max(x for x in gfx if isinstance(x, (int, float)))
+            mem = [v["clk"]["value"] for k, v in clk.items() if k.startswith("mem_") and isinstance(v, dict)]
+            state["mem_clk_mhz"] = mem[0] if mem else None
+        except (KeyError, TypeError, IndexError, ValueError):
+            pass
+        try:
+            p = out["process"]
+            p = (p["gpu_data"] if isinstance(p, dict) and "gpu_data" in p else p)[0]
+            procs = [q.get("process_info") for q in p.get("process_list", []) if isinstance(q, dict)]
+            state["gpu_processes"] = len([q for q in procs if isinstance(q, dict)])
+            state["other_processes"] = len([q for q in procs if isinstance(q, dict) and q.get("pid") != os.getpid()])
+        except (KeyError, TypeError, AttributeError, IndexError):
+            pass
+        return state
+
+    def close(self):
+        if self.proc is not None:
+            try:
+                self.proc.stdin.close()
+                self.proc.wait(timeout=30)
+            except (OSError, subprocess.SubprocessError):
+                self.proc.kill()
 
 
 # ------------------------------------------------------------------ helpers
@@ -644,6 +679,7 @@ def main():
     if args.samples < 10:
         raise SystemExit("--samples must be at least 10")
 
+    sampler = GpuStateSampler()                # before anything touches the GPU
     import torch
     import moe_inputs as mi
     import quantized_moe_decode_amd  # noqa: F401  (fails loudly without the built library)
@@ -658,7 +694,7 @@ def main():
             raise SystemExit(f"unknown workload {n}")
     if args.profile_run and len(names) != 1:
         raise SystemExit("--profile-run needs --config")
-    state_before = gpu_state()
+    state_before = sampler.sample()
     overhead = round_trip_overhead()
     results, stacks = {}, {}
     for n in names:
@@ -672,7 +708,8 @@ def main():
             torch.cuda.empty_cache()
     stacks.clear()
     torch.cuda.empty_cache()
-    state_after = gpu_state()
+    state_after = sampler.sample()
+    sampler.close()
 
     head = results[HEADLINE] if HEADLINE in results else results[names[0]]
     ceil = None
