@@ -169,6 +169,30 @@ moe_status moe_decode_expert_ffn(const void *x, moe_dtype x_dtype, int32_t n_tok
 size_t moe_decode_expert_ffn_workspace_bytes(int32_t n_tokens, int32_t top_k, int32_t n_experts);
 
 /*
+ * moe_decode_expert_ffn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation, kernels and results, with the
+ * workspace taken from a fixed device array the library holds, one per
+ * device, for the life of the process (moe_decode_expert_ffn_noalloc_max_bytes()
+ * bytes, enough for every call within the limits: up to 32 tokens, top-32,
+ * 1024 experts).  Nothing is allocated or freed; the array's device address
+ * is looked up once per device, on the first call made with that device
+ * current.  The caller still passes every input and output.
+ * Calls that overlap on one device (concurrent streams, or host threads)
+ * share that device's array and race: order them on one stream.  The array
+ * keeps the last call's contents; every call writes what it reads, so no
+ * clearing is needed.  Returns MOE_EINVAL for anything moe_decode_expert_ffn
+ * rejects or a workspace need beyond the array (not reachable within the
+ * limits), MOE_EHIP if the array's address cannot be obtained.
+ */
+moe_status moe_decode_expert_ffn_noalloc(const void *x, moe_dtype x_dtype, int32_t n_tokens,
+                                         const moe_qmat *gate, const moe_qmat *up, const moe_qmat *down,
+                                         const int32_t *expert_ids, const float *scores, int32_t top_k,
+                                         float *act, float *partial, void *stream);
+
+size_t moe_decode_expert_ffn_noalloc_max_bytes(void);
+
+/*
  * The two halves of moe_decode_expert_ffn as separate calls, for callers that
  * schedule kernel A and kernel B themselves (mlxcel PR #276, "What changed"
  * step 2: two dispatches with act staged in global memory between them).

@@ -67,6 +67,11 @@ def _load_library():
     L.moe_decode_expert_ffn.restype = i32
     L.moe_decode_expert_ffn_workspace_bytes.argtypes = [i32, i32, i32]
     L.moe_decode_expert_ffn_workspace_bytes.restype = sz
+    L.moe_decode_expert_ffn_noalloc.argtypes = [vp, i32, i32, ctypes.POINTER(CQMat), ctypes.POINTER(CQMat),
+                                                ctypes.POINTER(CQMat), vp, vp, i32, vp, vp, vp]
+    L.moe_decode_expert_ffn_noalloc.restype = i32
+    L.moe_decode_expert_ffn_noalloc_max_bytes.argtypes = []
+    L.moe_decode_expert_ffn_noalloc_max_bytes.restype = sz
     L.moe_decode_gate_up.argtypes = [vp, i32, i32, ctypes.POINTER(CQMat), ctypes.POINTER(CQMat),
                                      vp, i32, vp, vp, sz, vp]
     L.moe_decode_gate_up.restype = i32
@@ -197,6 +202,23 @@ def moe_decode_expert_ffn(x: torch.Tensor, gate: QuantStack, up: QuantStack, dow
     _check(st, "moe_decode_expert_ffn")
 
 
+def moe_decode_expert_ffn_noalloc(x: torch.Tensor, gate: QuantStack, up: QuantStack, down: QuantStack,
+                                  expert_ids: torch.Tensor, scores: Optional[torch.Tensor],
+                                  act: torch.Tensor, partial: torch.Tensor, stream=None) -> None:
+    """moe_decode_expert_ffn with the library's own device scratch instead of a workspace."""
+    T = x.shape[0]
+    K = expert_ids.shape[1]
+    g, u, d = gate.cstruct(), up.cstruct(), down.cstruct()
+    st = lib.moe_decode_expert_ffn_noalloc(_ptr(x), _dt(x), T, ctypes.byref(g), ctypes.byref(u),
+                                           ctypes.byref(d), _ptr(expert_ids), _ptr(scores), K,
+                                           _ptr(act), _ptr(partial), _stream(stream))
+    _check(st, "moe_decode_expert_ffn_noalloc")
+
+
+def expert_ffn_noalloc_max_bytes() -> int:
+    return int(lib.moe_decode_expert_ffn_noalloc_max_bytes())
+
+
 def moe_decode_gate_up(x: torch.Tensor, gate: QuantStack, up: QuantStack,
                        expert_ids: torch.Tensor, act: torch.Tensor,
                        workspace: Optional[torch.Tensor] = None, stream=None) -> None:
@@ -280,6 +302,7 @@ def moe_decode_read_probe(data: torch.Tensor, partial_sums: torch.Tensor, stream
 from .layer import DecodeLayer  # noqa: E402  (needs the functions above)
 
 __all__ = ["QuantStack", "DecodeLayer", "moe_decode_route", "moe_decode_expert_ffn",
+           "moe_decode_expert_ffn_noalloc", "expert_ffn_noalloc_max_bytes",
            "moe_decode_layer", "layer_weights", "layer_workspace_bytes",
            "moe_decode_gate_up", "moe_decode_down",
            "moe_decode_tail", "route_workspace_bytes", "expert_ffn_workspace_bytes",

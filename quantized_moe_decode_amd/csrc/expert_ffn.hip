@@ -23,6 +23,8 @@
 // LDS pass), so each touched expert's weights are read once per step.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "api.hpp"
 #include "common.hpp"
 #include "qgemv.hpp"
@@ -639,4 +641,56 @@ extern "C" moe_status moe_decode_expert_ffn(const void *x, moe_dtype x_dtype, in
     if ((st = launch_a(p)) != MOE_OK) return st;
     if ((st = launch_b(p)) != MOE_OK) return st;
     return finish();
+}
+
+// ------------------------------------------------- the call that allocates nothing
+
+namespace moe {
+
+// The bucketing workspace of the largest call the limits allow (32 tokens,
+// top-32, 1024 experts), as a device array: each device that the library
+// runs on holds one until the process ends.
+constexpr size_t kNoAllocScratchBytes =
+    ((1 + 2 * (size_t)((MOE_MAX_TOKENS * MOE_MAX_TOP_K + kBatchTok - 1) / kBatchTok + MOE_MAX_EXPERTS + 1) + 1 +
+      (size_t)MOE_MAX_TOKENS * MOE_MAX_TOP_K) * sizeof(int32_t) + 255) / 256 * 256;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex scratch_mu;
+static void *scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current); nullptr on failure.
+static void *device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        scratch_ptr[dev] = p;
+    }
+    return scratch_ptr[dev];
+}
+
+}  // namespace moe
+
+extern "C" size_t moe_decode_expert_ffn_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" moe_status moe_decode_expert_ffn_noalloc(const void *x, moe_dtype x_dtype, int32_t n_tokens,
+                                                    const moe_qmat *gate, const moe_qmat *up, const moe_qmat *down,
+                                                    const int32_t *expert_ids, const float *scores, int32_t top_k,
+                                                    float *act, float *partial, void *stream) {
+    if (n_tokens <= 1)        // one token needs no workspace
+        return moe_decode_expert_ffn(x, x_dtype, n_tokens, gate, up, down, expert_ids, scores, top_k, act,
+                                     partial, nullptr, 0, stream);
+    if (!gate || n_tokens > MOE_MAX_TOKENS || top_k < 1 || top_k > MOE_MAX_TOP_K || gate->n_experts < 1 ||
+        gate->n_experts > MOE_MAX_EXPERTS)
+        return MOE_EINVAL;
+    const size_t need = moe_decode_expert_ffn_workspace_bytes(n_tokens, top_k, gate->n_experts);
+    if (need == 0 || need > kNoAllocScratchBytes) return MOE_EINVAL;
+    void *ws = device_scratch();
+    if (!ws) return MOE_EHIP;
+    return moe_decode_expert_ffn(x, x_dtype, n_tokens, gate, up, down, expert_ids, scores, top_k, act, partial,
+                                 ws, need, stream);
 }

@@ -297,3 +297,17 @@ def test_binding_raises_on_error():
 
 class _FakeStream:
     cuda_stream = 0
+
+
+def test_noalloc_rejects_invalid_calls_on_the_host():
+    """moe_decode_expert_ffn_noalloc validates like moe_decode_expert_ffn, before
+    it looks up its device array: these calls never reach the device."""
+    f = lib.moe_decode_expert_ffn_noalloc
+    g = _qm(rows=768, cols=2048)
+    d = _qm(rows=2048, cols=768)
+    args = lambda T, gate=g: (P, MOE_BF16, T, ctypes.byref(gate) if gate is not None else None,
+                              ctypes.byref(g), ctypes.byref(d), P, P, 8, P, P, None)
+    assert f(*args(2, gate=None)) == MOE_EINVAL          # null stack
+    assert f(*args(33)) == MOE_EINVAL                   # more tokens than the limit
+    assert f(*args(0)) == MOE_EINVAL
+    assert qmd.expert_ffn_noalloc_max_bytes() == qmd.expert_ffn_workspace_bytes(32, 32, 1024)
