@@ -24,14 +24,23 @@ LIB = os.path.join(HERE, "liboracle.so")
 DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
-    if force or not os.path.exists(LIB):
-        tmp = LIB + ".tmp"
+SAN_LIB = os.path.join(HERE, "liboracle_san.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math).  sanitize=True
+    builds liboracle_san.so with AddressSanitizer and UndefinedBehaviorSanitizer
+    (any finding aborts); load it with MOE_ORACLE_LIB set to its path and gcc's
+    libasan preloaded."""
+    out = SAN_LIB if sanitize else LIB
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-                               "-Wall", "-Wextra", "-fno-fast-math", "-o", tmp, SRC, "-lm"])
-        os.replace(tmp, LIB)
-    return LIB
+                               "-Wall", "-Wextra", "-fno-fast-math", *(SANITIZE_FLAGS if sanitize else []),
+                               "-o", tmp, SRC, "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 class _QMat(ctypes.Structure):
@@ -70,9 +79,10 @@ def _load(path: str):
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
+        path = os.environ.get("MOE_ORACLE_LIB", LIB)
+        if path == LIB and not os.path.exists(LIB):
             build()
-        _lib = _load(LIB)
+        _lib = _load(path)
     return _lib
 
 

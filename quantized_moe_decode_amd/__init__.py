@@ -22,7 +22,8 @@ from typing import Optional
 import torch  # first: the library then binds to torch's HIP runtime
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "lib", "libmoe_decode.so")
+# MOE_DECODE_LIB selects another build of the library (the host-sanitizer build in the tests)
+LIB_PATH = os.environ.get("MOE_DECODE_LIB") or os.path.join(PKG, "lib", "libmoe_decode.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ETIMEOUT = 0, 1, 2, 3, 4
 MOE_WORKSPACE_HEAD_BYTES = 4

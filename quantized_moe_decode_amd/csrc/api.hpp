@@ -12,6 +12,18 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 inline bool valid_dtype(int dt) { return dt == MOE_F32 || dt == MOE_F16 || dt == MOE_BF16; }
 
+// The integer an enum argument or field holds, as the caller passed it.  A C
+// caller may pass any int, and in C++ an int outside an enum's enumerators is
+// not a value of that type (reading it as one is undefined), so the library
+// reads the bits of every moe_dtype and moe_status it is given.
+template <typename E>
+inline int raw_enum(const E &e) {
+    static_assert(sizeof(E) == sizeof(int), "enums of the C ABI are int-sized");
+    int v;
+    __builtin_memcpy(&v, &e, sizeof v);
+    return v;
+}
+
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Checks one projection stack in isolation.  Returns MOE_OK or the error.
@@ -19,7 +31,7 @@ inline moe_status check_qmat(const moe_qmat *m) {
     if (!m || !m->q || !m->scales || !m->biases) return MOE_EINVAL;
     if (m->bits != 4 && m->bits != 6 && m->bits != 8) return MOE_EUNSUPPORTED;
     if (m->group_size != 64) return MOE_EUNSUPPORTED;
-    if (m->sb_dtype != MOE_F16 && m->sb_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+    if (raw_enum(m->sb_dtype) != MOE_F16 && raw_enum(m->sb_dtype) != MOE_BF16) return MOE_EUNSUPPORTED;
     if (m->n_experts < 1 || m->n_experts > MOE_MAX_EXPERTS) return MOE_EINVAL;
     if (m->rows < 64 || m->rows > MOE_MAX_DIM || m->rows % 64) return MOE_EINVAL;
     if (m->cols < 64 || m->cols > MOE_MAX_DIM || m->cols % 64) return MOE_EINVAL;

@@ -414,7 +414,7 @@ static QM to_qm(const moe_qmat *m) {
     q.wpr = m->cols * m->bits / 32;
     q.gpr = m->cols / 64;
     q.bits_ = m->bits;
-    q.sb_ = m->sb_dtype;
+    q.sb_ = raw_enum(m->sb_dtype);
     return q;
 }
 
@@ -562,17 +562,18 @@ static moe_status finish() { return hipGetLastError() == hipSuccess ? MOE_OK : M
 
 }  // namespace moe
 
-extern "C" moe_status moe_decode_gate_up(const void *x, moe_dtype x_dtype, int32_t n_tokens,
+extern "C" moe_status moe_decode_gate_up(const void *x, moe_dtype x_dtype_arg, int32_t n_tokens,
                                          const moe_qmat *gate, const moe_qmat *up,
                                          const int32_t *expert_ids, int32_t top_k, float *act,
                                          void *workspace, size_t workspace_bytes, void *stream) {
+    const int x_dtype = raw_enum(x_dtype_arg);
     moe_status st = check_tokens(x, n_tokens, top_k);
     if (st != MOE_OK) return st;
     for (const moe_qmat *m : {gate, up})
         if ((st = check_qmat(m)) != MOE_OK) return st;
     if (!valid_dtype(x_dtype)) return MOE_EUNSUPPORTED;
     if (up->rows != gate->rows || up->cols != gate->cols || up->n_experts != gate->n_experts) return MOE_EINVAL;
-    if (up->sb_dtype != gate->sb_dtype || up->bits != gate->bits) return MOE_EUNSUPPORTED;
+    if (raw_enum(up->sb_dtype) != raw_enum(gate->sb_dtype) || up->bits != gate->bits) return MOE_EUNSUPPORTED;
     if (!act || !aligned16(act)) return MOE_EINVAL;
     Plan p = {};
     if ((st = plan_common(p, n_tokens, top_k, gate->n_experts, expert_ids, workspace, workspace_bytes,
@@ -610,11 +611,25 @@ extern "C" moe_status moe_decode_down(const float *act, int32_t n_tokens, const 
     return finish();
 }
 
+namespace moe {
+static moe_status expert_ffn(const void *x, int x_dtype, int32_t n_tokens, const moe_qmat *gate, const moe_qmat *up,
+                             const moe_qmat *down, const int32_t *expert_ids, const float *scores, int32_t top_k,
+                             float *act, float *partial, void *workspace, size_t workspace_bytes, void *stream);
+}  // namespace moe
+
 extern "C" moe_status moe_decode_expert_ffn(const void *x, moe_dtype x_dtype, int32_t n_tokens,
                                             const moe_qmat *gate, const moe_qmat *up, const moe_qmat *down,
                                             const int32_t *expert_ids, const float *scores, int32_t top_k,
                                             float *act, float *partial,
                                             void *workspace, size_t workspace_bytes, void *stream) {
+    return expert_ffn(x, raw_enum(x_dtype), n_tokens, gate, up, down, expert_ids, scores, top_k, act, partial,
+                      workspace, workspace_bytes, stream);
+}
+
+static moe_status moe::expert_ffn(const void *x, int x_dtype, int32_t n_tokens, const moe_qmat *gate,
+                                  const moe_qmat *up, const moe_qmat *down, const int32_t *expert_ids,
+                                  const float *scores, int32_t top_k, float *act, float *partial, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
     moe_status st = check_tokens(x, n_tokens, top_k);
     if (st != MOE_OK) return st;
     for (const moe_qmat *m : {gate, up, down})
@@ -623,7 +638,8 @@ extern "C" moe_status moe_decode_expert_ffn(const void *x, moe_dtype x_dtype, in
     const int d_in = gate->cols, d_ff = gate->rows, E = gate->n_experts;
     if (up->rows != d_ff || up->cols != d_in || down->rows != d_in || down->cols != d_ff) return MOE_EINVAL;
     if (up->n_experts != E || down->n_experts != E) return MOE_EINVAL;
-    if (up->sb_dtype != gate->sb_dtype || down->sb_dtype != gate->sb_dtype) return MOE_EUNSUPPORTED;
+    if (raw_enum(up->sb_dtype) != raw_enum(gate->sb_dtype) || raw_enum(down->sb_dtype) != raw_enum(gate->sb_dtype))
+        return MOE_EUNSUPPORTED;
     if (up->bits != gate->bits) return MOE_EUNSUPPORTED;
     if (!act || !partial || !aligned16(act) || !aligned16(partial)) return MOE_EINVAL;
     Plan p = {};
@@ -677,13 +693,14 @@ static void *device_scratch() {
 
 extern "C" size_t moe_decode_expert_ffn_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
 
-extern "C" moe_status moe_decode_expert_ffn_noalloc(const void *x, moe_dtype x_dtype, int32_t n_tokens,
+extern "C" moe_status moe_decode_expert_ffn_noalloc(const void *x, moe_dtype x_dtype_arg, int32_t n_tokens,
                                                     const moe_qmat *gate, const moe_qmat *up, const moe_qmat *down,
                                                     const int32_t *expert_ids, const float *scores, int32_t top_k,
                                                     float *act, float *partial, void *stream) {
+    const int x_dtype = raw_enum(x_dtype_arg);
     if (n_tokens <= 1)        // one token needs no workspace
-        return moe_decode_expert_ffn(x, x_dtype, n_tokens, gate, up, down, expert_ids, scores, top_k, act,
-                                     partial, nullptr, 0, stream);
+        return expert_ffn(x, x_dtype, n_tokens, gate, up, down, expert_ids, scores, top_k, act, partial, nullptr, 0,
+                          stream);
     if (!gate || n_tokens > MOE_MAX_TOKENS || top_k < 1 || top_k > MOE_MAX_TOP_K || gate->n_experts < 1 ||
         gate->n_experts > MOE_MAX_EXPERTS)
         return MOE_EINVAL;
@@ -691,6 +708,6 @@ extern "C" moe_status moe_decode_expert_ffn_noalloc(const void *x, moe_dtype x_d
     if (need == 0 || need > kNoAllocScratchBytes) return MOE_EINVAL;
     void *ws = device_scratch();
     if (!ws) return MOE_EHIP;
-    return moe_decode_expert_ffn(x, x_dtype, n_tokens, gate, up, down, expert_ids, scores, top_k, act, partial,
-                                 ws, need, stream);
+    return expert_ffn(x, x_dtype, n_tokens, gate, up, down, expert_ids, scores, top_k, act, partial, ws, need,
+                      stream);
 }

@@ -35,11 +35,12 @@ static moe_status plan_layer(const moe_layer_weights *w, int d_in_check, LayerPl
         return MOE_EINVAL;
     if (w->up.n_experts != E || w->down.n_experts != E || w->n_experts != E) return MOE_EINVAL;
     if (w->up.bits != w->gate.bits) return MOE_EUNSUPPORTED;
-    if (w->up.sb_dtype != w->gate.sb_dtype || w->down.sb_dtype != w->gate.sb_dtype) return MOE_EUNSUPPORTED;
+    const int sb = raw_enum(w->gate.sb_dtype);
+    if (raw_enum(w->up.sb_dtype) != sb || raw_enum(w->down.sb_dtype) != sb) return MOE_EUNSUPPORTED;
     if (d_in_check >= 0 && d_in_check != d_in) return MOE_EINVAL;
     if (w->top_k < 1 || w->top_k > MOE_MAX_TOP_K || w->top_k > E) return MOE_EINVAL;
     if (w->n_shared < 0 || w->n_shared > MOE_MAX_SHARED) return MOE_EINVAL;
-    if (!valid_dtype(w->w_router_dtype)) return MOE_EUNSUPPORTED;
+    if (!valid_dtype(raw_enum(w->w_router_dtype))) return MOE_EUNSUPPORTED;
     if (!aligned16(w->w_router)) return MOE_EINVAL;
     int d_ffs = 0;
     if (w->n_shared > 0) {
@@ -55,8 +56,8 @@ static moe_status plan_layer(const moe_layer_weights *w, int d_in_check, LayerPl
         if (w->shared_gate.bits != w->gate.bits || w->shared_up.bits != w->gate.bits ||
             w->shared_down.bits != w->down.bits)
             return MOE_EUNSUPPORTED;
-        if (w->shared_gate.sb_dtype != w->gate.sb_dtype || w->shared_up.sb_dtype != w->gate.sb_dtype ||
-            w->shared_down.sb_dtype != w->gate.sb_dtype)
+        if (raw_enum(w->shared_gate.sb_dtype) != sb || raw_enum(w->shared_up.sb_dtype) != sb ||
+            raw_enum(w->shared_down.sb_dtype) != sb)
             return MOE_EUNSUPPORTED;
     } else if (w->w_shared_gate) {
         return MOE_EINVAL;       // a shared gate needs shared experts
@@ -76,7 +77,7 @@ static moe_status plan_layer(const moe_layer_weights *w, int d_in_check, LayerPl
         q.b = reinterpret_cast<const uint16_t *>(m.biases);
         q.rows = m.rows; q.cols = m.cols;
         q.wpr = m.cols * m.bits / 32; q.gpr = m.cols / 64;
-        q.bits_ = m.bits; q.sb_ = m.sb_dtype;
+        q.bits_ = m.bits; q.sb_ = raw_enum(m.sb_dtype);
         return q;
     };
     a.gate = qm(w->gate); a.up = qm(w->up); a.down = qm(w->down);
@@ -99,7 +100,7 @@ static moe_status plan_layer(const moe_layer_weights *w, int d_in_check, LayerPl
     // dynamic LDS: kernel-B units stage act as fp32 chunks (+4 floats each),
     // kernel-A units stage x raw (+16 bytes per chunk)
     const int ca = codes_of(w->gate.bits);
-    const size_t x_elem = w->w_router_dtype == MOE_F32 ? 4 : 2;     // x has the router's dtype
+    const size_t x_elem = raw_enum(w->w_router_dtype) == MOE_F32 ? 4 : 2;     // x has the router's dtype
     const size_t lds_b = (size_t)(dmax / cb) * (cb + 4) * sizeof(float);
     const size_t lds_a = (size_t)(d_in / ca) * ((size_t)ca * x_elem + 16);
     p.lds = lds_b > lds_a ? lds_b : lds_a;
@@ -212,20 +213,22 @@ extern "C" size_t moe_decode_layer_workspace_bytes(const moe_layer_weights *weig
     return plan_layer(weights, -1, p) == MOE_OK ? p.ws_bytes : 0;
 }
 
-extern "C" moe_status moe_decode_layer(const moe_layer_weights *weights, const void *x, moe_dtype x_dtype,
-                                       const void *residual, moe_dtype residual_dtype, float *out,
+extern "C" moe_status moe_decode_layer(const moe_layer_weights *weights, const void *x, moe_dtype x_dtype_arg,
+                                       const void *residual, moe_dtype residual_dtype_arg, float *out,
                                        int32_t *expert_ids, float *scores, float *shared_gate,
                                        void *workspace, size_t workspace_bytes, void *stream) {
+    const int x_dtype = raw_enum(x_dtype_arg), residual_dtype = raw_enum(residual_dtype_arg);
     if (!x || !residual || !out || !workspace) return MOE_EINVAL;
     if (!valid_dtype(x_dtype) || !valid_dtype(residual_dtype)) return MOE_EUNSUPPORTED;
     if (!aligned16(x) || !aligned16(workspace)) return MOE_EINVAL;
     LayerPlan p;
     const moe_status st = plan_layer(weights, -1, p);
     if (st != MOE_OK) return st;
-    if (weights->w_router_dtype != x_dtype) return MOE_EUNSUPPORTED;
+    if (raw_enum(weights->w_router_dtype) != x_dtype) return MOE_EUNSUPPORTED;
     if (workspace_bytes < p.ws_bytes) return MOE_EINVAL;
-    LayerFn k1 = pick_layer(weights->gate.bits, weights->down.bits, weights->gate.sb_dtype, x_dtype, kLayerNRA);
-    LayerFn k2 = pick_layer(weights->gate.bits, weights->down.bits, weights->gate.sb_dtype, x_dtype, kLayerNRA2);
+    const int sb = raw_enum(weights->gate.sb_dtype);
+    LayerFn k1 = pick_layer(weights->gate.bits, weights->down.bits, sb, x_dtype, kLayerNRA);
+    LayerFn k2 = pick_layer(weights->gate.bits, weights->down.bits, sb, x_dtype, kLayerNRA2);
     if (!k1 || !k2) return MOE_EUNSUPPORTED;
     fit_a_passes(p, resident_capacity(k1, p.lds), resident_capacity(k2, p.lds));
     LayerFn k = p.a_nr == kLayerNRA ? k1 : k2;

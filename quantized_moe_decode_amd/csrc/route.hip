@@ -210,12 +210,14 @@ extern "C" moe_status moe_decode_workspace_status(const void *head, size_t head_
     return err ? MOE_ETIMEOUT : MOE_OK;
 }
 
-extern "C" moe_status moe_decode_route(const void *x, moe_dtype x_dtype, int32_t n_tokens, int32_t d_in,
-                                       const void *w_router, moe_dtype w_router_dtype,
+extern "C" moe_status moe_decode_route(const void *x, moe_dtype x_dtype_arg, int32_t n_tokens, int32_t d_in,
+                                       const void *w_router, moe_dtype w_router_dtype_arg,
                                        int32_t n_experts, int32_t top_k, int32_t renormalize,
-                                       const void *w_shared_gate, moe_dtype w_shared_gate_dtype,
+                                       const void *w_shared_gate, moe_dtype w_shared_gate_dtype_arg,
                                        int32_t *expert_ids, float *scores, float *shared_gate,
                                        void *workspace, size_t workspace_bytes, void *stream) {
+    const int x_dtype = raw_enum(x_dtype_arg), w_router_dtype = raw_enum(w_router_dtype_arg),
+              w_shared_gate_dtype = raw_enum(w_shared_gate_dtype_arg);
     if (!x || !w_router || !expert_ids || !scores || !workspace) return MOE_EINVAL;
     if ((w_shared_gate == nullptr) != (shared_gate == nullptr)) return MOE_EINVAL;
     if (n_tokens < 1 || n_tokens > MOE_MAX_TOKENS) return MOE_EINVAL;

@@ -51,7 +51,7 @@ using namespace moe;
 
 extern "C" moe_status moe_decode_tail(const float *partial, int32_t n_tokens, int32_t top_k, int32_t d_in,
                                       const float *shared, int32_t n_shared, const float *shared_gate,
-                                      const void *residual, moe_dtype residual_dtype, float *out,
+                                      const void *residual, moe_dtype residual_dtype_arg, float *out,
                                       void *stream) {
     if (!partial || !residual || !out) return MOE_EINVAL;
     if (n_tokens < 1 || n_tokens > MOE_MAX_TOKENS) return MOE_EINVAL;
@@ -59,6 +59,7 @@ extern "C" moe_status moe_decode_tail(const float *partial, int32_t n_tokens, in
     if (d_in < kGroup || d_in > MOE_MAX_DIM || d_in % kGroup) return MOE_EINVAL;
     if (n_shared < 0 || n_shared > MOE_MAX_TOP_K) return MOE_EINVAL;
     if ((n_shared == 0) != (shared == nullptr)) return MOE_EINVAL;
+    const int residual_dtype = raw_enum(residual_dtype_arg);
     if (!valid_dtype(residual_dtype)) return MOE_EUNSUPPORTED;
     TailArgs a;
     a.partial = partial; a.shared = shared; a.gate = shared_gate; a.resid = residual; a.out = out;
@@ -69,8 +70,8 @@ extern "C" moe_status moe_decode_tail(const float *partial, int32_t n_tokens, in
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-extern "C" const char *moe_decode_status_string(moe_status s) {
-    switch (s) {
+extern "C" const char *moe_decode_status_string(moe_status s_arg) {
+    switch (raw_enum(s_arg)) {
     case MOE_OK: return "MOE_OK";
     case MOE_EINVAL: return "MOE_EINVAL: invalid argument (null pointer, shape, size or alignment)";
     case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: bit width, group size or dtype not built";
