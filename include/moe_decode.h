@@ -144,8 +144,9 @@ moe_status moe_decode_workspace_status(const void *head, size_t head_bytes);
  *   partial[t][k][i] = score[t][k] * (W_down[e] act[t][k])[i]                  (kernel B)
  * where silu(z) = z * sigmoid(z) and score = 1 when `scores` is NULL.
  * An id outside [0, n_experts) yields all-zero act and partial rows.
- * With n_tokens > 1, each touched expert's weights are read once and applied
- * to all tokens routed to it.
+ * With n_tokens > 1, the pairs are regrouped by expert and an expert's weights
+ * are streamed once per work item of up to 4 of its tokens (an expert with
+ * more tokens is streamed again, mostly from cache).
  * A shared expert is run through this same call with its own stacks,
  * expert_ids[t][s] = s and scores = NULL; its partial is the `shared` input
  * of moe_decode_tail.
@@ -231,12 +232,19 @@ moe_status moe_decode_tail(const float *partial, int32_t n_tokens, int32_t top_k
 
 /*
  * The whole layer for ONE token in a single launch: route, kernel A and
- * kernel B for the K selected experts and the S shared experts, and the tail,
- * with the same arithmetic as moe_decode_route + moe_decode_expert_ffn (routed,
- * then shared) + moe_decode_tail (sources as cited above).  Workgroups hand
- * results to each other through the workspace and device-scope counters
- * instead of kernel boundaries, so the down-projection weights stream while
- * the gate/up projections run (the dependency [P1] "What changed" step 1
+ * kernel B for the K selected experts and the S shared experts, and the tail:
+ * the same computation as moe_decode_route + moe_decode_expert_ffn (routed,
+ * then shared) + moe_decode_tail (sources as cited above), the same routing
+ * bit for bit and the same summation order, but not the same rounding: with
+ * 4-bit weights and bf16 x the gate/up dot products use the packed bf16 dot
+ * (128 + q as exact bf16 pairs, one rounding per pair sum), and 4-bit down
+ * projections take act staged as fp16 after an exact power-of-two scaling
+ * (2^8, or a factor fitted to the slot's largest magnitude when that would
+ * overflow), with fp32 sums throughout; the three-call single-token kernels
+ * use fp32 FMAs.  Both stay within 2e-3 of the result's infinity norm.
+ * Workgroups hand results to each other through the workspace instead of
+ * kernel boundaries, so the down-projection weights stream while the gate/up
+ * projections run (the dependency mlxcel PR #276 "What changed" step 1
  * describes, resolved inside one launch).
  *
  * moe_layer_weights (host struct; every pointer in it is a device pointer):
