@@ -65,6 +65,8 @@ def _load(path: str):
     L.oracle_expert_ffn.restype = i32
     L.oracle_tail.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, i32, vp]
     L.oracle_tail.restype = i32
+    L.oracle_rmsnorm.argtypes = [vp, i32, i32, vp, i32, ctypes.c_double, vp]
+    L.oracle_rmsnorm.restype = i32
     L.oracle_unpack_row.argtypes = [vp, i32, i64, vp]
     L.oracle_unpack_row.restype = None
     L.oracle_dequant_row.argtypes = [ctypes.POINTER(_QMat), i64, i64, vp]
@@ -208,6 +210,21 @@ def tail(partial, resid, resid_dtype, shared=None, gate=None):
                            DTYPE_CODE[resid_dtype], _p(out))
     if rc != 0:
         raise ValueError("oracle_tail: invalid sizes")
+    return out
+
+
+def rmsnorm(y, weight, w_dtype, eps):
+    """The next layer's RMSNorm of the layer output y [T, d] (float64):
+    y / sqrt(mean(y^2) + eps) * weight, per token; weight [d] encoded in w_dtype."""
+    y = _c(y, np.float64)
+    if y.ndim == 1:
+        y = y[None]
+    T, d = y.shape
+    w = _c(weight)
+    out = np.empty((T, d))
+    rc = lib().oracle_rmsnorm(_p(y), T, d, _p(w), DTYPE_CODE[w_dtype], float(eps), _p(out))
+    if rc != 0:
+        raise ValueError("oracle_rmsnorm: invalid sizes")
     return out
 
 

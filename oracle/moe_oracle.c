@@ -303,3 +303,32 @@ int oracle_tail(const double *partial, int n_tokens, int top_k, int d_in,
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------- rmsnorm -- */
+/*
+ * The next layer's RMSNorm applied to the layer output (Red Lite dev39, "fused
+ * expert tail (GPU-routed decode)", section "Measurements": the tail variant
+ * that also computed the next layer's RMSNorm).  The standard definition, per
+ * token t:
+ *   ms             = (1 / d) * sum_i y[t, i]^2
+ *   normed[t, i]   = y[t, i] / sqrt(ms + eps) * weight[i]
+ * y is the layer output [n_tokens][d] (double), weight [d] of dtype w_dt,
+ * eps >= 0.  Returns 0, or -1 on invalid sizes.
+ */
+int oracle_rmsnorm(const double *y, int n_tokens, int d, const void *weight, int w_dt, double eps,
+                   double *normed)
+{
+    if (n_tokens < 1 || d < 1 || eps < 0.0)
+        return -1;
+    for (int t = 0; t < n_tokens; ++t) {
+        const double *yt = y + (size_t)t * d;
+        double ss = 0.0;
+        for (int i = 0; i < d; ++i)
+            ss += yt[i] * yt[i];
+        double ms = ss / (double)d;
+        double inv = 1.0 / sqrt(ms + eps);
+        for (int i = 0; i < d; ++i)
+            normed[(size_t)t * d + i] = yt[i] * inv * load_val(weight, w_dt, (size_t)i);
+    }
+    return 0;
+}

@@ -418,6 +418,69 @@ def pin_tokens_are_independent():
         assert np.array_equal(o1[0], out[t])
 
 
+def _gamma(d, seed):
+    """A non-symmetric RMSNorm weight in bf16 (exactly decodable)."""
+    g = np.random.default_rng([seed, d]).uniform(0.5, 1.5, d)
+    return mi.encode(g, mi.BF16), np_decode(mi.encode(g, mi.BF16), mi.BF16)
+
+
+def pin_rmsnorm_closed_forms():
+    """Constant vectors: y = c 1 gives ms = c^2, so normed = c / sqrt(c^2 + eps) * w
+    (sign(c) * w at eps = 0); a +-1 vector with eps = 0 gives y * w exactly."""
+    d = 96
+    wb, w = _gamma(d, 1)
+    for c, eps in ((3.0, 0.0), (-0.25, 0.0), (2.0, 1e-6), (1e-3, 1e-6), (0.5, 0.75)):
+        got = oracle.rmsnorm(np.full((1, d), c), wb, mi.BF16, eps)[0]
+        want = c / np.sqrt(c * c + eps) * w
+        assert np.max(np.abs(got - want)) <= 1e-15 * np.max(np.abs(want)), (c, eps)
+    y = np.where(np.random.default_rng(2).integers(0, 2, d) == 1, 1.0, -1.0)
+    assert np.array_equal(oracle.rmsnorm(y[None], wb, mi.BF16, 0.0)[0], y * w)
+
+
+def pin_rmsnorm_equals_l2_normalisation():
+    """At eps = 0, y / sqrt(mean(y^2)) = sqrt(d) * y / ||y||_2 (numpy's L2 norm);
+    with eps the scale is 1 / sqrt(||y||^2 / d + eps)."""
+    rng = np.random.default_rng(3)
+    for d in (64, 2048, 4096):
+        wb, w = _gamma(d, 4)
+        y = rng.standard_normal((3, d)) * rng.uniform(0.01, 10.0, (3, 1))
+        got = oracle.rmsnorm(y, wb, mi.BF16, 0.0)
+        want = np.sqrt(d) * y / np.linalg.norm(y, axis=1, keepdims=True) * w
+        assert np.max(np.abs(got - want)) <= 1e-13 * np.max(np.abs(want))
+        eps = 1e-2
+        got = oracle.rmsnorm(y, wb, mi.BF16, eps)
+        want = y / np.sqrt(np.linalg.norm(y, axis=1, keepdims=True) ** 2 / d + eps) * w
+        assert np.max(np.abs(got - want)) <= 1e-13 * np.max(np.abs(want))
+
+
+def pin_rmsnorm_scale_invariance_and_sum_of_squares():
+    """rmsnorm(a y, a^2 eps) = rmsnorm(y, eps) for a > 0, and with unit weight the
+    normed vector's sum of squares is d * ms / (ms + eps)."""
+    rng = np.random.default_rng(5)
+    d = 768
+    wb, _ = _gamma(d, 6)
+    one = mi.encode(np.ones(d), mi.F32)
+    y = rng.standard_normal((2, d))
+    for a, eps in ((7.0, 1e-6), (1e-3, 0.25), (1e4, 3.0)):
+        ref = oracle.rmsnorm(y, wb, mi.BF16, eps)
+        got = oracle.rmsnorm(a * y, wb, mi.BF16, eps * a * a)
+        assert np.max(np.abs(got - ref)) <= 1e-13 * np.max(np.abs(ref)), (a, eps)
+        n = oracle.rmsnorm(y, one, mi.F32, eps)
+        ms = np.mean(y * y, axis=1)
+        assert np.allclose(np.sum(n * n, axis=1), d * ms / (ms + eps), rtol=1e-13, atol=0)
+
+
+def pin_rmsnorm_tokens_independent():
+    """Each token is normalised by its own mean square."""
+    rng = np.random.default_rng(7)
+    d = 128
+    wb, _ = _gamma(d, 8)
+    y = rng.standard_normal((4, d)) * np.array([[1.0], [100.0], [1e-3], [5.0]])
+    both = oracle.rmsnorm(y, wb, mi.BF16, 1e-6)
+    for t in range(4):
+        assert np.array_equal(oracle.rmsnorm(y[t], wb, mi.BF16, 1e-6)[0], both[t])
+
+
 # cheap pins first, so that a broken oracle is usually rejected within a second
 _SLOW = ("pin_onehot_x_probes_every_index", "pin_decode_all_half_and_bf16_patterns",
          "pin_sampled_rows_real_shapes")

@@ -47,6 +47,12 @@ MUTATIONS = [
     ("only the last slot", "routed += partial[", "routed = partial["),
     ("fp16 exponent off by one", "expo - 25", "expo - 24"),
     ("bf16 decode shifted", "uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    ("rmsnorm sum instead of mean", "double ms = ss / (double)d;", "double ms = ss;"),
+    ("rmsnorm eps outside the root", "double inv = 1.0 / sqrt(ms + eps);", "double inv = 1.0 / (sqrt(ms) + eps);"),
+    ("rmsnorm weight dropped", "yt[i] * inv * load_val(weight, w_dt, (size_t)i);", "yt[i] * inv;"),
+    ("rmsnorm weight reversed", "load_val(weight, w_dt, (size_t)i);", "load_val(weight, w_dt, (size_t)(d - 1 - i));"),
+    ("rmsnorm first token's mean for all", "const double *yt = y + (size_t)t * d;\n        double ss = 0.0;\n        for (int i = 0; i < d; ++i)\n            ss += yt[i] * yt[i];",
+     "const double *yt = y + (size_t)t * d;\n        double ss = 0.0;\n        for (int i = 0; i < d; ++i)\n            ss += y[i] * y[i];"),
 ]
 
 
