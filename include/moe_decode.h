@@ -292,6 +292,51 @@ moe_status moe_decode_layer(const moe_layer_weights *weights, const void *x, moe
 size_t moe_decode_layer_workspace_bytes(const moe_layer_weights *weights);
 
 /*
+ * The next layer's RMSNorm of the layer output, folded into the tail (Red
+ * Lite dev39, "fused expert tail (GPU-routed decode)", section
+ * "Measurements": a tail that also computed the next layer's RMSNorm; there it
+ * ran on one threadgroup and lost to the separate dispatches, here the sum of
+ * squares is spread over the tail's workgroups).  For every token t:
+ *   normed[t][i] = out[t][i] / sqrt((1/d_in) sum_i out[t][i]^2 + eps) * weight[i]
+ * computed from the fp32 out the tail writes.  Each tail workgroup sums the
+ * squares of its own elements in a fixed order and the workgroups' sums are
+ * added in workgroup order, so repeated calls give the same bits.
+ *   weight  [d_in] device pointer, dtype `dtype` (F32, F16 or BF16), 4-byte aligned
+ *   eps     >= 0 and finite
+ *   normed  out fp32 [n_tokens][d_in] device pointer, 4-byte aligned; may not alias out
+ */
+typedef struct {
+    const void *weight;
+    moe_dtype dtype;
+    float eps;
+    float *normed;
+} moe_rmsnorm;
+
+/*
+ * moe_decode_tail, also writing norm->normed (norm must not be NULL).  The
+ * workspace (moe_decode_tail_rmsnorm_workspace_bytes() bytes, 16-byte aligned)
+ * is zero-filled before its first use and not written by the caller
+ * afterwards: like moe_decode_route's, it carries a launch epoch from call
+ * to call, its first MOE_WORKSPACE_HEAD_BYTES bytes are the error word
+ * (moe_decode_workspace_status), and calls that may overlap need separate
+ * workspaces.  MOE_EUNSUPPORTED if the device cannot hold all
+ * n_tokens * ceil(d_in / 256) workgroups at once.
+ */
+moe_status moe_decode_tail_rmsnorm(const float *partial, int32_t n_tokens, int32_t top_k, int32_t d_in,
+                                   const float *shared, int32_t n_shared, const float *shared_gate,
+                                   const void *residual, moe_dtype residual_dtype, float *out,
+                                   const moe_rmsnorm *norm, void *workspace, size_t workspace_bytes, void *stream);
+
+size_t moe_decode_tail_rmsnorm_workspace_bytes(int32_t n_tokens, int32_t d_in);
+
+/* moe_decode_layer, also writing norm->normed (norm must not be NULL); the
+ * same workspace as moe_decode_layer. */
+moe_status moe_decode_layer_rmsnorm(const moe_layer_weights *weights, const void *x, moe_dtype x_dtype,
+                                    const void *residual, moe_dtype residual_dtype, float *out,
+                                    const moe_rmsnorm *norm, int32_t *expert_ids, float *scores,
+                                    float *shared_gate, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Streaming-read probe: a measurement aid, not part of the layer.  Reads
  * `bytes` bytes at `data` (device memory, 16-byte aligned, bytes a nonzero
  * multiple of 16) exactly once with 16-byte loads and writes one fp32 partial

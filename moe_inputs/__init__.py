@@ -55,6 +55,7 @@ PROJ_SLOT = {"gate": 0, "up": 1, "down": 2, "shared_gate_proj": 3,
              "shared_up": 4, "shared_down": 5}
 TID_ROUTER = 100
 TID_SHARED_GATE_W = 101
+TID_NORM_W = 102
 
 
 @dataclasses.dataclass(frozen=True)
@@ -79,6 +80,7 @@ class LayerConfig:
     shared_gate: bool = False   # sigmoid(x . w_g) scalar gate on the shared sum
     n_tokens: int = 1
     n_layers: int = 1
+    norm_eps: float = 1e-6          # the next layer's RMSNorm, when folded into the tail
 
     def proj_shape(self, proj: str):
         """(n_experts, rows, cols, bits) of a projection stack."""
@@ -240,6 +242,12 @@ def gen_shared_gate_w(cfg: LayerConfig, layer: int) -> np.ndarray:
     """Shared-expert gate vector w_g [d_in] (bf16 bits)."""
     w = rng_for(cfg.weight_cfg_id, layer, TID_SHARED_GATE_W, 0).normal(
         0.0, 1.0 / np.sqrt(cfg.d_in), size=cfg.d_in)
+    return encode(w, BF16)
+
+
+def gen_norm_weight(cfg: LayerConfig, layer: int) -> np.ndarray:
+    """The next layer's RMSNorm weight [d_in] (bf16 bits), U(0.5, 1.5)."""
+    w = rng_for(cfg.weight_cfg_id, layer, TID_NORM_W, 0).uniform(0.5, 1.5, size=cfg.d_in)
     return encode(w, BF16)
 
 

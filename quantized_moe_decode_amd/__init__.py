@@ -53,6 +53,12 @@ class CLayerWeights(ctypes.Structure):
                 ("shared_down", CQMat), ("w_shared_gate", ctypes.c_void_p)]
 
 
+class CRMSNorm(ctypes.Structure):
+    """moe_rmsnorm of the C ABI."""
+    _fields_ = [("weight", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("normed", ctypes.c_void_p)]
+
+
 def _load_library():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python quantized_moe_decode_amd/build.py`")
@@ -85,6 +91,14 @@ def _load_library():
     L.moe_decode_layer_workspace_bytes.restype = sz
     L.moe_decode_tail.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp]
     L.moe_decode_tail.restype = i32
+    L.moe_decode_tail_rmsnorm.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, i32, vp,
+                                          ctypes.POINTER(CRMSNorm), vp, sz, vp]
+    L.moe_decode_tail_rmsnorm.restype = i32
+    L.moe_decode_tail_rmsnorm_workspace_bytes.argtypes = [i32, i32]
+    L.moe_decode_tail_rmsnorm_workspace_bytes.restype = sz
+    L.moe_decode_layer_rmsnorm.argtypes = [ctypes.POINTER(CLayerWeights), vp, i32, vp, i32, vp,
+                                           ctypes.POINTER(CRMSNorm), vp, vp, vp, vp, sz, vp]
+    L.moe_decode_layer_rmsnorm.restype = i32
     L.moe_decode_read_probe.argtypes = [vp, sz, vp, i32, vp]
     L.moe_decode_read_probe.restype = i32
     L.moe_decode_read_probe_blocks.argtypes = [sz]
@@ -276,6 +290,43 @@ def moe_decode_layer(weights: CLayerWeights, x: torch.Tensor, residual: torch.Te
     _check(st, "moe_decode_layer")
 
 
+def rmsnorm_struct(weight: torch.Tensor, eps: float, normed: torch.Tensor) -> CRMSNorm:
+    return CRMSNorm(weight.data_ptr(), _dt(weight), float(eps), normed.data_ptr())
+
+
+def tail_rmsnorm_workspace_bytes(n_tokens: int, d_in: int) -> int:
+    return int(lib.moe_decode_tail_rmsnorm_workspace_bytes(n_tokens, d_in))
+
+
+def moe_decode_tail_rmsnorm(partial: torch.Tensor, residual: torch.Tensor, out: torch.Tensor,
+                            norm_weight: torch.Tensor, eps: float, normed: torch.Tensor,
+                            workspace: torch.Tensor, shared: Optional[torch.Tensor] = None,
+                            shared_gate: Optional[torch.Tensor] = None, stream=None) -> None:
+    """moe_decode_tail plus the next layer's RMSNorm of out into normed [T, d_in]."""
+    T, K, d_in = partial.shape
+    S = 0 if shared is None else shared.shape[1]
+    nrm = rmsnorm_struct(norm_weight, eps, normed)
+    st = lib.moe_decode_tail_rmsnorm(_ptr(partial), T, K, d_in, _ptr(shared), S, _ptr(shared_gate),
+                                     _ptr(residual), _dt(residual), _ptr(out), ctypes.byref(nrm),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream))
+    _check(st, "moe_decode_tail_rmsnorm")
+
+
+def moe_decode_layer_rmsnorm(weights: CLayerWeights, x: torch.Tensor, residual: torch.Tensor,
+                             out: torch.Tensor, norm_weight: torch.Tensor, eps: float,
+                             normed: torch.Tensor, workspace: torch.Tensor,
+                             expert_ids: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
+                             shared_gate: Optional[torch.Tensor] = None, stream=None) -> None:
+    """The fused single-launch layer plus the next layer's RMSNorm of out into normed [d_in]."""
+    nrm = rmsnorm_struct(norm_weight, eps, normed)
+    st = lib.moe_decode_layer_rmsnorm(ctypes.byref(weights), _ptr(x), _dt(x), _ptr(residual), _dt(residual),
+                                      _ptr(out), ctypes.byref(nrm), _ptr(expert_ids), _ptr(scores),
+                                      _ptr(shared_gate), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "moe_decode_layer_rmsnorm")
+
+
 def moe_decode_tail(partial: torch.Tensor, residual: torch.Tensor, out: torch.Tensor,
                     shared: Optional[torch.Tensor] = None,
                     shared_gate: Optional[torch.Tensor] = None, stream=None) -> None:
@@ -304,6 +355,7 @@ from .layer import DecodeLayer  # noqa: E402  (needs the functions above)
 
 __all__ = ["QuantStack", "DecodeLayer", "moe_decode_route", "moe_decode_expert_ffn",
            "moe_decode_expert_ffn_noalloc", "expert_ffn_noalloc_max_bytes",
+           "moe_decode_tail_rmsnorm", "moe_decode_layer_rmsnorm", "tail_rmsnorm_workspace_bytes",
            "moe_decode_layer", "layer_weights", "layer_workspace_bytes",
            "moe_decode_gate_up", "moe_decode_down",
            "moe_decode_tail", "route_workspace_bytes", "expert_ffn_workspace_bytes",

@@ -22,7 +22,7 @@ struct LayerPlan {
     int grid;
     size_t lds;
     size_t ws_bytes;
-    size_t off_logits, off_act, off_act_sent, off_partial;
+    size_t off_logits, off_act, off_act_sent, off_partial, off_norm;
 };
 
 static moe_status plan_layer(const moe_layer_weights *w, int d_in_check, LayerPlan &p) {
@@ -116,6 +116,8 @@ static moe_status plan_layer(const moe_layer_weights *w, int d_in_check, LayerPl
     off = align_up(off + (size_t)slots * kActCopies * kSentStride * sizeof(uint64_t), 256);
     p.off_partial = off;
     off = align_up(off + (size_t)slots * d_in * sizeof(uint64_t), 256);
+    p.off_norm = off;                       // one tagged word per tail tile (a tile has >= 16 rows)
+    off = align_up(off + (size_t)(d_in / 16) * sizeof(uint64_t), 256);
     p.ws_bytes = off;
     return MOE_OK;
 }
@@ -213,16 +215,30 @@ extern "C" size_t moe_decode_layer_workspace_bytes(const moe_layer_weights *weig
     return plan_layer(weights, -1, p) == MOE_OK ? p.ws_bytes : 0;
 }
 
-extern "C" moe_status moe_decode_layer(const moe_layer_weights *weights, const void *x, moe_dtype x_dtype_arg,
-                                       const void *residual, moe_dtype residual_dtype_arg, float *out,
-                                       int32_t *expert_ids, float *scores, float *shared_gate,
-                                       void *workspace, size_t workspace_bytes, void *stream) {
-    const int x_dtype = raw_enum(x_dtype_arg), residual_dtype = raw_enum(residual_dtype_arg);
+namespace moe {
+
+// Host checks of an RMSNorm descriptor (null: no norm).
+static moe_status check_norm(const moe_rmsnorm *norm) {
+    if (!norm) return MOE_OK;
+    if (!norm->weight || !norm->normed) return MOE_EINVAL;
+    if (!valid_dtype(raw_enum(norm->dtype))) return MOE_EUNSUPPORTED;
+    if (!(norm->eps >= 0.0f) || norm->eps > 3.0e38f) return MOE_EINVAL;     // NaN fails the first test
+    if ((reinterpret_cast<uintptr_t>(norm->weight) & 3u) || (reinterpret_cast<uintptr_t>(norm->normed) & 3u))
+        return MOE_EINVAL;
+    return MOE_OK;
+}
+
+static moe_status layer_impl(const moe_layer_weights *weights, const void *x, int x_dtype, const void *residual,
+                             int residual_dtype, float *out, int32_t *expert_ids, float *scores,
+                             float *shared_gate, const moe_rmsnorm *norm, void *workspace, size_t workspace_bytes,
+                             void *stream) {
     if (!x || !residual || !out || !workspace) return MOE_EINVAL;
     if (!valid_dtype(x_dtype) || !valid_dtype(residual_dtype)) return MOE_EUNSUPPORTED;
     if (!aligned16(x) || !aligned16(workspace)) return MOE_EINVAL;
+    moe_status st = check_norm(norm);
+    if (st != MOE_OK) return st;
     LayerPlan p;
-    const moe_status st = plan_layer(weights, -1, p);
+    st = plan_layer(weights, -1, p);
     if (st != MOE_OK) return st;
     if (raw_enum(weights->w_router_dtype) != x_dtype) return MOE_EUNSUPPORTED;
     if (workspace_bytes < p.ws_bytes) return MOE_EINVAL;
@@ -241,6 +257,33 @@ extern "C" moe_status moe_decode_layer(const moe_layer_weights *weights, const v
     a.act = reinterpret_cast<uint64_t *>(ws + p.off_act);
     a.act_sent = reinterpret_cast<uint64_t *>(ws + p.off_act_sent);
     a.partial = reinterpret_cast<uint64_t *>(ws + p.off_partial);
+    a.norm_part = reinterpret_cast<uint64_t *>(ws + p.off_norm);
+    if (norm) {
+        a.norm_w = norm->weight;
+        a.norm_dt = raw_enum(norm->dtype);
+        a.norm_eps = norm->eps;
+        a.norm_out = norm->normed;
+    }
     hipLaunchKernelGGL(k, dim3(p.grid), dim3(kLayerThreads), p.lds, reinterpret_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+}  // namespace moe
+
+extern "C" moe_status moe_decode_layer(const moe_layer_weights *weights, const void *x, moe_dtype x_dtype_arg,
+                                       const void *residual, moe_dtype residual_dtype_arg, float *out,
+                                       int32_t *expert_ids, float *scores, float *shared_gate,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+    return layer_impl(weights, x, raw_enum(x_dtype_arg), residual, raw_enum(residual_dtype_arg), out, expert_ids,
+                      scores, shared_gate, nullptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" moe_status moe_decode_layer_rmsnorm(const moe_layer_weights *weights, const void *x,
+                                               moe_dtype x_dtype_arg, const void *residual,
+                                               moe_dtype residual_dtype_arg, float *out, const moe_rmsnorm *norm,
+                                               int32_t *expert_ids, float *scores, float *shared_gate,
+                                               void *workspace, size_t workspace_bytes, void *stream) {
+    if (!norm) return MOE_EINVAL;
+    return layer_impl(weights, x, raw_enum(x_dtype_arg), residual, raw_enum(residual_dtype_arg), out, expert_ids,
+                      scores, shared_gate, norm, workspace, workspace_bytes, stream);
 }

@@ -94,6 +94,12 @@ struct LayerArgs {
     int act_stride;
     uint64_t *partial;              // [K + S][d_in] tagged
     uint32_t *ctr;                  // control words
+    // the next layer's RMSNorm of out, folded into the tail (norm_out null: none)
+    const void *norm_w;             // [d_in], dtype norm_dt
+    int norm_dt;
+    float norm_eps;
+    float *norm_out;                // [d_in] fp32
+    uint64_t *norm_part;            // [b_tiles] tagged: each tail tile's sum of squares
     int n_route;
     int by_xcd;                     // units in slot-interleaved order: slot s's units on XCD s (8 slots)
     int a_lr_shift, a_tile, a_tiles_r, a_tiles_s;
@@ -524,6 +530,54 @@ __device__ void layer_a_unit_pipelined(const LayerArgs &a, uint32_t tag, int slo
     }
 }
 
+// Sum of v over the workgroup in a fixed order (DPP tree within each wave,
+// then the waves' sums in wave order): the same bits on every run.  Every
+// thread gets the sum.  Contains barriers.
+__device__ __forceinline__ float block_sum_fixed(float v) {
+    __shared__ float s_wsum[kLayerWaves];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_sum_last<kWave>(v)), kWave - 1));
+    __syncthreads();
+    if (lane == 0) s_wsum[wave] = w;
+    __syncthreads();
+    float sum = s_wsum[0];
+#pragma unroll
+    for (int i = 1; i < kLayerWaves; ++i) sum += s_wsum[i];
+    return sum;
+}
+
+// The next layer's RMSNorm of out, folded into the tail (Red Lite dev39,
+// "Measurements": the tail that also computed the next layer's RMSNorm; there
+// on one threadgroup, here spread over every tail tile).  Each tail tile
+// publishes the sum of squares of its rows of out (a fixed-order workgroup
+// sum) as a tagged word, gathers every tile's word, adds them in tile order
+// (a fixed-order sum again), and writes its own rows of
+//   norm_out[i] = out[i] / sqrt(sum_i out[i]^2 / d_in + eps) * weight[i].
+// own[k]: this thread's row row0 + tid + k * kLayerThreads of out (0 past
+// row_end).  s_part: LDS for every tile's sum (at least b_tiles floats; the
+// unit's logits array, no longer needed).
+template <int NROWS>
+__device__ void tail_rmsnorm(const LayerArgs &a, uint32_t tag, int tile, int row0, int row_end,
+                             const float (&own)[NROWS], float *s_part) {
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NROWS; ++k) ss += own[k] * own[k];
+    const float tile_ss = block_sum_fixed(ss);
+    if (threadIdx.x == 0) st_tagged(a.norm_part + tile, tile_ss, tag);
+    gather_tagged<kTailSleep>(a, a.b_tiles, nullptr, tag, [&](int i) { return a.norm_part + i; },
+                              [&](int i, float v) { s_part[i] = v; });
+    __syncthreads();
+    float part = 0.f;                               // tiles tid, tid + 256, ... in order
+    for (int i = threadIdx.x; i < a.b_tiles; i += blockDim.x) part += s_part[i];
+    const float total = block_sum_fixed(part);
+    const float inv = 1.0f / sqrtf(total / (float)a.d_in + a.norm_eps);
+#pragma unroll
+    for (int k = 0; k < NROWS; ++k) {
+        const int r = row0 + threadIdx.x + k * kLayerThreads;
+        if (r < row_end) a.norm_out[r] = own[k] * inv * load_act(a.norm_w, a.norm_dt, r);
+    }
+}
+
 // Kernel B unit: rows [row0, row0 + b_tile) of d_in for slot `slot`.  The
 // unit of the last slot also runs the tail for those rows.
 template <int BB, int SB>
@@ -669,7 +723,14 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     const float g = s_gate;
     const int ns = n_slots(a);
     constexpr int kTailPer = 8;             // slots read together per batch
-    for (int r = row0 + tid; r < row_end; r += blockDim.x) {
+    // a tile has at most 4 waves x 64 lane groups x kLayerNRB rows: at most kTailRows per thread
+    constexpr int kTailRows = 4 * kWave * kLayerNRB / kLayerThreads;
+    float own[kTailRows];                   // this thread's rows of out, kept for the RMSNorm
+#pragma unroll
+    for (int k = 0; k < kTailRows; ++k) {
+        const int r = row0 + tid + k * kLayerThreads;
+        own[k] = 0.f;
+        if (r >= row_end) continue;
         float routed_sum = 0.f, sh = 0.f;   // 0 + x == x: the sums start at slot 0 and slot K
         for (int s0 = 0; s0 < ns; s0 += kTailPer) {
             float v[kTailPer];
@@ -686,8 +747,11 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
                 }
             }
         }
-        a.out[r] = load_act(a.resid, a.resid_dt, r) + (routed_sum + sh * g);
+        const float o = load_act(a.resid, a.resid_dt, r) + (routed_sum + sh * g);
+        a.out[r] = o;
+        own[k] = o;
     }
+    if (a.norm_out) tail_rmsnorm<kTailRows>(a, tag, tile, row0, row_end, own, s_logits);
     // the last tile to finish moves the workspace to the next epoch
     __syncthreads();
     if (tid == 0) {

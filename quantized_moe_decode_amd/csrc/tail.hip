@@ -5,6 +5,8 @@
 // per-expert partial rows, taken left to right in slot order.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "api.hpp"
 #include "common.hpp"
 
@@ -45,9 +47,133 @@ __global__ __launch_bounds__(256) void tail_kernel(TailArgs a) {
     a.out[idx] = load_act(a.resid, a.resid_dt, idx) + (routed + sh * g);
 }
 
+// ---------------------------------------------- tail + the next layer's RMSNorm
+
+// The tail of moe_decode_tail_rmsnorm: the workgroup (bx, t) computes token
+// t's elements [256 bx, 256 bx + 256) of out as tail_kernel does, publishes
+// their sum of squares (a fixed-order workgroup sum) as a word tagged with
+// the launch's epoch, gathers token t's words of every chunk, adds them in
+// chunk order, and writes its elements of
+//   normed = out / sqrt(sum out^2 / D + eps) * weight.
+// The workspace: control words (error, epoch, finished workgroups), 256 bytes
+// apart, then [T][chunks] tagged words.  Every workgroup waits only on
+// workgroups of its own token, all of which are resident (the host checks that
+// the grid fits the device).  Every wait is bounded: on time-out the error
+// word is raised and the launch drains.
+constexpr int kTailNormThreads = 256;
+constexpr int kTailCtrStride = 64;
+constexpr int kTailCtrErr = 0, kTailCtrEpoch = 1, kTailCtrDone = 2;
+constexpr size_t kTailHeadBytes = 1024;
+constexpr uint32_t kTailSpinLimit = 1u << 22;
+
+struct TailNormArgs {
+    TailArgs t;
+    const void *norm_w;
+    int norm_dt;
+    float eps;
+    float *normed;
+    uint32_t *ctr;
+    uint64_t *part;         // [T][chunks]
+    int chunks;
+};
+
+__device__ __forceinline__ float block_sum_fixed256(float v, float *s_w) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_sum_last<kWave>(v)), kWave - 1));
+    __syncthreads();
+    if (lane == 0) s_w[wave] = w;
+    __syncthreads();
+    return ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
+}
+
+__global__ __launch_bounds__(kTailNormThreads) void tail_norm_kernel(TailNormArgs a) {
+    __shared__ uint32_t s_tag;
+    __shared__ float s_w[kTailNormThreads / kWave];
+    __shared__ float s_part[MOE_MAX_DIM / kTailNormThreads];
+    const int t = blockIdx.y, bx = blockIdx.x, tid = threadIdx.x;
+    const int D = a.t.D;
+    if (tid == 0)
+        s_tag = __hip_atomic_load(a.ctr + kTailCtrEpoch * kTailCtrStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    __syncthreads();
+    const uint32_t tag = s_tag;
+    const int i = bx * kTailNormThreads + tid;
+    float o = 0.f;
+    if (i < D) {
+        const int64_t idx = (int64_t)t * D + i;
+        const float routed = sum_rows(a.t.partial + (int64_t)t * a.t.K * D + i, a.t.K, D);
+        const float sh = a.t.S > 0 ? sum_rows(a.t.shared + (int64_t)t * a.t.S * D + i, a.t.S, D) : 0.f;
+        const float g = a.t.gate ? a.t.gate[t] : 1.0f;
+        o = load_act(a.t.resid, a.t.resid_dt, idx) + (routed + sh * g);
+        a.t.out[idx] = o;
+    }
+    const float ss = block_sum_fixed256(o * o, s_w);
+    uint64_t *part = a.part + (int64_t)t * a.chunks;
+    if (tid == 0)
+        __hip_atomic_store(part + bx, ((uint64_t)tag << 32) | __float_as_uint(ss), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < a.chunks) {
+        float v = 0.f;
+        uint32_t spin = 0;
+        for (;; ++spin) {
+            const uint64_t w = __hip_atomic_load(part + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((uint32_t)(w >> 32) == tag) {
+                v = __uint_as_float((uint32_t)w);
+                break;
+            }
+            if (spin == kTailSpinLimit) {
+                __hip_atomic_fetch_or(a.ctr + kTailCtrErr * kTailCtrStride, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        s_part[tid] = v;
+    }
+    __syncthreads();
+    float total = 0.f;
+    for (int c = 0; c < a.chunks; ++c) total += s_part[c];      // chunk order
+    const float inv = 1.0f / sqrtf(total / (float)D + a.eps);
+    if (i < D) a.normed[(int64_t)t * D + i] = o * inv * load_act(a.norm_w, a.norm_dt, i);
+    // every word of this token was read: the last workgroup moves the workspace to the next epoch
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t *done = a.ctr + kTailCtrDone * kTailCtrStride;
+        const uint32_t total_wg = gridDim.x * gridDim.y;
+        if (__hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total_wg - 1) {
+            __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.ctr + kTailCtrEpoch * kTailCtrStride, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// Workgroups of tail_norm_kernel that can be resident at once on the current
+// device, looked up once per device (0 if the runtime cannot tell).
+static int tail_norm_capacity() {
+    static std::mutex mu;
+    static int cap[64];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cap[dev]) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(tail_norm_kernel),
+                                                         kTailNormThreads, 0) != hipSuccess)
+            return 0;
+        cap[dev] = cus * per_cu;
+    }
+    return cap[dev];
+}
+
 }  // namespace moe
 
 using namespace moe;
+
+extern "C" size_t moe_decode_tail_rmsnorm_workspace_bytes(int32_t n_tokens, int32_t d_in) {
+    if (n_tokens < 1 || d_in < 1) return 0;
+    const size_t chunks = (size_t)(d_in + kTailNormThreads - 1) / kTailNormThreads;
+    return kTailHeadBytes + align_up((size_t)n_tokens * chunks * sizeof(uint64_t), 256);
+}
 
 extern "C" moe_status moe_decode_tail(const float *partial, int32_t n_tokens, int32_t top_k, int32_t d_in,
                                       const float *shared, int32_t n_shared, const float *shared_gate,
@@ -82,3 +208,38 @@ extern "C" const char *moe_decode_status_string(moe_status s_arg) {
 }
 
 extern "C" int32_t moe_decode_abi_version(void) { return MOE_DECODE_ABI_VERSION; }
+
+extern "C" moe_status moe_decode_tail_rmsnorm(const float *partial, int32_t n_tokens, int32_t top_k, int32_t d_in,
+                                              const float *shared, int32_t n_shared, const float *shared_gate,
+                                              const void *residual, moe_dtype residual_dtype_arg, float *out,
+                                              const moe_rmsnorm *norm, void *workspace, size_t workspace_bytes,
+                                              void *stream) {
+    const int residual_dtype = raw_enum(residual_dtype_arg);
+    if (!partial || !residual || !out || !norm || !workspace) return MOE_EINVAL;
+    if (n_tokens < 1 || n_tokens > MOE_MAX_TOKENS) return MOE_EINVAL;
+    if (top_k < 1 || top_k > MOE_MAX_TOP_K) return MOE_EINVAL;
+    if (d_in < kGroup || d_in > MOE_MAX_DIM || d_in % kGroup) return MOE_EINVAL;
+    if (n_shared < 0 || n_shared > MOE_MAX_TOP_K) return MOE_EINVAL;
+    if ((n_shared == 0) != (shared == nullptr)) return MOE_EINVAL;
+    if (!valid_dtype(residual_dtype)) return MOE_EUNSUPPORTED;
+    if (!norm->weight || !norm->normed) return MOE_EINVAL;
+    if (!valid_dtype(raw_enum(norm->dtype))) return MOE_EUNSUPPORTED;
+    if (!(norm->eps >= 0.0f) || norm->eps > 3.0e38f) return MOE_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(norm->weight) & 3u) || (reinterpret_cast<uintptr_t>(norm->normed) & 3u) ||
+        !aligned16(workspace))
+        return MOE_EINVAL;
+    if (workspace_bytes < moe_decode_tail_rmsnorm_workspace_bytes(n_tokens, d_in)) return MOE_EINVAL;
+    const int chunks = (d_in + kTailNormThreads - 1) / kTailNormThreads;
+    const int cap = tail_norm_capacity();
+    if (cap > 0 && n_tokens * chunks > cap) return MOE_EUNSUPPORTED;
+    TailNormArgs a;
+    a.t.partial = partial; a.t.shared = shared; a.t.gate = shared_gate; a.t.resid = residual; a.t.out = out;
+    a.t.resid_dt = residual_dtype; a.t.T = n_tokens; a.t.K = top_k; a.t.D = d_in; a.t.S = n_shared;
+    a.norm_w = norm->weight; a.norm_dt = raw_enum(norm->dtype); a.eps = norm->eps; a.normed = norm->normed;
+    a.ctr = reinterpret_cast<uint32_t *>(workspace);
+    a.part = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(workspace) + kTailHeadBytes);
+    a.chunks = chunks;
+    hipLaunchKernelGGL(tail_norm_kernel, dim3(chunks, n_tokens), dim3(kTailNormThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), a);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}

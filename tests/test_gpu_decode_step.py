@@ -24,14 +24,17 @@ def _gpu():
     yield
 
 
-def build_step(specs, n_distinct, path, n_tokens=1):
+def build_step(specs, n_distinct, path, n_tokens=1, norm=False):
     """Layers (cfg, layer index) on the device, margin tokens per layer, and the
-    oracle's result for every (token, layer)."""
+    oracle's result for every (token, layer).  norm: every layer's tail also
+    computes the next layer's RMSNorm (weight gen_norm_weight, the workload's eps)."""
     from quantized_moe_decode_amd.layer import DecodeStep, layer_from_host, tensor_from_encoded
     layers, host_x, host_r = [], [], []
     for cfg, li in specs:
         w = mi.gen_layer_weights(cfg, li)
         layers.append(layer_from_host(cfg, w, DEV, n_tokens=n_tokens))
+        if norm:
+            layers[-1].set_next_norm(tensor_from_encoded(mi.gen_norm_weight(cfg, li), mi.BF16, DEV), cfg.norm_eps)
         x, r, _ = pick_tokens(cfg, li, n_distinct * n_tokens, w["router"])
         host_x.append(x.reshape(n_distinct, n_tokens, -1))
         host_r.append(r.reshape(n_distinct, n_tokens, -1))
@@ -64,6 +67,12 @@ def check_replays(step, specs, host_x, host_r, refs, order, label):
                 gpu["gate"] = lay.shared_gate.cpu().numpy()
             compare_layer(cfg, None, host_x[l][t], host_r[l][t], gpu,
                           f"{label} replay {i} token {t} layer {l} ({cfg.name} L{li})", ref=refs[(t, l)])
+            if lay.normed is not None:
+                import oracle
+                from helpers import rel_err
+                want = oracle.rmsnorm(refs[(t, l)]["out"], mi.gen_norm_weight(cfg, li), mi.BF16, cfg.norm_eps)
+                e = rel_err(lay.normed.cpu().numpy(), want)
+                assert e <= 2e-3, f"{label} replay {i} token {t} layer {l}: normed relative error {e}"
 
 
 MIXED = [(mi.QWEN3, 0), (mi.QWEN3, 1), (mi.QWEN3, 2), (mi.QWEN3, 3), (mi.QWEN15, 0), (mi.QWEN15, 1)]
@@ -88,3 +97,16 @@ def test_batch32_step():
     say("case decode step: 32 tokens per step, 3 Qwen3 layers, 2 token batches")
     step, hx, hr, refs = build_step(specs, 2, "three-call", n_tokens=32)
     check_replays(step, specs, hx, hr, refs, [0, 1, 0], "batch-32 step")
+
+
+def test_fused_step_with_folded_rmsnorm():
+    say("case decode step: fused, 4 Qwen3 + 2 Qwen1.5 layers, next-layer RMSNorm folded, 2 tokens")
+    step, hx, hr, refs = build_step(MIXED, 2, "fused", norm=True)
+    check_replays(step, MIXED, hx, hr, refs, [0, 1, 1, 0], "fused step + rmsnorm")
+
+
+def test_three_call_step_with_folded_rmsnorm():
+    specs = [(mi.QWEN3_B32, 0), (mi.QWEN3_B32, 1)]
+    say("case decode step: 32 tokens, 2 Qwen3 layers, next-layer RMSNorm folded, 2 batches")
+    step, hx, hr, refs = build_step(specs, 2, "three-call", n_tokens=32, norm=True)
+    check_replays(step, specs, hx, hr, refs, [0, 1, 0], "batch-32 step + rmsnorm")
