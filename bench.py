@@ -594,6 +594,40 @@ def cpu_leg(wl, args, seconds):
     return cpu, validated
 
 
+def rmsnorm_fold_cost(wl, meas, dev):
+    """The next layer's RMSNorm on every layer of the step: folded into the tail
+    against a separate moe_decode_rmsnorm launch after each layer, each timed
+    like the plain step (same n, 5 samples, median) in this process."""
+    import torch
+    import moe_inputs as mi
+    from quantized_moe_decode_amd.layer import tensor_from_encoded
+    cfg, L, n = wl.cfg, wl.L, meas["n"]
+    weights = [tensor_from_encoded(mi.gen_norm_weight(cfg, li), mi.BF16, dev) for li in range(L)]
+
+    def step_ms():
+        wl.step.capture()
+        for i in range(max(10, wl.R)):
+            wl.step.replay(i % wl.R)
+        return statistics.median(timed_replays(wl.step, n, wl.R, offset=k * n) / n for k in range(5)) * 1e3
+
+    plain = step_ms()
+    res = {"ms_per_step_plain": round(plain, 4)}
+    for fold in (True, False):
+        for lay, w in zip(wl.layers, weights):
+            lay.set_next_norm(w, cfg.norm_eps, fold=fold)
+        ms = step_ms()
+        if wl.step.error_words():
+            raise SystemExit(f"{cfg.name}: a wait timed out with the RMSNorm")
+        key = "folded" if fold else "separate_launch"
+        res[f"ms_per_step_{key}"] = round(ms, 4)
+        res[f"{key}_us_per_layer"] = round((ms - plain) * 1e3 / L, 3)
+    for lay in wl.layers:
+        lay.norm_w, lay.normed, lay.tail_ws = None, None, None
+    wl.step.capture()
+    torch.cuda.synchronize()
+    return res
+
+
 def dtype_of(cfg) -> str:
     w = f"u{cfg.bits_gate_up}" if cfg.bits_gate_up == cfg.bits_down else f"u{cfg.bits_gate_up}/u{cfg.bits_down}"
     acc = f"{cfg.x_dtype} x, f32 accumulation"
@@ -651,6 +685,8 @@ def run_workload(name, args, dev, overhead, shared_stacks):
         res["cpu_baseline"], res["validated"] = cpu_leg(wl, args, secs)
     else:
         res["cpu_baseline"], res["validated"] = None, None
+    if name in (HEADLINE, "qwen3_30b_a3b_moe_batch32"):
+        res["rmsnorm_fold"] = rmsnorm_fold_cost(wl, meas, dev)
     log(f"[bench] {name}: {res['ms_per_step']} ms/step, {res['value']} GB/s, "
         f"{res['tokens_per_s']} tok/s (n={meas['n']}, 2n ratio {res['amortisation_ratio_2n']})")
     keep = wl.stacks
@@ -760,6 +796,7 @@ def main():
         "roofline": head.get("roofline"),
         "cpu_baseline": head.get("cpu_baseline"),
         "validated": head.get("validated"),
+        "rmsnorm_fold": head.get("rmsnorm_fold"),
         "ceiling": ceil,
         "gpu_state": {"before": state_before, "after": state_after},
         "configs": {n: r for n, r in results.items() if r is not head},

@@ -329,6 +329,14 @@ moe_status moe_decode_tail_rmsnorm(const float *partial, int32_t n_tokens, int32
 
 size_t moe_decode_tail_rmsnorm_workspace_bytes(int32_t n_tokens, int32_t d_in);
 
+/*
+ * The same RMSNorm as a call of its own, one workgroup per token: normed =
+ * y / sqrt(mean(y^2) + eps) * weight for y [n_tokens][d] fp32 (device).  The
+ * separate dispatch the folded forms are measured against.
+ */
+moe_status moe_decode_rmsnorm(const float *y, int32_t n_tokens, int32_t d, const moe_rmsnorm *norm,
+                              void *stream);
+
 /* moe_decode_layer, also writing norm->normed (norm must not be NULL); the
  * same workspace as moe_decode_layer. */
 moe_status moe_decode_layer_rmsnorm(const moe_layer_weights *weights, const void *x, moe_dtype x_dtype,

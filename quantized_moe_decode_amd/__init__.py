@@ -99,6 +99,8 @@ def _load_library():
     L.moe_decode_layer_rmsnorm.argtypes = [ctypes.POINTER(CLayerWeights), vp, i32, vp, i32, vp,
                                            ctypes.POINTER(CRMSNorm), vp, vp, vp, vp, sz, vp]
     L.moe_decode_layer_rmsnorm.restype = i32
+    L.moe_decode_rmsnorm.argtypes = [vp, i32, i32, ctypes.POINTER(CRMSNorm), vp]
+    L.moe_decode_rmsnorm.restype = i32
     L.moe_decode_read_probe.argtypes = [vp, sz, vp, i32, vp]
     L.moe_decode_read_probe.restype = i32
     L.moe_decode_read_probe_blocks.argtypes = [sz]
@@ -327,6 +329,14 @@ def moe_decode_layer_rmsnorm(weights: CLayerWeights, x: torch.Tensor, residual: 
     _check(st, "moe_decode_layer_rmsnorm")
 
 
+def moe_decode_rmsnorm(y: torch.Tensor, norm_weight: torch.Tensor, eps: float, normed: torch.Tensor,
+                       stream=None) -> None:
+    """normed [T, d] = y / sqrt(mean(y^2) + eps) * weight, one workgroup per token."""
+    T, d = y.shape
+    nrm = rmsnorm_struct(norm_weight, eps, normed)
+    _check(lib.moe_decode_rmsnorm(_ptr(y), T, d, ctypes.byref(nrm), _stream(stream)), "moe_decode_rmsnorm")
+
+
 def moe_decode_tail(partial: torch.Tensor, residual: torch.Tensor, out: torch.Tensor,
                     shared: Optional[torch.Tensor] = None,
                     shared_gate: Optional[torch.Tensor] = None, stream=None) -> None:
@@ -356,6 +366,7 @@ from .layer import DecodeLayer  # noqa: E402  (needs the functions above)
 __all__ = ["QuantStack", "DecodeLayer", "moe_decode_route", "moe_decode_expert_ffn",
            "moe_decode_expert_ffn_noalloc", "expert_ffn_noalloc_max_bytes",
            "moe_decode_tail_rmsnorm", "moe_decode_layer_rmsnorm", "tail_rmsnorm_workspace_bytes",
+           "moe_decode_rmsnorm",
            "moe_decode_layer", "layer_weights", "layer_workspace_bytes",
            "moe_decode_gate_up", "moe_decode_down",
            "moe_decode_tail", "route_workspace_bytes", "expert_ffn_workspace_bytes",

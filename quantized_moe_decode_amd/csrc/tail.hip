@@ -146,6 +146,21 @@ __global__ __launch_bounds__(kTailNormThreads) void tail_norm_kernel(TailNormArg
     }
 }
 
+// Plain RMSNorm, one workgroup per token: normed[t] = y[t] / sqrt(mean(y[t]^2)
+// + eps) * weight, the sum of squares in a fixed order (each thread's
+// elements in order, then the fixed workgroup tree).
+__global__ __launch_bounds__(kTailNormThreads) void rmsnorm_kernel(const float *y, int D, const void *w, int w_dt,
+                                                                   float eps, float *normed) {
+    __shared__ float s_w[kTailNormThreads / kWave];
+    const float *yt = y + (int64_t)blockIdx.x * D;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < D; i += kTailNormThreads) ss += yt[i] * yt[i];
+    const float total = block_sum_fixed256(ss, s_w);
+    const float inv = 1.0f / sqrtf(total / (float)D + eps);
+    for (int i = threadIdx.x; i < D; i += kTailNormThreads)
+        normed[(int64_t)blockIdx.x * D + i] = yt[i] * inv * load_act(w, w_dt, i);
+}
+
 // Workgroups of tail_norm_kernel that can be resident at once on the current
 // device, looked up once per device (0 if the runtime cannot tell).
 static int tail_norm_capacity() {
@@ -241,5 +256,19 @@ extern "C" moe_status moe_decode_tail_rmsnorm(const float *partial, int32_t n_to
     a.chunks = chunks;
     hipLaunchKernelGGL(tail_norm_kernel, dim3(chunks, n_tokens), dim3(kTailNormThreads), 0,
                        reinterpret_cast<hipStream_t>(stream), a);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+extern "C" moe_status moe_decode_rmsnorm(const float *y, int32_t n_tokens, int32_t d, const moe_rmsnorm *norm,
+                                         void *stream) {
+    if (!y || !norm || !norm->weight || !norm->normed) return MOE_EINVAL;
+    if (n_tokens < 1 || n_tokens > MOE_MAX_TOKENS || d < 1 || d > MOE_MAX_DIM) return MOE_EINVAL;
+    if (!valid_dtype(raw_enum(norm->dtype))) return MOE_EUNSUPPORTED;
+    if (!(norm->eps >= 0.0f) || norm->eps > 3.0e38f) return MOE_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(y) & 3u) || (reinterpret_cast<uintptr_t>(norm->weight) & 3u) ||
+        (reinterpret_cast<uintptr_t>(norm->normed) & 3u))
+        return MOE_EINVAL;
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(n_tokens), dim3(kTailNormThreads), 0, reinterpret_cast<hipStream_t>(stream),
+                       y, d, norm->weight, raw_enum(norm->dtype), norm->eps, norm->normed);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }

@@ -13,7 +13,8 @@ import numpy as np
 import torch
 
 from . import (QuantStack, expert_ffn_workspace_bytes, layer_weights, layer_workspace_bytes,
-               moe_decode_expert_ffn, moe_decode_layer, moe_decode_layer_rmsnorm, moe_decode_route,
+               moe_decode_expert_ffn, moe_decode_layer, moe_decode_layer_rmsnorm, moe_decode_rmsnorm,
+               moe_decode_route,
                moe_decode_tail, moe_decode_tail_rmsnorm, route_workspace_bytes,
                tail_rmsnorm_workspace_bytes)
 
@@ -76,13 +77,14 @@ class DecodeLayer:
                                       shared_gate_w)
         nb = layer_workspace_bytes(self.cweights)
         self.fused_ws = torch.zeros(nb, device=dev, dtype=torch.uint8) if nb else None
-        self.norm_w, self.norm_eps, self.normed, self.tail_ws = None, 0.0, None, None
+        self.norm_w, self.norm_eps, self.normed, self.tail_ws, self.fold_norm = None, 0.0, None, None, True
 
-    def set_next_norm(self, weight: torch.Tensor, eps: float) -> None:
-        """Fold the next layer's RMSNorm (weight [d_in], eps) into this layer's
-        tail: every forward also writes self.normed [T, d_in] fp32."""
+    def set_next_norm(self, weight: torch.Tensor, eps: float, fold: bool = True) -> None:
+        """The next layer's RMSNorm (weight [d_in], eps) of this layer's output:
+        every forward also writes self.normed [T, d_in] fp32, folded into the
+        tail (fold=True) or as a separate moe_decode_rmsnorm launch after it."""
         dev = self.router.device
-        self.norm_w, self.norm_eps = weight, float(eps)
+        self.norm_w, self.norm_eps, self.fold_norm = weight, float(eps), fold
         self.normed = torch.zeros(self.n_tokens, self.d_in, device=dev, dtype=torch.float32)
         self.tail_ws = torch.zeros(tail_rmsnorm_workspace_bytes(self.n_tokens, self.d_in), device=dev,
                                    dtype=torch.uint8)
@@ -101,11 +103,13 @@ class DecodeLayer:
 
     def tail(self, resid: torch.Tensor, out: torch.Tensor, stream=None) -> None:
         shared = self.shared_partial if self.shared is not None else None
-        if self.norm_w is not None:
+        if self.norm_w is not None and self.fold_norm:
             moe_decode_tail_rmsnorm(self.partial, resid, out, self.norm_w, self.norm_eps, self.normed,
                                     self.tail_ws, shared, self.shared_gate, stream)
         else:
             moe_decode_tail(self.partial, resid, out, shared, self.shared_gate, stream)
+            if self.norm_w is not None:
+                moe_decode_rmsnorm(out.view(-1, self.d_in), self.norm_w, self.norm_eps, self.normed, stream)
 
     def forward(self, x: torch.Tensor, resid: torch.Tensor, out: torch.Tensor, stream=None) -> None:
         """out [T, d_in] fp32 = the layer applied to x [T, d_in] with residual resid."""
@@ -120,11 +124,13 @@ class DecodeLayer:
             raise ValueError("layer not supported by the fused launch")
         rec = (self.ids if record else None, self.scores if record else None,
                self.shared_gate if record else None)
-        if self.norm_w is not None:
+        if self.norm_w is not None and self.fold_norm:
             moe_decode_layer_rmsnorm(self.cweights, x, resid, out, self.norm_w, self.norm_eps, self.normed,
                                      self.fused_ws, *rec, stream=stream)
         else:
             moe_decode_layer(self.cweights, x, resid, out, self.fused_ws, *rec, stream)
+            if self.norm_w is not None:
+                moe_decode_rmsnorm(out.view(-1, self.d_in), self.norm_w, self.norm_eps, self.normed, stream)
 
     def fused_error_word(self) -> int:
         """Nonzero if a wait inside a fused launch ever timed out (reads device memory)."""

@@ -25,14 +25,14 @@ def _gpu():
     yield
 
 
-def run_norm(cfg, w, x, resid, fused, eps=None, reps=1):
+def run_norm(cfg, w, x, resid, fused, eps=None, reps=1, fold=True):
     """The layer with the RMSNorm folded in; returns out, normed, ids, error state."""
     import quantized_moe_decode_amd as q
     from quantized_moe_decode_amd.layer import layer_from_host, tensor_from_encoded
     T = x.shape[0]
     layer = layer_from_host(cfg, w, DEV, n_tokens=T)
     nw = mi.gen_norm_weight(cfg, 0)
-    layer.set_next_norm(tensor_from_encoded(nw, mi.BF16, DEV), cfg.norm_eps if eps is None else eps)
+    layer.set_next_norm(tensor_from_encoded(nw, mi.BF16, DEV), cfg.norm_eps if eps is None else eps, fold=fold)
     xd = tensor_from_encoded(x, cfg.x_dtype, DEV)
     rd = tensor_from_encoded(resid, cfg.resid_dtype, DEV)
     out = torch.zeros(T, cfg.d_in, device=DEV)
@@ -43,7 +43,8 @@ def run_norm(cfg, w, x, resid, fused, eps=None, reps=1):
         torch.cuda.synchronize()
         results.append((out.cpu().numpy().copy(), layer.normed.cpu().numpy().copy()))
     err = (layer.fused_error_word() if fused else
-           int(q.workspace_status(layer.tail_ws) != q.MOE_OK or q.workspace_status(layer.route_ws) != q.MOE_OK))
+           int((fold and q.workspace_status(layer.tail_ws) != q.MOE_OK) or
+               q.workspace_status(layer.route_ws) != q.MOE_OK))
     gpu = dict(ids=layer.ids.cpu().numpy(), scores=layer.scores.cpu().numpy(), act=None, partial=None,
                out=results[-1][0], error_word=err)
     if layer.shared_gate is not None:
@@ -51,8 +52,8 @@ def run_norm(cfg, w, x, resid, fused, eps=None, reps=1):
     return gpu, results, nw
 
 
-def check(cfg, w, x, resid, fused, label, eps=None, reps=2):
-    gpu, results, nw = run_norm(cfg, w, x, resid, fused, eps, reps)
+def check(cfg, w, x, resid, fused, label, eps=None, reps=2, fold=True):
+    gpu, results, nw = run_norm(cfg, w, x, resid, fused, eps, reps, fold)
     ref = oracle.layer(cfg, w, x, resid)
     compare_layer(cfg, w, x, resid, gpu, label, ref=ref)
     want = oracle.rmsnorm(ref["out"], nw, mi.BF16, cfg.norm_eps if eps is None else eps)
@@ -105,3 +106,16 @@ def test_rmsnorm_eps_dominates():
     x, resid = margin_tokens(cfg, 2, w, 1)
     for fused in (True, False):
         check(cfg, w, x, resid, fused, f"rmsnorm eps=1e4 fused={fused}", eps=1e4)
+
+
+@pytest.mark.parametrize("T", [1, 32])
+def test_separate_rmsnorm_launch(T):
+    """moe_decode_rmsnorm (one workgroup per token) after the layer: the
+    separate dispatch the folded forms are measured against."""
+    cfg = small_cfg(d_in=1024, d_ff=256, n_experts=8, top_k=2)
+    say(f"case separate rmsnorm T={T}")
+    w = mi.gen_layer_weights(cfg, 3, threads=4)
+    x, resid = margin_tokens(cfg, 3, w, T)
+    if T == 1:
+        check(cfg, w, x, resid, True, "separate rmsnorm fused layer", fold=False)
+    check(cfg, w, x, resid, False, f"separate rmsnorm three-call T={T}", fold=False)
