@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOE_DECODE_ABI_VERSION 2
+#define MOE_DECODE_ABI_VERSION 3
 
 typedef enum {
     MOE_OK = 0,
@@ -223,11 +223,19 @@ moe_status moe_decode_down(const float *act, int32_t n_tokens, const moe_qmat *d
  *   shared   [n_tokens][n_shared][d_in] float, or NULL iff n_shared == 0
  *   shared_gate [n_tokens] float or NULL (gate 1)
  *   residual [n_tokens][d_in], dtype residual_dtype
- *   out      out float [n_tokens][d_in]; may not alias the inputs
+ *   out      out [n_tokens][d_in], dtype out_dtype, aligned to its element
+ *            size; may not alias the inputs
+ * Output dtype: the fp32 sum above is what F32 stores; BF16 and F16 store it
+ * rounded once to the nearest value of that type, ties to even (overflow to
+ * infinity), so the layer drops into an engine that keeps its hidden state in
+ * 16 bits (mlxcel PR #276, "Validation": the fused path checked inside the
+ * engine's own decode loop; Red Lite dev39, "Scope boundary": parity checked
+ * by error bounds rather than bit identity).  Everything before the store
+ * (partial, shared, the sums) stays at least as precise as with F32 output.
  */
 moe_status moe_decode_tail(const float *partial, int32_t n_tokens, int32_t top_k, int32_t d_in,
                            const float *shared, int32_t n_shared, const float *shared_gate,
-                           const void *residual, moe_dtype residual_dtype, float *out,
+                           const void *residual, moe_dtype residual_dtype, void *out, moe_dtype out_dtype,
                            void *stream);
 
 /*
@@ -257,7 +265,8 @@ moe_status moe_decode_tail(const float *partial, int32_t n_tokens, int32_t top_k
  *                              routed stacks); ignored when n_shared == 0
  *   w_shared_gate              [d_in] in the dtype of x, or NULL (gate 1); only
  *                              with n_shared > 0
- * Arguments: x [d_in] and residual [d_in] (one token); out [d_in] fp32;
+ * Arguments: x [d_in] and residual [d_in] (one token); out [d_in] of dtype
+ * out_dtype, rounded as moe_decode_tail's;
  * expert_ids [top_k], scores [top_k], shared_gate [1]: optional outputs (NULL
  * to skip); workspace of moe_decode_layer_workspace_bytes() bytes, 16-byte
  * aligned, zero-filled before its first use and not written by the caller
@@ -284,7 +293,7 @@ typedef struct {
 } moe_layer_weights;
 
 moe_status moe_decode_layer(const moe_layer_weights *weights, const void *x, moe_dtype x_dtype,
-                            const void *residual, moe_dtype residual_dtype, float *out,
+                            const void *residual, moe_dtype residual_dtype, void *out, moe_dtype out_dtype,
                             int32_t *expert_ids, float *scores, float *shared_gate,
                             void *workspace, size_t workspace_bytes, void *stream);
 
@@ -298,18 +307,23 @@ size_t moe_decode_layer_workspace_bytes(const moe_layer_weights *weights);
  * ran on one threadgroup and lost to the separate dispatches, here the sum of
  * squares is spread over the tail's workgroups).  For every token t:
  *   normed[t][i] = out[t][i] / sqrt((1/d_in) sum_i out[t][i]^2 + eps) * weight[i]
- * computed from the fp32 out the tail writes.  Each tail workgroup sums the
+ * computed from out as stored (after its rounding to out's dtype), in fp32,
+ * and rounded to normed_dtype as out is.  Each tail workgroup sums the
  * squares of its own elements in a fixed order and the workgroups' sums are
  * added in workgroup order, so repeated calls give the same bits.
- *   weight  [d_in] device pointer, dtype `dtype` (F32, F16 or BF16), 4-byte aligned
- *   eps     >= 0 and finite
- *   normed  out fp32 [n_tokens][d_in] device pointer, 4-byte aligned; may not alias out
+ *   weight        [d_in] device pointer, dtype `dtype` (F32, F16 or BF16),
+ *                 aligned to its element size
+ *   eps           >= 0 and finite
+ *   normed        out [n_tokens][d_in] device pointer, dtype normed_dtype,
+ *                 aligned to its element size; may not alias out
+ *   normed_dtype  F32, F16 or BF16
  */
 typedef struct {
     const void *weight;
     moe_dtype dtype;
     float eps;
-    float *normed;
+    void *normed;
+    moe_dtype normed_dtype;
 } moe_rmsnorm;
 
 /*
@@ -324,24 +338,27 @@ typedef struct {
  */
 moe_status moe_decode_tail_rmsnorm(const float *partial, int32_t n_tokens, int32_t top_k, int32_t d_in,
                                    const float *shared, int32_t n_shared, const float *shared_gate,
-                                   const void *residual, moe_dtype residual_dtype, float *out,
-                                   const moe_rmsnorm *norm, void *workspace, size_t workspace_bytes, void *stream);
+                                   const void *residual, moe_dtype residual_dtype, void *out,
+                                   moe_dtype out_dtype, const moe_rmsnorm *norm, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 size_t moe_decode_tail_rmsnorm_workspace_bytes(int32_t n_tokens, int32_t d_in);
 
 /*
  * The same RMSNorm as a call of its own, one workgroup per token: normed =
- * y / sqrt(mean(y^2) + eps) * weight for y [n_tokens][d] fp32 (device).  The
- * separate dispatch the folded forms are measured against.
+ * y / sqrt(mean(y^2) + eps) * weight for y [n_tokens][d] of dtype y_dtype
+ * (device, aligned to its element size), computed in fp32 and rounded to
+ * norm->normed_dtype.  The separate dispatch the folded forms are measured
+ * against.
  */
-moe_status moe_decode_rmsnorm(const float *y, int32_t n_tokens, int32_t d, const moe_rmsnorm *norm,
-                              void *stream);
+moe_status moe_decode_rmsnorm(const void *y, moe_dtype y_dtype, int32_t n_tokens, int32_t d,
+                              const moe_rmsnorm *norm, void *stream);
 
 /* moe_decode_layer, also writing norm->normed (norm must not be NULL); the
  * same workspace as moe_decode_layer. */
 moe_status moe_decode_layer_rmsnorm(const moe_layer_weights *weights, const void *x, moe_dtype x_dtype,
-                                    const void *residual, moe_dtype residual_dtype, float *out,
-                                    const moe_rmsnorm *norm, int32_t *expert_ids, float *scores,
+                                    const void *residual, moe_dtype residual_dtype, void *out,
+                                    moe_dtype out_dtype, const moe_rmsnorm *norm, int32_t *expert_ids, float *scores,
                                     float *shared_gate, void *workspace, size_t workspace_bytes, void *stream);
 
 /*

@@ -67,6 +67,8 @@ def _load(path: str):
     L.oracle_tail.restype = i32
     L.oracle_rmsnorm.argtypes = [vp, i32, i32, vp, i32, ctypes.c_double, vp]
     L.oracle_rmsnorm.restype = i32
+    L.oracle_round_to_dtype.argtypes = [vp, ctypes.c_size_t, i32]
+    L.oracle_round_to_dtype.restype = i32
     L.oracle_unpack_row.argtypes = [vp, i32, i64, vp]
     L.oracle_unpack_row.restype = None
     L.oracle_dequant_row.argtypes = [ctypes.POINTER(_QMat), i64, i64, vp]
@@ -226,6 +228,16 @@ def rmsnorm(y, weight, w_dtype, eps):
     if rc != 0:
         raise ValueError("oracle_rmsnorm: invalid sizes")
     return out
+
+
+def round_to(values, dtype):
+    """values (float64) rounded to the nearest value of dtype ("f32" leaves them
+    as they are; "bf16", "f16": ties to even, overflow to infinity), as float64."""
+    v = np.array(values, dtype=np.float64, copy=True, order="C")
+    rc = lib().oracle_round_to_dtype(_p(v), v.size, DTYPE_CODE[dtype])
+    if rc != 0:
+        raise ValueError(f"oracle_round_to_dtype: dtype {dtype}")
+    return v
 
 
 def layer(cfg, weights: dict, x, resid, ids=None, scores=None):

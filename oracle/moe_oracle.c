@@ -332,3 +332,55 @@ int oracle_rmsnorm(const double *y, int n_tokens, int d, const void *weight, int
     }
     return 0;
 }
+
+/* ----------------------------------------------------- 16-bit output dtype -- */
+/*
+ * The layer output (and the RMSNorm output) stored in a 16-bit dtype, as an
+ * engine that keeps its hidden state in bf16 would hold it (mlxcel PR #276,
+ * "Validation": the fused path checked inside the engine's decode loop).  The
+ * reading taken: the exact result rounded once to the nearest value of the
+ * dtype, ties to the value whose last significand bit is 0 (IEEE 754
+ * round-to-nearest-even), past the largest finite value to infinity.
+ *
+ * A binary floating-point format with p significand bits (the leading one
+ * included) and exponents emin..emax holds, in each binade [2^e, 2^(e+1)),
+ * the multiples of 2^(e - p + 1); below 2^emin (subnormals) the multiples of
+ * 2^(emin - p + 1).  Rounding is therefore: take the spacing q of v's binade,
+ * round v / q to an integer with ties to even (rint in the default rounding
+ * mode; v / q and the product back are exact in double), and overflow past
+ * the largest finite value (2 - 2^(1-p)) * 2^emax to infinity.
+ *   bfloat16: p = 8,  emin = -126, emax = 127
+ *   binary16: p = 11, emin = -14,  emax = 15
+ * v is rounded in place, n values; dt 0 leaves v unchanged.  Returns 0, or -1
+ * for an unknown dtype.
+ */
+int oracle_round_to_dtype(double *v, size_t n, int dt)
+{
+    int p, emin, emax;
+    if (dt == 0)
+        return 0;
+    if (dt == 2) {
+        p = 8; emin = -126; emax = 127;
+    } else if (dt == 1) {
+        p = 11; emin = -14; emax = 15;
+    } else {
+        return -1;
+    }
+    const double vmax = ldexp(2.0 - ldexp(1.0, 1 - p), emax);
+    for (size_t i = 0; i < n; ++i) {
+        const double x = v[i];
+        if (x == 0.0 || !isfinite(x))
+            continue;
+        int e2;
+        frexp(x, &e2);                  /* |x| in [2^(e2-1), 2^e2) */
+        int e = e2 - 1;
+        if (e < emin)
+            e = emin;
+        const double q = ldexp(1.0, e - p + 1);
+        double r = rint(x / q) * q;
+        if (fabs(r) > vmax)
+            r = copysign(INFINITY, x);
+        v[i] = r;
+    }
+    return 0;
+}

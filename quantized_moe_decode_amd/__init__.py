@@ -56,7 +56,7 @@ class CLayerWeights(ctypes.Structure):
 class CRMSNorm(ctypes.Structure):
     """moe_rmsnorm of the C ABI."""
     _fields_ = [("weight", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("eps", ctypes.c_float),
-                ("normed", ctypes.c_void_p)]
+                ("normed", ctypes.c_void_p), ("normed_dtype", ctypes.c_int32)]
 
 
 def _load_library():
@@ -84,22 +84,22 @@ def _load_library():
     L.moe_decode_gate_up.restype = i32
     L.moe_decode_down.argtypes = [vp, i32, ctypes.POINTER(CQMat), vp, vp, i32, vp, vp, sz, vp]
     L.moe_decode_down.restype = i32
-    L.moe_decode_layer.argtypes = [ctypes.POINTER(CLayerWeights), vp, i32, vp, i32, vp, vp, vp, vp,
+    L.moe_decode_layer.argtypes = [ctypes.POINTER(CLayerWeights), vp, i32, vp, i32, vp, i32, vp, vp, vp,
                                    vp, sz, vp]
     L.moe_decode_layer.restype = i32
     L.moe_decode_layer_workspace_bytes.argtypes = [ctypes.POINTER(CLayerWeights)]
     L.moe_decode_layer_workspace_bytes.restype = sz
-    L.moe_decode_tail.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp]
+    L.moe_decode_tail.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, i32, vp, i32, vp]
     L.moe_decode_tail.restype = i32
-    L.moe_decode_tail_rmsnorm.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, i32, vp,
+    L.moe_decode_tail_rmsnorm.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, i32, vp, i32,
                                           ctypes.POINTER(CRMSNorm), vp, sz, vp]
     L.moe_decode_tail_rmsnorm.restype = i32
     L.moe_decode_tail_rmsnorm_workspace_bytes.argtypes = [i32, i32]
     L.moe_decode_tail_rmsnorm_workspace_bytes.restype = sz
-    L.moe_decode_layer_rmsnorm.argtypes = [ctypes.POINTER(CLayerWeights), vp, i32, vp, i32, vp,
+    L.moe_decode_layer_rmsnorm.argtypes = [ctypes.POINTER(CLayerWeights), vp, i32, vp, i32, vp, i32,
                                            ctypes.POINTER(CRMSNorm), vp, vp, vp, vp, sz, vp]
     L.moe_decode_layer_rmsnorm.restype = i32
-    L.moe_decode_rmsnorm.argtypes = [vp, i32, i32, ctypes.POINTER(CRMSNorm), vp]
+    L.moe_decode_rmsnorm.argtypes = [vp, i32, i32, i32, ctypes.POINTER(CRMSNorm), vp]
     L.moe_decode_rmsnorm.restype = i32
     L.moe_decode_read_probe.argtypes = [vp, sz, vp, i32, vp]
     L.moe_decode_read_probe.restype = i32
@@ -284,16 +284,16 @@ def moe_decode_layer(weights: CLayerWeights, x: torch.Tensor, residual: torch.Te
                      out: torch.Tensor, workspace: torch.Tensor,
                      expert_ids: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
                      shared_gate: Optional[torch.Tensor] = None, stream=None) -> None:
-    """The fused single-launch layer for one token: out [d_in] fp32."""
+    """The fused single-launch layer for one token: out [d_in] (fp32, bf16 or fp16)."""
     st = lib.moe_decode_layer(ctypes.byref(weights), _ptr(x), _dt(x), _ptr(residual), _dt(residual),
-                              _ptr(out), _ptr(expert_ids), _ptr(scores), _ptr(shared_gate),
+                              _ptr(out), _dt(out), _ptr(expert_ids), _ptr(scores), _ptr(shared_gate),
                               _ptr(workspace), workspace.numel() * workspace.element_size(),
                               _stream(stream))
     _check(st, "moe_decode_layer")
 
 
 def rmsnorm_struct(weight: torch.Tensor, eps: float, normed: torch.Tensor) -> CRMSNorm:
-    return CRMSNorm(weight.data_ptr(), _dt(weight), float(eps), normed.data_ptr())
+    return CRMSNorm(weight.data_ptr(), _dt(weight), float(eps), normed.data_ptr(), _dt(normed))
 
 
 def tail_rmsnorm_workspace_bytes(n_tokens: int, d_in: int) -> int:
@@ -309,7 +309,7 @@ def moe_decode_tail_rmsnorm(partial: torch.Tensor, residual: torch.Tensor, out: 
     S = 0 if shared is None else shared.shape[1]
     nrm = rmsnorm_struct(norm_weight, eps, normed)
     st = lib.moe_decode_tail_rmsnorm(_ptr(partial), T, K, d_in, _ptr(shared), S, _ptr(shared_gate),
-                                     _ptr(residual), _dt(residual), _ptr(out), ctypes.byref(nrm),
+                                     _ptr(residual), _dt(residual), _ptr(out), _dt(out), ctypes.byref(nrm),
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream))
     _check(st, "moe_decode_tail_rmsnorm")
@@ -323,7 +323,7 @@ def moe_decode_layer_rmsnorm(weights: CLayerWeights, x: torch.Tensor, residual: 
     """The fused single-launch layer plus the next layer's RMSNorm of out into normed [d_in]."""
     nrm = rmsnorm_struct(norm_weight, eps, normed)
     st = lib.moe_decode_layer_rmsnorm(ctypes.byref(weights), _ptr(x), _dt(x), _ptr(residual), _dt(residual),
-                                      _ptr(out), ctypes.byref(nrm), _ptr(expert_ids), _ptr(scores),
+                                      _ptr(out), _dt(out), ctypes.byref(nrm), _ptr(expert_ids), _ptr(scores),
                                       _ptr(shared_gate), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "moe_decode_layer_rmsnorm")
@@ -334,7 +334,8 @@ def moe_decode_rmsnorm(y: torch.Tensor, norm_weight: torch.Tensor, eps: float, n
     """normed [T, d] = y / sqrt(mean(y^2) + eps) * weight, one workgroup per token."""
     T, d = y.shape
     nrm = rmsnorm_struct(norm_weight, eps, normed)
-    _check(lib.moe_decode_rmsnorm(_ptr(y), T, d, ctypes.byref(nrm), _stream(stream)), "moe_decode_rmsnorm")
+    _check(lib.moe_decode_rmsnorm(_ptr(y), _dt(y), T, d, ctypes.byref(nrm), _stream(stream)),
+           "moe_decode_rmsnorm")
 
 
 def moe_decode_tail(partial: torch.Tensor, residual: torch.Tensor, out: torch.Tensor,
@@ -344,7 +345,7 @@ def moe_decode_tail(partial: torch.Tensor, residual: torch.Tensor, out: torch.Te
     T, K, d_in = partial.shape
     S = 0 if shared is None else shared.shape[1]
     st = lib.moe_decode_tail(_ptr(partial), T, K, d_in, _ptr(shared), S, _ptr(shared_gate),
-                             _ptr(residual), _dt(residual), _ptr(out), _stream(stream))
+                             _ptr(residual), _dt(residual), _ptr(out), _dt(out), _stream(stream))
     _check(st, "moe_decode_tail")
 
 

@@ -25,6 +25,20 @@ inline int raw_enum(const E &e) {
 }
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// p is aligned to the size of an element of dtype dt (a valid dtype).
+inline bool aligned_elem(const void *p, int dt) {
+    return (reinterpret_cast<uintptr_t>(p) & (dt == MOE_F32 ? 3u : 1u)) == 0;
+}
+
+// Host checks of an RMSNorm descriptor (not null).
+inline moe_status check_rmsnorm(const moe_rmsnorm *norm) {
+    if (!norm || !norm->weight || !norm->normed) return MOE_EINVAL;
+    const int w_dt = raw_enum(norm->dtype), n_dt = raw_enum(norm->normed_dtype);
+    if (!valid_dtype(w_dt) || !valid_dtype(n_dt)) return MOE_EUNSUPPORTED;
+    if (!(norm->eps >= 0.0f) || norm->eps > 3.0e38f) return MOE_EINVAL;     // NaN fails the first test
+    if (!aligned_elem(norm->weight, w_dt) || !aligned_elem(norm->normed, n_dt)) return MOE_EINVAL;
+    return MOE_OK;
+}
 
 // Checks one projection stack in isolation.  Returns MOE_OK or the error.
 inline moe_status check_qmat(const moe_qmat *m) {

@@ -108,6 +108,48 @@ __device__ __forceinline__ float load_act(const void *p, int dt, int64_t i) {
     return (float)f;
 }
 
+// Rounding to the output dtypes: the nearest value of dtype dt, ties to even.
+// bf16 keeps the top 16 bits of the fp32 pattern after adding half of the
+// dropped part's range (plus the kept part's lowest bit, for ties to even);
+// NaN stays a quiet NaN.  fp16 uses the hardware conversion, which rounds to
+// nearest even in the default mode.  Both are computed and one is selected,
+// so the callers' code has no branches on dt but the store width.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return (u & 0x7fffffffu) > 0x7f800000u ? ((u >> 16) | 0x40u) : r;
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float v) {
+    const _Float16 h = (_Float16)v;
+    uint16_t b;
+    __builtin_memcpy(&b, &h, 2);
+    return b;
+}
+
+// v rounded to dtype dt, as a float (F32: v itself).
+__device__ __forceinline__ float round_to_dtype(int dt, float v) {
+    const float b = __uint_as_float(f32_to_bf16_rne(v) << 16);
+    const float h = (float)(_Float16)v;
+    return dt == MOE_BF16 ? b : (dt == MOE_F16 ? h : v);
+}
+
+// Element i of p, of dtype dt, set to v, which already holds a value of dt
+// (round_to_dtype): the conversion back to 16 bits is exact.
+__device__ __forceinline__ void store_rounded(void *p, int dt, int64_t i, float v) {
+    if (dt == MOE_F32) {
+        reinterpret_cast<float *>(p)[i] = v;
+    } else {
+        const uint32_t bits = dt == MOE_BF16 ? (__float_as_uint(v) >> 16) : f32_to_f16_bits(v);
+        reinterpret_cast<uint16_t *>(p)[i] = (uint16_t)bits;
+    }
+}
+
+// Element i of p, of dtype dt, set to v rounded to dt.
+__device__ __forceinline__ void store_act(void *p, int dt, int64_t i, float v) {
+    store_rounded(p, dt, i, round_to_dtype(dt, v));
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));

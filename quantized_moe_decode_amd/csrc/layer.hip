@@ -97,11 +97,11 @@ static moe_status plan_layer(const moe_layer_weights *w, int d_in_check, LayerPl
     const int dmax = d_ffs > d_ff ? d_ffs : d_ff;
     a.act_stride = dmax;
     p.grid = a.n_route + a.K * a.a_tiles_r + a.S * a.a_tiles_s + slots * a.b_tiles;
-    // dynamic LDS: kernel-B units stage act as fp32 chunks (+4 floats each),
+    // dynamic LDS: kernel-B units stage act as fp16 chunks (f16_chunk_bytes),
     // kernel-A units stage x raw (+16 bytes per chunk)
     const int ca = codes_of(w->gate.bits);
     const size_t x_elem = raw_enum(w->w_router_dtype) == MOE_F32 ? 4 : 2;     // x has the router's dtype
-    const size_t lds_b = (size_t)(dmax / cb) * (cb + 4) * sizeof(float);
+    const size_t lds_b = (size_t)(dmax / cb) * (cb == 32 ? f16_chunk_bytes<4>() : f16_chunk_bytes<8>());
     const size_t lds_a = (size_t)(d_in / ca) * ((size_t)ca * x_elem + 16);
     p.lds = lds_b > lds_a ? lds_b : lds_a;
     if (p.lds > 64 * 1024) return MOE_EUNSUPPORTED;
@@ -217,25 +217,14 @@ extern "C" size_t moe_decode_layer_workspace_bytes(const moe_layer_weights *weig
 
 namespace moe {
 
-// Host checks of an RMSNorm descriptor (null: no norm).
-static moe_status check_norm(const moe_rmsnorm *norm) {
-    if (!norm) return MOE_OK;
-    if (!norm->weight || !norm->normed) return MOE_EINVAL;
-    if (!valid_dtype(raw_enum(norm->dtype))) return MOE_EUNSUPPORTED;
-    if (!(norm->eps >= 0.0f) || norm->eps > 3.0e38f) return MOE_EINVAL;     // NaN fails the first test
-    if ((reinterpret_cast<uintptr_t>(norm->weight) & 3u) || (reinterpret_cast<uintptr_t>(norm->normed) & 3u))
-        return MOE_EINVAL;
-    return MOE_OK;
-}
-
 static moe_status layer_impl(const moe_layer_weights *weights, const void *x, int x_dtype, const void *residual,
-                             int residual_dtype, float *out, int32_t *expert_ids, float *scores,
+                             int residual_dtype, void *out, int out_dtype, int32_t *expert_ids, float *scores,
                              float *shared_gate, const moe_rmsnorm *norm, void *workspace, size_t workspace_bytes,
                              void *stream) {
     if (!x || !residual || !out || !workspace) return MOE_EINVAL;
-    if (!valid_dtype(x_dtype) || !valid_dtype(residual_dtype)) return MOE_EUNSUPPORTED;
-    if (!aligned16(x) || !aligned16(workspace)) return MOE_EINVAL;
-    moe_status st = check_norm(norm);
+    if (!valid_dtype(x_dtype) || !valid_dtype(residual_dtype) || !valid_dtype(out_dtype)) return MOE_EUNSUPPORTED;
+    if (!aligned16(x) || !aligned16(workspace) || !aligned_elem(out, out_dtype)) return MOE_EINVAL;
+    moe_status st = norm ? check_rmsnorm(norm) : MOE_OK;
     if (st != MOE_OK) return st;
     LayerPlan p;
     st = plan_layer(weights, -1, p);
@@ -249,7 +238,7 @@ static moe_status layer_impl(const moe_layer_weights *weights, const void *x, in
     fit_a_passes(p, resident_capacity(k1, p.lds), resident_capacity(k2, p.lds));
     LayerFn k = p.a_nr == kLayerNRA ? k1 : k2;
     LayerArgs &a = p.a;
-    a.x = x; a.resid = residual; a.resid_dt = residual_dtype; a.out = out;
+    a.x = x; a.resid = residual; a.resid_dt = residual_dtype; a.out = out; a.out_dt = out_dtype;
     a.ids_out = expert_ids; a.scores_out = scores; a.gate_out = shared_gate;
     char *ws = reinterpret_cast<char *>(workspace);
     a.ctr = reinterpret_cast<uint32_t *>(ws);
@@ -263,6 +252,7 @@ static moe_status layer_impl(const moe_layer_weights *weights, const void *x, in
         a.norm_dt = raw_enum(norm->dtype);
         a.norm_eps = norm->eps;
         a.norm_out = norm->normed;
+        a.norm_out_dt = raw_enum(norm->normed_dtype);
     }
     hipLaunchKernelGGL(k, dim3(p.grid), dim3(kLayerThreads), p.lds, reinterpret_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
@@ -271,19 +261,22 @@ static moe_status layer_impl(const moe_layer_weights *weights, const void *x, in
 }  // namespace moe
 
 extern "C" moe_status moe_decode_layer(const moe_layer_weights *weights, const void *x, moe_dtype x_dtype_arg,
-                                       const void *residual, moe_dtype residual_dtype_arg, float *out,
-                                       int32_t *expert_ids, float *scores, float *shared_gate,
-                                       void *workspace, size_t workspace_bytes, void *stream) {
-    return layer_impl(weights, x, raw_enum(x_dtype_arg), residual, raw_enum(residual_dtype_arg), out, expert_ids,
-                      scores, shared_gate, nullptr, workspace, workspace_bytes, stream);
+                                       const void *residual, moe_dtype residual_dtype_arg, void *out,
+                                       moe_dtype out_dtype_arg, int32_t *expert_ids, float *scores,
+                                       float *shared_gate, void *workspace, size_t workspace_bytes, void *stream) {
+    return layer_impl(weights, x, raw_enum(x_dtype_arg), residual, raw_enum(residual_dtype_arg), out,
+                      raw_enum(out_dtype_arg), expert_ids, scores, shared_gate, nullptr, workspace, workspace_bytes,
+                      stream);
 }
 
 extern "C" moe_status moe_decode_layer_rmsnorm(const moe_layer_weights *weights, const void *x,
                                                moe_dtype x_dtype_arg, const void *residual,
-                                               moe_dtype residual_dtype_arg, float *out, const moe_rmsnorm *norm,
-                                               int32_t *expert_ids, float *scores, float *shared_gate,
-                                               void *workspace, size_t workspace_bytes, void *stream) {
+                                               moe_dtype residual_dtype_arg, void *out, moe_dtype out_dtype_arg,
+                                               const moe_rmsnorm *norm, int32_t *expert_ids, float *scores,
+                                               float *shared_gate, void *workspace, size_t workspace_bytes,
+                                               void *stream) {
     if (!norm) return MOE_EINVAL;
-    return layer_impl(weights, x, raw_enum(x_dtype_arg), residual, raw_enum(residual_dtype_arg), out, expert_ids,
-                      scores, shared_gate, norm, workspace, workspace_bytes, stream);
+    return layer_impl(weights, x, raw_enum(x_dtype_arg), residual, raw_enum(residual_dtype_arg), out,
+                      raw_enum(out_dtype_arg), expert_ids, scores, shared_gate, norm, workspace, workspace_bytes,
+                      stream);
 }

@@ -53,6 +53,10 @@ constexpr int kLayerNRA = 3;        // rows per lane group, kernel A units with 
                                     // (16-row units put two on half of them, which finished last)
 constexpr int kLayerNRA2 = 2;       // rows per lane group and stage, kernel A units with several (two in flight)
 constexpr int kLayerNRB = 4;        // rows per lane group, kernel B units
+// stages a kernel-B unit keeps in flight with 6- and 8-bit down projections
+// (register buffers): all of them are loaded before act arrives, and each
+// buffer is refilled as soon as its stage is done
+constexpr int kLayerBDepth = 2;
 constexpr int kLayerThreads = 256;  // threads per workgroup (the launch's block size)
 constexpr int kLayerWaves = kLayerThreads / kWave;
 constexpr int kCtrStride = 64;      // uint32 words between control words (256 bytes)
@@ -83,7 +87,8 @@ struct LayerArgs {
     int d_in, d_ff, d_ffs;
     QM gate, up, down;
     QM sgate, sup, sdown;
-    float *out;
+    void *out;                      // [d_in], dtype out_dt
+    int out_dt;
     int32_t *ids_out;
     float *scores_out;
     float *gate_out;
@@ -98,7 +103,8 @@ struct LayerArgs {
     const void *norm_w;             // [d_in], dtype norm_dt
     int norm_dt;
     float norm_eps;
-    float *norm_out;                // [d_in] fp32
+    void *norm_out;                 // [d_in], dtype norm_out_dt
+    int norm_out_dt;
     uint64_t *norm_part;            // [b_tiles] tagged: each tail tile's sum of squares
     int n_route;
     int by_xcd;                     // units in slot-interleaved order: slot s's units on XCD s (8 slots)
@@ -190,15 +196,17 @@ __device__ __forceinline__ void gather_tagged(const LayerArgs &a, int n, const u
     }
 }
 
-// The act gather of a kernel-B unit with 4-bit down weights: act[0, n) (n a
-// multiple of 32) into LDS as fp16 pair chunks of 32 values (kF16ChunkBytes
-// each, placed as dot_block_q4_f16 reads them), each value times
+// The act gather of a kernel-B unit: act[0, n) (n a multiple of the chunk
+// size) into LDS as fp16 chunks placed as the packed dots read them
+// (f16_stage_offset: 4-bit chunks of 32 values for dot_block_q4_f16, 6- and
+// 8-bit chunks of 16 for dot_block_f16x16), each value times
 // kActF16Prescale.  Returns the factor by which the dot products of the
 // staged values are to be multiplied: kActF16Postscale, unless some value
 // would overflow fp16 that way (one compare per value; the waves' ballots
 // meet in LDS over the barrier that ends the gather).  Then every thread
 // reads its words again (all are present by then) and the vector is staged
 // with the factor fitted to its largest magnitude (f16_stage_scale).
+template <int BB>
 __device__ __forceinline__ float gather_act_f16(const LayerArgs &a, int n, const uint64_t *sentinel, uint32_t tag,
                                                 const uint64_t *act, char *lds) {
     static_assert(kLayerWaves == 4, "one flag word per wave, read as one 16-byte word");
@@ -206,7 +214,7 @@ __device__ __forceinline__ float gather_act_f16(const LayerArgs &a, int n, const
     constexpr int nt = kLayerThreads;
     const int t = threadIdx.x, lane = t & (kWave - 1), wave = t >> 6;
     auto place = [&](int i, float v) {
-        *reinterpret_cast<_Float16 *>(lds + (i >> 5) * kF16ChunkBytes + f16_pair_offset(i & 31)) = (_Float16)v;
+        *reinterpret_cast<_Float16 *>(lds + f16_stage_offset<BB>(i)) = (_Float16)v;
     };
     if (t == 0) (void)wait_tagged<kActSleep>(a, sentinel, tag);
     __syncthreads();
@@ -552,9 +560,9 @@ __device__ __forceinline__ float block_sum_fixed(float v) {
 // publishes the sum of squares of its rows of out (a fixed-order workgroup
 // sum) as a tagged word, gathers every tile's word, adds them in tile order
 // (a fixed-order sum again), and writes its own rows of
-//   norm_out[i] = out[i] / sqrt(sum_i out[i]^2 / d_in + eps) * weight[i].
-// own[k]: this thread's row row0 + tid + k * kLayerThreads of out (0 past
-// row_end).  s_part: LDS for every tile's sum (at least b_tiles floats; the
+//   norm_out[i] = out[i] / sqrt(sum_i out[i]^2 / d_in + eps) * weight[i]
+// (rounded to norm_out's dtype).  own[k]: this thread's row row0 + tid +
+// k * kLayerThreads of out as stored (0 past row_end).  s_part: LDS for every tile's sum (at least b_tiles floats; the
 // unit's logits array, no longer needed).
 template <int NROWS>
 __device__ void tail_rmsnorm(const LayerArgs &a, uint32_t tag, int tile, int row0, int row_end,
@@ -574,7 +582,7 @@ __device__ void tail_rmsnorm(const LayerArgs &a, uint32_t tag, int tile, int row
 #pragma unroll
     for (int k = 0; k < NROWS; ++k) {
         const int r = row0 + threadIdx.x + k * kLayerThreads;
-        if (r < row_end) a.norm_out[r] = own[k] * inv * load_act(a.norm_w, a.norm_dt, r);
+        if (r < row_end) store_act(a.norm_out, a.norm_out_dt, r, own[k] * inv * load_act(a.norm_w, a.norm_dt, r));
     }
 }
 
@@ -605,13 +613,30 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
     // groups of one lane x kLayerNRB rows
     __shared__ float s_own[4 * kWave * kLayerNRB];
 
-    // stages = (row pass, chunk position); stage 0 is loaded before act is ready
+    // stages = (row pass, chunk position); the first kDepth stages are loaded
+    // before act is ready, into a ring of register buffers: stage st uses
+    // buffer st % kDepth, which is refilled with stage st + kDepth once st is
+    // done.  4-bit down projections keep one buffer (their first stage is
+    // also unpacked before act arrives, which takes the registers).
+    constexpr int kDepth = BB == 4 ? 1 : kLayerBDepth;
     const int rb0 = row0 + wave * rpw * NR, pass_rows = 4 * rpw * NR;
     const int n_pass = (valid && rb0 < row_end) ? (row_end - rb0 + pass_rows - 1) / pass_rows : 0;
     const int n_chunk = (cpr + lr - 1) / lr;
     const int n_stage = n_pass * n_chunk;
-    BlockRegs<BB, 1, NR> cur;
-    if (n_stage > 0) load_block<BB, 1, NR, kLayerSBase>(cur, mats, erow0, rb0 + rsub, rpw, row_end, j, cpr);
+    auto load_stage = [&](BlockRegs<BB, 1, NR> &R, int st) __attribute__((always_inline)) {
+        const int ps = st / n_chunk, ch = st - ps * n_chunk;
+        load_block<BB, 1, NR, kLayerSBase>(R, mats, erow0, rb0 + ps * pass_rows + rsub, rpw, row_end, ch * lr + j,
+                                           cpr);
+    };
+    static_assert(kDepth >= 1 && kDepth <= 3, "the stage loop below is written for up to three buffers");
+    BlockRegs<BB, 1, NR> b0, b1, b2;        // separate variables: they stay in registers
+    if (n_stage > 0) load_stage(b0, 0);
+    if constexpr (kDepth >= 2) {
+        if (n_stage > 1) load_stage(b1, 1);
+    }
+    if constexpr (kDepth >= 3) {
+        if (n_stage > 2) load_stage(b2, 2);
+    }
 
     if (routed && wave == 0) {   // scores while the weights and act are in flight
         with_per(a.E, [&](auto per) { softmax_scores<decltype(per)::value>(a.E, a.K, a.renorm, s_logits, lane, sel); });
@@ -628,53 +653,40 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
         const uint64_t *act = a.act + (int64_t)slot * a.act_stride;
         const int n_act = cpr * CODES;
         const uint64_t *sent = a.act_sent + ((int64_t)slot * kActCopies + tile % kActCopies) * kSentStride;
-        // 4-bit down projections take act as fp16 pairs (packed dot), staged
-        // with a power-of-two factor whose inverse joins the score
-        // (gather_act_f16); the others take act as fp32 chunks
-        constexpr bool kF16 = BB == 4;
-        // the first stage's codes unpacked while act is on its way: after it
-        // arrives only the dot products remain
+        // act as fp16 pairs for the packed dots, staged with a power-of-two
+        // factor whose inverse joins the score (gather_act_f16).  With 4-bit
+        // codes the first stage's codes are unpacked while act is on its way:
+        // after it arrives only the dot products remain.
         [[maybe_unused]] uint32_t pre[1][NR][16];
-        float cs = 1.0f;
-        if constexpr (kF16) {
-            if (n_stage > 0) unpack_q4_f16<1, NR>(cur, pre);
-            cs = gather_act_f16(a, n_act, sent, tag, act, reinterpret_cast<char *>(xs));
-        } else {
-            gather_tagged<kActSleep>(a, n_act, sent, tag, [&](int i) { return act + i; }, [&](int i, float v) {
-                const int c = i / CODES;
-                xs[c * (CODES + 4) + (i - c * CODES)] = v;
-            });
-            __syncthreads();
+        if constexpr (BB == 4) {
+            if (n_stage > 0) unpack_q4_f16<1, NR>(b0, pre);
         }
+        const float cs = gather_act_f16<BB>(a, n_act, sent, tag, act, reinterpret_cast<char *>(xs));
         if (routed) score = sel->scores[slot];
         const float sc = score * cs;         // exact: cs is a power of two
         float acc[1][NR];
-        for (int st = 0; st < n_stage; ++st) {
+        auto run_stage = [&](BlockRegs<BB, 1, NR> &cur, int st) __attribute__((always_inline)) {
             const int ps = st / n_chunk, ch = st - ps * n_chunk;
             const int r0 = rb0 + ps * pass_rows + rsub;
             if (ch == 0) {
 #pragma unroll
                 for (int n = 0; n < NR; ++n) acc[0][n] = 0.f;
             }
-            if (st > 0) load_block<BB, 1, NR, kLayerSBase>(cur, mats, erow0, r0, rpw, row_end, ch * lr + j, cpr);
-            if constexpr (kF16) {
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(xs) +
-                                                                   cur.cc * kF16ChunkBytes);
-                uint32_t ap[16];
+            constexpr int NP = CODES / 2;           // staged pairs per chunk
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(xs) +
+                                                               cur.cc * f16_chunk_bytes<BB>());
+            uint32_t ap[NP];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u32x4 v = src[i];
+            for (int i = 0; i < NP / 4; ++i) {
+                const u32x4 v = src[i];
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) ap[4 * i + k] = v[k];
-                }
-                if constexpr (BB == 4) {
-                    if (st == 0) dot_pre_q4_f16<SB, 1, NR>(cur, pre, ap, f16_pairs_sum(ap), acc);
-                    else dot_block_q4_f16<SB, 1, NR>(cur, ap, f16_pairs_sum(ap), acc);
-                }
+                for (int k = 0; k < 4; ++k) ap[4 * i + k] = v[k];
+            }
+            if constexpr (BB == 4) {
+                if (st == 0) dot_pre_q4_f16<SB, 1, NR>(cur, pre, ap, f16_pairs_sum<NP>(ap), acc);
+                else dot_block_q4_f16<SB, 1, NR>(cur, ap, f16_pairs_sum<NP>(ap), acc);
             } else {
-                float xv[CODES];
-                read_staged<CODES>(staged_chunk<CODES>(xs, 0, cpr, cur.cc), xv);
-                dot_block<BB, SB, 1, NR>(cur, xv, sum_n<CODES>(xv), acc);
+                dot_block_f16x16<BB, SB, 1, NR>(cur, ap, f16_pairs_sum<NP>(ap), acc);
             }
             if (ch == n_chunk - 1) {
                 auto put = [&](int r, float v) {
@@ -703,6 +715,24 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
                         }
                     }
                 });
+            }
+        };
+        if constexpr (kDepth == 1) {
+            for (int st = 0; st < n_stage; ++st) {
+                if (st > 0) load_stage(b0, st);
+                run_stage(b0, st);
+            }
+        } else {
+            auto step = [&](BlockRegs<BB, 1, NR> &cur, int st) __attribute__((always_inline)) {
+                if (st < n_stage) {
+                    run_stage(cur, st);
+                    if (st + kDepth < n_stage) load_stage(cur, st + kDepth);
+                }
+            };
+            for (int st0 = 0; st0 < n_stage; st0 += kDepth) {
+                step(b0, st0);
+                step(b1, st0 + 1);
+                if constexpr (kDepth >= 3) step(b2, st0 + 2);
             }
         }
     } else {
@@ -747,8 +777,8 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
                 }
             }
         }
-        const float o = load_act(a.resid, a.resid_dt, r) + (routed_sum + sh * g);
-        a.out[r] = o;
+        const float o = round_to_dtype(a.out_dt, load_act(a.resid, a.resid_dt, r) + (routed_sum + sh * g));
+        store_rounded(a.out, a.out_dt, r, o);
         own[k] = o;
     }
     if (a.norm_out) tail_rmsnorm<kTailRows>(a, tag, tile, row0, row_end, own, s_logits);

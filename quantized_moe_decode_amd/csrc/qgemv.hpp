@@ -401,13 +401,98 @@ __device__ __forceinline__ void dot_pre_q4_f16(const BlockRegs<4, NM, NR> &R, co
         }
 }
 
-// Sum of a chunk's 16 staged fp16 pairs, in fp32.
+// Sum of a chunk's NP staged fp16 pairs, in fp32.
+template <int NP = 16>
 __device__ __forceinline__ float f16_pairs_sum(const uint32_t *ap) {
     const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, ap[i]), one, s, false);
+    for (int i = 0; i < NP; ++i) s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, ap[i]), one, s, false);
     return s;
+}
+
+// fp16 inputs of one 6- or 8-bit chunk (16 values) staged for
+// dot_block_f16x16: in order, pair p = (input 2p, input 2p + 1), then 16 bytes
+// of padding.
+constexpr int kF16Chunk16Bytes = 16 * 2 + 16;
+
+// Bytes of one staged fp16 input chunk of a BITS-bit down projection, and the
+// LDS byte offset of input i of the whole vector in that staging.
+template <int BITS>
+constexpr int f16_chunk_bytes() { return BITS == 4 ? kF16ChunkBytes : kF16Chunk16Bytes; }
+
+template <int BITS>
+__device__ __forceinline__ int f16_stage_offset(int i) {
+    if constexpr (BITS == 4) return (i >> 5) * kF16ChunkBytes + f16_pair_offset(i & 31);
+    else return (i >> 4) * kF16Chunk16Bytes + (i & 15) * 2;
+}
+
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// The eight code pairs (2p, 2p + 1) of a 6- or 8-bit chunk as fp16 pairs
+// whose bit patterns are the codes themselves: an fp16 pattern q < 1024 is the
+// subnormal q 2^-24, exact, so a packed fp16 dot of such a pair with two
+// inputs is 2^-24 (q x + q' x') with exact products, and the 2^24 joins the
+// scale.  8-bit: one byte permute per pair.  6-bit: the four codes of each
+// 3-byte group lie in two 16-bit windows (bytes B0 B1 and B1 B2); a permute
+// puts a window in both halves of a word, a packed 16-bit shift moves each
+// half's code to bit 0 (shifts 0 and 6 in B0 B1, 4 and 10 in B1 B2) and a
+// mask keeps 6 bits.
+template <int BITS>
+__device__ __forceinline__ void code_pairs16(const Chunk<BITS> &c, uint32_t (&q)[8]) {
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            q[2 * k] = __builtin_amdgcn_perm(0u, c.w[k], 0x04010400u);         // bytes 0, 1
+            q[2 * k + 1] = __builtin_amdgcn_perm(0u, c.w[k], 0x04030402u);     // bytes 2, 3
+        }
+    } else {
+        static_assert(BITS == 6, "code_pairs16 takes 6- or 8-bit chunks");
+        // group g: bytes 3g .. 3g + 2 of the 12; perm(hi, lo, sel) picks bytes
+        // 0-3 from lo and 4-7 from hi
+        const uint32_t lo[4] = {c.w[0], c.w[0], c.w[1], c.w[2]};
+        const uint32_t hi[4] = {c.w[0], c.w[1], c.w[2], c.w[2]};
+        constexpr uint32_t b0[4] = {0, 3, 2, 1};           // selector of the group's first byte
+        const u16x2_t sh01 = {0, 6}, sh23 = {4, 10};
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint32_t B0 = b0[g], B1 = b0[g] + 1, B2 = b0[g] + 2;
+            const uint32_t t01 = __builtin_amdgcn_perm(hi[g], lo[g], B0 | B1 << 8 | B0 << 16 | B1 << 24);
+            const uint32_t t23 = __builtin_amdgcn_perm(hi[g], lo[g], B1 | B2 << 8 | B1 << 16 | B2 << 24);
+            q[2 * g] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, t01) >> sh01) & 0x003F003Fu;
+            q[2 * g + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, t23) >> sh23) & 0x003F003Fu;
+        }
+    }
+}
+
+// 6- or 8-bit codes against fp16 inputs staged in order (kF16Chunk16Bytes per
+// chunk) with the packed fp16 dot instruction: the code pairs of
+// code_pairs16, eight dots per row, the scale times 2^24 (exact).  ap: the
+// chunk's 8 staged pairs; asum: their sum.
+template <int BITS, int SB, int NM, int NR>
+__device__ __forceinline__ void dot_block_f16x16(const BlockRegs<BITS, NM, NR> &R, const uint32_t *ap, float asum,
+                                                 float (&acc)[NM][NR]) {
+    float d[NM][NR];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int n = 0; n < NR; ++n) {
+            uint32_t qp[8];
+            code_pairs16<BITS>(R.w[m][n], qp);
+            d[m][n] = 0.f;
+#pragma unroll
+            for (int p = 0; p < 8; ++p)
+                d[m][n] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, qp[p]), __builtin_bit_cast(f16x2_t, ap[p]),
+                                                 d[m][n], false);
+        }
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int n = 0; n < NR; ++n) {
+            const float s = R.live[n] ? sb_to_float<SB>(R.sr[m][n]) * 16777216.0f : 0.f;
+            const float b = R.live[n] ? sb_to_float<SB>(R.br[m][n]) : 0.f;
+            acc[m][n] += s * d[m][n] + b * asum;
+        }
 }
 
 // Input chunks staged raw in LDS: chunk c at byte c * xraw_stride (16 bytes of

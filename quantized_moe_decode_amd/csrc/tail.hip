@@ -17,8 +17,8 @@ struct TailArgs {
     const float *shared;
     const float *gate;
     const void *resid;
-    float *out;
-    int resid_dt, T, K, D, S;
+    void *out;
+    int resid_dt, out_dt, T, K, D, S;
 };
 
 // p[0] + p[D] + ... + p[(n-1) D], added in that order; the loads are issued
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void tail_kernel(TailArgs a) {
     const float routed = sum_rows(a.partial + (int64_t)t * a.K * a.D + i, a.K, a.D);
     const float sh = a.S > 0 ? sum_rows(a.shared + (int64_t)t * a.S * a.D + i, a.S, a.D) : 0.f;
     const float g = a.gate ? a.gate[t] : 1.0f;
-    a.out[idx] = load_act(a.resid, a.resid_dt, idx) + (routed + sh * g);
+    store_act(a.out, a.out_dt, idx, load_act(a.resid, a.resid_dt, idx) + (routed + sh * g));
 }
 
 // ---------------------------------------------- tail + the next layer's RMSNorm
@@ -54,7 +54,8 @@ __global__ __launch_bounds__(256) void tail_kernel(TailArgs a) {
 // their sum of squares (a fixed-order workgroup sum) as a word tagged with
 // the launch's epoch, gathers token t's words of every chunk, adds them in
 // chunk order, and writes its elements of
-//   normed = out / sqrt(sum out^2 / D + eps) * weight.
+//   normed = out / sqrt(sum out^2 / D + eps) * weight,
+// out taken as stored (rounded to its dtype), normed rounded to its own.
 // The workspace: control words (error, epoch, finished workgroups), 256 bytes
 // apart, then [T][chunks] tagged words.  Every workgroup waits only on
 // workgroups of its own token, all of which are resident (the host checks that
@@ -71,7 +72,8 @@ struct TailNormArgs {
     const void *norm_w;
     int norm_dt;
     float eps;
-    float *normed;
+    void *normed;
+    int normed_dt;
     uint32_t *ctr;
     uint64_t *part;         // [T][chunks]
     int chunks;
@@ -103,8 +105,8 @@ __global__ __launch_bounds__(kTailNormThreads) void tail_norm_kernel(TailNormArg
         const float routed = sum_rows(a.t.partial + (int64_t)t * a.t.K * D + i, a.t.K, D);
         const float sh = a.t.S > 0 ? sum_rows(a.t.shared + (int64_t)t * a.t.S * D + i, a.t.S, D) : 0.f;
         const float g = a.t.gate ? a.t.gate[t] : 1.0f;
-        o = load_act(a.t.resid, a.t.resid_dt, idx) + (routed + sh * g);
-        a.t.out[idx] = o;
+        o = round_to_dtype(a.t.out_dt, load_act(a.t.resid, a.t.resid_dt, idx) + (routed + sh * g));
+        store_rounded(a.t.out, a.t.out_dt, idx, o);
     }
     const float ss = block_sum_fixed256(o * o, s_w);
     uint64_t *part = a.part + (int64_t)t * a.chunks;
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kTailNormThreads) void tail_norm_kernel(TailNormArg
     float total = 0.f;
     for (int c = 0; c < a.chunks; ++c) total += s_part[c];      // chunk order
     const float inv = 1.0f / sqrtf(total / (float)D + a.eps);
-    if (i < D) a.normed[(int64_t)t * D + i] = o * inv * load_act(a.norm_w, a.norm_dt, i);
+    if (i < D) store_act(a.normed, a.normed_dt, (int64_t)t * D + i, o * inv * load_act(a.norm_w, a.norm_dt, i));
     // every word of this token was read: the last workgroup moves the workspace to the next epoch
     __syncthreads();
     if (tid == 0) {
@@ -149,16 +151,19 @@ __global__ __launch_bounds__(kTailNormThreads) void tail_norm_kernel(TailNormArg
 // Plain RMSNorm, one workgroup per token: normed[t] = y[t] / sqrt(mean(y[t]^2)
 // + eps) * weight, the sum of squares in a fixed order (each thread's
 // elements in order, then the fixed workgroup tree).
-__global__ __launch_bounds__(kTailNormThreads) void rmsnorm_kernel(const float *y, int D, const void *w, int w_dt,
-                                                                   float eps, float *normed) {
+__global__ __launch_bounds__(kTailNormThreads) void rmsnorm_kernel(const void *y, int y_dt, int D, const void *w,
+                                                                   int w_dt, float eps, void *normed, int normed_dt) {
     __shared__ float s_w[kTailNormThreads / kWave];
-    const float *yt = y + (int64_t)blockIdx.x * D;
+    const int64_t t0 = (int64_t)blockIdx.x * D;
     float ss = 0.f;
-    for (int i = threadIdx.x; i < D; i += kTailNormThreads) ss += yt[i] * yt[i];
+    for (int i = threadIdx.x; i < D; i += kTailNormThreads) {
+        const float v = load_act(y, y_dt, t0 + i);
+        ss += v * v;
+    }
     const float total = block_sum_fixed256(ss, s_w);
     const float inv = 1.0f / sqrtf(total / (float)D + eps);
     for (int i = threadIdx.x; i < D; i += kTailNormThreads)
-        normed[(int64_t)blockIdx.x * D + i] = yt[i] * inv * load_act(w, w_dt, i);
+        store_act(normed, normed_dt, t0 + i, load_act(y, y_dt, t0 + i) * inv * load_act(w, w_dt, i));
 }
 
 // Workgroups of tail_norm_kernel that can be resident at once on the current
@@ -192,19 +197,20 @@ extern "C" size_t moe_decode_tail_rmsnorm_workspace_bytes(int32_t n_tokens, int3
 
 extern "C" moe_status moe_decode_tail(const float *partial, int32_t n_tokens, int32_t top_k, int32_t d_in,
                                       const float *shared, int32_t n_shared, const float *shared_gate,
-                                      const void *residual, moe_dtype residual_dtype_arg, float *out,
-                                      void *stream) {
+                                      const void *residual, moe_dtype residual_dtype_arg, void *out,
+                                      moe_dtype out_dtype_arg, void *stream) {
     if (!partial || !residual || !out) return MOE_EINVAL;
     if (n_tokens < 1 || n_tokens > MOE_MAX_TOKENS) return MOE_EINVAL;
     if (top_k < 1 || top_k > MOE_MAX_TOP_K) return MOE_EINVAL;
     if (d_in < kGroup || d_in > MOE_MAX_DIM || d_in % kGroup) return MOE_EINVAL;
     if (n_shared < 0 || n_shared > MOE_MAX_TOP_K) return MOE_EINVAL;
     if ((n_shared == 0) != (shared == nullptr)) return MOE_EINVAL;
-    const int residual_dtype = raw_enum(residual_dtype_arg);
-    if (!valid_dtype(residual_dtype)) return MOE_EUNSUPPORTED;
+    const int residual_dtype = raw_enum(residual_dtype_arg), out_dtype = raw_enum(out_dtype_arg);
+    if (!valid_dtype(residual_dtype) || !valid_dtype(out_dtype)) return MOE_EUNSUPPORTED;
+    if (!aligned_elem(out, out_dtype)) return MOE_EINVAL;
     TailArgs a;
     a.partial = partial; a.shared = shared; a.gate = shared_gate; a.resid = residual; a.out = out;
-    a.resid_dt = residual_dtype; a.T = n_tokens; a.K = top_k; a.D = d_in; a.S = n_shared;
+    a.resid_dt = residual_dtype; a.out_dt = out_dtype; a.T = n_tokens; a.K = top_k; a.D = d_in; a.S = n_shared;
     const int64_t n = (int64_t)n_tokens * d_in;
     hipLaunchKernelGGL(tail_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), a);
@@ -226,31 +232,31 @@ extern "C" int32_t moe_decode_abi_version(void) { return MOE_DECODE_ABI_VERSION;
 
 extern "C" moe_status moe_decode_tail_rmsnorm(const float *partial, int32_t n_tokens, int32_t top_k, int32_t d_in,
                                               const float *shared, int32_t n_shared, const float *shared_gate,
-                                              const void *residual, moe_dtype residual_dtype_arg, float *out,
-                                              const moe_rmsnorm *norm, void *workspace, size_t workspace_bytes,
-                                              void *stream) {
-    const int residual_dtype = raw_enum(residual_dtype_arg);
+                                              const void *residual, moe_dtype residual_dtype_arg, void *out,
+                                              moe_dtype out_dtype_arg, const moe_rmsnorm *norm, void *workspace,
+                                              size_t workspace_bytes, void *stream) {
+    const int residual_dtype = raw_enum(residual_dtype_arg), out_dtype = raw_enum(out_dtype_arg);
     if (!partial || !residual || !out || !norm || !workspace) return MOE_EINVAL;
     if (n_tokens < 1 || n_tokens > MOE_MAX_TOKENS) return MOE_EINVAL;
     if (top_k < 1 || top_k > MOE_MAX_TOP_K) return MOE_EINVAL;
     if (d_in < kGroup || d_in > MOE_MAX_DIM || d_in % kGroup) return MOE_EINVAL;
     if (n_shared < 0 || n_shared > MOE_MAX_TOP_K) return MOE_EINVAL;
     if ((n_shared == 0) != (shared == nullptr)) return MOE_EINVAL;
-    if (!valid_dtype(residual_dtype)) return MOE_EUNSUPPORTED;
-    if (!norm->weight || !norm->normed) return MOE_EINVAL;
-    if (!valid_dtype(raw_enum(norm->dtype))) return MOE_EUNSUPPORTED;
-    if (!(norm->eps >= 0.0f) || norm->eps > 3.0e38f) return MOE_EINVAL;
-    if ((reinterpret_cast<uintptr_t>(norm->weight) & 3u) || (reinterpret_cast<uintptr_t>(norm->normed) & 3u) ||
-        !aligned16(workspace))
-        return MOE_EINVAL;
+    if (!valid_dtype(residual_dtype) || !valid_dtype(out_dtype)) return MOE_EUNSUPPORTED;
+    if (!aligned_elem(out, out_dtype)) return MOE_EINVAL;
+    const moe_status nst = check_rmsnorm(norm);
+    if (nst != MOE_OK) return nst;
+    if (!aligned16(workspace)) return MOE_EINVAL;
     if (workspace_bytes < moe_decode_tail_rmsnorm_workspace_bytes(n_tokens, d_in)) return MOE_EINVAL;
     const int chunks = (d_in + kTailNormThreads - 1) / kTailNormThreads;
     const int cap = tail_norm_capacity();
     if (cap > 0 && n_tokens * chunks > cap) return MOE_EUNSUPPORTED;
     TailNormArgs a;
     a.t.partial = partial; a.t.shared = shared; a.t.gate = shared_gate; a.t.resid = residual; a.t.out = out;
-    a.t.resid_dt = residual_dtype; a.t.T = n_tokens; a.t.K = top_k; a.t.D = d_in; a.t.S = n_shared;
-    a.norm_w = norm->weight; a.norm_dt = raw_enum(norm->dtype); a.eps = norm->eps; a.normed = norm->normed;
+    a.t.resid_dt = residual_dtype; a.t.out_dt = out_dtype;
+    a.t.T = n_tokens; a.t.K = top_k; a.t.D = d_in; a.t.S = n_shared;
+    a.norm_w = norm->weight; a.norm_dt = raw_enum(norm->dtype); a.eps = norm->eps;
+    a.normed = norm->normed; a.normed_dt = raw_enum(norm->normed_dtype);
     a.ctr = reinterpret_cast<uint32_t *>(workspace);
     a.part = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(workspace) + kTailHeadBytes);
     a.chunks = chunks;
@@ -259,16 +265,17 @@ extern "C" moe_status moe_decode_tail_rmsnorm(const float *partial, int32_t n_to
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-extern "C" moe_status moe_decode_rmsnorm(const float *y, int32_t n_tokens, int32_t d, const moe_rmsnorm *norm,
-                                         void *stream) {
-    if (!y || !norm || !norm->weight || !norm->normed) return MOE_EINVAL;
+extern "C" moe_status moe_decode_rmsnorm(const void *y, moe_dtype y_dtype_arg, int32_t n_tokens, int32_t d,
+                                         const moe_rmsnorm *norm, void *stream) {
+    const int y_dtype = raw_enum(y_dtype_arg);
+    if (!y) return MOE_EINVAL;
+    const moe_status nst = check_rmsnorm(norm);
+    if (nst != MOE_OK) return nst;
     if (n_tokens < 1 || n_tokens > MOE_MAX_TOKENS || d < 1 || d > MOE_MAX_DIM) return MOE_EINVAL;
-    if (!valid_dtype(raw_enum(norm->dtype))) return MOE_EUNSUPPORTED;
-    if (!(norm->eps >= 0.0f) || norm->eps > 3.0e38f) return MOE_EINVAL;
-    if ((reinterpret_cast<uintptr_t>(y) & 3u) || (reinterpret_cast<uintptr_t>(norm->weight) & 3u) ||
-        (reinterpret_cast<uintptr_t>(norm->normed) & 3u))
-        return MOE_EINVAL;
+    if (!valid_dtype(y_dtype)) return MOE_EUNSUPPORTED;
+    if (!aligned_elem(y, y_dtype)) return MOE_EINVAL;
     hipLaunchKernelGGL(rmsnorm_kernel, dim3(n_tokens), dim3(kTailNormThreads), 0, reinterpret_cast<hipStream_t>(stream),
-                       y, d, norm->weight, raw_enum(norm->dtype), norm->eps, norm->normed);
+                       y, y_dtype, d, norm->weight, raw_enum(norm->dtype), norm->eps, norm->normed,
+                       raw_enum(norm->normed_dtype));
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }

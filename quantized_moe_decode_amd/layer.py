@@ -79,13 +79,15 @@ class DecodeLayer:
         self.fused_ws = torch.zeros(nb, device=dev, dtype=torch.uint8) if nb else None
         self.norm_w, self.norm_eps, self.normed, self.tail_ws, self.fold_norm = None, 0.0, None, None, True
 
-    def set_next_norm(self, weight: torch.Tensor, eps: float, fold: bool = True) -> None:
+    def set_next_norm(self, weight: torch.Tensor, eps: float, fold: bool = True,
+                      dtype: torch.dtype = torch.float32) -> None:
         """The next layer's RMSNorm (weight [d_in], eps) of this layer's output:
-        every forward also writes self.normed [T, d_in] fp32, folded into the
-        tail (fold=True) or as a separate moe_decode_rmsnorm launch after it."""
+        every forward also writes self.normed [T, d_in] of `dtype` (fp32, bf16
+        or fp16), folded into the tail (fold=True) or as a separate
+        moe_decode_rmsnorm launch after it."""
         dev = self.router.device
         self.norm_w, self.norm_eps, self.fold_norm = weight, float(eps), fold
-        self.normed = torch.zeros(self.n_tokens, self.d_in, device=dev, dtype=torch.float32)
+        self.normed = torch.zeros(self.n_tokens, self.d_in, device=dev, dtype=dtype)
         self.tail_ws = torch.zeros(tail_rmsnorm_workspace_bytes(self.n_tokens, self.d_in), device=dev,
                                    dtype=torch.uint8)
 
@@ -112,7 +114,7 @@ class DecodeLayer:
                 moe_decode_rmsnorm(out.view(-1, self.d_in), self.norm_w, self.norm_eps, self.normed, stream)
 
     def forward(self, x: torch.Tensor, resid: torch.Tensor, out: torch.Tensor, stream=None) -> None:
-        """out [T, d_in] fp32 = the layer applied to x [T, d_in] with residual resid."""
+        """out [T, d_in] (fp32, bf16 or fp16) = the layer applied to x [T, d_in] with residual resid."""
         self.route(x, stream)
         self.experts(x, stream)
         self.tail(resid, out, stream)
@@ -169,20 +171,21 @@ class DecodeStep:
     all layers sharing one fused workspace; path "three-call": route, expert
     FFN (routed, then shared) and tail per layer (any token count).  Inputs
     are given per distinct token (or token batch) r and layer l as device
-    tensors xs[r][l], rs[r][l]; layer l writes outs[l] [T, d_in] fp32 and its
-    routing into layers[l].ids / .scores.  Layers run back to back: no work
-    of layer l + 1 starts before layer l has finished.
+    tensors xs[r][l], rs[r][l]; layer l writes outs[l] [T, d_in] of
+    out_dtype (fp32, bf16 or fp16) and its routing into layers[l].ids /
+    .scores.  Layers run back to back: no work of layer l + 1 starts before
+    layer l has finished.
     """
 
     def __init__(self, layers: Sequence[DecodeLayer], xs, rs, path: str = "fused",
-                 share_workspace: bool = True):
+                 share_workspace: bool = True, out_dtype: torch.dtype = torch.float32):
         if path not in ("fused", "three-call"):
             raise ValueError(path)
         if path == "fused" and any(l.n_tokens != 1 for l in layers):
             raise ValueError("the fused launch takes one token per step")
         self.layers, self.xs, self.rs, self.path = list(layers), xs, rs, path
         dev = layers[0].router.device
-        self.outs = [torch.zeros(l.n_tokens, l.d_in, device=dev) for l in layers]
+        self.outs = [torch.zeros(l.n_tokens, l.d_in, device=dev, dtype=out_dtype) for l in layers]
         self.fused_ws = share_fused_workspace(self.layers) if (path == "fused" and share_workspace) else None
         self.graphs = []
 

@@ -481,9 +481,110 @@ def pin_rmsnorm_tokens_independent():
         assert np.array_equal(oracle.rmsnorm(y[t], wb, mi.BF16, 1e-6)[0], both[t])
 
 
+def _bf16_table():
+    """Every finite bf16 value in increasing order, with its bit pattern."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    vals = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    ok = np.isfinite(vals) & ~((bits == 0x8000))           # one zero
+    order = np.argsort(vals[ok], kind="stable")
+    return vals[ok][order], bits[ok][order]
+
+
+def _round_bf16_bruteforce(x):
+    """Nearest finite bf16 value by search over the sorted table; on a tie the
+    one with an even pattern; beyond the largest finite value by at least half
+    its spacing, infinity."""
+    vals, bits = _bf16_table()
+    vmax, half = vals[-1], (vals[-1] - vals[-2]) / 2
+    out = np.empty_like(x)
+    for n, v in enumerate(x):
+        if abs(v) >= vmax + half:
+            out[n] = np.copysign(np.inf, v)
+            continue
+        i = int(np.searchsorted(vals, v))
+        cand = [j for j in (i - 1, i) if 0 <= j < len(vals)]
+        dist = [abs(vals[j] - v) for j in cand]
+        best = [cand[k] for k in range(len(cand)) if dist[k] == min(dist)]
+        if len(best) > 1:
+            best = [j for j in best if bits[j] % 2 == 0]
+        out[n] = vals[best[0]] if vals[best[0]] != 0 else np.copysign(0.0, v)
+    return out
+
+
+def _round_samples(rng, table):
+    """Values spread over the whole range (subnormals to overflow), exact ties
+    (midpoints of neighbouring table values, exact in double) and values just
+    beside them."""
+    pos = table[table > 0]
+    i = rng.integers(0, len(pos) - 1, 300)
+    mids = (pos[i] + pos[i + 1]) / 2
+    near = np.concatenate([np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf)])
+    mag = np.exp2(rng.uniform(-150, 140, 400)) * rng.uniform(1, 2, 400)
+    x = np.concatenate([mids, near, mag, pos[i]])
+    return x * np.where(rng.integers(0, 2, x.size) == 1, 1.0, -1.0)
+
+
+def pin_round_bf16_bruteforce():
+    """bf16 rounding equals the brute-force nearest value (ties to an even
+    pattern), over ties, their neighbours, subnormals and overflow."""
+    rng = np.random.default_rng(11)
+    vals, _ = _bf16_table()
+    x = _round_samples(rng, vals)
+    x = x[np.abs(x) < 1e39]
+    got = oracle.round_to(x, mi.BF16)
+    want = _round_bf16_bruteforce(x)
+    assert np.array_equal(got, want), np.flatnonzero(got != want)[:5]
+
+
+def pin_round_f16_library():
+    """binary16 rounding equals numpy's float64 -> float16 conversion (IEEE
+    round to nearest even, done from the double directly)."""
+    rng = np.random.default_rng(12)
+    table = np.arange(1 << 16, dtype=np.uint16).view(np.float16).astype(np.float64)
+    table = np.unique(table[np.isfinite(table)])
+    x = _round_samples(rng, table)
+    x = x[np.abs(x) < 1e6]
+    got = oracle.round_to(x, mi.F16)
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).astype(np.float64)
+    assert np.array_equal(got, want), np.flatnonzero(got != want)[:5]
+
+
+def pin_round_closed_forms():
+    """Hand-worked cases: ties to even at 1 (bf16 spacing 2^-7, binary16 2^-10),
+    the largest finite values and the overflow tie, the smallest subnormals,
+    and f32 leaving values alone."""
+    e = np.exp2
+    cases = [
+        (mi.BF16, 1 + e(-8), 1.0), (mi.BF16, 1 + 3 * e(-8), 1 + e(-6)), (mi.BF16, -(1 + e(-8)), -1.0),
+        (mi.BF16, 1 + e(-8) + e(-30), 1 + e(-7)), (mi.BF16, 3.0 + e(-7), 3.0),
+        (mi.BF16, (2 - e(-7)) * e(127), (2 - e(-7)) * e(127)),
+        (mi.BF16, (2 - e(-8)) * e(127), np.inf), (mi.BF16, (2 - e(-8)) * e(127) - e(100), (2 - e(-7)) * e(127)),
+        (mi.BF16, e(-133), e(-133)), (mi.BF16, e(-134), 0.0), (mi.BF16, 3 * e(-134), e(-132)),
+        (mi.F16, 1 + e(-11), 1.0), (mi.F16, 1 + 3 * e(-11), 1 + e(-9)), (mi.F16, 65504.0, 65504.0),
+        (mi.F16, 65519.0, 65504.0), (mi.F16, 65520.0, np.inf), (mi.F16, -65520.0, -np.inf),
+        (mi.F16, e(-24), e(-24)), (mi.F16, e(-25), 0.0), (mi.F16, 3 * e(-25), e(-23)),
+        (mi.F16, 2049.0, 2048.0), (mi.F16, 2051.0, 2052.0),
+        (mi.F32, 1 + e(-40), 1 + e(-40)),
+    ]
+    for dt, v, want in cases:
+        got = float(oracle.round_to(np.array([v]), dt)[0])
+        assert got == want, (dt, v, got, want)
+
+
+def pin_round_idempotent_monotone():
+    """Rounding a rounded value changes nothing, and rounding keeps order."""
+    rng = np.random.default_rng(13)
+    x = np.sort(rng.standard_normal(5000) * np.exp2(rng.uniform(-20, 20, 5000)))
+    for dt in (mi.BF16, mi.F16):
+        r = oracle.round_to(x, dt)
+        assert np.array_equal(oracle.round_to(r, dt), r)
+        assert np.all(r[1:] >= r[:-1])
+
+
 # cheap pins first, so that a broken oracle is usually rejected within a second
 _SLOW = ("pin_onehot_x_probes_every_index", "pin_decode_all_half_and_bf16_patterns",
-         "pin_sampled_rows_real_shapes")
+         "pin_round_bf16_bruteforce", "pin_sampled_rows_real_shapes")
 ALL_PINS = ([v for k, v in sorted(globals().items())
              if k.startswith("pin_") and callable(v) and k not in _SLOW]
             + [globals()[k] for k in _SLOW])

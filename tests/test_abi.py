@@ -40,7 +40,7 @@ def test_library_exports_declared_symbol(name):
 
 
 def test_abi_version_and_status_strings():
-    assert qmd.abi_version() == 2
+    assert qmd.abi_version() == 3
     for code in (0, 1, 2, 3, 4):
         assert qmd.status_string(code).startswith("MOE_")
     assert "unknown" in qmd.status_string(99)
@@ -202,10 +202,10 @@ def _lw(**kw):
 
 
 def _layer(w=None, **kw):
-    a = dict(x=P, x_dt=MOE_BF16, resid=P, rdt=MOE_BF16, out=P, ws=P, ws_bytes=1 << 30)
+    a = dict(x=P, x_dt=MOE_BF16, resid=P, rdt=MOE_BF16, out=P, odt=MOE_F32, ws=P, ws_bytes=1 << 30)
     a.update(kw)
     w = w or _lw()
-    return lib.moe_decode_layer(ctypes.byref(w), a["x"], a["x_dt"], a["resid"], a["rdt"], a["out"],
+    return lib.moe_decode_layer(ctypes.byref(w), a["x"], a["x_dt"], a["resid"], a["rdt"], a["out"], a["odt"],
                                 None, None, None, a["ws"], a["ws_bytes"], None)
 
 
@@ -225,6 +225,9 @@ def test_layer_workspace_bytes():
     (dict(x=MIS), MOE_EINVAL),
     (dict(x_dt=6), MOE_EUNSUPPORTED),
     (dict(x_dt=MOE_F32), MOE_EUNSUPPORTED),                   # router dtype must match x
+    (dict(odt=3), MOE_EUNSUPPORTED),
+    (dict(out=P + 2), MOE_EINVAL),                            # fp32 out not 4-byte aligned
+    (dict(out=P + 1, odt=MOE_BF16), MOE_EINVAL),              # bf16 out not 2-byte aligned
     (dict(w=_lw(wr=None)), MOE_EINVAL),
     (dict(w=_lw(K=0)), MOE_EINVAL),
     (dict(w=_lw(K=33)), MOE_EINVAL),
@@ -244,10 +247,11 @@ def test_layer_rejects(case, want):
 
 
 def _tail(**kw):
-    a = dict(partial=P, T=1, K=8, D=2048, shared=None, S=0, gate=None, resid=P, rdt=MOE_BF16, out=P)
+    a = dict(partial=P, T=1, K=8, D=2048, shared=None, S=0, gate=None, resid=P, rdt=MOE_BF16, out=P,
+             odt=MOE_F32)
     a.update(kw)
     return lib.moe_decode_tail(a["partial"], a["T"], a["K"], a["D"], a["shared"], a["S"], a["gate"],
-                               a["resid"], a["rdt"], a["out"], None)
+                               a["resid"], a["rdt"], a["out"], a["odt"], None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -260,9 +264,57 @@ def _tail(**kw):
     (dict(shared=P), MOE_EINVAL),        # buffer without a count
     (dict(S=-1, shared=P), MOE_EINVAL),
     (dict(rdt=3), MOE_EUNSUPPORTED),
+    (dict(odt=-1), MOE_EUNSUPPORTED),
+    (dict(out=P + 2), MOE_EINVAL),
+    (dict(out=P + 1, odt=MOE_F16), MOE_EINVAL),
 ])
 def test_tail_rejects(kw, want):
     assert _tail(**kw) == want
+
+
+def _norm(**kw):
+    a = dict(weight=P, dt=MOE_BF16, eps=1e-6, normed=P, ndt=MOE_F32)
+    a.update(kw)
+    return qmd.CRMSNorm(a["weight"], a["dt"], a["eps"], a["normed"], a["ndt"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(weight=None), MOE_EINVAL),
+    (dict(normed=None), MOE_EINVAL),
+    (dict(dt=7), MOE_EUNSUPPORTED),
+    (dict(ndt=7), MOE_EUNSUPPORTED),
+    (dict(eps=-1.0), MOE_EINVAL),
+    (dict(eps=float("nan")), MOE_EINVAL),
+    (dict(eps=float("inf")), MOE_EINVAL),
+    (dict(weight=P + 1), MOE_EINVAL),                    # bf16 weight not 2-byte aligned
+    (dict(normed=P + 2), MOE_EINVAL),                    # fp32 normed not 4-byte aligned
+    (dict(normed=P + 1, ndt=MOE_BF16), MOE_EINVAL),
+])
+def test_rmsnorm_descriptor_rejected_by_every_entry_point(kw, want):
+    """The same checks of the RMSNorm descriptor in the separate call, the
+    folded three-call tail and the folded fused layer."""
+    n = _norm(**kw)
+    assert lib.moe_decode_rmsnorm(P, MOE_F32, 1, 2048, ctypes.byref(n), None) == want
+    assert lib.moe_decode_tail_rmsnorm(P, 1, 8, 2048, None, 0, None, P, MOE_BF16, P, MOE_F32,
+                                       ctypes.byref(n), P, 1 << 20, None) == want
+    w = _lw()
+    assert lib.moe_decode_layer_rmsnorm(ctypes.byref(w), P, MOE_BF16, P, MOE_BF16, P, MOE_F32,
+                                        ctypes.byref(n), None, None, None, P, 1 << 30, None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(y=None), MOE_EINVAL),
+    (dict(ydt=9), MOE_EUNSUPPORTED),
+    (dict(y=P + 1, ydt=MOE_BF16), MOE_EINVAL),
+    (dict(T=0), MOE_EINVAL),
+    (dict(T=33), MOE_EINVAL),
+    (dict(d=0), MOE_EINVAL),
+])
+def test_rmsnorm_rejects(kw, want):
+    a = dict(y=P, ydt=MOE_F32, T=1, d=2048)
+    a.update(kw)
+    n = _norm()
+    assert lib.moe_decode_rmsnorm(a["y"], a["ydt"], a["T"], a["d"], ctypes.byref(n), None) == want
 
 
 @pytest.mark.parametrize("data,nbytes,out,n,want", [

@@ -1,6 +1,7 @@
 """Activations outside fp16's normal range, through every path that stages act
-as fp16 before a 4-bit down projection (the fused kernel-B units and the
-multi-token kernels), against the oracle.
+as fp16 for a packed fp16 dot of the down projection (the fused kernel-B
+units, with 4-, 6- and 8-bit codes, and the multi-token kernels, 4-bit),
+against the oracle.
 
 The gate and up scales and biases are multiplied by 2^8 (act around 2.6e5,
 past fp16's largest finite value 65504) or by 2^-10 (act around 4e-6, where
@@ -73,6 +74,21 @@ def test_act_outside_fp16_range(path, T, log2f):
     else:
         gpu, _ = run_gpu_layer(cfg, w, x, resid)
     compare_layer(cfg, w, x, resid, gpu, f"act range 2^{log2f} {path} T={T}")
+
+
+@pytest.mark.parametrize("log2f", [8, -10], ids=["large", "tiny"])
+@pytest.mark.parametrize("bits_down", [6, 8])
+def test_act_outside_fp16_range_fused_6_8_bit_down(bits_down, log2f):
+    cfg = small_cfg(d_in=1024, d_ff=768, n_experts=8, top_k=4, bits_down=bits_down)
+    say(f"case act range 2^{log2f} fused {bits_down}-bit down")
+    w = scale_gate_up(mi.gen_layer_weights(cfg, 7, threads=4), log2f)
+    x, resid = margin_tokens(cfg, 7, w, 1)
+    resid = np.zeros_like(resid)
+    amax = check_range(cfg, w, x, log2f)
+    say(f"  oracle act max {amax:.3e}")
+    gpu, layer = run_gpu_layer(cfg, w, x, resid, fused=True)
+    assert not np.any(layer.fused_ws.cpu().numpy()[:4]), "error word set"
+    compare_layer(cfg, w, x, resid, gpu, f"act range 2^{log2f} fused {bits_down}-bit down")
 
 
 def test_act_outside_fp16_range_full_size_fused():

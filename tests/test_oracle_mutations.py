@@ -51,6 +51,13 @@ MUTATIONS = [
     ("rmsnorm eps outside the root", "double inv = 1.0 / sqrt(ms + eps);", "double inv = 1.0 / (sqrt(ms) + eps);"),
     ("rmsnorm weight dropped", "yt[i] * inv * load_val(weight, w_dt, (size_t)i);", "yt[i] * inv;"),
     ("rmsnorm weight reversed", "load_val(weight, w_dt, (size_t)i);", "load_val(weight, w_dt, (size_t)(d - 1 - i));"),
+    ("rounding truncates", "double r = rint(x / q) * q;", "double r = trunc(x / q) * q;"),
+    ("rounding ties away from zero", "double r = rint(x / q) * q;", "double r = round(x / q) * q;"),
+    ("rounding one significand bit short", "const double q = ldexp(1.0, e - p + 1);",
+     "const double q = ldexp(1.0, e - p + 2);"),
+    ("rounding without subnormals", "        if (e < emin)\n            e = emin;\n", ""),
+    ("rounding never overflows", "            r = copysign(INFINITY, x);", "            r = copysign(vmax, x);"),
+    ("bf16 rounded as binary16", "p = 8; emin = -126; emax = 127;", "p = 11; emin = -14; emax = 15;"),
     ("rmsnorm first token's mean for all", "const double *yt = y + (size_t)t * d;\n        double ss = 0.0;\n        for (int i = 0; i < d; ++i)\n            ss += yt[i] * yt[i];",
      "const double *yt = y + (size_t)t * d;\n        double ss = 0.0;\n        for (int i = 0; i < d; ++i)\n            ss += y[i] * y[i];"),
 ]
