@@ -53,7 +53,22 @@ __device__ __forceinline__ void row_block(const QM *mats, int64_t erow0, int r0,
     for (int c0 = 0; c0 < cpr; c0 += lr) {          // same trip count on every lane
         BlockRegs<BITS, NM, kNR> R;
         load_block<BITS, NM, kNR>(R, mats, erow0, r0, rstep, row_end, c0 + j, cpr);
-        if constexpr (MAXT == 1) {
+        if constexpr (MAXT == 1 && BITS == 4 && XT == MOE_BF16) {
+            // raw bf16 inputs for the packed bf16 dot (exact products)
+            XRaw<XT, CODES> xr;
+            load_x_raw<XT, CODES>(x_src, x_off + (int64_t)R.cc * CODES, xr);
+            uint32_t xw[16];
+            float xsum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t v = xr.v[i][k];
+                    xw[4 * i + k] = v;
+                    xsum += __uint_as_float(v << 16) + __uint_as_float(v & 0xFFFF0000u);
+                }
+            dot_block_q4_bf16<SB, NM, kNR>(R, xw, xsum, a1);
+        } else if constexpr (MAXT == 1) {
             float xv[CODES];
             load_x_chunk<XT, CODES>(x_src, x_off + (int64_t)R.cc * CODES, xv);
             dot_block<BITS, SB, NM, kNR>(R, xv, sum_n<CODES>(xv), a1);
@@ -213,6 +228,82 @@ __global__ __launch_bounds__(256) void down_kernel(FfnArgs a) {
     }
 }
 
+// Kernel B for one token with the packed fp16 dots (the arithmetic of the
+// fused layer's kernel-B units): the workgroup stages its slot's act row in
+// LDS as fp16, multiplied by the power of two fitted to the row's largest
+// magnitude (f16_stage_scale: exact, and the inverse joins the score), in
+// the layout the dots read (f16_stage_offset), then streams its rows: 4-bit
+// codes through dot_block_q4_f16, 6- and 8-bit codes through
+// dot_block_f16x16.
+template <int BITS, int SB>
+__global__ __launch_bounds__(kFfnThreads) void down_kernel_t1(FfnArgs a) {
+    using F = Fmt<BITS>;
+    constexpr int CODES = F::kCodes, NP = CODES / 2;
+    extern __shared__ __align__(16) char lds_h[];
+    __shared__ uint32_t s_max[kFfnThreads / kWave];
+    const int k = blockIdx.y;
+    const int e = a.ids[k];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int row0 = blockIdx.x * a.rows_per_wg;
+    const int row_end = min(row0 + a.rows_per_wg, a.d_in);
+    float *part = a.partial + (int64_t)k * a.d_in;
+    if (e < 0 || e >= a.E) {
+        for (int r = row0 + tid; r < row_end; r += kFfnThreads) part[r] = 0.f;
+        return;
+    }
+    const float *act = a.act + (int64_t)k * a.d_ff;
+    const int n = a.d_ff;
+    uint32_t mx = 0;                     // magnitudes order like their bit patterns
+    for (int i = tid; i < n; i += kFfnThreads) mx = max(mx, __float_as_uint(act[i]) & 0x7FFFFFFFu);
+    const float wm = wave_max(__uint_as_float(mx));
+    if (lane == 0) s_max[wave] = __float_as_uint(wm);
+    __syncthreads();
+    uint32_t m = 0;
+#pragma unroll
+    for (int w = 0; w < kFfnThreads / kWave; ++w) m = max(m, s_max[w]);
+    float inv;
+    const float cs = f16_stage_scale(m, inv);
+    for (int i = tid; i < n; i += kFfnThreads)
+        *reinterpret_cast<_Float16 *>(lds_h + f16_stage_offset<BITS>(i)) = (_Float16)(act[i] * inv);
+    __syncthreads();
+    const float sc = (a.scores ? a.scores[k] : 1.0f) * cs;      // exact: cs is a power of two
+    const int cpr = n / CODES;
+    const int lr = 1 << a.lr_shift, j = lane & (lr - 1), rsub = lane >> a.lr_shift, rpw = kWave >> a.lr_shift;
+    const QM mats[1] = {a.down};
+    const int64_t erow0 = (int64_t)e * a.d_in;
+    for (int rb = row0 + wave * rpw * kNR; rb < row_end; rb += 4 * rpw * kNR) {
+        const int r0 = rb + rsub;
+        float acc[1][kNR];
+#pragma unroll
+        for (int r = 0; r < kNR; ++r) acc[0][r] = 0.f;
+        for (int c0 = 0; c0 < cpr; c0 += lr) {          // same trip count on every lane
+            BlockRegs<BITS, 1, kNR> R;
+            load_block<BITS, 1, kNR>(R, mats, erow0, r0, rpw, row_end, c0 + j, cpr);
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(lds_h + R.cc * f16_chunk_bytes<BITS>());
+            uint32_t ap[NP];
+#pragma unroll
+            for (int i = 0; i < NP / 4; ++i) {
+                const u32x4 v = src[i];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) ap[4 * i + q] = v[q];
+            }
+            if constexpr (BITS == 4) dot_block_q4_f16<SB, 1, kNR>(R, ap, f16_pairs_sum<NP>(ap), acc);
+            else dot_block_f16x16<BITS, SB, 1, kNR>(R, ap, f16_pairs_sum<NP>(ap), acc);
+        }
+        with_width(__builtin_ctz(lr), [&](auto w) {
+#pragma unroll
+            for (int r = 0; r < kNR; ++r) acc[0][r] = group_sum_last<decltype(w)::value>(acc[0][r]);
+        });
+        if (j == lr - 1) {
+#pragma unroll
+            for (int r = 0; r < kNR; ++r) {
+                const int row = r0 + r * rpw;
+                if (row < row_end) part[row] = sc * acc[0][r];
+            }
+        }
+    }
+}
+
 // Small-batch bucketing: groups the (token, slot) pairs by expert with a
 // stable counting sort (pairs stay in ascending t*K + k order inside an
 // expert) and cuts each expert's list into work items of at most max_tok
@@ -360,7 +451,7 @@ static KernelFn pick_gate_up(int x_dt, bool multi) {
 
 template <int BITS, int SB>
 static KernelFn pick_down(bool multi) {
-    return multi ? down_kernel<BITS, SB, 8> : down_kernel<BITS, SB, 1>;
+    return multi ? down_kernel<BITS, SB, 8> : down_kernel_t1<BITS, SB>;
 }
 
 static KernelFn select_gate_up(int bits, int sb, int x_dt, bool multi) {
@@ -552,6 +643,11 @@ static moe_status launch_b(Plan &p) {
         if (!k) return MOE_EUNSUPPORTED;
         const moe_status st = geometry(p.a, p.maxt, p.a.d_ff, p.a.down.bits_, lds);
         if (st != MOE_OK) return st;
+        if (p.maxt == 1) {       // down_kernel_t1 stages act as fp16 chunks
+            const int bits = p.a.down.bits_;
+            lds = (size_t)(p.a.d_ff / codes_per_chunk(bits)) *
+                  (bits == 4 ? f16_chunk_bytes<4>() : f16_chunk_bytes<8>());
+        }
     }
     dim3 grid((p.a.d_in + p.a.rows_per_wg - 1) / p.a.rows_per_wg, p.n_items);
     hipLaunchKernelGGL(k, grid, dim3(kFfnThreads), lds, p.s, p.a);
