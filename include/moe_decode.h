@@ -153,10 +153,10 @@ moe_status moe_decode_workspace_status(const void *head, size_t head_bytes);
  * Arithmetic: fp32 sums throughout.  Kernel A with 4-bit codes and bf16 x
  * uses the packed bf16 dot (the code q as the exact bf16 128 + q, products
  * exact); other gate/up formats convert codes and inputs to fp32.  Kernel B
- * stages each act row as fp16 after an exact power-of-two scaling (one
- * token: fitted to the row's largest magnitude; several tokens: 2^8, or
- * fitted when that would overflow) and uses the packed fp16 dot (codes as
- * exact fp16 values).  The result stays within 2e-3 of its infinity norm.
+ * stages each act row as fp16 after an exact power-of-two scaling (2^8, or
+ * the factor fitted to the row's largest magnitude when 2^8 would overflow)
+ * and uses the packed fp16 dot (codes as exact fp16 values).  The result
+ * stays within 2e-3 of its infinity norm.
  * Arguments:
  *   x        [n_tokens][d_in], dtype x_dtype; d_in = gate->cols
  *   gate, up : stacks with rows = d_ff, cols = d_in; down: rows = d_in, cols = d_ff;
@@ -255,8 +255,7 @@ moe_status moe_decode_tail(const float *partial, int32_t n_tokens, int32_t top_k
  * (128 + q as exact bf16 pairs, one rounding per pair sum), and the down
  * projections take act staged as fp16 after an exact power-of-two scaling
  * (2^8, or a factor fitted to the slot's largest magnitude when that would
- * overflow; the single-token moe_decode_expert_ffn always fits it), with
- * fp32 sums throughout.  Both stay within 2e-3 of the result's infinity norm.
+ * overflow, as in moe_decode_expert_ffn), with fp32 sums throughout.  Both stay within 2e-3 of the result's infinity norm.
  * Workgroups hand results to each other through the workspace instead of
  * kernel boundaries, so the down-projection weights stream while the gate/up
  * projections run (the dependency mlxcel PR #276 "What changed" step 1

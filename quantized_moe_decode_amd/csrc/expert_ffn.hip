@@ -229,18 +229,22 @@ __global__ __launch_bounds__(256) void down_kernel(FfnArgs a) {
 }
 
 // Kernel B for one token with the packed fp16 dots (the arithmetic of the
-// fused layer's kernel-B units): the workgroup stages its slot's act row in
-// LDS as fp16, multiplied by the power of two fitted to the row's largest
-// magnitude (f16_stage_scale: exact, and the inverse joins the score), in
-// the layout the dots read (f16_stage_offset), then streams its rows: 4-bit
-// codes through dot_block_q4_f16, 6- and 8-bit codes through
-// dot_block_f16x16.
+// fused layer's kernel-B units): the workgroup issues the loads of its first
+// block of weights, stages its slot's act row in LDS as fp16 in the layout
+// the dots read (f16_stage_offset), each value times 2^8 (exact; the inverse
+// joins the score), and if some value would overflow fp16 that way (one
+// compare per value, flags exchanged over the staging's barrier) stages it
+// again with the power of two fitted to the row's largest magnitude
+// (f16_stage_scale).  Then it streams its rows: 4-bit codes through
+// dot_block_q4_f16, 6- and 8-bit codes through dot_block_f16x16.
 template <int BITS, int SB>
 __global__ __launch_bounds__(kFfnThreads) void down_kernel_t1(FfnArgs a) {
     using F = Fmt<BITS>;
     constexpr int CODES = F::kCodes, NP = CODES / 2;
+    constexpr int kWaves = kFfnThreads / kWave;
+    static_assert(kWaves == 4, "one flag word per wave, read as one 16-byte word");
     extern __shared__ __align__(16) char lds_h[];
-    __shared__ uint32_t s_max[kFfnThreads / kWave];
+    __shared__ __align__(16) uint32_t s_wave[2][kWaves];      // per wave: overflow flag, largest magnitude
     const int k = blockIdx.y;
     const int e = a.ids[k];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
@@ -253,32 +257,71 @@ __global__ __launch_bounds__(kFfnThreads) void down_kernel_t1(FfnArgs a) {
     }
     const float *act = a.act + (int64_t)k * a.d_ff;
     const int n = a.d_ff;
-    uint32_t mx = 0;                     // magnitudes order like their bit patterns
-    for (int i = tid; i < n; i += kFfnThreads) mx = max(mx, __float_as_uint(act[i]) & 0x7FFFFFFFu);
-    const float wm = wave_max(__uint_as_float(mx));
-    if (lane == 0) s_max[wave] = __float_as_uint(wm);
-    __syncthreads();
-    uint32_t m = 0;
-#pragma unroll
-    for (int w = 0; w < kFfnThreads / kWave; ++w) m = max(m, s_max[w]);
-    float inv;
-    const float cs = f16_stage_scale(m, inv);
-    for (int i = tid; i < n; i += kFfnThreads)
-        *reinterpret_cast<_Float16 *>(lds_h + f16_stage_offset<BITS>(i)) = (_Float16)(act[i] * inv);
-    __syncthreads();
-    const float sc = (a.scores ? a.scores[k] : 1.0f) * cs;      // exact: cs is a power of two
     const int cpr = n / CODES;
     const int lr = 1 << a.lr_shift, j = lane & (lr - 1), rsub = lane >> a.lr_shift, rpw = kWave >> a.lr_shift;
     const QM mats[1] = {a.down};
     const int64_t erow0 = (int64_t)e * a.d_in;
-    for (int rb = row0 + wave * rpw * kNR; rb < row_end; rb += 4 * rpw * kNR) {
+    const int rb_first = row0 + wave * rpw * kNR, rb_step = 4 * rpw * kNR;
+    // the first block's weights are on their way while act is staged
+    BlockRegs<BITS, 1, kNR> R;
+    if (rb_first < row_end) load_block<BITS, 1, kNR>(R, mats, erow0, rb_first + rsub, rpw, row_end, j, cpr);
+    auto place = [&](int i, float v) { *reinterpret_cast<_Float16 *>(lds_h + f16_stage_offset<BITS>(i)) = (_Float16)v; };
+    // fn(i, act[i]) for every i: 16-byte loads of four values (n is a multiple
+    // of 64), eight per thread in flight at a time
+    auto each_act = [&](auto fn) __attribute__((always_inline)) {
+        constexpr int kPer = 8;
+        const f32x4 *act4 = reinterpret_cast<const f32x4 *>(act);
+        const int n4 = n / 4;
+        for (int base = 0; base < n4; base += kPer * kFfnThreads) {
+            f32x4 v[kPer];
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+                const int i = base + u * kFfnThreads + tid;
+                v[u] = i < n4 ? act4[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+                const int i = base + u * kFfnThreads + tid;
+                if (i < n4) {
+                    fn(4 * i, v[u].x);
+                    fn(4 * i + 1, v[u].y);
+                    fn(4 * i + 2, v[u].z);
+                    fn(4 * i + 3, v[u].w);
+                }
+            }
+        }
+    };
+    bool over = false;
+    each_act([&](int i, float v) {
+        over |= !(__builtin_fabsf(v) < kActF16Overflow);      // NaN counts as over
+        place(i, v * kActF16Prescale);
+    });
+    if (lane == 0) s_wave[0][wave] = __ballot(over) ? 1u : 0u;
+    __syncthreads();
+    float cs = kActF16Postscale;
+    const u32x4 f = *reinterpret_cast<const u32x4 *>(s_wave[0]);
+    if (f.x | f.y | f.z | f.w) {
+        uint32_t mx = 0;                 // magnitudes order like their bit patterns
+        each_act([&](int, float v) { mx = max(mx, __float_as_uint(v) & 0x7FFFFFFFu); });
+        const float wm = wave_max(__uint_as_float(mx));
+        if (lane == 0) s_wave[1][wave] = __float_as_uint(wm);
+        __syncthreads();
+        uint32_t m = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) m = max(m, s_wave[1][w]);
+        float inv;
+        cs = f16_stage_scale(m, inv);
+        each_act([&](int i, float v) { place(i, v * inv); });
+        __syncthreads();
+    }
+    const float sc = (a.scores ? a.scores[k] : 1.0f) * cs;      // exact: cs is a power of two
+    for (int rb = rb_first; rb < row_end; rb += rb_step) {
         const int r0 = rb + rsub;
         float acc[1][kNR];
 #pragma unroll
         for (int r = 0; r < kNR; ++r) acc[0][r] = 0.f;
         for (int c0 = 0; c0 < cpr; c0 += lr) {          // same trip count on every lane
-            BlockRegs<BITS, 1, kNR> R;
-            load_block<BITS, 1, kNR>(R, mats, erow0, r0, rpw, row_end, c0 + j, cpr);
+            if (rb != rb_first || c0 != 0) load_block<BITS, 1, kNR>(R, mats, erow0, r0, rpw, row_end, c0 + j, cpr);
             const u32x4 *src = reinterpret_cast<const u32x4 *>(lds_h + R.cc * f16_chunk_bytes<BITS>());
             uint32_t ap[NP];
 #pragma unroll
