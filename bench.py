@@ -630,9 +630,7 @@ def rmsnorm_fold_cost(wl, meas, dev):
 
 def dtype_of(cfg) -> str:
     w = f"u{cfg.bits_gate_up}" if cfg.bits_gate_up == cfg.bits_down else f"u{cfg.bits_gate_up}/u{cfg.bits_down}"
-    acc = f"{cfg.x_dtype} x, f32 accumulation"
-    if cfg.bits_down == 4:
-        acc += ", act staged as f16 (power-of-two scaled) for the 4-bit down projection"
+    acc = f"{cfg.x_dtype} x, f32 accumulation, act staged as f16 (power-of-two scaled) for the down projection"
     return f"{w} weights ({cfg.sb_dtype} scale/bias), {acc}"
 
 
