@@ -123,6 +123,17 @@ __device__ __forceinline__ uint64_t ld_tagged(const uint64_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A tagged word read past the CU's L1 but from the XCD's L2: a relaxed
+// atomic load of workgroup scope, which this target serves from the L2 (the
+// sc0 policy) where the device-scope ld_tagged goes to memory.  Units of one
+// XCD that read the same words then share the lines their first reads
+// brought in.  Nothing guarantees that such a read sees a word written by
+// another workgroup, and a line cached before its words were written holds
+// older tags, so the pollers that use it return to ld_tagged every eighth try.
+__device__ __forceinline__ uint64_t ld_tagged_l2(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 __device__ __forceinline__ void raise_error(const LayerArgs &a) {
     __hip_atomic_fetch_or(ctr_at(a, kCtrErr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -200,13 +211,65 @@ __device__ __forceinline__ void gather_tagged(const LayerArgs &a, int n, const u
 // size) into LDS as fp16 chunks placed as the packed dots read them
 // (f16_stage_offset: 4-bit chunks of 32 values for dot_block_q4_f16, 6- and
 // 8-bit chunks of 16 for dot_block_f16x16), each value times
-// kActF16Prescale.  Returns the factor by which the dot products of the
+// kActF16Prescale; with L2 the sentinel and the words are read through the
+// XCD's L2 first (ld_tagged_l2).  Returns the factor by which the dot products of the
 // staged values are to be multiplied: kActF16Postscale, unless some value
 // would overflow fp16 that way (one compare per value; the waves' ballots
 // meet in LDS over the barrier that ends the gather).  Then every thread
 // reads its words again (all are present by then) and the vector is staged
 // with the factor fitted to its largest magnitude (f16_stage_scale).
-template <int BB>
+// wait_tagged and poll_batch with their reads through the L2 (L2:
+// ld_tagged_l2, and ld_tagged every eighth try) or from memory (ld_tagged).
+template <int SLEEP, bool L2>
+__device__ __forceinline__ float wait_tagged_via(const LayerArgs &a, const uint64_t *p, uint32_t tag) {
+    if constexpr (!L2) {
+        return wait_tagged<SLEEP>(a, p, tag);
+    } else {
+        for (uint32_t i = 0; i < kSpinLimit; ++i) {
+            const uint64_t w = (i & 7) != 7 ? ld_tagged_l2(p) : ld_tagged(p);
+            if ((uint32_t)(w >> 32) == tag) return __uint_as_float((uint32_t)w);
+            __builtin_amdgcn_s_sleep(SLEEP);
+        }
+        raise_error(a);
+        return 0.f;
+    }
+}
+
+template <int N, int SLEEP, bool L2, typename Addr>
+__device__ __forceinline__ void poll_batch_via(const LayerArgs &a, uint32_t tag, int cnt, Addr addr, float *v) {
+    if constexpr (!L2) {
+        poll_batch<N, SLEEP>(a, tag, cnt, addr, v);
+    } else {
+        uint64_t w[N];
+        const uint64_t ready = (uint64_t)tag << 32;
+#pragma unroll
+        for (int u = 0; u < N; ++u) w[u] = u < cnt ? ld_tagged_l2(addr(u)) : ready;
+        for (uint32_t spin = 0;; ++spin) {
+            bool all = true;
+#pragma unroll
+            for (int u = 0; u < N; ++u) all = all && (uint32_t)(w[u] >> 32) == tag;
+            if (all) break;
+            if (spin == kSpinLimit) {
+                raise_error(a);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(SLEEP);
+            if ((spin & 7) != 7) {
+#pragma unroll
+                for (int u = 0; u < N; ++u)
+                    if ((uint32_t)(w[u] >> 32) != tag) w[u] = ld_tagged_l2(addr(u));
+            } else {
+#pragma unroll
+                for (int u = 0; u < N; ++u)
+                    if ((uint32_t)(w[u] >> 32) != tag) w[u] = ld_tagged(addr(u));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < N; ++u) v[u] = (uint32_t)(w[u] >> 32) == tag ? __uint_as_float((uint32_t)w[u]) : 0.f;
+    }
+}
+
+template <int BB, bool L2>
 __device__ __forceinline__ float gather_act_f16(const LayerArgs &a, int n, const uint64_t *sentinel, uint32_t tag,
                                                 const uint64_t *act, char *lds) {
     static_assert(kLayerWaves == 4, "one flag word per wave, read as one 16-byte word");
@@ -216,14 +279,14 @@ __device__ __forceinline__ float gather_act_f16(const LayerArgs &a, int n, const
     auto place = [&](int i, float v) {
         *reinterpret_cast<_Float16 *>(lds + f16_stage_offset<BB>(i)) = (_Float16)v;
     };
-    if (t == 0) (void)wait_tagged<kActSleep>(a, sentinel, tag);
+    if (t == 0) (void)wait_tagged_via<kActSleep, L2>(a, sentinel, tag);
     __syncthreads();
     bool over = false;
     for (int base = 0; base < n; base += kGatherPer * nt) {
         const int left = n - base - t;
         const int cnt = left <= 0 ? 0 : min(kGatherPer, (left + nt - 1) / nt);
         float v[kGatherPer];
-        poll_batch<kGatherPer, kActSleep>(a, tag, cnt, [&](int u) { return act + base + u * nt + t; }, v);
+        poll_batch_via<kGatherPer, kActSleep, L2>(a, tag, cnt, [&](int u) { return act + base + u * nt + t; }, v);
 #pragma unroll
         for (int u = 0; u < kGatherPer; ++u)
             if (u < cnt) {
@@ -587,8 +650,9 @@ __device__ void tail_rmsnorm(const LayerArgs &a, uint32_t tag, int tile, int row
 }
 
 // Kernel B unit: rows [row0, row0 + b_tile) of d_in for slot `slot`.  The
-// unit of the last slot also runs the tail for those rows.
-template <int BB, int SB>
+// unit of the last slot also runs the tail for those rows.  L2: act read
+// through the XCD's L2 first (gather_act_f16).
+template <int BB, int SB, bool L2>
 __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int tile, int e, float *s_logits,
                              Selection *sel, float *xs) {
     constexpr int NR = kLayerNRB;
@@ -661,7 +725,7 @@ __device__ void layer_b_unit(const LayerArgs &a, uint32_t tag, int slot, int til
         if constexpr (BB == 4) {
             if (n_stage > 0) unpack_q4_f16<1, NR>(b0, pre);
         }
-        const float cs = gather_act_f16<BB>(a, n_act, sent, tag, act, reinterpret_cast<char *>(xs));
+        const float cs = gather_act_f16<BB, L2>(a, n_act, sent, tag, act, reinterpret_cast<char *>(xs));
         if (routed) score = sel->scores[slot];
         const float sc = score * cs;         // exact: cs is a power of two
         float acc[1][NR];
@@ -864,7 +928,13 @@ __global__ __launch_bounds__(kLayerThreads, 3) void layer_kernel(LayerArgs a) {
         if constexpr (ANR == kLayerNRA) layer_a_unit_single<BA, SB, XT>(a, tag, slot, tile, e, xs);
         else layer_a_unit_pipelined<BA, SB, XT>(a, tag, slot, tile, e, xs);
     }
-    else layer_b_unit<BB, SB>(a, tag, slot, tile, e, s_logits, &sel, xs);
+    // the kernels with pipelined kernel-A units (the large layers) read act
+    // through the L2 first: there each slot's act vector is read by a hundred
+    // or more kernel-B units, and sharing the lines within an XCD took the
+    // Qwen1.5- and dots.llm1-shaped layers from 31.1 / 36.5 to 30.6 / 35.7 us
+    // per launch, while the Qwen3-shaped layer (single-stage units, 768-word
+    // act vectors) measured 14.7 -> 14.9-15.2 us with it
+    else layer_b_unit<BB, SB, ANR == kLayerNRA2>(a, tag, slot, tile, e, s_logits, &sel, xs);
 }
 
 using LayerFn = void (*)(LayerArgs);
