@@ -80,10 +80,15 @@ typedef struct {
     moe_dtype sb_dtype;
 } moe_qmat;
 
-/* Limits checked by every call. */
+/* Limits checked by every call.  MOE_MAX_TOKENS: tokens per call of the
+ * fused layer and of moe_decode_expert_ffn, moe_decode_gate_up and
+ * moe_decode_down (and their variants). */
 #define MOE_MAX_TOKENS 32
 #define MOE_MAX_TOP_K 32
 #define MOE_MAX_EXPERTS 1024
+/* tokens per call of moe_decode_expert_ffn_grouped, and of moe_decode_route,
+ * moe_decode_tail and the RMSNorm calls that feed or follow it */
+#define MOE_MAX_GROUPED_TOKENS 1024
 #define MOE_MAX_DIM 8192
 
 /*
@@ -199,6 +204,31 @@ moe_status moe_decode_expert_ffn_noalloc(const void *x, moe_dtype x_dtype, int32
                                          float *act, float *partial, void *stream);
 
 size_t moe_decode_expert_ffn_noalloc_max_bytes(void);
+
+/*
+ * moe_decode_expert_ffn for larger batches and prefill, on the matrix cores:
+ * the same outputs (act and partial, same layouts, same zero rows for ids
+ * outside [0, n_experts)) for up to MOE_MAX_GROUPED_TOKENS tokens.  The
+ * (token, slot) pairs are grouped by expert into work items of up to 16, and
+ * each work item is a small GEMM per expert (meTile PR #30, the GB/s table
+ * and its reading: a GEMM path pays only from about 32 rows, i.e. batch or
+ * prefill, not single-token decode).  Supported: 4-bit gate, up and down
+ * codes with bf16 or fp16 scales, bf16 x; anything else is MOE_EUNSUPPORTED.
+ * Arithmetic: codes exact in the products (bf16 128 + q for gate/up, fp16 q
+ * for down), fp32 accumulation, the affine scale and bias applied per group
+ * of 64 inputs; act enters the down projection as fp16 after a power of two
+ * fitted to each pair's largest magnitude (exact, folded into the score).
+ * Within 2e-3 of the result's infinity norm.  workspace:
+ * moe_decode_expert_ffn_grouped_workspace_bytes() bytes, 16-byte aligned, no
+ * zeroing needed; asynchronous on `stream`.
+ */
+moe_status moe_decode_expert_ffn_grouped(const void *x, moe_dtype x_dtype, int32_t n_tokens,
+                                         const moe_qmat *gate, const moe_qmat *up, const moe_qmat *down,
+                                         const int32_t *expert_ids, const float *scores, int32_t top_k,
+                                         float *act, float *partial, void *workspace, size_t workspace_bytes,
+                                         void *stream);
+
+size_t moe_decode_expert_ffn_grouped_workspace_bytes(int32_t n_tokens, int32_t top_k, int32_t n_experts);
 
 /*
  * The two halves of moe_decode_expert_ffn as separate calls, for callers that

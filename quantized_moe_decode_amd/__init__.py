@@ -28,6 +28,7 @@ LIB_PATH = os.environ.get("MOE_DECODE_LIB") or os.path.join(PKG, "lib", "libmoe_
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ETIMEOUT = 0, 1, 2, 3, 4
 MOE_WORKSPACE_HEAD_BYTES = 4
 MOE_F32, MOE_F16, MOE_BF16 = 0, 1, 2
+MOE_MAX_TOKENS, MOE_MAX_GROUPED_TOKENS = 32, 1024     # tokens per call: the decode calls, the grouped call
 TORCH_DTYPE_CODE = {torch.float32: MOE_F32, torch.float16: MOE_F16, torch.bfloat16: MOE_BF16}
 
 
@@ -79,6 +80,11 @@ def _load_library():
     L.moe_decode_expert_ffn_noalloc.restype = i32
     L.moe_decode_expert_ffn_noalloc_max_bytes.argtypes = []
     L.moe_decode_expert_ffn_noalloc_max_bytes.restype = sz
+    L.moe_decode_expert_ffn_grouped.argtypes = [vp, i32, i32, ctypes.POINTER(CQMat), ctypes.POINTER(CQMat),
+                                                ctypes.POINTER(CQMat), vp, vp, i32, vp, vp, vp, sz, vp]
+    L.moe_decode_expert_ffn_grouped.restype = i32
+    L.moe_decode_expert_ffn_grouped_workspace_bytes.argtypes = [i32, i32, i32]
+    L.moe_decode_expert_ffn_grouped_workspace_bytes.restype = sz
     L.moe_decode_gate_up.argtypes = [vp, i32, i32, ctypes.POINTER(CQMat), ctypes.POINTER(CQMat),
                                      vp, i32, vp, vp, sz, vp]
     L.moe_decode_gate_up.restype = i32
@@ -217,6 +223,25 @@ def moe_decode_expert_ffn(x: torch.Tensor, gate: QuantStack, up: QuantStack, dow
                                    _ptr(act), _ptr(partial), _ptr(workspace), ws_bytes,
                                    _stream(stream))
     _check(st, "moe_decode_expert_ffn")
+
+
+def expert_ffn_grouped_workspace_bytes(n_tokens: int, top_k: int, n_experts: int) -> int:
+    return int(lib.moe_decode_expert_ffn_grouped_workspace_bytes(n_tokens, top_k, n_experts))
+
+
+def moe_decode_expert_ffn_grouped(x: torch.Tensor, gate: QuantStack, up: QuantStack, down: QuantStack,
+                                  expert_ids: torch.Tensor, scores: Optional[torch.Tensor],
+                                  act: torch.Tensor, partial: torch.Tensor, workspace: torch.Tensor,
+                                  stream=None) -> None:
+    """The grouped (matrix-core) expert FFN for many tokens: act [T, K, d_ff], partial [T, K, d_in]."""
+    T = x.shape[0]
+    K = expert_ids.shape[1]
+    g, u, d = gate.cstruct(), up.cstruct(), down.cstruct()
+    st = lib.moe_decode_expert_ffn_grouped(_ptr(x), _dt(x), T, ctypes.byref(g), ctypes.byref(u),
+                                           ctypes.byref(d), _ptr(expert_ids), _ptr(scores), K,
+                                           _ptr(act), _ptr(partial), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "moe_decode_expert_ffn_grouped")
 
 
 def moe_decode_expert_ffn_noalloc(x: torch.Tensor, gate: QuantStack, up: QuantStack, down: QuantStack,
@@ -369,6 +394,7 @@ __all__ = ["QuantStack", "DecodeLayer", "moe_decode_route", "moe_decode_expert_f
            "moe_decode_tail_rmsnorm", "moe_decode_layer_rmsnorm", "tail_rmsnorm_workspace_bytes",
            "moe_decode_rmsnorm",
            "moe_decode_layer", "layer_weights", "layer_workspace_bytes",
+           "moe_decode_expert_ffn_grouped", "expert_ffn_grouped_workspace_bytes",
            "moe_decode_gate_up", "moe_decode_down",
            "moe_decode_tail", "route_workspace_bytes", "expert_ffn_workspace_bytes",
            "moe_decode_read_probe", "read_probe_blocks", "workspace_status",

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmoe_decode.so")
 SOURCES = ["route.hip", "expert_ffn.hip", "tail.hip", "layer.hip", "layer_a4.hip", "layer_a6.hip",
-           "layer_a8.hip", "layer_a4p.hip", "layer_a6p.hip", "layer_a8p.hip", "probe.hip", "batch.hip"]
+           "layer_a8.hip", "layer_a4p.hip", "layer_a6p.hip", "layer_a8p.hip", "probe.hip", "batch.hip", "grouped.hip"]
 ARCH = "gfx950"
 
 

@@ -220,7 +220,7 @@ extern "C" moe_status moe_decode_route(const void *x, moe_dtype x_dtype_arg, int
               w_shared_gate_dtype = raw_enum(w_shared_gate_dtype_arg);
     if (!x || !w_router || !expert_ids || !scores || !workspace) return MOE_EINVAL;
     if ((w_shared_gate == nullptr) != (shared_gate == nullptr)) return MOE_EINVAL;
-    if (n_tokens < 1 || n_tokens > MOE_MAX_TOKENS) return MOE_EINVAL;
+    if (n_tokens < 1 || n_tokens > MOE_MAX_GROUPED_TOKENS) return MOE_EINVAL;
     if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS) return MOE_EINVAL;
     if (top_k < 1 || top_k > MOE_MAX_TOP_K || top_k > n_experts) return MOE_EINVAL;
     if (d_in < kGroup || d_in > MOE_MAX_DIM || d_in % kGroup) return MOE_EINVAL;

@@ -200,7 +200,7 @@ extern "C" moe_status moe_decode_tail(const float *partial, int32_t n_tokens, in
                                       const void *residual, moe_dtype residual_dtype_arg, void *out,
                                       moe_dtype out_dtype_arg, void *stream) {
     if (!partial || !residual || !out) return MOE_EINVAL;
-    if (n_tokens < 1 || n_tokens > MOE_MAX_TOKENS) return MOE_EINVAL;
+    if (n_tokens < 1 || n_tokens > MOE_MAX_GROUPED_TOKENS) return MOE_EINVAL;
     if (top_k < 1 || top_k > MOE_MAX_TOP_K) return MOE_EINVAL;
     if (d_in < kGroup || d_in > MOE_MAX_DIM || d_in % kGroup) return MOE_EINVAL;
     if (n_shared < 0 || n_shared > MOE_MAX_TOP_K) return MOE_EINVAL;
@@ -237,7 +237,7 @@ extern "C" moe_status moe_decode_tail_rmsnorm(const float *partial, int32_t n_to
                                               size_t workspace_bytes, void *stream) {
     const int residual_dtype = raw_enum(residual_dtype_arg), out_dtype = raw_enum(out_dtype_arg);
     if (!partial || !residual || !out || !norm || !workspace) return MOE_EINVAL;
-    if (n_tokens < 1 || n_tokens > MOE_MAX_TOKENS) return MOE_EINVAL;
+    if (n_tokens < 1 || n_tokens > MOE_MAX_GROUPED_TOKENS) return MOE_EINVAL;
     if (top_k < 1 || top_k > MOE_MAX_TOP_K) return MOE_EINVAL;
     if (d_in < kGroup || d_in > MOE_MAX_DIM || d_in % kGroup) return MOE_EINVAL;
     if (n_shared < 0 || n_shared > MOE_MAX_TOP_K) return MOE_EINVAL;
@@ -271,7 +271,7 @@ extern "C" moe_status moe_decode_rmsnorm(const void *y, moe_dtype y_dtype_arg, i
     if (!y) return MOE_EINVAL;
     const moe_status nst = check_rmsnorm(norm);
     if (nst != MOE_OK) return nst;
-    if (n_tokens < 1 || n_tokens > MOE_MAX_TOKENS || d < 1 || d > MOE_MAX_DIM) return MOE_EINVAL;
+    if (n_tokens < 1 || n_tokens > MOE_MAX_GROUPED_TOKENS || d < 1 || d > MOE_MAX_DIM) return MOE_EINVAL;
     if (!valid_dtype(y_dtype)) return MOE_EUNSUPPORTED;
     if (!aligned_elem(y, y_dtype)) return MOE_EINVAL;
     hipLaunchKernelGGL(rmsnorm_kernel, dim3(n_tokens), dim3(kTailNormThreads), 0, reinterpret_cast<hipStream_t>(stream),

@@ -12,8 +12,9 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (QuantStack, expert_ffn_workspace_bytes, layer_weights, layer_workspace_bytes,
-               moe_decode_expert_ffn, moe_decode_layer, moe_decode_layer_rmsnorm, moe_decode_rmsnorm,
+from . import (MOE_MAX_TOKENS, QuantStack, expert_ffn_grouped_workspace_bytes, expert_ffn_workspace_bytes,
+               layer_weights, layer_workspace_bytes, moe_decode_expert_ffn, moe_decode_expert_ffn_grouped,
+               moe_decode_layer, moe_decode_layer_rmsnorm, moe_decode_rmsnorm,
                moe_decode_route,
                moe_decode_tail, moe_decode_tail_rmsnorm, route_workspace_bytes,
                tail_rmsnorm_workspace_bytes)
@@ -38,13 +39,20 @@ def stack_to_device(stack, device) -> QuantStack:
 
 
 class DecodeLayer:
-    """A quantized MoE layer resident on one GPU, for a fixed number of tokens per step."""
+    """A quantized MoE layer resident on one GPU, for a fixed number of tokens per step.
+
+    The expert step uses moe_decode_expert_ffn up to MOE_MAX_TOKENS tokens and
+    the grouped matrix-core call (moe_decode_expert_ffn_grouped) above that;
+    grouped=True or False forces one of them."""
 
     def __init__(self, router: torch.Tensor, top_k: int, renormalize: bool,
                  gate: QuantStack, up: QuantStack, down: QuantStack,
                  shared: Optional[Sequence[QuantStack]] = None,
-                 shared_gate_w: Optional[torch.Tensor] = None, n_tokens: int = 1):
+                 shared_gate_w: Optional[torch.Tensor] = None, n_tokens: int = 1,
+                 grouped: Optional[bool] = None):
         dev = router.device
+        self.grouped = n_tokens > MOE_MAX_TOKENS if grouped is None else bool(grouped)
+        ws_bytes = expert_ffn_grouped_workspace_bytes if self.grouped else expert_ffn_workspace_bytes
         self.router, self.top_k, self.renormalize = router, top_k, renormalize
         self.gate, self.up, self.down = gate, up, down
         self.shared = tuple(shared) if shared is not None else None
@@ -60,7 +68,7 @@ class DecodeLayer:
         self.act = torch.zeros(T, top_k, d_ff, **f32)
         self.partial = torch.zeros(T, top_k, d_in, **f32)
         self.route_ws = torch.zeros(route_workspace_bytes(T, E), device=dev, dtype=torch.uint8)
-        nb = expert_ffn_workspace_bytes(T, top_k, E)
+        nb = ws_bytes(T, top_k, E)
         self.ffn_ws = torch.zeros(max(nb, 1), device=dev, dtype=torch.uint8) if nb else None
         if self.shared is not None:
             S = self.shared[0].n_experts
@@ -68,7 +76,7 @@ class DecodeLayer:
             self.shared_ids = torch.arange(S, device=dev, dtype=torch.int32).repeat(T, 1).contiguous()
             self.shared_act = torch.zeros(T, S, self.shared[0].rows, **f32)
             self.shared_partial = torch.zeros(T, S, d_in, **f32)
-            nb = expert_ffn_workspace_bytes(T, S, S)
+            nb = ws_bytes(T, S, S)
             self.shared_ws = torch.zeros(max(nb, 1), device=dev, dtype=torch.uint8) if nb else None
         else:
             self.n_shared = 0
@@ -96,12 +104,11 @@ class DecodeLayer:
                          self.route_ws, self.shared_gate_w, self.shared_gate, stream)
 
     def experts(self, x: torch.Tensor, stream=None) -> None:
-        moe_decode_expert_ffn(x, self.gate, self.up, self.down, self.ids, self.scores, self.act,
-                              self.partial, self.ffn_ws, stream)
+        ffn = moe_decode_expert_ffn_grouped if self.grouped else moe_decode_expert_ffn
+        ffn(x, self.gate, self.up, self.down, self.ids, self.scores, self.act, self.partial, self.ffn_ws, stream)
         if self.shared is not None:
             g, u, d = self.shared
-            moe_decode_expert_ffn(x, g, u, d, self.shared_ids, None, self.shared_act,
-                                  self.shared_partial, self.shared_ws, stream)
+            ffn(x, g, u, d, self.shared_ids, None, self.shared_act, self.shared_partial, self.shared_ws, stream)
 
     def tail(self, resid: torch.Tensor, out: torch.Tensor, stream=None) -> None:
         shared = self.shared_partial if self.shared is not None else None
@@ -235,7 +242,8 @@ class DecodeStep:
         return int(any(workspace_status(l.route_ws) != MOE_OK for l in self.layers))
 
 
-def layer_from_host(cfg, weights: dict, device, n_tokens: Optional[int] = None) -> DecodeLayer:
+def layer_from_host(cfg, weights: dict, device, n_tokens: Optional[int] = None,
+                    grouped: Optional[bool] = None) -> DecodeLayer:
     """Build a DecodeLayer from host weights in the generator's layout."""
     router = tensor_from_encoded(weights["router"], cfg.router_dtype, device)
     gate, up, down = (stack_to_device(weights[p], device) for p in ("gate", "up", "down"))
@@ -247,4 +255,4 @@ def layer_from_host(cfg, weights: dict, device, n_tokens: Optional[int] = None) 
     if cfg.shared_gate:
         wg = tensor_from_encoded(weights["shared_gate_w"], "bf16", device)
     return DecodeLayer(router, cfg.top_k, cfg.renormalize, gate, up, down, shared, wg,
-                       n_tokens if n_tokens is not None else cfg.n_tokens)
+                       n_tokens if n_tokens is not None else cfg.n_tokens, grouped)

@@ -83,7 +83,7 @@ def _route(**kw):
     (dict(ids=None), MOE_EINVAL),
     (dict(ws=None), MOE_EINVAL),
     (dict(T=0), MOE_EINVAL),
-    (dict(T=33), MOE_EINVAL),
+    (dict(T=1025), MOE_EINVAL),
     (dict(K=0), MOE_EINVAL),
     (dict(K=33), MOE_EINVAL),
     (dict(E=4, K=5), MOE_EINVAL),
@@ -145,6 +145,58 @@ def _ffn(gate=None, up=None, down=None, **kw):
 ])
 def test_expert_ffn_rejects(case, want):
     assert _ffn(**case) == want
+
+
+def _grouped(gate=None, up=None, down=None, **kw):
+    a = dict(x=P, x_dt=MOE_BF16, T=256, ids=P, scores=P, K=8, act=P, partial=P, ws=P, ws_bytes=1 << 20)
+    a.update(kw)
+    g, u = gate or _qm(), up or _qm()
+    d = down or _qm(rows=2048, cols=768)
+    return lib.moe_decode_expert_ffn_grouped(a["x"], a["x_dt"], a["T"], ctypes.byref(g), ctypes.byref(u),
+                                             ctypes.byref(d), a["ids"], a["scores"], a["K"], a["act"],
+                                             a["partial"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("case,want", [
+    (dict(x=None), MOE_EINVAL),
+    (dict(ids=None), MOE_EINVAL),
+    (dict(partial=None), MOE_EINVAL),
+    (dict(ws=None), MOE_EINVAL),
+    (dict(T=0), MOE_EINVAL),
+    (dict(T=1025), MOE_EINVAL),
+    (dict(K=0), MOE_EINVAL),
+    (dict(K=33), MOE_EINVAL),
+    (dict(x=MIS), MOE_EINVAL),
+    (dict(act=P + 4), MOE_EINVAL),
+    (dict(ws=P + 8), MOE_EINVAL),
+    (dict(ws_bytes=64), MOE_EINVAL),
+    (dict(x_dt=MOE_F16), MOE_EUNSUPPORTED),                    # bf16 x only
+    (dict(down=_qm(rows=2048, cols=768, bits=6)), MOE_EUNSUPPORTED),
+    (dict(gate=_qm(bits=8), up=_qm(bits=8)), MOE_EUNSUPPORTED),
+    (dict(down=_qm(rows=2048, cols=768, dt=MOE_F16)), MOE_EUNSUPPORTED),   # one scale dtype per call
+    (dict(up=_qm(rows=512)), MOE_EINVAL),
+    (dict(down=_qm(rows=1024, cols=768)), MOE_EINVAL),
+    (dict(down=_qm(rows=2048, cols=768, E=64)), MOE_EINVAL),
+    (dict(gate=_qm(E=2000), up=_qm(E=2000), down=_qm(rows=2048, cols=768, E=2000)), MOE_EINVAL),
+])
+def test_expert_ffn_grouped_rejects(case, want):
+    assert _grouped(**case) == want
+
+
+def test_token_limits_match_the_header():
+    h = open(HEADER).read()
+    for name in ("MOE_MAX_TOKENS", "MOE_MAX_GROUPED_TOKENS"):
+        assert int(re.search(rf"#define {name} (\d+)", h).group(1)) == getattr(qmd, name)
+
+
+def test_grouped_workspace_bytes():
+    """One count, then expert, first pair and pair count per work item (at most
+    ceil(pairs / 16) + n_experts + 1 items), then the pair list, in int32."""
+    f = qmd.expert_ffn_grouped_workspace_bytes
+    for T, K, E in [(1, 1, 1), (256, 8, 128), (1024, 32, 1024), (17, 3, 9)]:
+        mw = (T * K + 15) // 16 + E + 1
+        assert f(T, K, E) >= (1 + 3 * mw + T * K) * 4 and f(T, K, E) % 256 == 0
+    assert f(0, 8, 128) == 0 and f(4, 0, 128) == 0 and f(4, 8, 0) == 0
 
 
 def _gate_up(gate=None, up=None, **kw):
@@ -258,6 +310,7 @@ def _tail(**kw):
     (dict(partial=None), MOE_EINVAL),
     (dict(out=None), MOE_EINVAL),
     (dict(T=0), MOE_EINVAL),
+    (dict(T=1025), MOE_EINVAL),
     (dict(K=0), MOE_EINVAL),
     (dict(D=96), MOE_EINVAL),
     (dict(S=1), MOE_EINVAL),             # shared count without the buffer
@@ -307,7 +360,7 @@ def test_rmsnorm_descriptor_rejected_by_every_entry_point(kw, want):
     (dict(ydt=9), MOE_EUNSUPPORTED),
     (dict(y=P + 1, ydt=MOE_BF16), MOE_EINVAL),
     (dict(T=0), MOE_EINVAL),
-    (dict(T=33), MOE_EINVAL),
+    (dict(T=1025), MOE_EINVAL),
     (dict(d=0), MOE_EINVAL),
 ])
 def test_rmsnorm_rejects(kw, want):
