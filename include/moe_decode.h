@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOE_DECODE_ABI_VERSION 3
+#define MOE_DECODE_ABI_VERSION 4
 
 typedef enum {
     MOE_OK = 0,
@@ -117,7 +117,7 @@ typedef struct {
  *               workspace's error word is raised, stays raised, and
  *               moe_decode_workspace_status reports MOE_ETIMEOUT.  Calls that
  *               may run concurrently need separate workspaces.
- * Limits: 1 <= n_tokens <= 32, 1 <= top_k <= min(n_experts, 32),
+ * Limits: 1 <= n_tokens <= MOE_MAX_GROUPED_TOKENS, 1 <= top_k <= min(n_experts, 32),
  *         n_experts <= 1024, d_in a multiple of 64 and <= 8192.
  */
 moe_status moe_decode_route(const void *x, moe_dtype x_dtype, int32_t n_tokens, int32_t d_in,
@@ -209,18 +209,20 @@ size_t moe_decode_expert_ffn_noalloc_max_bytes(void);
  * moe_decode_expert_ffn for larger batches and prefill, on the matrix cores:
  * the same outputs (act and partial, same layouts, same zero rows for ids
  * outside [0, n_experts)) for up to MOE_MAX_GROUPED_TOKENS tokens.  The
- * (token, slot) pairs are grouped by expert into work items of up to 16, and
- * each work item is a small GEMM per expert (meTile PR #30, the GB/s table
- * and its reading: a GEMM path pays only from about 32 rows, i.e. batch or
- * prefill, not single-token decode).  Supported: 4-bit gate, up and down
- * codes with bf16 or fp16 scales, bf16 x; anything else is MOE_EUNSUPPORTED.
+ * (token, slot) pairs are grouped by expert into work items of up to 16, 32
+ * or 64 pairs, and each work item is a small GEMM per expert (meTile PR #30,
+ * the GB/s table and its reading: a GEMM path pays only from about 32 rows,
+ * i.e. batch or prefill, not single-token decode).  Supported: 4-bit gate,
+ * up and down codes with bf16 or fp16 scales, bf16 x; anything else is
+ * MOE_EUNSUPPORTED.  scores may be NULL (every pair weighted 1).
  * Arithmetic: codes exact in the products (bf16 128 + q for gate/up, fp16 q
  * for down), fp32 accumulation, the affine scale and bias applied per group
  * of 64 inputs; act enters the down projection as fp16 after a power of two
- * fitted to each pair's largest magnitude (exact, folded into the score).
- * Within 2e-3 of the result's infinity norm.  workspace:
- * moe_decode_expert_ffn_grouped_workspace_bytes() bytes, 16-byte aligned, no
- * zeroing needed; asynchronous on `stream`.
+ * fitted to the largest magnitude of each block of 128 of a pair's values
+ * (exact, undone per group).  Within 2e-3 of the result's infinity norm.
+ * workspace: moe_decode_expert_ffn_grouped_workspace_bytes() bytes (the work
+ * lists and the fp16 copy of act), 16-byte aligned, no zeroing needed;
+ * asynchronous on `stream`.
  */
 moe_status moe_decode_expert_ffn_grouped(const void *x, moe_dtype x_dtype, int32_t n_tokens,
                                          const moe_qmat *gate, const moe_qmat *up, const moe_qmat *down,
@@ -228,7 +230,9 @@ moe_status moe_decode_expert_ffn_grouped(const void *x, moe_dtype x_dtype, int32
                                          float *act, float *partial, void *workspace, size_t workspace_bytes,
                                          void *stream);
 
-size_t moe_decode_expert_ffn_grouped_workspace_bytes(int32_t n_tokens, int32_t top_k, int32_t n_experts);
+/* d_ff: rows of gate (columns of down).  0 for a size below 1. */
+size_t moe_decode_expert_ffn_grouped_workspace_bytes(int32_t n_tokens, int32_t top_k, int32_t n_experts,
+                                                     int32_t d_ff);
 
 /*
  * The two halves of moe_decode_expert_ffn as separate calls, for callers that

@@ -83,7 +83,7 @@ def _load_library():
     L.moe_decode_expert_ffn_grouped.argtypes = [vp, i32, i32, ctypes.POINTER(CQMat), ctypes.POINTER(CQMat),
                                                 ctypes.POINTER(CQMat), vp, vp, i32, vp, vp, vp, sz, vp]
     L.moe_decode_expert_ffn_grouped.restype = i32
-    L.moe_decode_expert_ffn_grouped_workspace_bytes.argtypes = [i32, i32, i32]
+    L.moe_decode_expert_ffn_grouped_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.moe_decode_expert_ffn_grouped_workspace_bytes.restype = sz
     L.moe_decode_gate_up.argtypes = [vp, i32, i32, ctypes.POINTER(CQMat), ctypes.POINTER(CQMat),
                                      vp, i32, vp, vp, sz, vp]
@@ -225,8 +225,8 @@ def moe_decode_expert_ffn(x: torch.Tensor, gate: QuantStack, up: QuantStack, dow
     _check(st, "moe_decode_expert_ffn")
 
 
-def expert_ffn_grouped_workspace_bytes(n_tokens: int, top_k: int, n_experts: int) -> int:
-    return int(lib.moe_decode_expert_ffn_grouped_workspace_bytes(n_tokens, top_k, n_experts))
+def expert_ffn_grouped_workspace_bytes(n_tokens: int, top_k: int, n_experts: int, d_ff: int) -> int:
+    return int(lib.moe_decode_expert_ffn_grouped_workspace_bytes(n_tokens, top_k, n_experts, d_ff))
 
 
 def moe_decode_expert_ffn_grouped(x: torch.Tensor, gate: QuantStack, up: QuantStack, down: QuantStack,

@@ -7,11 +7,21 @@
 // With tens of tokens per expert the same work becomes a small GEMM per
 // expert, and the point at which a GEMM path starts to beat the GEMV path is
 // the one meTile PR #30 measures (its GB/s table: parity at 8 rows, a win
-// only from 32 rows, batch or prefill).  Here a work item is one expert and up
-// to 16 of its (token, slot) pairs; a workgroup takes 64 weight rows of it,
-// each wave 16 rows x 16 tokens, and multiplies with v_mfma_f32_16x16x32
-// (lane l holds A[l % 16][8 (l / 16) + i], B[8 (l / 16) + i][l % 16] for
-// i = 0..7, and D[4 (l / 16) + r][l % 16] for r = 0..3).
+// only from 32 rows, batch or prefill).
+//
+// Work decomposition.  The (token, slot) pairs are grouped by expert and each
+// expert's list is cut into work items of up to NT = 16 NB pairs (NB = 1, 2
+// or 4, chosen from the average number of pairs per expert).  A workgroup of
+// eight waves takes one work item and 128 weight rows of it; each wave owns
+// 16 rows and multiplies them with every 16-pair block of the item using
+// v_mfma_f32_16x16x32 (lane l holds A[l % 16][8 (l / 16) + i],
+// B[8 (l / 16) + i][l % 16] for i = 0..7, and D[4 (l / 16) + r][l % 16] for
+// r = 0..3), so a weight row is read once per work item whatever NB is.  The
+// item's inputs (x for kernel A, act for kernel B) and the row block's scales
+// and biases are staged in LDS four groups of 64 inputs at a time, double
+// buffered, and shared by the eight waves; each lane keeps the code words of
+// the next four groups in flight.  Workgroups are placed so that the row
+// blocks of one work item run on one XCD and share its L2 copy of the inputs.
 //
 // Codes stay exact: kernel A turns a 4-bit code q into the bf16 number 128 + q
 // (nibble_pairs), kernel B into the fp16 number q (1024 + q, minus 1024 in a
@@ -19,12 +29,16 @@
 // the affine scale and bias are applied per group of 64 inputs afterwards:
 //   sum_i (s q_i + b) x_i = s * sum_i (128 + q_i) x_i + (b - 128 s) * sum_i x_i.
 // A lane's 8 values of a k-step are one code word; its nibble pairs come in
-// the order (q0, q4, q1, q5, q2, q6, q3, q7), and the inputs are permuted to
-// the same order (pair_words), which leaves the dot products unchanged.  Each
-// k-step stays inside one group: lane group g takes code words 2g and 2g + 1
-// of the group, one per k-step.  act enters kernel B as fp16 multiplied by a
-// power of two fitted to each token's largest magnitude (f16_stage_scale);
-// the inverse joins the score.
+// the order (q0, q4, q1, q5, q2, q6, q3, q7) and the inputs are permuted to
+// the same order (pair_inputs), which leaves the dot products unchanged.  Each
+// k-step stays inside one group, and the four lane groups take four different
+// words of it per k-step (spread_code_pair).
+//
+// Kernel A writes act in fp32 (the call's output) and, for kernel B, in fp16
+// multiplied by a power of two fitted to the largest magnitude of each pair's
+// 128 values in the workgroup's row block (f16_stage_scale); the factor's
+// inverse is kept per (pair, block) and applied to each group's dot products
+// in kernel B (exact: a power of two).
 #include <hip/hip_runtime.h>
 
 #include "api.hpp"
@@ -33,97 +47,180 @@
 
 namespace moe {
 
-constexpr int kGrpTok = 16;          // pairs per work item (the MFMA's N)
-constexpr int kGrpRows = 64;         // weight rows per workgroup: 4 waves x 16
-constexpr int kGrpThreads = 256;
-constexpr int kGrpDepth = 4;         // groups of code words in flight per lane
-constexpr int kGrpActChunk = 512;    // act inputs staged in LDS at a time (kernel B)
-constexpr int kGrpBucketThreads = 1024;
+constexpr int kGW = 8;                           // waves per workgroup
+constexpr int kGThreads = kGW * kWave;           // 512
+constexpr int kGRows = kGW * 16;                 // weight rows per workgroup (also the act16 block)
+constexpr int kGChunkGroups = 4;                 // groups of 64 inputs per staged chunk
+constexpr int kGChunk = kGChunkGroups * kGroup;  // 256 inputs
+constexpr int kGPad = kGChunk + 8;               // 16-bit values per staged token row
+constexpr int kGMinTok = 16;                     // smallest work item tile (sizes the workspace)
+constexpr int kGBucketThreads = 1024;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct GroupedArgs {
-    const void *x;                   // [T][d_in] bf16
-    int T, K, E, d_in, d_ff;
+    const uint16_t *x;               // [T][d_in] bf16
+    int T, K, E, d_in, d_ff, n_blk;  // n_blk = ceil(d_ff / 128)
     QM gate, up, down;
-    const int32_t *ids;
     const float *scores;
     float *act;                      // [T*K][d_ff]
     float *partial;                  // [T*K][d_in]
+    uint16_t *act16;                 // [T*K][d_ff] fp16 bits, scaled per (pair, block)
+    float *act_cs;                   // [T*K][n_blk] the factor that undoes the scaling
     const int32_t *n_work;
     const int32_t *work_expert;      // [max_work]: expert, or -1 for the out-of-range ids
     const int32_t *work_begin;       // [max_work]: first index into pair_list
-    const int32_t *work_count;       // [max_work]: pairs (1..16)
+    const int32_t *work_count;       // [max_work]: pairs (1..NT)
     const int32_t *pair_list;        // [T*K] pair indices t*K + k, grouped by expert
+    int row_blocks;                  // workgroups per work item
 };
 
-// Pairs (v[8k+p], v[8k+p+4]) of 8 consecutive 16-bit inputs held as 4 words:
-// the order nibble_pairs gives the codes.
-__device__ __forceinline__ void pair_inputs(const u32x4 &w, uint32_t (&o)[4]) {
+// Pairs (v[p], v[p+4]) of 8 consecutive 16-bit inputs held as 4 words: the
+// order nibble_pairs gives the codes.
+__device__ __forceinline__ void pair_inputs(const uint32_t (&w)[4], uint32_t (&o)[4]) {
     o[0] = __builtin_amdgcn_perm(w[2], w[0], 0x05040100u);
     o[1] = __builtin_amdgcn_perm(w[2], w[0], 0x07060302u);
     o[2] = __builtin_amdgcn_perm(w[3], w[1], 0x05040100u);
     o[3] = __builtin_amdgcn_perm(w[3], w[1], 0x07060302u);
 }
 
-// Sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (every lane gets the same bits).
-__device__ __forceinline__ float sum_lane_groups(float v) {
+__device__ __forceinline__ void words_of(const u32x4 &v, uint32_t (&w)[4]) {
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+}
+
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48.
+__device__ __forceinline__ float max_lane_groups(float v) {
     float r0, r1;
     swap_across<4>(v, v, r0, r1);
-    v = r0 + r1;
+    v = fmaxf(r0, r1);
     swap_across<5>(v, v, r0, r1);
-    return r0 + r1;
+    return fmaxf(r0, r1);
+}
+
+// Code words of two groups G and G + 1 of a weight row: one 16-byte load
+// per lane gives lane group g words 4 (g & 1) .. 4 (g & 1) + 3 of group
+// G + (g >> 1) (a group past the row's end is clamped to the last one; its
+// words are never used), and two swaps across the wave halves leave every lane
+// with words w[0], w[1] of group G and w[2], w[3] of group G + 1: word
+// 4 (g & 1) + 2 (g >> 1) + s of the group for k-step s (code_word_input
+// gives the inputs of that word).  Each load instruction reads 64 contiguous
+// bytes of each of the wave's 16 rows.
+__device__ __forceinline__ const u32x4 *code_pair_addr(const uint32_t *row, int G, int n_grp, int g) {
+    return reinterpret_cast<const u32x4 *>(row + min(G + (g >> 1), n_grp - 1) * 8 + 4 * (g & 1));
+}
+
+__device__ __forceinline__ void spread_code_pair(const u32x4 &v, uint32_t (&w)[4]) {
+    // v_permlane32_swap: lanes 32..63 of the first operand trade places with
+    // lanes 0..31 of the second
+    const auto r02 = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+    const auto r13 = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+    w[0] = r02[0];
+    w[2] = r02[1];
+    w[1] = r13[0];
+    w[3] = r13[1];
+}
+
+// Offset (in inputs) within a group of the 8 inputs lane group g multiplies
+// in k-step 0 (k-step 1: the next 8).
+__device__ __forceinline__ int code_word_input(int g) { return 32 * (g & 1) + 16 * (g >> 1); }
+
+// Sum of 8 bf16 (BF16) or fp16 values held as 4 words: products by one are
+// exact, the sums are fp32.
+template <bool BF16>
+__device__ __forceinline__ float sum8(const uint32_t (&w)[4]) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (BF16) {
+            const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]), one, s, false);
+        } else {
+            const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+            s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w[i]), one, s, false);
+        }
+    }
+    return s;
+}
+
+// Workgroup -> (work item, row block): the row blocks of one item are eight
+// linear workgroup indices apart, so they share an XCD (workgroups are
+// dealt to the eight XCDs in turn).
+__device__ __forceinline__ void item_and_block(int row_blocks, int &w, int &rb) {
+    const int b = blockIdx.x, lane8 = b & 7, q = b >> 3;
+    rb = q % row_blocks;
+    w = (q / row_blocks) * 8 + lane8;
 }
 
 // ------------------------------------------------------------------ bucketing
 // One workgroup: the (token, slot) pairs grouped by expert (bucket E collects
-// the ids outside [0, E)), each bucket cut into work items of at most
-// kGrpTok pairs.  The order of pairs inside a bucket does not matter: every
-// pair's results depend only on its own inputs.
-__global__ __launch_bounds__(kGrpBucketThreads) void grouped_bucket_kernel(const int32_t *ids, int n_pairs, int E,
-                                                                          int32_t *n_work, int32_t *work_expert,
-                                                                          int32_t *work_begin, int32_t *work_count,
-                                                                          int32_t *pair_list) {
-    __shared__ int cnt[MOE_MAX_EXPERTS + 1], base[MOE_MAX_EXPERTS + 1], tiles[MOE_MAX_EXPERTS + 1];
-    __shared__ int s_total[2];
-    const int tid = threadIdx.x, nb = E + 1;
-    for (int b = tid; b < nb; b += kGrpBucketThreads) cnt[b] = 0;
+// the ids outside [0, E)), each bucket cut into work items of at most nt
+// pairs.  The order of pairs inside a bucket does not matter: every pair's
+// results depend only on its own inputs.
+__global__ __launch_bounds__(kGBucketThreads) void grouped_bucket_kernel(const int32_t *ids, int n_pairs, int E,
+                                                                        int nt, int32_t *n_work,
+                                                                        int32_t *work_expert, int32_t *work_begin,
+                                                                        int32_t *work_count, int32_t *pair_list) {
+    constexpr int kWaves = kGBucketThreads / kWave;
+    __shared__ int cnt[2 * kGBucketThreads], base[2 * kGBucketThreads], tiles[2 * kGBucketThreads];
+    __shared__ int s_wp[kWaves], s_wt[kWaves];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, nb = E + 1;
+    cnt[2 * tid] = 0;
+    cnt[2 * tid + 1] = 0;
     __syncthreads();
-    for (int p = tid; p < n_pairs; p += kGrpBucketThreads) {
+    for (int p = tid; p < n_pairs; p += kGBucketThreads) {
         const int e = ids[p];
         atomicAdd(&cnt[e >= 0 && e < E ? e : E], 1);
     }
     __syncthreads();
-    if (tid == 0) {                  // exclusive scans of pair and work-item counts (E + 1 <= 1025 entries)
-        int pb = 0, tb = 0;
-        for (int b = 0; b < nb; ++b) {
-            base[b] = pb;
-            tiles[b] = tb;
-            pb += cnt[b];
-            tb += (cnt[b] + kGrpTok - 1) / kGrpTok;
+    // exclusive scans of the pair and work-item counts: thread t owns buckets
+    // 2t and 2t + 1 (nb <= 1025 <= 2048), wave prefix sums, then the waves'
+    const int c0 = cnt[2 * tid], c1 = cnt[2 * tid + 1];
+    const int t0 = (c0 + nt - 1) / nt, t1 = (c1 + nt - 1) / nt;
+    int ip = c0 + c1, it = t0 + t1;                        // inclusive within the wave
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int up = __shfl_up(ip, d), ut = __shfl_up(it, d);
+        if (lane >= d) {
+            ip += up;
+            it += ut;
         }
-        s_total[0] = tb;
+    }
+    if (lane == kWave - 1) {
+        s_wp[wave] = ip;
+        s_wt[wave] = it;
     }
     __syncthreads();
-    for (int b = tid; b < nb; b += kGrpBucketThreads) {
+    int op = 0, ot = 0;
+    for (int w = 0; w < wave; ++w) {
+        op += s_wp[w];
+        ot += s_wt[w];
+    }
+    const int ep = op + ip - (c0 + c1), et = ot + it - (t0 + t1);   // exclusive
+    base[2 * tid] = ep;
+    base[2 * tid + 1] = ep + c0;
+    tiles[2 * tid] = et;
+    tiles[2 * tid + 1] = et + t0;
+    if (tid == kGBucketThreads - 1) *n_work = ot + it;
+    __syncthreads();
+    for (int b = tid; b < nb; b += kGBucketThreads) {
         const int n = cnt[b];
-        for (int i = 0; i * kGrpTok < n; ++i) {
+        for (int i = 0; i * nt < n; ++i) {
             const int w = tiles[b] + i;
             work_expert[w] = b < E ? b : -1;
-            work_begin[w] = base[b] + i * kGrpTok;
-            work_count[w] = min(kGrpTok, n - i * kGrpTok);
+            work_begin[w] = base[b] + i * nt;
+            work_count[w] = min(nt, n - i * nt);
         }
-        cnt[b] = 0;                  // reused as the placement cursor
     }
     __syncthreads();
-    for (int p = tid; p < n_pairs; p += kGrpBucketThreads) {
+    for (int b = tid; b < nb; b += kGBucketThreads) cnt[b] = 0;   // reused as the placement cursor
+    __syncthreads();
+    for (int p = tid; p < n_pairs; p += kGBucketThreads) {
         const int e = ids[p];
         const int b = e >= 0 && e < E ? e : E;
         pair_list[base[b] + atomicAdd(&cnt[b], 1)] = p;
     }
-    if (tid == 0) *n_work = s_total[0];
 }
 
 // Zero rows [row0, row_end) of the item's pairs in out ([pairs][n]).
@@ -131,215 +228,430 @@ __device__ __forceinline__ void zero_rows(float *out, int n, const GroupedArgs &
                                           int row_end) {
     for (int i = 0; i < count; ++i) {
         float *o = out + (int64_t)a.pair_list[begin + i] * n;
-        for (int r = row0 + (int)threadIdx.x; r < row_end; r += kGrpThreads) o[r] = 0.f;
+        for (int r = row0 + (int)threadIdx.x; r < row_end; r += kGThreads) o[r] = 0.f;
     }
 }
 
+// ------------------------------------------------------------ input staging
+// The item's NT 16-bit input rows (x rows of the pairs' tokens, or the pairs'
+// act16 rows), kGChunk values at a time: thread i loads 16 bytes (piece
+// i % 32) of slots i / 32 + 16 r, r < NB; slots past the item's count and
+// pieces past the row's end stage zeros.  Each 8-value piece is one lane's
+// k-step operand and is stored already in the codes' pair order
+// (pair_inputs), with the per-group sums beside the rows.
+template <int NB>
+struct InStage {
+    u32x4 v[NB];
+    bool ok[NB];
+};
+
+// row[r]: element offset of the slot's row in src (a valid row for an empty
+// slot: the load always happens, an address clamped into range, and its value
+// is replaced by zeros when the slot is empty or the piece lies past n.  No
+// load sits behind a branch, so the wait counts stay exact and the code word
+// ring stays in flight across the chunk's end).
+template <int NB>
+__device__ __forceinline__ void in_load(InStage<NB> &st, const uint16_t *src, const int64_t (&row)[NB],
+                                        const bool (&live)[NB], int k0, int n) {
+    const int c = 8 * (threadIdx.x & 31);
+    const bool in_range = k0 + c < n;
+    const int kc = in_range ? k0 + c : n - 8;
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+        st.v[r] = *reinterpret_cast<const u32x4 *>(src + row[r] + kc);
+        st.ok[r] = live[r] && in_range;
+    }
+}
+
+// buf: [NT][kGPad] 16-bit values; sums: [kGChunkGroups][NT] fp32.
+template <int NB, bool BF16>
+__device__ __forceinline__ void in_store(const InStage<NB> &st, uint16_t *buf, float *sums) {
+    const int p = threadIdx.x & 31, t0 = threadIdx.x >> 5;
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+        const int t = t0 + 16 * r;
+        uint32_t w[4], wp[4];
+        words_of(st.v[r], w);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = st.ok[r] ? w[i] : 0u;
+        pair_inputs(w, wp);
+        *reinterpret_cast<u32x4 *>(buf + t * kGPad + 8 * p) = u32x4{wp[0], wp[1], wp[2], wp[3]};
+        float s = sum8<BF16>(w);
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+        if ((p & 7) == 0) sums[(p >> 3) * (16 * NB) + t] = s;
+    }
+}
+
+// Maximum over the 16 lanes of each DPP row (lanes 16 g .. 16 g + 15); the
+// result is valid in the row's last lane.
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmax_dpp<0x111, 0xf>(v);   // row_shr:1
+    v = fmax_dpp<0x112, 0xf>(v);   // row_shr:2
+    v = fmax_dpp<0x114, 0xf>(v);   // row_shr:4
+    return fmax_dpp<0x118, 0xf>(v);   // row_shr:8
+}
+
 // ------------------------------------------------------------------ kernel A
-// act[pair][r] = silu(g_r) u_r for the item's pairs and rows [64 bx, 64 bx + 64).
-template <int SB>
-__global__ __launch_bounds__(kGrpThreads) void gate_up_grouped(GroupedArgs a) {
-    const int w = blockIdx.y;
+// act[pair][r] = silu(g_r) u_r for the item's pairs and the workgroup's 128
+// rows; act16 and act_cs as described at the top.  The inputs are the MFMA's
+// A operand and the codes its B operand, so lane (j, g) of wave w ends with
+// D[4 g + r][j]: pairs 16 n + 4 g + r of weight row 16 w + j, and needs the
+// scales of that one row.
+template <int SB, int NB>
+__global__ __launch_bounds__(kGThreads) void gate_up_grouped(GroupedArgs a) {
+    constexpr int NT = 16 * NB;
+    __shared__ __align__(16) uint16_t s_x[2][NT * kGPad];
+    __shared__ __align__(16) float s_sb[2][kGChunkGroups * kGRows * 4];      // [group][row][sg, cg, su, cu]
+    __shared__ __align__(16) float s_xs[2][kGChunkGroups * NT];             // [group][slot]
+    __shared__ float s_max[kGW][NT];
+    __shared__ float s_inv[NT];
+    __shared__ int s_pair[NT];
+    int w, rb;
+    item_and_block(a.row_blocks, w, rb);
     if (w >= *a.n_work) return;
     const int e = a.work_expert[w], begin = a.work_begin[w], count = a.work_count[w];
-    const int row0 = blockIdx.x * kGrpRows;
+    const int row0 = rb * kGRows;
     if (e < 0) {
-        zero_rows(a.act, a.d_ff, a, begin, count, row0, min(row0 + kGrpRows, a.d_ff));
+        zero_rows(a.act, a.d_ff, a, begin, count, row0, min(row0 + kGRows, a.d_ff));
         return;
     }
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int g = lane >> 4, j = lane & 15;
-    const int rw = row0 + wave * 16;                      // the wave's first row
-    const int ra = min(rw + j, a.d_ff - 1);               // the lane's A row (clamped; results masked)
-    const int pair_j = a.pair_list[begin + (j < count ? j : 0)];
-    const uint16_t *xr = reinterpret_cast<const uint16_t *>(a.x) + (int64_t)(pair_j / a.K) * a.d_in + 16 * g;
+    const int n_grp = a.d_in / kGroup, n_chunk = (n_grp + kGChunkGroups - 1) / kGChunkGroups;
     const int64_t erow = (int64_t)e * a.d_ff;
-    const uint32_t *qg = a.gate.q + (erow + ra) * a.gate.wpr + 2 * g;
-    const uint32_t *qu = a.up.q + (erow + ra) * a.up.wpr + 2 * g;
-    // the lane's D rows rw + 4 g + r: their scales and biases per group
-    int64_t srow[4];
+    if (tid < NT) s_pair[tid] = tid < count ? a.pair_list[begin + tid] : -1;
+    // staging roles: x rows of the slots this thread loads; scale row and kind
+    int64_t xrow[NB];
+    bool xlive[NB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) srow[r] = (erow + min(rw + 4 * g + r, a.d_ff - 1)) * a.gate.gpr;
-    const int n_grp = a.d_in / kGroup;
-    f32x4 acc_g = {0.f, 0.f, 0.f, 0.f}, acc_u = {0.f, 0.f, 0.f, 0.f};
-    u32x2 wg[kGrpDepth], wu[kGrpDepth];
-#pragma unroll
-    for (int d = 0; d < kGrpDepth; ++d) {
-        if (d < n_grp) {
-            wg[d] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(qg + d * 8));
-            wu[d] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(qu + d * 8));
-        }
+    for (int r = 0; r < NB; ++r) {
+        const int t = (tid >> 5) + 16 * r;
+        xlive[r] = t < count;
+        xrow[r] = (int64_t)(a.pair_list[begin + (xlive[r] ? t : 0)] / a.K) * a.d_in;
     }
-    for (int G0 = 0; G0 < n_grp; G0 += kGrpDepth) {
+    // scale staging: thread -> (row, matrix, pair of groups); c = b - 128 s
+    const int sb_row = tid >> 2, sb_m = (tid >> 1) & 1, sb_h = tid & 1;
+    const int64_t sb_off = (erow + min(row0 + sb_row, a.d_ff - 1)) * a.gate.gpr;
+    const uint16_t *sb_s = (sb_m ? a.up.s : a.gate.s) + sb_off, *sb_b = (sb_m ? a.up.b : a.gate.b) + sb_off;
+    // the lane's weight row and its code words
+    const int rowl = wave * 16 + j;
+    const int ra = min(row0 + rowl, a.d_ff - 1);
+    const uint32_t *qg = a.gate.q + (erow + ra) * a.gate.wpr;
+    const uint32_t *qu = a.up.q + (erow + ra) * a.up.wpr;
+    const int xo = code_word_input(g);
+    u32x4 rg[2], ru[2];                                      // the chunk's code words, two groups each
 #pragma unroll
-        for (int d = 0; d < kGrpDepth; ++d) {
-            const int G = G0 + d;
-            if (G >= n_grp) break;
-            const u32x4 x0 = *reinterpret_cast<const u32x4 *>(xr + G * kGroup);
-            const u32x4 x1 = *reinterpret_cast<const u32x4 *>(xr + G * kGroup + 8);
-            float sg[4], bg[4], su[4], bu[4];
+    for (int p = 0; p < 2; ++p) {
+        rg[p] = *code_pair_addr(qg, 2 * p, n_grp, g);
+        ru[p] = *code_pair_addr(qu, 2 * p, n_grp, g);
+    }
+    InStage<NB> st;
+    uint16_t sbv[4];                                         // s, b of groups 2h and 2h + 1
+    int sb_g0 = 0;                                           // first group of the staged chunk
+    auto load_chunk = [&](int c) {
+        in_load<NB>(st, a.x, xrow, xlive, c * kGChunk, a.d_in);
+        sb_g0 = c * kGChunkGroups + 2 * sb_h;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sg[r] = load_sb<SB>(a.gate.s, srow[r] + G);
-                bg[r] = load_sb<SB>(a.gate.b, srow[r] + G);
-                su[r] = load_sb<SB>(a.up.s, srow[r] + G);
-                bu[r] = load_sb<SB>(a.up.b, srow[r] + G);
-            }
-            f32x4 tg = {0.f, 0.f, 0.f, 0.f}, tu = {0.f, 0.f, 0.f, 0.f};
-            float xs = 0.f;
+        for (int i = 0; i < 2; ++i) {
+            const int G = min(sb_g0 + i, n_grp - 1);
+            sbv[2 * i] = sb_s[G];
+            sbv[2 * i + 1] = sb_b[G];
+        }
+    };
+    auto store_chunk = [&](int buf) {
+        in_store<NB, true>(st, s_x[buf], s_xs[buf]);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const u32x4 xw = s == 0 ? x0 : x1;
-                uint32_t xp[4], pg[4], pu[4];
-                pair_inputs(xw, xp);
+        for (int i = 0; i < 2; ++i) {           // groups past the end: zero scale and bias
+            const bool ok = sb_g0 + i < n_grp;
+            const float sv = ok ? sb_to_float<SB>(sbv[2 * i]) : 0.f, bv = ok ? sb_to_float<SB>(sbv[2 * i + 1]) : 0.f;
+            *reinterpret_cast<float2 *>(&s_sb[buf][((2 * sb_h + i) * kGRows + sb_row) * 4 + 2 * sb_m]) =
+                make_float2(sv, bv - 128.0f * sv);
+        }
+    };
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+
+    f32x4 acc_g[NB], acc_u[NB];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    xs += __uint_as_float(xw[i] << 16) + __uint_as_float(xw[i] & 0xFFFF0000u);
-                nibble_pairs<0x43u>(wg[d][s], pg);
-                nibble_pairs<0x43u>(wu[d][s], pu);
-                const bf16x8_t B = __builtin_bit_cast(bf16x8_t, u32x4{xp[0], xp[1], xp[2], xp[3]});
-                tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u32x4{pg[0], pg[1], pg[2], pg[3]}),
-                                                             B, tg, 0, 0, 0);
-                tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u32x4{pu[0], pu[1], pu[2], pu[3]}),
-                                                             B, tu, 0, 0, 0);
-            }
-            if (G + kGrpDepth < n_grp) {             // refill this slot of the ring
-                wg[d] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(qg + (G + kGrpDepth) * 8));
-                wu[d] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(qu + (G + kGrpDepth) * 8));
-            }
-            const float xsum = sum_lane_groups(xs);  // token j's inputs of group G
+    for (int n = 0; n < NB; ++n) {
+        acc_g[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc_u[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int c = 0; c < n_chunk; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < n_chunk) load_chunk(c + 1);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                acc_g[r] += sg[r] * tg[r] + (bg[r] - 128.0f * sg[r]) * xsum;
-                acc_u[r] += su[r] * tu[r] + (bu[r] - 128.0f * su[r]) * xsum;
+        for (int p = 0; p < 2; ++p) {
+            uint32_t wg[4], wu[4];
+            spread_code_pair(rg[p], wg);
+            spread_code_pair(ru[p], wu);
+            // refill the ring slot: no load sits behind a branch, so the wait
+            // counts stay exact across the chunk's end
+            rg[p] = *code_pair_addr(qg, (c + 1) * kGChunkGroups + 2 * p, n_grp, g);
+            ru[p] = *code_pair_addr(qu, (c + 1) * kGChunkGroups + 2 * p, n_grp, g);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int d = 2 * p + h, G = c * kGChunkGroups + d;
+                if (G >= n_grp) continue;                    // the last chunk of a ragged d_in
+                const f32x4 sc = *reinterpret_cast<const f32x4 *>(&s_sb[buf][(d * kGRows + rowl) * 4]);
+                uint32_t pg[2][4], pu[2][4];
+                nibble_pairs<0x43u>(wg[2 * h], pg[0]);
+                nibble_pairs<0x43u>(wg[2 * h + 1], pg[1]);
+                nibble_pairs<0x43u>(wu[2 * h], pu[0]);
+                nibble_pairs<0x43u>(wu[2 * h + 1], pu[1]);
+#pragma unroll
+                for (int n = 0; n < NB; ++n) {
+                    const uint16_t *xr = s_x[buf] + (16 * n + j) * kGPad + d * kGroup + xo;
+                    f32x4 tg = {0.f, 0.f, 0.f, 0.f}, tu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const bf16x8_t A =
+                            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4 *>(xr + 8 * s));
+                        tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            A, __builtin_bit_cast(bf16x8_t, u32x4{pg[s][0], pg[s][1], pg[s][2], pg[s][3]}), tg, 0, 0,
+                            0);
+                        tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            A, __builtin_bit_cast(bf16x8_t, u32x4{pu[s][0], pu[s][1], pu[s][2], pu[s][3]}), tu, 0, 0,
+                            0);
+                    }
+                    const f32x4 xs = *reinterpret_cast<const f32x4 *>(&s_xs[buf][d * NT + 16 * n + 4 * g]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        acc_g[n][r] += sc.x * tg[r] + sc.y * xs[r];
+                        acc_u[n][r] += sc.z * tu[r] + sc.w * xs[r];
+                    }
+                }
             }
         }
+        if (c + 1 < n_chunk) store_chunk(buf ^ 1);
+        __syncthreads();
     }
-    if (j < count) {
-        float *o = a.act + (int64_t)pair_j * a.d_ff;
+
+    // act in fp32, then the block's fp16 copy
+    const int row = row0 + rowl;
+    const bool row_ok = row < a.d_ff;
+    f32x4 v[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = rw + 4 * g + r;
-            if (row < a.d_ff) o[row] = acc_g[r] * sigmoidf_(acc_g[r]) * acc_u[r];
+            v[n][r] = acc_g[n][r] * sigmoidf_(acc_g[n][r]) * acc_u[n][r];
+            const int t = 16 * n + 4 * g + r;
+            const float m = row16_max(row_ok ? fabsf(v[n][r]) : 0.f);
+            if (j == 15) s_max[wave][t] = m;
+            if (t < count && row_ok) a.act[(int64_t)s_pair[t] * a.d_ff + row] = v[n][r];
         }
+    }
+    __syncthreads();
+    if (tid < NT) {
+        float m = 0.f;
+#pragma unroll
+        for (int q = 0; q < kGW; ++q) m = fmaxf(m, s_max[q][tid]);
+        float inv;
+        const float cs = f16_stage_scale(__float_as_uint(m), inv);
+        s_inv[tid] = inv;
+        if (tid < count) a.act_cs[(int64_t)s_pair[tid] * a.n_blk + rb] = cs;
+    }
+    __syncthreads();
+    if (row_ok) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * n + 4 * g + r;
+                if (t < count)
+                    a.act16[(int64_t)s_pair[t] * a.d_ff + row] = (uint16_t)f32_to_f16_bits(v[n][r] * s_inv[t]);
+            }
     }
 }
 
 // ------------------------------------------------------------------ kernel B
 // partial[pair][i] = score * (W_down[e] act[pair])_i for the item's pairs and
-// rows [64 bx, 64 bx + 64).  act is staged kGrpActChunk inputs at a time as
-// fp16 rows of 16 tokens (8 halves of padding per row: the 16 lanes of a
-// k-step read 16 different rows without bank conflicts).
-template <int SB>
-__global__ __launch_bounds__(kGrpThreads) void down_grouped(GroupedArgs a) {
-    constexpr int kRow = kGrpActChunk + 8;            // halves per staged row
-    __shared__ __align__(16) _Float16 s_act[kGrpTok * kRow];
-    __shared__ float s_inv[kGrpTok], s_cs[kGrpTok];
-    __shared__ uint32_t s_max[kGrpTok];
-    const int w = blockIdx.y;
+// the workgroup's 128 rows, from act16 and act_cs; the same operand roles as
+// kernel A.
+template <int SB, int NB>
+__global__ __launch_bounds__(kGThreads) void down_grouped(GroupedArgs a) {
+    constexpr int NT = 16 * NB;
+    constexpr int kBlkPerChunk = kGChunk / kGRows;           // act16 blocks per chunk (2)
+    __shared__ __align__(16) uint16_t s_a[2][NT * kGPad];
+    __shared__ __align__(16) float s_sb[2][kGChunkGroups * kGRows * 2];      // [group][row][s, b]
+    __shared__ __align__(16) float s_as[2][kGChunkGroups * NT];             // [group][slot]
+    __shared__ __align__(16) float s_cs[2][kBlkPerChunk * NT];              // [block][slot]
+    __shared__ int s_pair[NT];
+    __shared__ float s_score[NT];
+    int w, rb;
+    item_and_block(a.row_blocks, w, rb);
     if (w >= *a.n_work) return;
     const int e = a.work_expert[w], begin = a.work_begin[w], count = a.work_count[w];
-    const int row0 = blockIdx.x * kGrpRows;
+    const int row0 = rb * kGRows;
     if (e < 0) {
-        zero_rows(a.partial, a.d_in, a, begin, count, row0, min(row0 + kGrpRows, a.d_in));
+        zero_rows(a.partial, a.d_in, a, begin, count, row0, min(row0 + kGRows, a.d_in));
         return;
     }
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int g = lane >> 4, j = lane & 15;
-    const int n = a.d_ff;
-    // each token's largest act magnitude: wave w scans token rows w, w + 4, ...
-    for (int t = wave; t < kGrpTok; t += kGrpThreads / kWave) {
-        uint32_t mx = 0;
-        if (t < count) {
-            const float *src = a.act + (int64_t)a.pair_list[begin + t] * n;
-            for (int i = lane; i < n; i += kWave) mx = max(mx, __float_as_uint(src[i]) & 0x7FFFFFFFu);
-        }
-        const float wm = wave_max(__uint_as_float(mx));
-        if (lane == 0) s_max[t] = __float_as_uint(wm);
-    }
-    __syncthreads();
-    if (tid < kGrpTok) {
-        float inv;
-        s_cs[tid] = f16_stage_scale(s_max[tid], inv);
-        s_inv[tid] = inv;
-    }
-    const int rw = row0 + wave * 16;
-    const int ra = min(rw + j, a.d_in - 1);
+    const int n = a.d_ff, n_grp = n / kGroup, n_chunk = (n_grp + kGChunkGroups - 1) / kGChunkGroups;
     const int64_t erow = (int64_t)e * a.d_in;
-    const uint32_t *qd = a.down.q + (erow + ra) * a.down.wpr + 2 * g;
-    int64_t srow[4];
+    if (tid < NT) {
+        const int p = tid < count ? a.pair_list[begin + tid] : -1;
+        s_pair[tid] = p;
+        s_score[tid] = p >= 0 && a.scores ? a.scores[p] : 1.0f;
+    }
+    int64_t arow[NB];
+    bool alive[NB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) srow[r] = (erow + min(rw + 4 * g + r, a.d_in - 1)) * a.down.gpr;
-    const int pair_j = a.pair_list[begin + (j < count ? j : 0)];
-    const f16x2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < n; k0 += kGrpActChunk) {
-        const int kn = min(kGrpActChunk, n - k0);
-        __syncthreads();                                 // the previous chunk's readers are done
-        for (int idx = tid; idx < kGrpTok * (kn / 4); idx += kGrpThreads) {
-            const int t = idx / (kn / 4), c = (idx - t * (kn / 4)) * 4;
-            f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (t < count)
-                v = *reinterpret_cast<const f32x4 *>(a.act + (int64_t)a.pair_list[begin + t] * n + k0 + c);
-            const float inv = s_inv[t];
-            _Float16 *d = s_act + t * kRow + c;
-            d[0] = (_Float16)(v.x * inv);
-            d[1] = (_Float16)(v.y * inv);
-            d[2] = (_Float16)(v.z * inv);
-            d[3] = (_Float16)(v.w * inv);
+    for (int r = 0; r < NB; ++r) {
+        const int t = (tid >> 5) + 16 * r;
+        alive[r] = t < count;
+        arow[r] = (int64_t)a.pair_list[begin + (alive[r] ? t : 0)] * n;
+    }
+    // scale staging, threads < 256: (row, pair of groups)
+    const int sb_row = (tid >> 1) & (kGRows - 1), sb_h = tid & 1;
+    const int64_t sb_off = (erow + min(row0 + sb_row, a.d_in - 1)) * a.down.gpr;
+    const int cs_t = (tid >> 1) & (NT - 1), cs_k = tid & 1;           // threads < 2 NT: (slot, block)
+    const bool cs_live = cs_t < count;
+    const int64_t cs_row = (int64_t)a.pair_list[begin + (cs_live ? cs_t : 0)] * a.n_blk;
+    const int rowl = wave * 16 + j;
+    const int ra = min(row0 + rowl, a.d_in - 1);
+    const uint32_t *qd = a.down.q + (erow + ra) * a.down.wpr;
+    const int xo = code_word_input(g);
+    u32x4 rw[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) rw[p] = *code_pair_addr(qd, 2 * p, n_grp, g);
+    InStage<NB> st;
+    uint16_t sbv[4];
+    float csv = 1.f;
+    int sb_g0 = 0, blk = 0;
+    // every thread loads (clamped addresses); only the staging threads store
+    auto load_chunk = [&](int c) {
+        in_load<NB>(st, a.act16, arow, alive, c * kGChunk, n);
+        sb_g0 = c * kGChunkGroups + 2 * sb_h;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int G = min(sb_g0 + i, n_grp - 1);
+            sbv[2 * i] = a.down.s[sb_off + G];
+            sbv[2 * i + 1] = a.down.b[sb_off + G];
         }
+        blk = c * kBlkPerChunk + cs_k;
+        csv = a.act_cs[cs_row + min(blk, a.n_blk - 1)];
+    };
+    auto store_chunk = [&](int buf) {
+        in_store<NB, false>(st, s_a[buf], s_as[buf]);
+        if (tid < 2 * kGRows) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {       // groups past the end: zero scale and bias
+                const bool ok = sb_g0 + i < n_grp;
+                *reinterpret_cast<float2 *>(&s_sb[buf][((2 * sb_h + i) * kGRows + sb_row) * 2]) =
+                    make_float2(ok ? sb_to_float<SB>(sbv[2 * i]) : 0.f, ok ? sb_to_float<SB>(sbv[2 * i + 1]) : 0.f);
+            }
+        }
+        if (tid < kBlkPerChunk * NT) s_cs[buf][cs_k * NT + cs_t] = cs_live && blk < a.n_blk ? csv : 0.f;
+    };
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+
+    const f16x2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
+    f32x4 acc[NB];
+#pragma unroll
+    for (int m = 0; m < NB; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < n_chunk; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < n_chunk) load_chunk(c + 1);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            uint32_t wd[4];
+            spread_code_pair(rw[p], wd);
+            rw[p] = *code_pair_addr(qd, (c + 1) * kGChunkGroups + 2 * p, n_grp, g);   // as in kernel A
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int d = 2 * p + h, G = c * kGChunkGroups + d;
+                if (G >= n_grp) continue;
+                const float2 sb = *reinterpret_cast<const float2 *>(&s_sb[buf][(d * kGRows + rowl) * 2]);
+                uint32_t pq[2][4];
+                nibble_pairs<0x64u>(wd[2 * h], pq[0]);
+                nibble_pairs<0x64u>(wd[2 * h + 1], pq[1]);
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        pq[s][i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, pq[s][i]) - off);
+#pragma unroll
+                for (int m = 0; m < NB; ++m) {
+                    const uint16_t *ar = s_a[buf] + (16 * m + j) * kGPad + d * kGroup + xo;
+                    f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+                        t4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4 *>(ar + 8 * s)),
+                            __builtin_bit_cast(f16x8_t, u32x4{pq[s][0], pq[s][1], pq[s][2], pq[s][3]}), t4, 0, 0, 0);
+                    const f32x4 as = *reinterpret_cast<const f32x4 *>(&s_as[buf][d * NT + 16 * m + 4 * g]);
+                    const f32x4 cs =
+                        *reinterpret_cast<const f32x4 *>(&s_cs[buf][((d * kGroup) / kGRows) * NT + 16 * m + 4 * g]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[m][r] += cs[r] * (sb.x * t4[r] + sb.y * as[r]);
+                }
+            }
+        }
+        if (c + 1 < n_chunk) store_chunk(buf ^ 1);
         __syncthreads();
-        const int g0 = k0 / kGroup, n_grp = kn / kGroup;
-        for (int G = 0; G < n_grp; ++G) {
-            const u32x2 wd = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(qd + (g0 + G) * 8));
-            float sd[4], bd[4];
+    }
+    const int row = row0 + rowl;
+    if (row < a.d_in) {
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                sd[r] = load_sb<SB>(a.down.s, srow[r] + g0 + G);
-                bd[r] = load_sb<SB>(a.down.b, srow[r] + g0 + G);
+                const int t = 16 * m + 4 * g + r;
+                if (t < count) a.partial[(int64_t)s_pair[t] * a.d_in + row] = s_score[t] * acc[m][r];
             }
-            f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
-            float as = 0.f;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const u32x4 aw = *reinterpret_cast<const u32x4 *>(s_act + j * kRow + G * kGroup + 16 * g + 8 * s);
-                uint32_t ap[4], pq[4];
-                pair_inputs(aw, ap);
-                as += f16_pairs_sum<4>(ap);              // products by 1 exact, fp32 sums
-                nibble_pairs<0x64u>(wd[s], pq);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    pq[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, pq[i]) - off);
-                t4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, u32x4{pq[0], pq[1], pq[2], pq[3]}),
-                                                            __builtin_bit_cast(f16x8_t, u32x4{ap[0], ap[1], ap[2], ap[3]}),
-                                                            t4, 0, 0, 0);
-            }
-            const float asum = sum_lane_groups(as);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] += sd[r] * t4[r] + bd[r] * asum;
-        }
-    }
-    if (j < count) {
-        const float sc = (a.scores ? a.scores[pair_j] : 1.0f) * s_cs[j];     // exact: s_cs is a power of two
-        float *o = a.partial + (int64_t)pair_j * a.d_in;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = rw + 4 * g + r;
-            if (row < a.d_in) o[row] = sc * acc[r];
-        }
     }
 }
 
-static int grouped_max_work(int n_pairs, int E) { return (n_pairs + kGrpTok - 1) / kGrpTok + E + 1; }
+static int grouped_max_work(int n_pairs, int E, int nt) { return (n_pairs + nt - 1) / nt + E + 1; }
+
+// Pairs per work item: 16 NB, from the average number of pairs per expert.
+static int grouped_nb(int n_pairs, int E) {
+    const int avg = n_pairs / E;
+    return avg <= 12 ? 1 : avg <= 40 ? 2 : 4;
+}
+
+// Workspace: the work lists (int32), then act16, then act_cs, each 256-byte aligned.
+struct GroupedLayout {
+    size_t act16, act_cs, total;
+};
+
+static GroupedLayout grouped_layout(int n_tokens, int top_k, int n_experts, int d_ff) {
+    GroupedLayout L;
+    const size_t n_pairs = (size_t)n_tokens * top_k;
+    const size_t mw = (size_t)grouped_max_work((int)n_pairs, n_experts, kGMinTok);
+    L.act16 = align_up((1 + 3 * mw + n_pairs) * sizeof(int32_t), 256);
+    L.act_cs = L.act16 + align_up(n_pairs * d_ff * sizeof(uint16_t), 256);
+    L.total = L.act_cs + align_up(n_pairs * ((d_ff + kGRows - 1) / kGRows) * sizeof(float), 256);
+    return L;
+}
+
+template <int SB, int NB>
+static void launch_grouped(const GroupedArgs &a, int mw, hipStream_t s) {
+    const int items8 = (mw + 7) / 8 * 8;
+    GroupedArgs ga = a, gb = a;
+    ga.row_blocks = (a.d_ff + kGRows - 1) / kGRows;
+    gb.row_blocks = (a.d_in + kGRows - 1) / kGRows;
+    hipLaunchKernelGGL((gate_up_grouped<SB, NB>), dim3(items8 * ga.row_blocks), dim3(kGThreads), 0, s, ga);
+    hipLaunchKernelGGL((down_grouped<SB, NB>), dim3(items8 * gb.row_blocks), dim3(kGThreads), 0, s, gb);
+}
 
 }  // namespace moe
 
 using namespace moe;
 
-extern "C" size_t moe_decode_expert_ffn_grouped_workspace_bytes(int32_t n_tokens, int32_t top_k, int32_t n_experts) {
-    if (n_tokens < 1 || top_k < 1 || n_experts < 1) return 0;
-    const size_t n_pairs = (size_t)n_tokens * top_k, mw = (size_t)grouped_max_work((int)n_pairs, n_experts);
-    return align_up((1 + 3 * mw + n_pairs) * sizeof(int32_t), 256);
+extern "C" size_t moe_decode_expert_ffn_grouped_workspace_bytes(int32_t n_tokens, int32_t top_k, int32_t n_experts,
+                                                                int32_t d_ff) {
+    if (n_tokens < 1 || top_k < 1 || n_experts < 1 || d_ff < 1) return 0;
+    return grouped_layout(n_tokens, top_k, n_experts, d_ff).total;
 }
 
 extern "C" moe_status moe_decode_expert_ffn_grouped(const void *x, moe_dtype x_dtype_arg, int32_t n_tokens,
@@ -361,10 +673,14 @@ extern "C" moe_status moe_decode_expert_ffn_grouped(const void *x, moe_dtype x_d
     if (up->rows != d_ff || up->cols != d_in || down->rows != d_in || down->cols != d_ff) return MOE_EINVAL;
     if (up->n_experts != E || down->n_experts != E) return MOE_EINVAL;
     if (!aligned16(x) || !aligned16(act) || !aligned16(partial) || !aligned16(workspace)) return MOE_EINVAL;
-    if (workspace_bytes < moe_decode_expert_ffn_grouped_workspace_bytes(n_tokens, top_k, E)) return MOE_EINVAL;
-    const int n_pairs = n_tokens * top_k, mw = grouped_max_work(n_pairs, E);
+    const GroupedLayout L = grouped_layout(n_tokens, top_k, E, d_ff);
+    if (workspace_bytes < L.total) return MOE_EINVAL;
+    const int n_pairs = n_tokens * top_k, nb = grouped_nb(n_pairs, E), nt = 16 * nb;
+    const int mw = grouped_max_work(n_pairs, E, nt), mw_ws = grouped_max_work(n_pairs, E, kGMinTok);
     GroupedArgs a;
-    a.x = x; a.T = n_tokens; a.K = top_k; a.E = E; a.d_in = d_in; a.d_ff = d_ff;
+    a.x = reinterpret_cast<const uint16_t *>(x);
+    a.T = n_tokens; a.K = top_k; a.E = E; a.d_in = d_in; a.d_ff = d_ff;
+    a.n_blk = (d_ff + kGRows - 1) / kGRows;
     auto qm = [](const moe_qmat *m) {
         QM q;
         q.q = m->q;
@@ -376,19 +692,25 @@ extern "C" moe_status moe_decode_expert_ffn_grouped(const void *x, moe_dtype x_d
         return q;
     };
     a.gate = qm(gate); a.up = qm(up); a.down = qm(down);
-    a.ids = expert_ids; a.scores = scores; a.act = act; a.partial = partial;
-    int32_t *ws = reinterpret_cast<int32_t *>(workspace);
+    a.scores = scores; a.act = act; a.partial = partial;
+    char *wsb = reinterpret_cast<char *>(workspace);
+    int32_t *ws = reinterpret_cast<int32_t *>(wsb);
     a.n_work = ws;
     a.work_expert = ws + 1;
-    a.work_begin = ws + 1 + mw;
-    a.work_count = ws + 1 + 2 * mw;
-    a.pair_list = ws + 1 + 3 * mw;
+    a.work_begin = ws + 1 + mw_ws;
+    a.work_count = ws + 1 + 2 * mw_ws;
+    a.pair_list = ws + 1 + 3 * mw_ws;
+    a.act16 = reinterpret_cast<uint16_t *>(wsb + L.act16);
+    a.act_cs = reinterpret_cast<float *>(wsb + L.act_cs);
+    a.row_blocks = 1;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(grouped_bucket_kernel, dim3(1), dim3(kGrpBucketThreads), 0, s, expert_ids, n_pairs, E, ws,
-                       ws + 1, ws + 1 + mw, ws + 1 + 2 * mw, ws + 1 + 3 * mw);
-    const auto ka = sb == MOE_BF16 ? gate_up_grouped<MOE_BF16> : gate_up_grouped<MOE_F16>;
-    const auto kb = sb == MOE_BF16 ? down_grouped<MOE_BF16> : down_grouped<MOE_F16>;
-    hipLaunchKernelGGL(ka, dim3((d_ff + kGrpRows - 1) / kGrpRows, mw), dim3(kGrpThreads), 0, s, a);
-    hipLaunchKernelGGL(kb, dim3((d_in + kGrpRows - 1) / kGrpRows, mw), dim3(kGrpThreads), 0, s, a);
+    hipLaunchKernelGGL(grouped_bucket_kernel, dim3(1), dim3(kGBucketThreads), 0, s, expert_ids, n_pairs, E, nt, ws,
+                       ws + 1, ws + 1 + mw_ws, ws + 1 + 2 * mw_ws, ws + 1 + 3 * mw_ws);
+    const bool bf = sb == MOE_BF16;
+    switch (nb) {
+    case 1: bf ? launch_grouped<MOE_BF16, 1>(a, mw, s) : launch_grouped<MOE_F16, 1>(a, mw, s); break;
+    case 2: bf ? launch_grouped<MOE_BF16, 2>(a, mw, s) : launch_grouped<MOE_F16, 2>(a, mw, s); break;
+    default: bf ? launch_grouped<MOE_BF16, 4>(a, mw, s) : launch_grouped<MOE_F16, 4>(a, mw, s); break;
+    }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }

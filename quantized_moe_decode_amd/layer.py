@@ -52,7 +52,11 @@ class DecodeLayer:
                  grouped: Optional[bool] = None):
         dev = router.device
         self.grouped = n_tokens > MOE_MAX_TOKENS if grouped is None else bool(grouped)
-        ws_bytes = expert_ffn_grouped_workspace_bytes if self.grouped else expert_ffn_workspace_bytes
+
+        def ws_bytes(T, K, E, d_ff):
+            if self.grouped:
+                return expert_ffn_grouped_workspace_bytes(T, K, E, d_ff)
+            return expert_ffn_workspace_bytes(T, K, E)
         self.router, self.top_k, self.renormalize = router, top_k, renormalize
         self.gate, self.up, self.down = gate, up, down
         self.shared = tuple(shared) if shared is not None else None
@@ -68,7 +72,7 @@ class DecodeLayer:
         self.act = torch.zeros(T, top_k, d_ff, **f32)
         self.partial = torch.zeros(T, top_k, d_in, **f32)
         self.route_ws = torch.zeros(route_workspace_bytes(T, E), device=dev, dtype=torch.uint8)
-        nb = ws_bytes(T, top_k, E)
+        nb = ws_bytes(T, top_k, E, d_ff)
         self.ffn_ws = torch.zeros(max(nb, 1), device=dev, dtype=torch.uint8) if nb else None
         if self.shared is not None:
             S = self.shared[0].n_experts
@@ -76,7 +80,7 @@ class DecodeLayer:
             self.shared_ids = torch.arange(S, device=dev, dtype=torch.int32).repeat(T, 1).contiguous()
             self.shared_act = torch.zeros(T, S, self.shared[0].rows, **f32)
             self.shared_partial = torch.zeros(T, S, d_in, **f32)
-            nb = ws_bytes(T, S, S)
+            nb = ws_bytes(T, S, S, self.shared[0].rows)
             self.shared_ws = torch.zeros(max(nb, 1), device=dev, dtype=torch.uint8) if nb else None
         else:
             self.n_shared = 0

@@ -40,7 +40,7 @@ def test_library_exports_declared_symbol(name):
 
 
 def test_abi_version_and_status_strings():
-    assert qmd.abi_version() == 3
+    assert qmd.abi_version() == 4
     for code in (0, 1, 2, 3, 4):
         assert qmd.status_string(code).startswith("MOE_")
     assert "unknown" in qmd.status_string(99)
@@ -190,13 +190,16 @@ def test_token_limits_match_the_header():
 
 
 def test_grouped_workspace_bytes():
-    """One count, then expert, first pair and pair count per work item (at most
-    ceil(pairs / 16) + n_experts + 1 items), then the pair list, in int32."""
+    """The work lists (one count, then expert, first pair and pair count per
+    work item, at most ceil(pairs / 16) + n_experts + 1 items, then the pair
+    list, int32), the fp16 copy of act and one fp32 factor per pair and block
+    of 128 act values, each 256-byte aligned."""
     f = qmd.expert_ffn_grouped_workspace_bytes
-    for T, K, E in [(1, 1, 1), (256, 8, 128), (1024, 32, 1024), (17, 3, 9)]:
+    for T, K, E, F in [(1, 1, 1, 64), (256, 8, 128, 768), (1024, 32, 1024, 8192), (17, 3, 9, 704)]:
         mw = (T * K + 15) // 16 + E + 1
-        assert f(T, K, E) >= (1 + 3 * mw + T * K) * 4 and f(T, K, E) % 256 == 0
-    assert f(0, 8, 128) == 0 and f(4, 0, 128) == 0 and f(4, 8, 0) == 0
+        need = (1 + 3 * mw + T * K) * 4 + T * K * F * 2 + T * K * ((F + 127) // 128) * 4
+        assert need <= f(T, K, E, F) <= need + 3 * 256 and f(T, K, E, F) % 256 == 0
+    assert f(0, 8, 128, 768) == 0 and f(4, 0, 128, 768) == 0 and f(4, 8, 0, 768) == 0 and f(4, 8, 8, 0) == 0
 
 
 def _gate_up(gate=None, up=None, **kw):

@@ -50,7 +50,7 @@ def run_grouped(cfg, w, x, ids, scores):
     scd = torch.from_numpy(scores).to(DEV)
     act = torch.full((T, K, cfg.d_ff), -7.0, device=DEV)
     part = torch.full((T, K, cfg.d_in), -7.0, device=DEV)
-    ws = torch.zeros(q.expert_ffn_grouped_workspace_bytes(T, K, cfg.n_experts), device=DEV, dtype=torch.uint8)
+    ws = torch.zeros(q.expert_ffn_grouped_workspace_bytes(T, K, cfg.n_experts, cfg.d_ff), device=DEV, dtype=torch.uint8)
     q.moe_decode_expert_ffn_grouped(xd, g, u, d, idd, scd, act, part, ws)
     torch.cuda.synchronize()
     return act.cpu().numpy(), part.cpu().numpy(), (xd, g, u, d, idd, scd, act, part, ws)
@@ -87,10 +87,11 @@ def test_grouped_small(kw, T):
     check(cfg, w, x, ids, scores, f"grouped {kw} T={T}")
 
 
-@pytest.mark.parametrize("T", [15, 16, 17, 48])
+@pytest.mark.parametrize("T", [15, 16, 17, 48, 150])
 def test_grouped_one_expert_takes_every_token(T):
     """Every token on experts 0..K-1: each expert's list is cut into work items
-    of 16 pairs, the last one part-full (or full)."""
+    of 16, 32 or 64 pairs (by the average pairs per expert), the last one
+    part-full or full."""
     cfg = small_cfg(d_in=512, d_ff=384, n_experts=6, top_k=2)
     say(f"case grouped skew T={T}")
     w = mi.gen_layer_weights(cfg, 1, threads=4)
@@ -144,6 +145,18 @@ def test_grouped_full_size_256_tokens_and_repeatable():
     act, part = check(cfg, w, x, ids, scores, "grouped qwen3 T=256", tokens=np.arange(0, T, 11))
     act2, part2, _ = run_grouped(cfg, w, x, ids, scores)
     assert np.array_equal(act, act2) and np.array_equal(part, part2), "repeated call differs"
+
+
+def test_grouped_full_size_1024_tokens():
+    """1024 tokens x top-8 on the Qwen3-30B-A3B-shaped layer: 64 pairs per
+    expert on average, the 64-pair work items; 16 tokens checked."""
+    cfg = mi.QWEN3
+    say("case grouped qwen3 T=1024")
+    w = mi.gen_layer_weights(cfg, 1)
+    T = 1024
+    x, _ = mi.gen_tokens(cfg, 1, T)
+    ids, scores = random_routing(T, cfg.top_k, cfg.n_experts, seed=1024)
+    check(cfg, w, x, ids, scores, "grouped qwen3 T=1024", tokens=np.arange(5, T, 67))
 
 
 def test_grouped_rejects_unsupported_formats():
