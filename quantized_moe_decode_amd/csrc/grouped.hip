@@ -163,16 +163,28 @@ __global__ __launch_bounds__(kGBucketThreads) void grouped_bucket_kernel(const i
                                                                         int32_t *work_expert, int32_t *work_begin,
                                                                         int32_t *work_count, int32_t *pair_list) {
     constexpr int kWaves = kGBucketThreads / kWave;
+    constexpr int kPer = MOE_MAX_GROUPED_TOKENS * MOE_MAX_TOP_K / kGBucketThreads;   // ids per thread, at most
     __shared__ int cnt[2 * kGBucketThreads], base[2 * kGBucketThreads], tiles[2 * kGBucketThreads];
     __shared__ int s_wp[kWaves], s_wt[kWaves];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, nb = E + 1;
+    const int per = (n_pairs + kGBucketThreads - 1) / kGBucketThreads;
     cnt[2 * tid] = 0;
     cnt[2 * tid + 1] = 0;
-    __syncthreads();
-    for (int p = tid; p < n_pairs; p += kGBucketThreads) {
-        const int e = ids[p];
-        atomicAdd(&cnt[e >= 0 && e < E ? e : E], 1);
+    // this thread's pairs tid + i * kGBucketThreads: their buckets, all loads in flight at once
+    int bk[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        bk[i] = -1;
+        if (i < per) {
+            const int p = tid + i * kGBucketThreads;
+            const int e = ids[min(p, n_pairs - 1)];
+            bk[i] = p < n_pairs ? (e >= 0 && e < E ? e : E) : -1;
+        }
     }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if (bk[i] >= 0) atomicAdd(&cnt[bk[i]], 1);
     __syncthreads();
     // exclusive scans of the pair and work-item counts: thread t owns buckets
     // 2t and 2t + 1 (nb <= 1025 <= 2048), wave prefix sums, then the waves'
@@ -216,11 +228,9 @@ __global__ __launch_bounds__(kGBucketThreads) void grouped_bucket_kernel(const i
     __syncthreads();
     for (int b = tid; b < nb; b += kGBucketThreads) cnt[b] = 0;   // reused as the placement cursor
     __syncthreads();
-    for (int p = tid; p < n_pairs; p += kGBucketThreads) {
-        const int e = ids[p];
-        const int b = e >= 0 && e < E ? e : E;
-        pair_list[base[b] + atomicAdd(&cnt[b], 1)] = p;
-    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if (bk[i] >= 0) pair_list[base[bk[i]] + atomicAdd(&cnt[bk[i]], 1)] = tid + i * kGBucketThreads;
 }
 
 // Zero rows [row0, row_end) of the item's pairs in out ([pairs][n]).
@@ -396,7 +406,7 @@ __global__ __launch_bounds__(kGThreads) void gate_up_grouped(GroupedArgs a) {
             for (int h = 0; h < 2; ++h) {
                 const int d = 2 * p + h, G = c * kGChunkGroups + d;
                 if (G >= n_grp) continue;                    // the last chunk of a ragged d_in
-                const f32x4 sc = *reinterpret_cast<const f32x4 *>(&s_sb[buf][(d * kGRows + rowl) * 4]);
+                const float2 sc = make_float2(s_sb[buf][(d * kGRows + rowl) * 4], s_sb[buf][(d * kGRows + rowl) * 4 + 2]);
                 uint32_t pg[2][4], pu[2][4];
                 nibble_pairs<0x43u>(wg[2 * h], pg[0]);
                 nibble_pairs<0x43u>(wg[2 * h + 1], pg[1]);
@@ -417,13 +427,25 @@ __global__ __launch_bounds__(kGThreads) void gate_up_grouped(GroupedArgs a) {
                             A, __builtin_bit_cast(bf16x8_t, u32x4{pu[s][0], pu[s][1], pu[s][2], pu[s][3]}), tu, 0, 0,
                             0);
                     }
-                    const f32x4 xs = *reinterpret_cast<const f32x4 *>(&s_xs[buf][d * NT + 16 * n + 4 * g]);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        acc_g[n][r] += sc.x * tg[r] + sc.y * xs[r];
-                        acc_u[n][r] += sc.z * tu[r] + sc.w * xs[r];
+                        acc_g[n][r] += sc.x * tg[r];
+                        acc_u[n][r] += sc.y * tu[r];
                     }
                 }
+            }
+        }
+        // the chunk's bias terms, sum over its groups d of xsum[d][pair] c[d][row],
+        // as one fp32 matrix product per 16-pair block (16x16x4: lane (j, g)
+        // supplies xsum of pair 16 n + j and c of row j, both of group g; a
+        // group past the end has both zero)
+        {
+            const float cgv = s_sb[buf][(g * kGRows + rowl) * 4 + 1], cuv = s_sb[buf][(g * kGRows + rowl) * 4 + 3];
+#pragma unroll
+            for (int n = 0; n < NB; ++n) {
+                const float xv = s_xs[buf][g * NT + 16 * n + j];
+                acc_g[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv, cgv, acc_g[n], 0, 0, 0);
+                acc_u[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv, cuv, acc_u[n], 0, 0, 0);
             }
         }
         if (c + 1 < n_chunk) store_chunk(buf ^ 1);
@@ -566,11 +588,12 @@ __global__ __launch_bounds__(kGThreads) void down_grouped(GroupedArgs a) {
             uint32_t wd[4];
             spread_code_pair(rw[p], wd);
             rw[p] = *code_pair_addr(qd, (c + 1) * kGChunkGroups + 2 * p, n_grp, g);   // as in kernel A
+            // groups 2p and 2p + 1 are act16 block p of the chunk
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int d = 2 * p + h, G = c * kGChunkGroups + d;
                 if (G >= n_grp) continue;
-                const float2 sb = *reinterpret_cast<const float2 *>(&s_sb[buf][(d * kGRows + rowl) * 2]);
+                const float sd = s_sb[buf][(d * kGRows + rowl) * 2];
                 uint32_t pq[2][4];
                 nibble_pairs<0x64u>(wd[2 * h], pq[0]);
                 nibble_pairs<0x64u>(wd[2 * h + 1], pq[1]);
@@ -588,12 +611,21 @@ __global__ __launch_bounds__(kGThreads) void down_grouped(GroupedArgs a) {
                         t4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                             __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4 *>(ar + 8 * s)),
                             __builtin_bit_cast(f16x8_t, u32x4{pq[s][0], pq[s][1], pq[s][2], pq[s][3]}), t4, 0, 0, 0);
-                    const f32x4 as = *reinterpret_cast<const f32x4 *>(&s_as[buf][d * NT + 16 * m + 4 * g]);
-                    const f32x4 cs =
-                        *reinterpret_cast<const f32x4 *>(&s_cs[buf][((d * kGroup) / kGRows) * NT + 16 * m + 4 * g]);
+                    const f32x4 cs = *reinterpret_cast<const f32x4 *>(&s_cs[buf][p * NT + 16 * m + 4 * g]);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[m][r] += cs[r] * (sb.x * t4[r] + sb.y * as[r]);
+                    for (int r = 0; r < 4; ++r) acc[m][r] += (cs[r] * sd) * t4[r];
                 }
+            }
+        }
+        // the chunk's bias terms, sum over its groups d of b[d][row] asum[d][pair]
+        // times the block factor, as one fp32 matrix product per 16-pair block
+        // (as in kernel A; lane (j, g): pair 16 m + j, row j, group g)
+        {
+            const float bv = s_sb[buf][(g * kGRows + rowl) * 2 + 1];
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+                const float av = s_as[buf][g * NT + 16 * m + j] * s_cs[buf][(g >> 1) * NT + 16 * m + j];
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[m], 0, 0, 0);
             }
         }
         if (c + 1 < n_chunk) store_chunk(buf ^ 1);
