@@ -62,10 +62,13 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0
 HEADLINE = "qwen3_30b_a3b_moe"
-# the 32-token workload right after the headline: it runs on the headline's device weights
-ALL_CONFIGS = [HEADLINE, "qwen3_30b_a3b_moe_batch32", "tiny_e8_top2", "qwen1.5_moe_a2.7b", "dots_llm1_mixed_bit"]
+# the 32- and 256-token workloads right after the headline: they run on the headline's device weights
+ALL_CONFIGS = [HEADLINE, "qwen3_30b_a3b_moe_batch32", "qwen3_30b_a3b_moe_prefill256", "tiny_e8_top2",
+               "qwen1.5_moe_a2.7b", "dots_llm1_mixed_bit"]
 FUSED_KERNEL = "moe::layer_kernel"
 BATCH_GATE_UP_KERNEL = "moe::gate_up_batch_q4"
+GROUPED_GATE_UP_KERNEL = "moe::gate_up_grouped"
+MAX_DECODE_TOKENS = 32          # above this the layer takes the grouped (matrix-core) expert FFN
 COPY_KERNEL = "MulFunctor"
 TOL = 2e-3
 MARGIN = 1e-3
@@ -93,7 +96,9 @@ def counters_path(workload: str) -> str:
 
 
 def dominant_kernel(cfg) -> str:
-    return FUSED_KERNEL if cfg.n_tokens == 1 else BATCH_GATE_UP_KERNEL
+    if cfg.n_tokens == 1:
+        return FUSED_KERNEL
+    return BATCH_GATE_UP_KERNEL if cfg.n_tokens <= MAX_DECODE_TOKENS else GROUPED_GATE_UP_KERNEL
 
 
 def summarize_counters(fetch_csv, write_csv, workload, copy_mib, command) -> dict:
@@ -410,19 +415,26 @@ def roofline_of(wl, meas, args):
         alg = float(np.mean(wl.step_bytes)) / L
         name = "layer_kernel (route + kernel A + kernel B + tail, one launch per layer)"
     else:
-        # kernel A (multi-token gate/up) alone: graphs of its launches only, for
-        # the same layers and tokens (each layer's ids left by a replay of the step)
+        # kernel A (multi-token gate/up) alone, or for the grouped path the
+        # grouped expert FFN call (its bucketing, gate/up and down launches):
+        # graphs of those launches only, for the same layers and tokens (each
+        # layer's ids left by a replay of the step)
         graphs, a_bytes = [], []
-        per_gu = wl.layers[0].gate.nbytes() + wl.layers[0].up.nbytes()
+        grouped = wl.layers[0].grouped
+        per_unit = (wl.per_expert if grouped else wl.layers[0].gate.nbytes() + wl.layers[0].up.nbytes())
         for r in range(R):
             wl.step.replay(r)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for li, lay in enumerate(wl.layers):
-                    qmd.moe_decode_gate_up(wl.step.xs[r][li], lay.gate, lay.up, lay.ids, lay.act, lay.ffn_ws)
+                    if grouped:
+                        qmd.moe_decode_expert_ffn_grouped(wl.step.xs[r][li], lay.gate, lay.up, lay.down, lay.ids,
+                                                          lay.scores, lay.act, lay.partial, lay.ffn_ws)
+                    else:
+                        qmd.moe_decode_gate_up(wl.step.xs[r][li], lay.gate, lay.up, lay.ids, lay.act, lay.ffn_ws)
             graphs.append(g)
-            a_bytes.append(wl.step_touched[r] * per_gu)
+            a_bytes.append(wl.step_touched[r] * per_unit)
         for g in graphs:
             g.replay()
         torch.cuda.synchronize()
@@ -437,7 +449,9 @@ def roofline_of(wl, meas, args):
         torch.cuda.synchronize()
         avg_s = e0.elapsed_time(e1) / 1000.0 / (reps * L)
         alg = sum(a_bytes[i % R] for i in range(reps)) / (reps * L)
-        name = "gate_up_batch_q4 (kernel A: gate/up GEMV + SwiGLU for every token of a touched expert)"
+        name = ("expert_ffn_grouped (bucketing + gate_up_grouped + down_grouped: the matrix-core expert FFN "
+                "of every touched expert, per layer)" if grouped else
+                "gate_up_batch_q4 (kernel A: gate/up GEMV + SwiGLU for every token of a touched expert)")
         del graphs
     achieved = alg / avg_s / 1e9
     traffic = traffic_per_launch(cfg.name)

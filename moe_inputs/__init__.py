@@ -124,8 +124,11 @@ DOTS = LayerConfig("dots_llm1_mixed_bit", 3, 3, d_in=4096, d_ff=1408, n_experts=
                    n_shared=2, d_ff_shared=1408, shared_gate=False, n_layers=12)
 QWEN3_B32 = dataclasses.replace(QWEN3, name="qwen3_30b_a3b_moe_batch32", cfg_id=4,
                                 weight_cfg_id=1, n_tokens=32)
+# 256 tokens per step (a prefill chunk) on the same weights: the grouped expert FFN
+QWEN3_P256 = dataclasses.replace(QWEN3, name="qwen3_30b_a3b_moe_prefill256", cfg_id=5,
+                                 weight_cfg_id=1, n_tokens=256)
 
-CONFIGS: Dict[str, LayerConfig] = {c.name: c for c in (TINY, QWEN3, QWEN15, DOTS, QWEN3_B32)}
+CONFIGS: Dict[str, LayerConfig] = {c.name: c for c in (TINY, QWEN3, QWEN15, DOTS, QWEN3_B32, QWEN3_P256)}
 
 
 def rng_for(*key: int) -> np.random.Generator:

@@ -47,3 +47,14 @@ def test_batch_workload_counts_its_gate_up_kernel():
     import moe_inputs as mi
     assert bench.dominant_kernel(mi.CONFIGS["qwen3_30b_a3b_moe_batch32"]) == bench.BATCH_GATE_UP_KERNEL
     assert bench.dominant_kernel(mi.CONFIGS["qwen3_30b_a3b_moe"]) == bench.FUSED_KERNEL
+    assert bench.dominant_kernel(mi.CONFIGS["qwen3_30b_a3b_moe_prefill256"]) == bench.GROUPED_GATE_UP_KERNEL
+
+
+def test_prefill_workload_reuses_the_headline_weights_and_takes_the_grouped_path():
+    import moe_inputs as mi
+    import quantized_moe_decode_amd as qmd
+    p, h = mi.CONFIGS["qwen3_30b_a3b_moe_prefill256"], mi.CONFIGS["qwen3_30b_a3b_moe"]
+    assert p.weight_cfg_id == h.weight_cfg_id and p.cfg_id != h.cfg_id
+    assert qmd.MOE_MAX_TOKENS < p.n_tokens <= qmd.MOE_MAX_GROUPED_TOKENS
+    assert bench.MAX_DECODE_TOKENS == qmd.MOE_MAX_TOKENS
+    assert bench.ALL_CONFIGS.index("qwen3_30b_a3b_moe_prefill256") == 2
