@@ -17,6 +17,16 @@
 // never matches a later launch's tag.  Every wait is bounded; on time-out the
 // workspace's error word is raised and stays raised.  No cache-wide fence is
 // involved.
+//
+// Many tokens (a prefill chunk, more than MOE_MAX_TOKENS) with bf16 x, router
+// and gate vector take two launches instead: the logits of every token as one
+// matrix product on the matrix cores (route_logits_mfma: each wave a tile of
+// 16 tokens x 16 router rows, v_mfma_f32_16x16x32_bf16, products exact and
+// fp32 sums), so the router matrix is read once per 16 tokens instead of once
+// per token; then one workgroup per token selects and scores
+// (route_select_kernel), stream-ordered after the first, so no tags or waits.
+// Its logits go to the same workspace words with tag 0, which no tagged
+// launch ever expects (tags are 1 + the epoch).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -166,6 +176,74 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     if (lane == 0 && a.wg) a.gate[t] = 1.0f / (1.0f + expf(-s_gate_logit));
 }
 
+// ------------------------------------------------------------ many tokens
+typedef __bf16 bf16x8r_t __attribute__((ext_vector_type(8)));
+constexpr int kRouteMfmaRing = 4;                // k-steps of loads in flight per lane
+
+// logits[t][row] (tag 0) for rows < E + (wg ? 1 : 0): lane (j, g) of a wave
+// loads 8 inputs of token 16 by + j (the A operand) and 8 weights of row
+// 64 bx + 16 w + j (B) per 32-wide k-step and ends with D[4 g + r][j]:
+// token 4 g + r of the tile, row j.  Rows and tokens past the end are read
+// clamped and not written.
+__global__ __launch_bounds__(256) void route_logits_mfma(RouteArgs a) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    const int g = lane >> 4, j = lane & 15;
+    const int n_rows = a.E + (a.wg ? 1 : 0);
+    const int row = blockIdx.x * 64 + wave * 16 + j, t0 = blockIdx.y * 16;
+    const int rc = min(row, n_rows - 1);
+    const uint16_t *w = rc < a.E ? reinterpret_cast<const uint16_t *>(a.wr) + (int64_t)rc * a.d_in
+                                 : reinterpret_cast<const uint16_t *>(a.wg);
+    const uint16_t *x = reinterpret_cast<const uint16_t *>(a.x) + (int64_t)min(t0 + j, a.T - 1) * a.d_in;
+    const int n_step = a.d_in / 32;
+    u32x4 xa[kRouteMfmaRing], wb[kRouteMfmaRing];
+#pragma unroll
+    for (int d = 0; d < kRouteMfmaRing; ++d) {
+        const int sd = min(d, n_step - 1);
+        xa[d] = *reinterpret_cast<const u32x4 *>(x + 32 * sd + 8 * g);
+        wb[d] = *reinterpret_cast<const u32x4 *>(w + 32 * sd + 8 * g);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < n_step; s0 += kRouteMfmaRing) {
+#pragma unroll
+        for (int d = 0; d < kRouteMfmaRing; ++d) {
+            const u32x4 av = xa[d], bv = wb[d];
+            const int sn = min(s0 + d + kRouteMfmaRing, n_step - 1);      // refill (clamped, never skipped)
+            xa[d] = *reinterpret_cast<const u32x4 *>(x + 32 * sn + 8 * g);
+            wb[d] = *reinterpret_cast<const u32x4 *>(w + 32 * sn + 8 * g);
+            if (s0 + d < n_step)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8r_t, av),
+                                                              __builtin_bit_cast(bf16x8r_t, bv), acc, 0, 0, 0);
+        }
+    }
+    if (row < n_rows) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 4 * g + r;
+            if (t < a.T) a.logits[(int64_t)t * (a.E + 1) + row] = (uint64_t)__float_as_uint(acc[r]);
+        }
+    }
+}
+
+// One workgroup per token: the token's logits (left by route_logits_mfma on
+// the same stream) staged in LDS, the block-wide top-k, the scores and the
+// shared gate, as in route_kernel's selector.
+__global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const uint64_t *logits = a.logits + (int64_t)t * (a.E + 1);
+    __shared__ __align__(16) float s_logits[MOE_MAX_EXPERTS];
+    __shared__ Selection sel;
+    stage_logits(a.E, s_logits, &sel, [&](int e) { return __uint_as_float((uint32_t)logits[e]); });
+    __syncthreads();
+    select_all(a.E, a.K, s_logits, &sel);
+    if (wave != 0) return;
+    with_per(a.E, [&](auto per) { softmax_scores<decltype(per)::value>(a.E, a.K, a.renorm, s_logits, lane, &sel); });
+    if (lane < a.K) {
+        a.ids[t * a.K + lane] = sel.ids[lane];
+        a.scores[t * a.K + lane] = sel.scores[lane];
+    }
+    if (lane == 0 && a.wg) a.gate[t] = 1.0f / (1.0f + expf(-__uint_as_float((uint32_t)logits[a.E])));
+}
+
 using RouteFn = void (*)(RouteArgs);
 
 template <int XT, int WT>
@@ -241,6 +319,13 @@ extern "C" moe_status moe_decode_route(const void *x, moe_dtype x_dtype_arg, int
     a.logits = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(workspace) + kRouteHeadBytes);
 
     const int n_rows = n_experts + (w_shared_gate ? 1 : 0);
+    if (n_tokens > MOE_MAX_TOKENS && x_dtype == MOE_BF16 && w_router_dtype == MOE_BF16 &&
+        (!w_shared_gate || w_shared_gate_dtype == MOE_BF16)) {
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        hipLaunchKernelGGL(route_logits_mfma, dim3((n_rows + 63) / 64, (n_tokens + 15) / 16), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(route_select_kernel, dim3(n_tokens), dim3(256), 0, s, a);
+        return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+    }
     dim3 grid((n_rows + kRouteWaves - 1) / kRouteWaves, n_tokens);
     RouteFn k = pick_route(x_dtype, w_router_dtype, w_shared_gate ? w_shared_gate_dtype : MOE_BF16);
     hipLaunchKernelGGL(k, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(stream), a);
