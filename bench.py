@@ -68,6 +68,8 @@ ALL_CONFIGS = [HEADLINE, "qwen3_30b_a3b_moe_batch32", "qwen3_30b_a3b_moe_prefill
 FUSED_KERNEL = "moe::layer_kernel"
 BATCH_GATE_UP_KERNEL = "moe::gate_up_batch_q4"
 GROUPED_GATE_UP_KERNEL = "moe::gate_up_grouped"
+GROUPED_DOWN_KERNEL = "moe::down_grouped"
+GROUPED_BUCKET_KERNEL = "moe::grouped_bucket_kernel"
 MAX_DECODE_TOKENS = 32          # above this the layer takes the grouped (matrix-core) expert FFN
 COPY_KERNEL = "MulFunctor"
 TOL = 2e-3
@@ -101,27 +103,37 @@ def dominant_kernel(cfg) -> str:
     return BATCH_GATE_UP_KERNEL if cfg.n_tokens <= MAX_DECODE_TOKENS else GROUPED_GATE_UP_KERNEL
 
 
+def unit_kernels(cfg) -> list:
+    """The kernels of the roofline unit: the dominant kernel, or for the
+    grouped path the three launches of one grouped expert FFN call."""
+    k = dominant_kernel(cfg)
+    return [GROUPED_BUCKET_KERNEL, k, GROUPED_DOWN_KERNEL] if k == GROUPED_GATE_UP_KERNEL else [k]
+
+
 def summarize_counters(fetch_csv, write_csv, workload, copy_mib, command) -> dict:
-    """Per-launch HBM bytes of the workload's dominant kernel from two rocprofv3
+    """Per-launch HBM bytes of the workload's roofline unit from two rocprofv3
     --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what
-    the same counter reads for the calibration copy kernel of known size."""
+    the same counter reads for the calibration copy kernel of known size (a
+    unit of several kernels: the sum of their per-dispatch means)."""
     import csv
     import moe_inputs as mi
-    kernel = dominant_kernel(mi.CONFIGS[workload])
+    kernels = unit_kernels(mi.CONFIGS[workload])
+    kernel = " + ".join(kernels)
 
     def per_kernel(path, counter):
-        k, copy = [], []
+        k, copy = {n: [] for n in kernels}, []
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
             v = float(r["Counter_Value"])
-            if kernel in r["Kernel_Name"]:
-                k.append(v)
-            elif COPY_KERNEL in r["Kernel_Name"]:
+            for n in kernels:
+                if n in r["Kernel_Name"]:
+                    k[n].append(v)
+            if COPY_KERNEL in r["Kernel_Name"]:
                 copy.append(v)
-        if not k or not copy:
+        if not all(k.values()) or not copy:
             raise SystemExit(f"{path}: no {counter} rows for {kernel} or the copy kernel")
-        return statistics.mean(k), len(k), statistics.mean(copy)
+        return sum(statistics.mean(v) for v in k.values()), min(len(v) for v in k.values()), statistics.mean(copy)
 
     known_kib = copy_mib * 1024.0
     f_k, n_f, f_copy = per_kernel(fetch_csv, "FETCH_SIZE")

@@ -287,9 +287,7 @@ __device__ __forceinline__ void in_store(const InStage<NB> &st, uint16_t *buf, f
         pair_inputs(w, wp);
         *reinterpret_cast<u32x4 *>(buf + t * kGPad + 8 * p) = u32x4{wp[0], wp[1], wp[2], wp[3]};
         float s = sum8<BF16>(w);
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
+        s = group_sum_last<8>(s);                    // DPP: every lane of the 8 gets the sum
         if ((p & 7) == 0) sums[(p >> 3) * (16 * NB) + t] = s;
     }
 }
