@@ -244,6 +244,13 @@ class GpuStateSampler:
 
 
 # ------------------------------------------------------------------ helpers
+def state_sampler(profile_run: bool):
+    """The amd-smi helper, started before anything touches the GPU; a profile
+    run starts none: under rocprofv3 the profiler has initialised the GPU
+    before this program runs, and a process that has must not start others."""
+    return None if profile_run else GpuStateSampler()
+
+
 def rel_err(got, ref) -> float:
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
@@ -739,7 +746,7 @@ def main():
     if args.samples < 10:
         raise SystemExit("--samples must be at least 10")
 
-    sampler = GpuStateSampler()                # before anything touches the GPU
+    sampler = state_sampler(args.profile_run)
     import torch
     import moe_inputs as mi
     import quantized_moe_decode_amd  # noqa: F401  (fails loudly without the built library)
@@ -754,7 +761,7 @@ def main():
             raise SystemExit(f"unknown workload {n}")
     if args.profile_run and len(names) != 1:
         raise SystemExit("--profile-run needs --config")
-    state_before = sampler.sample()
+    state_before = sampler.sample() if sampler else None
     overhead = round_trip_overhead()
     results, stacks = {}, {}
     for n in names:
@@ -768,8 +775,9 @@ def main():
             torch.cuda.empty_cache()
     stacks.clear()
     torch.cuda.empty_cache()
-    state_after = sampler.sample()
-    sampler.close()
+    state_after = sampler.sample() if sampler else None
+    if sampler:
+        sampler.close()
 
     head = results[HEADLINE] if HEADLINE in results else results[names[0]]
     ceil = None

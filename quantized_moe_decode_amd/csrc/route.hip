@@ -20,10 +20,10 @@
 //
 // Many tokens (a prefill chunk, more than MOE_MAX_TOKENS) with bf16 x, router
 // and gate vector take two launches instead: the logits of every token as one
-// matrix product on the matrix cores (route_logits_mfma: each wave a tile of
-// 16 tokens x 16 router rows, v_mfma_f32_16x16x32_bf16, products exact and
-// fp32 sums), so the router matrix is read once per 16 tokens instead of once
-// per token; then one workgroup per token selects and scores
+// matrix product on the matrix cores (route_logits_mfma: each workgroup a
+// tile of 16 tokens x 16 router rows, its four waves splitting the
+// contraction, v_mfma_f32_16x16x32_bf16, products exact and fp32 sums), so
+// the router matrix is read once per 16 tokens instead of once per token; then one workgroup per token selects and scores
 // (route_select_kernel), stream-ordered after the first, so no tags or waits.
 // Its logits go to the same workspace words with tag 0, which no tagged
 // launch ever expects (tags are 1 + the epoch).
@@ -178,42 +178,55 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
 
 // ------------------------------------------------------------ many tokens
 typedef __bf16 bf16x8r_t __attribute__((ext_vector_type(8)));
-constexpr int kRouteMfmaRing = 4;                // k-steps of loads in flight per lane
+constexpr int kRouteMfmaRing = 8;                // k-steps of loads in flight per lane
+constexpr int kRouteKSplit = 4;                  // waves per tile, each a share of the contraction
 
-// logits[t][row] (tag 0) for rows < E + (wg ? 1 : 0): lane (j, g) of a wave
-// loads 8 inputs of token 16 by + j (the A operand) and 8 weights of row
-// 64 bx + 16 w + j (B) per 32-wide k-step and ends with D[4 g + r][j]:
-// token 4 g + r of the tile, row j.  Rows and tokens past the end are read
-// clamped and not written.
-__global__ __launch_bounds__(256) void route_logits_mfma(RouteArgs a) {
+// logits[t][row] (tag 0) for rows < E + (wg ? 1 : 0), one 16-token x 16-row
+// tile per workgroup: wave w takes the 32-wide k-steps w, w + 4, ...; lane
+// (j, g) loads 8 inputs of token 16 by + j (the A operand) and 8 weights of
+// row 16 bx + j (B) per k-step and ends with D[4 g + r][j]: token 4 g + r of
+// the tile, row j.  The four waves' partial tiles are added through LDS in
+// wave order.  Rows and tokens past the end are read clamped and not written.
+__global__ __launch_bounds__(kRouteKSplit * kWave) void route_logits_mfma(RouteArgs a) {
+    __shared__ f32x4 s_part[kRouteKSplit - 1][kWave];
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
     const int g = lane >> 4, j = lane & 15;
     const int n_rows = a.E + (a.wg ? 1 : 0);
-    const int row = blockIdx.x * 64 + wave * 16 + j, t0 = blockIdx.y * 16;
+    const int row = blockIdx.x * 16 + j, t0 = blockIdx.y * 16;
     const int rc = min(row, n_rows - 1);
     const uint16_t *w = rc < a.E ? reinterpret_cast<const uint16_t *>(a.wr) + (int64_t)rc * a.d_in
                                  : reinterpret_cast<const uint16_t *>(a.wg);
     const uint16_t *x = reinterpret_cast<const uint16_t *>(a.x) + (int64_t)min(t0 + j, a.T - 1) * a.d_in;
-    const int n_step = a.d_in / 32;
+    const int n_step = a.d_in / 32;                  // this wave's k-steps: wave, wave + 4, ... < n_step
+    const int n_mine = (n_step - wave + kRouteKSplit - 1) / kRouteKSplit;
     u32x4 xa[kRouteMfmaRing], wb[kRouteMfmaRing];
 #pragma unroll
     for (int d = 0; d < kRouteMfmaRing; ++d) {
-        const int sd = min(d, n_step - 1);
+        const int sd = min(wave + kRouteKSplit * d, n_step - 1);
         xa[d] = *reinterpret_cast<const u32x4 *>(x + 32 * sd + 8 * g);
         wb[d] = *reinterpret_cast<const u32x4 *>(w + 32 * sd + 8 * g);
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < n_step; s0 += kRouteMfmaRing) {
+    for (int i0 = 0; i0 < n_mine; i0 += kRouteMfmaRing) {
 #pragma unroll
         for (int d = 0; d < kRouteMfmaRing; ++d) {
             const u32x4 av = xa[d], bv = wb[d];
-            const int sn = min(s0 + d + kRouteMfmaRing, n_step - 1);      // refill (clamped, never skipped)
+            const int sn = min(wave + kRouteKSplit * (i0 + d + kRouteMfmaRing), n_step - 1);   // refill (clamped)
             xa[d] = *reinterpret_cast<const u32x4 *>(x + 32 * sn + 8 * g);
             wb[d] = *reinterpret_cast<const u32x4 *>(w + 32 * sn + 8 * g);
-            if (s0 + d < n_step)
+            if (i0 + d < n_mine)
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8r_t, av),
                                                               __builtin_bit_cast(bf16x8r_t, bv), acc, 0, 0, 0);
         }
+    }
+    if (wave > 0) s_part[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int q = 0; q < kRouteKSplit - 1; ++q) {
+        const f32x4 p = s_part[q][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += p[r];
     }
     if (row < n_rows) {
 #pragma unroll
@@ -322,7 +335,8 @@ extern "C" moe_status moe_decode_route(const void *x, moe_dtype x_dtype_arg, int
     if (n_tokens > MOE_MAX_TOKENS && x_dtype == MOE_BF16 && w_router_dtype == MOE_BF16 &&
         (!w_shared_gate || w_shared_gate_dtype == MOE_BF16)) {
         hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-        hipLaunchKernelGGL(route_logits_mfma, dim3((n_rows + 63) / 64, (n_tokens + 15) / 16), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(route_logits_mfma, dim3((n_rows + 15) / 16, (n_tokens + 15) / 16), dim3(kRouteKSplit * kWave),
+                           0, s, a);
         hipLaunchKernelGGL(route_select_kernel, dim3(n_tokens), dim3(256), 0, s, a);
         return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
     }

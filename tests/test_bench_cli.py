@@ -76,3 +76,10 @@ def test_counter_summary_of_the_grouped_unit_sums_its_three_kernels(tmp_path):
                                          bench.GROUPED_DOWN_KERNEL])
     assert rec["hbm_bytes_per_launch"] == (2 + 1000 + 500 + 100 + 200) * 1024
     assert rec["launches"] == [2, 2]
+
+
+def test_a_profile_run_starts_no_helper_process(monkeypatch):
+    def refuse():
+        raise AssertionError("a profile run started the amd-smi helper")
+    monkeypatch.setattr(bench, "GpuStateSampler", refuse)
+    assert bench.state_sampler(True) is None
