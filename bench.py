@@ -269,6 +269,9 @@ def parse():
     ap.add_argument("--tokens", type=int, default=8,
                     help="distinct pre-generated tokens (or token batches) rotated over the steps")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
+    ap.add_argument("--expert-path", choices=["auto", "decode", "grouped"], default="auto",
+                    help="expert FFN of a multi-token step: the decode kernels (up to 32 tokens), the "
+                         "grouped matrix-core call, or auto (grouped above 32 tokens)")
     ap.add_argument("--bytes-per-sample", type=float, default=1e9,
                     help="minimum expert-weight bytes per timed sample (lower it to see the amortisation trap)")
     ap.add_argument("--min-sample-ms", type=float, default=20.0)
@@ -292,7 +295,7 @@ def parse():
 class Workload:
     """Device layers, tokens and the captured step of one workload."""
 
-    def __init__(self, cfg, n_layers, n_distinct, dev, stacks=None):
+    def __init__(self, cfg, n_layers, n_distinct, dev, stacks=None, grouped=None):
         import torch
         import moe_inputs as mi
         from quantized_moe_decode_amd.layer import (DecodeLayer, DecodeStep, stack_to_device,
@@ -313,8 +316,8 @@ class Workload:
                 if li % 12 == 11 or li == n_layers - 1:
                     log(f"[bench] {cfg.name}: {li + 1}/{n_layers} layers resident ({time.time() - t0:.1f}s)")
         self.stacks = stacks
-        self.layers = [DecodeLayer(s[0], cfg.top_k, cfg.renormalize, s[1], s[2], s[3], s[4], s[5], self.T)
-                       for s in stacks]
+        self.layers = [DecodeLayer(s[0], cfg.top_k, cfg.renormalize, s[1], s[2], s[3], s[4], s[5], self.T,
+                                   grouped=grouped) for s in stacks]
         # token r of layer l: x and resid for tokens r*T .. r*T+T-1 (first draw of each)
         self.host_x, self.host_r = [], []
         xs, rs = [], []
@@ -675,7 +678,8 @@ def run_workload(name, args, dev, overhead, shared_stacks):
     stacks = shared_stacks.get(cfg.weight_cfg_id) if cfg.n_tokens > 1 else None
     if stacks is not None and len(stacks) < L:
         stacks = None
-    wl = Workload(cfg, L, args.tokens, dev, stacks=stacks[:L] if stacks else None)
+    grouped = {"auto": None, "decode": False, "grouped": True}[args.expert_path] if cfg.n_tokens > 1 else None
+    wl = Workload(cfg, L, args.tokens, dev, stacks=stacks[:L] if stacks else None, grouped=grouped)
     shared_stacks[cfg.weight_cfg_id] = wl.stacks
     if args.profile_run:
         # for counter collection: a few plain replays of the step
@@ -702,6 +706,7 @@ def run_workload(name, args, dev, overhead, shared_stacks):
         "round_trip_overhead_us": round(overhead * 1e6, 1),
         "expert_bytes_per_step": int(mean_bytes), "other_bytes_per_step": int(wl.other_bytes_per_step()),
         "layers": L, "tokens_per_step": cfg.n_tokens, "distinct_tokens": wl.R, "path": wl.path,
+        "expert_ffn": "fused" if wl.T == 1 else ("grouped" if wl.layers[0].grouped else "decode"),
         "dtype": dtype_of(cfg),
         "config": {"workload": name, "layers": L, "tokens_per_step": cfg.n_tokens, "d_in": cfg.d_in,
                    "d_ff": cfg.d_ff, "experts": cfg.n_experts, "top_k": cfg.top_k,

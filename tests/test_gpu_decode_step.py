@@ -110,3 +110,43 @@ def test_three_call_step_with_folded_rmsnorm():
     say("case decode step: 32 tokens, 2 Qwen3 layers, next-layer RMSNorm folded, 2 batches")
     step, hx, hr, refs = build_step(specs, 2, "three-call", n_tokens=32, norm=True)
     check_replays(step, specs, hx, hr, refs, [0, 1, 0], "batch-32 step + rmsnorm")
+
+
+def test_prefill_step_grouped():
+    """256 tokens per step on 2 Qwen3-shaped layers: batched routing, the
+    grouped expert FFN and the tail captured in one graph per batch, replayed
+    in rotated order; sampled tokens of every layer against the oracle after
+    every replay."""
+    from quantized_moe_decode_amd.layer import DecodeStep, layer_from_host, tensor_from_encoded
+    cfg, T, n_b = mi.QWEN3_P256, 256, 2
+    say("case decode step: 256 tokens per step (grouped), 2 Qwen3 layers, 2 batches")
+    sample = np.array([0, 37, 128, 255])
+    layers, hx, hr, refs = [], [], [], {}
+    for li in range(2):
+        w = mi.gen_layer_weights(cfg, li)
+        lay = layer_from_host(cfg, w, DEV, n_tokens=T)
+        assert lay.grouped
+        layers.append(lay)
+        x, r, _ = pick_tokens(cfg, li, n_b * T, w["router"])
+        hx.append(x.reshape(n_b, T, -1))
+        hr.append(r.reshape(n_b, T, -1))
+        for b in range(n_b):
+            refs[(b, li)] = oracle_layer_selected(cfg, li, hx[li][b][sample], hr[li][b][sample])
+        del w
+    xs = [[tensor_from_encoded(hx[l][b], cfg.x_dtype, DEV) for l in range(2)] for b in range(n_b)]
+    rs = [[tensor_from_encoded(hr[l][b], cfg.resid_dtype, DEV) for l in range(2)] for b in range(n_b)]
+    step = DecodeStep(layers, xs, rs, path="three-call")
+    step.capture()
+    for i, b in enumerate([0, 1, 1, 0]):
+        for o in step.outs:
+            o.fill_(-1.0)
+        for lay in step.layers:
+            lay.ids.fill_(-1)
+        step.replay(b)
+        torch.cuda.synchronize()
+        for l in range(2):
+            lay = step.layers[l]
+            gpu = dict(ids=lay.ids.cpu().numpy()[sample], scores=lay.scores.cpu().numpy()[sample],
+                       act=None, partial=None, out=step.outs[l].cpu().numpy()[sample])
+            compare_layer(cfg, None, hx[l][b][sample], hr[l][b][sample], gpu,
+                          f"prefill step replay {i} batch {b} layer {l}", ref=refs[(b, l)])
