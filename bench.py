@@ -264,11 +264,16 @@ def parse():
     ap.add_argument("--steps", type=int, default=300,
                     help="headline: at least this many timed steps over all samples")
     ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup-ms", type=float, default=200.0,
+                    help="after the warm-up steps, keep replaying for at least this long before timing")
     ap.add_argument("--samples", type=int, default=10)
     ap.add_argument("--config", default="all", help="a workload name, or 'all'")
     ap.add_argument("--tokens", type=int, default=8,
                     help="distinct pre-generated tokens (or token batches) rotated over the steps")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
+    ap.add_argument("--steps-per-graph", type=int, default=0,
+                    help="steps captured per graph replay (0: 32 for a one-layer workload, whose step is "
+                         "shorter than the host's graph launch, else 1)")
     ap.add_argument("--expert-path", choices=["auto", "decode", "grouped"], default="auto",
                     help="expert FFN of a multi-token step: the decode kernels (up to 32 tokens), the "
                          "grouped matrix-core call, or auto (grouped above 32 tokens)")
@@ -295,7 +300,7 @@ def parse():
 class Workload:
     """Device layers, tokens and the captured step of one workload."""
 
-    def __init__(self, cfg, n_layers, n_distinct, dev, stacks=None, grouped=None):
+    def __init__(self, cfg, n_layers, n_distinct, dev, stacks=None, grouped=None, repeat=1):
         import torch
         import moe_inputs as mi
         from quantized_moe_decode_amd.layer import (DecodeLayer, DecodeStep, stack_to_device,
@@ -336,7 +341,7 @@ class Workload:
             xs.append(dx)
             rs.append(dr)
         self.path = "fused" if self.T == 1 else "three-call"
-        self.step = DecodeStep(self.layers, xs, rs, path=self.path)
+        self.step = DecodeStep(self.layers, xs, rs, path=self.path, repeat=repeat)
         self.step.capture()
         g0 = self.layers[0]
         self.per_expert = g0.gate.nbytes() + g0.up.nbytes() + g0.down.nbytes()
@@ -405,20 +410,25 @@ def round_trip_overhead() -> float:
 def measure(wl, args, overhead, min_steps=0):
     """The sample protocol: n sized from the round trip, the sample bytes and
     duration; >= args.samples samples; a 2n sample for the amortisation check."""
-    R = wl.R
+    R, rep = wl.R, wl.step.repeat                  # one replay = rep steps
     for i in range(args.warmup):
         wl.step.replay(i % R)
-    pilot = timed_replays(wl.step, max(3, R), R) / max(3, R)
+    # and at least --warmup-ms of replays, so that the clocks have left their
+    # idle state before a short step is timed
+    t_end = time.perf_counter() + args.warmup_ms * 1e-3
+    while time.perf_counter() < t_end:
+        timed_replays(wl.step, 4 * R, R)
+    pilot = timed_replays(wl.step, max(3, R), R) / max(3, R)    # per replay
     mean_bytes = float(np.mean(wl.step_bytes))
     n = max(1, int(np.ceil(50.0 * overhead / pilot)),            # round trip < 2% of a sample
-            int(np.ceil(args.bytes_per_sample / mean_bytes)),    # >= bytes_per_sample per sample
+            int(np.ceil(args.bytes_per_sample / (mean_bytes * rep))),   # >= bytes_per_sample per sample
             int(np.ceil(args.min_sample_ms * 1e-3 / pilot)),
-            int(np.ceil(min_steps / args.samples)))
-    samples = [timed_replays(wl.step, n, R, offset=k * n) / n for k in range(args.samples)]
-    two_n = timed_replays(wl.step, 2 * n, R) / (2 * n)
+            int(np.ceil(min_steps / (args.samples * rep))))
+    samples = [timed_replays(wl.step, n, R, offset=k * n) / (n * rep) for k in range(args.samples)]
+    two_n = timed_replays(wl.step, 2 * n, R) / (2 * n * rep)
     med = statistics.median(samples)
-    return dict(n=n, samples=samples, median=med, min=min(samples), max=max(samples),
-                amortisation_ratio_2n=two_n / med, pilot=pilot)
+    return dict(n=n * rep, samples=samples, median=med, min=min(samples), max=max(samples),
+                amortisation_ratio_2n=two_n / med, pilot=pilot / rep)
 
 
 def step_bytes_for(wl, n, offset=0):
@@ -500,7 +510,7 @@ def other_path(wl, args):
         graphs[i % wl.R].replay()
     e1.record(stream)
     torch.cuda.synchronize()
-    secs = e0.elapsed_time(e1) / 1000.0
+    secs = e0.elapsed_time(e1) / 1000.0 / wl.step.repeat     # one replay = repeat steps
     import quantized_moe_decode_amd as qmd
     ok = all(qmd.workspace_status(l.route_ws) == qmd.MOE_OK for l in wl.layers)
     if not ok:
@@ -644,7 +654,8 @@ def rmsnorm_fold_cost(wl, meas, dev):
         wl.step.capture()
         for i in range(max(10, wl.R)):
             wl.step.replay(i % wl.R)
-        return statistics.median(timed_replays(wl.step, n, wl.R, offset=k * n) / n for k in range(5)) * 1e3
+        return statistics.median(timed_replays(wl.step, n, wl.R, offset=k * n) / (n * wl.step.repeat)
+                                 for k in range(5)) * 1e3
 
     plain = step_ms()
     res = {"ms_per_step_plain": round(plain, 4)}
@@ -679,7 +690,8 @@ def run_workload(name, args, dev, overhead, shared_stacks):
     if stacks is not None and len(stacks) < L:
         stacks = None
     grouped = {"auto": None, "decode": False, "grouped": True}[args.expert_path] if cfg.n_tokens > 1 else None
-    wl = Workload(cfg, L, args.tokens, dev, stacks=stacks[:L] if stacks else None, grouped=grouped)
+    repeat = args.steps_per_graph or (32 if L == 1 else 1)
+    wl = Workload(cfg, L, args.tokens, dev, stacks=stacks[:L] if stacks else None, grouped=grouped, repeat=repeat)
     shared_stacks[cfg.weight_cfg_id] = wl.stacks
     if args.profile_run:
         # for counter collection: a few plain replays of the step
@@ -707,6 +719,7 @@ def run_workload(name, args, dev, overhead, shared_stacks):
         "expert_bytes_per_step": int(mean_bytes), "other_bytes_per_step": int(wl.other_bytes_per_step()),
         "layers": L, "tokens_per_step": cfg.n_tokens, "distinct_tokens": wl.R, "path": wl.path,
         "expert_ffn": "fused" if wl.T == 1 else ("grouped" if wl.layers[0].grouped else "decode"),
+        "steps_per_graph": wl.step.repeat,
         "dtype": dtype_of(cfg),
         "config": {"workload": name, "layers": L, "tokens_per_step": cfg.n_tokens, "d_in": cfg.d_in,
                    "d_ff": cfg.d_ff, "experts": cfg.n_experts, "top_k": cfg.top_k,
@@ -812,6 +825,7 @@ def main():
         "n_gpus": 1,
         "steps": head["samples"] * head["steps_per_sample"],
         "warmup": args.warmup,
+        "warmup_ms": args.warmup_ms,
         "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",

@@ -185,16 +185,19 @@ class DecodeStep:
     tensors xs[r][l], rs[r][l]; layer l writes outs[l] [T, d_in] of
     out_dtype (fp32, bf16 or fp16) and its routing into layers[l].ids /
     .scores.  Layers run back to back: no work of layer l + 1 starts before
-    layer l has finished.
+    layer l has finished.  repeat > 1 captures the step that many times into
+    each token's graph (one replay = repeat steps on the same token), for
+    steps so short that the host's graph launches would set the pace.
     """
 
     def __init__(self, layers: Sequence[DecodeLayer], xs, rs, path: str = "fused",
-                 share_workspace: bool = True, out_dtype: torch.dtype = torch.float32):
+                 share_workspace: bool = True, out_dtype: torch.dtype = torch.float32, repeat: int = 1):
         if path not in ("fused", "three-call"):
             raise ValueError(path)
         if path == "fused" and any(l.n_tokens != 1 for l in layers):
             raise ValueError("the fused launch takes one token per step")
         self.layers, self.xs, self.rs, self.path = list(layers), xs, rs, path
+        self.repeat = max(1, int(repeat))
         dev = layers[0].router.device
         self.outs = [torch.zeros(l.n_tokens, l.d_in, device=dev, dtype=out_dtype) for l in layers]
         self.fused_ws = share_fused_workspace(self.layers) if (path == "fused" and share_workspace) else None
@@ -226,7 +229,8 @@ class DecodeStep:
         for r in range(self.n_distinct):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                self.eager(r, path)
+                for _ in range(self.repeat):
+                    self.eager(r, path)
             graphs.append(g)
         torch.cuda.synchronize()
         if path is None or path == self.path:

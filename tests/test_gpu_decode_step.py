@@ -150,3 +150,26 @@ def test_prefill_step_grouped():
                        act=None, partial=None, out=step.outs[l].cpu().numpy()[sample])
             compare_layer(cfg, None, hx[l][b][sample], hr[l][b][sample], gpu,
                           f"prefill step replay {i} batch {b} layer {l}", ref=refs[(b, l)])
+
+
+def test_steps_repeated_in_one_graph_give_the_single_step():
+    """DecodeStep(repeat=4): each replay runs the step four times on the same
+    token; the outputs equal those of the one-step graph bit for bit and the
+    oracle's (the tiny layer, fused and three-call)."""
+    from quantized_moe_decode_amd.layer import DecodeStep
+    specs = [(mi.TINY, 0)]
+    for path in ("fused", "three-call"):
+        say(f"case decode step: tiny layer, 4 steps per graph, {path}")
+        step, hx, hr, refs = build_step(specs, 2, path)
+        step.capture()
+        single = []
+        for t in range(2):
+            step.replay(t)
+            torch.cuda.synchronize()
+            single.append(step.outs[0].clone())
+        rstep = DecodeStep(step.layers, step.xs, step.rs, path=path, repeat=4)
+        check_replays(rstep, specs, hx, hr, refs, [0, 1, 1, 0], f"{path} x4")
+        for t in range(2):
+            rstep.replay(t)
+            torch.cuda.synchronize()
+            assert torch.equal(rstep.outs[0], single[t]), f"{path}: repeated step differs from one step"
