@@ -209,8 +209,8 @@ size_t moe_decode_expert_ffn_noalloc_max_bytes(void);
  * moe_decode_expert_ffn for larger batches and prefill, on the matrix cores:
  * the same outputs (act and partial, same layouts, same zero rows for ids
  * outside [0, n_experts)) for up to MOE_MAX_GROUPED_TOKENS tokens.  The
- * (token, slot) pairs are grouped by expert into work items of up to 16, 32
- * or 64 pairs, and each work item is a small GEMM per expert (meTile PR #30,
+ * (token, slot) pairs are grouped by expert into work items of up to 16 or
+ * 32 pairs, and each work item is a small GEMM per expert (meTile PR #30,
  * the GB/s table and its reading: a GEMM path pays only from about 32 rows,
  * i.e. batch or prefill, not single-token decode).  Supported: 4-bit gate,
  * up and down codes with bf16 or fp16 scales, bf16 x; anything else is

@@ -10,8 +10,8 @@
 // only from 32 rows, batch or prefill).
 //
 // Work decomposition.  The (token, slot) pairs are grouped by expert and each
-// expert's list is cut into work items of up to NT = 16 NB pairs (NB = 1, 2
-// or 4, chosen from the average number of pairs per expert).  A workgroup of
+// expert's list is cut into work items of up to NT = 16 NB pairs (NB = 1 or
+// 2, chosen from the average number of pairs per expert).  A workgroup of
 // eight waves takes one work item and 128 weight rows of it; each wave owns
 // 16 rows and multiplies them with every 16-pair block of the item using
 // v_mfma_f32_16x16x32 (lane l holds A[l % 16][8 (l / 16) + i],
@@ -644,10 +644,12 @@ __global__ __launch_bounds__(kGThreads) void down_grouped(GroupedArgs a) {
 static int grouped_max_work(int n_pairs, int E, int nt) { return (n_pairs + nt - 1) / nt + E + 1; }
 
 // Pairs per work item: 16 NB, from the average number of pairs per expert.
-static int grouped_nb(int n_pairs, int E) {
-    const int avg = n_pairs / E;
-    return avg <= 12 ? 1 : avg <= 40 ? 2 : 4;
-}
+// Measured on the Qwen3-shaped layer: 16-pair items are faster up to about 8
+// pairs per expert (128 tokens: 108 against 116 us per call), 32-pair items
+// above (192 tokens: 117 against 129 us); 64-pair items (each expert read
+// once up to 64 pairs, but 166 VGPRs: two waves per SIMD) were never faster
+// (256 tokens 203 against 136 us, 1024 tokens 308 against 292 us).
+static int grouped_nb(int n_pairs, int E) { return n_pairs / E <= 9 ? 1 : 2; }
 
 // Workspace: the work lists (int32), then act16, then act_cs, each 256-byte aligned.
 struct GroupedLayout {
@@ -737,10 +739,9 @@ extern "C" moe_status moe_decode_expert_ffn_grouped(const void *x, moe_dtype x_d
     hipLaunchKernelGGL(grouped_bucket_kernel, dim3(1), dim3(kGBucketThreads), 0, s, expert_ids, n_pairs, E, nt, ws,
                        ws + 1, ws + 1 + mw_ws, ws + 1 + 2 * mw_ws, ws + 1 + 3 * mw_ws);
     const bool bf = sb == MOE_BF16;
-    switch (nb) {
-    case 1: bf ? launch_grouped<MOE_BF16, 1>(a, mw, s) : launch_grouped<MOE_F16, 1>(a, mw, s); break;
-    case 2: bf ? launch_grouped<MOE_BF16, 2>(a, mw, s) : launch_grouped<MOE_F16, 2>(a, mw, s); break;
-    default: bf ? launch_grouped<MOE_BF16, 4>(a, mw, s) : launch_grouped<MOE_F16, 4>(a, mw, s); break;
-    }
+    if (nb == 1)
+        bf ? launch_grouped<MOE_BF16, 1>(a, mw, s) : launch_grouped<MOE_F16, 1>(a, mw, s);
+    else
+        bf ? launch_grouped<MOE_BF16, 2>(a, mw, s) : launch_grouped<MOE_F16, 2>(a, mw, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
