@@ -75,6 +75,7 @@ struct GroupedArgs {
     const int32_t *work_count;       // [max_work]: pairs (1..NT)
     const int32_t *pair_list;        // [T*K] pair indices t*K + k, grouped by expert
     int row_blocks;                  // workgroups per work item
+    int res_rb;                      // down_grouped_res: row blocks per workgroup
 };
 
 // Pairs (v[p], v[p+4]) of 8 consecutive 16-bit inputs held as 4 words: the
@@ -641,6 +642,161 @@ __global__ __launch_bounds__(kGThreads) void down_grouped(GroupedArgs a) {
     }
 }
 
+// Kernel B with the item's whole act resident in LDS (when it fits): act16,
+// its group sums and block factors staged once per workgroup, then res_rb
+// row blocks of 128 rows in turn, each with all its groups' scales staged at
+// once, so the contraction runs without a barrier per chunk.  Same operand
+// roles and arithmetic as down_grouped.  Dynamic LDS: [NT][d_ff + 8] act16,
+// [n_grp][NT] sums, [n_blk][NT] factors, [n_grp][128][2] scales.
+// Row blocks per workgroup: 4 with at least 64 work items (1 / 2 / 4
+// measured on the Qwen3-shaped layer, 4 fastest from 128 tokens: 256 tokens
+// 125 -> 117 us per call), else 1 (with few experts touched, fewer
+// workgroups would leave CUs idle: 1 token 30 -> 40 us at 4).
+constexpr int kGResRBMany = 4, kGResManyItems = 64;
+constexpr size_t kGResLdsMax = 64 * 1024 - 512;    // dynamic LDS within the default per-workgroup limit
+
+__host__ __device__ constexpr int res_row_pad(int d_ff) { return d_ff + 8; }
+
+static size_t res_lds_bytes(int nt, int d_ff) {
+    const int n_grp = d_ff / kGroup, n_blk = (d_ff + kGRows - 1) / kGRows;
+    return align_up((size_t)nt * res_row_pad(d_ff) * 2, 16) + (size_t)n_grp * nt * 4 + (size_t)n_blk * nt * 4 +
+           (size_t)n_grp * kGRows * 8;
+}
+
+template <int SB, int NB>
+__global__ __launch_bounds__(kGThreads) void down_grouped_res(GroupedArgs a) {
+    constexpr int NT = 16 * NB;
+    extern __shared__ __align__(16) unsigned char g_lds[];
+    __shared__ int s_pair[NT];
+    __shared__ float s_score[NT];
+    int w, rbb;
+    item_and_block(a.row_blocks, w, rbb);          // row_blocks counts groups of res_rb row blocks
+    if (w >= *a.n_work) return;
+    const int e = a.work_expert[w], begin = a.work_begin[w], count = a.work_count[w];
+    const int n_rb = (a.d_in + kGRows - 1) / kGRows;
+    if (e < 0) {
+        zero_rows(a.partial, a.d_in, a, begin, count, rbb * a.res_rb * kGRows,
+                  min((rbb + 1) * a.res_rb * kGRows, a.d_in));
+        return;
+    }
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int g = lane >> 4, j = lane & 15;
+    const int n = a.d_ff, n_grp = n / kGroup, n_chunk = (n_grp + kGChunkGroups - 1) / kGChunkGroups;
+    const int pad = res_row_pad(n);
+    uint16_t *s_a = reinterpret_cast<uint16_t *>(g_lds);
+    float *s_as = reinterpret_cast<float *>(g_lds + ((size_t)NT * pad * 2 + 15) / 16 * 16);
+    float *s_cs = s_as + n_grp * NT;
+    float *s_sb = s_cs + a.n_blk * NT;
+    if (tid < NT) {
+        const int p = tid < count ? a.pair_list[begin + tid] : -1;
+        s_pair[tid] = p;
+        s_score[tid] = p >= 0 && a.scores ? a.scores[p] : 1.0f;
+    }
+    // the item's act16 rows: 16-byte pieces q = tid + 512 i, slot q / (n / 8),
+    // piece q % (n / 8) (eight consecutive lanes hold one group of 64), stored
+    // in the codes' pair order with their group sums
+    {
+        const int ppr = n / 8, n_pc = NT * ppr;
+        for (int q0 = 0; q0 < n_pc; q0 += kGThreads) {
+            const int q = q0 + tid, t = min(q / ppr, NT - 1), c = q % ppr;
+            const bool live = q < n_pc && t < count;
+            const int64_t row = (int64_t)a.pair_list[begin + (t < count ? t : 0)] * n;
+            uint32_t wv[4], wp[4];
+            words_of(*reinterpret_cast<const u32x4 *>(a.act16 + row + 8 * c), wv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wv[i] = live ? wv[i] : 0u;
+            pair_inputs(wv, wp);
+            if (q < n_pc) *reinterpret_cast<u32x4 *>(s_a + t * pad + 8 * c) = u32x4{wp[0], wp[1], wp[2], wp[3]};
+            const float sm = group_sum_last<8>(sum8<false>(wv));
+            if (q < n_pc && (c & 7) == 0) s_as[(c >> 3) * NT + t] = sm;
+        }
+        for (int i = tid; i < a.n_blk * NT; i += kGThreads) {
+            const int blk = i / NT, t = i % NT;
+            s_cs[i] = t < count ? a.act_cs[(int64_t)a.pair_list[begin + t] * a.n_blk + blk] : 0.f;
+        }
+    }
+    const f16x2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
+    const int64_t erow = (int64_t)e * a.d_in;
+    const int rowl = wave * 16 + j, xo = code_word_input(g);
+    for (int rbi = 0; rbi < a.res_rb; ++rbi) {
+        const int rb = rbb * a.res_rb + rbi;
+        if (rb >= n_rb) break;                               // uniform over the workgroup
+        const int row0 = rb * kGRows;
+        const int ra = min(row0 + rowl, a.d_in - 1);
+        const uint32_t *qd = a.down.q + (erow + ra) * a.down.wpr;
+        u32x4 rw[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) rw[p] = *code_pair_addr(qd, 2 * p, n_grp, g);
+        __syncthreads();                                     // the previous row block's scale readers are done
+        for (int i = tid; i < n_grp * kGRows; i += kGThreads) {
+            const int G = i / kGRows, r = i % kGRows;
+            const int64_t o = (erow + min(row0 + r, a.d_in - 1)) * a.down.gpr + G;
+            *reinterpret_cast<float2 *>(&s_sb[(G * kGRows + r) * 2]) =
+                make_float2(sb_to_float<SB>(a.down.s[o]), sb_to_float<SB>(a.down.b[o]));
+        }
+        __syncthreads();
+        f32x4 acc[NB];
+#pragma unroll
+        for (int m = 0; m < NB; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < n_chunk; ++c) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                uint32_t wd[4];
+                spread_code_pair(rw[p], wd);
+                rw[p] = *code_pair_addr(qd, (c + 1) * kGChunkGroups + 2 * p, n_grp, g);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int G = c * kGChunkGroups + 2 * p + h;
+                    if (G >= n_grp) continue;
+                    const float sd = s_sb[(G * kGRows + rowl) * 2];
+                    uint32_t pq[2][4];
+                    nibble_pairs<0x64u>(wd[2 * h], pq[0]);
+                    nibble_pairs<0x64u>(wd[2 * h + 1], pq[1]);
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            pq[s2][i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, pq[s2][i]) - off);
+#pragma unroll
+                    for (int m = 0; m < NB; ++m) {
+                        const uint16_t *ar = s_a + (16 * m + j) * pad + G * kGroup + xo;
+                        f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s2 = 0; s2 < 2; ++s2)
+                            t4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4 *>(ar + 8 * s2)),
+                                __builtin_bit_cast(f16x8_t, u32x4{pq[s2][0], pq[s2][1], pq[s2][2], pq[s2][3]}), t4,
+                                0, 0, 0);
+                        const f32x4 cs = *reinterpret_cast<const f32x4 *>(&s_cs[(G * kGroup / kGRows) * NT + 16 * m + 4 * g]);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[m][r] += (cs[r] * sd) * t4[r];
+                    }
+                }
+            }
+            // the chunk's bias terms as one fp32 16x16x4 MFMA per pair block (a
+            // group past the end: zero sum and zero bias)
+            const int Gb = c * kGChunkGroups + g;
+            const bool gok = Gb < n_grp;
+            const float bv = gok ? s_sb[(Gb * kGRows + rowl) * 2 + 1] : 0.f;
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+                const float av = gok ? s_as[Gb * NT + 16 * m + j] * s_cs[(Gb * kGroup / kGRows) * NT + 16 * m + j] : 0.f;
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[m], 0, 0, 0);
+            }
+        }
+        const int row = row0 + rowl;
+        if (row < a.d_in) {
+#pragma unroll
+            for (int m = 0; m < NB; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * m + 4 * g + r;
+                    if (t < count) a.partial[(int64_t)s_pair[t] * a.d_in + row] = s_score[t] * acc[m][r];
+                }
+        }
+    }
+}
+
 static int grouped_max_work(int n_pairs, int E, int nt) { return (n_pairs + nt - 1) / nt + E + 1; }
 
 // Pairs per work item: 16 NB, from the average number of pairs per expert.
@@ -671,9 +827,17 @@ static void launch_grouped(const GroupedArgs &a, int mw, hipStream_t s) {
     const int items8 = (mw + 7) / 8 * 8;
     GroupedArgs ga = a, gb = a;
     ga.row_blocks = (a.d_ff + kGRows - 1) / kGRows;
-    gb.row_blocks = (a.d_in + kGRows - 1) / kGRows;
     hipLaunchKernelGGL((gate_up_grouped<SB, NB>), dim3(items8 * ga.row_blocks), dim3(kGThreads), 0, s, ga);
-    hipLaunchKernelGGL((down_grouped<SB, NB>), dim3(items8 * gb.row_blocks), dim3(kGThreads), 0, s, gb);
+    const int n_rb = (a.d_in + kGRows - 1) / kGRows;
+    const size_t lds = res_lds_bytes(16 * NB, a.d_ff);
+    if (lds <= kGResLdsMax) {
+        gb.res_rb = a.T * a.K / (16 * NB) >= kGResManyItems ? kGResRBMany : 1;
+        gb.row_blocks = (n_rb + gb.res_rb - 1) / gb.res_rb;
+        hipLaunchKernelGGL((down_grouped_res<SB, NB>), dim3(items8 * gb.row_blocks), dim3(kGThreads), lds, s, gb);
+    } else {
+        gb.row_blocks = n_rb;
+        hipLaunchKernelGGL((down_grouped<SB, NB>), dim3(items8 * gb.row_blocks), dim3(kGThreads), 0, s, gb);
+    }
 }
 
 }  // namespace moe
@@ -735,6 +899,7 @@ extern "C" moe_status moe_decode_expert_ffn_grouped(const void *x, moe_dtype x_d
     a.act16 = reinterpret_cast<uint16_t *>(wsb + L.act16);
     a.act_cs = reinterpret_cast<float *>(wsb + L.act_cs);
     a.row_blocks = 1;
+    a.res_rb = 1;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipLaunchKernelGGL(grouped_bucket_kernel, dim3(1), dim3(kGBucketThreads), 0, s, expert_ids, n_pairs, E, nt, ws,
                        ws + 1, ws + 1 + mw_ws, ws + 1 + 2 * mw_ws, ws + 1 + 3 * mw_ws);

@@ -159,6 +159,31 @@ def test_grouped_full_size_1024_tokens():
     check(cfg, w, x, ids, scores, "grouped qwen3 T=1024", tokens=np.arange(5, T, 67))
 
 
+def test_grouped_resident_down_many_items_ragged_row_blocks():
+    """512 tokens x top-4 on 9 experts (64 work items of 32 pairs): the down
+    kernel keeps act resident in LDS and takes four row blocks per workgroup;
+    d_in 1088 has 9 row blocks, so the last workgroup of an item has one."""
+    cfg = small_cfg(d_in=1088, d_ff=704, n_experts=9, top_k=4)
+    say("case grouped resident down, 4 row blocks per workgroup, ragged")
+    w = mi.gen_layer_weights(cfg, 5, threads=4)
+    T = 512
+    x, _ = mi.gen_tokens(cfg, 5, T)
+    ids, scores = random_routing(T, cfg.top_k, cfg.n_experts, seed=512)
+    check(cfg, w, x, ids, scores, "grouped resident ragged", tokens=np.arange(0, T, 9))
+
+
+def test_grouped_chunked_down_when_act_does_not_fit():
+    """d_ff 1408 with 32-pair items: act (89 KB as fp16) does not fit the
+    resident kernel's LDS, so the down projection takes the chunked kernel."""
+    cfg = small_cfg(d_in=256, d_ff=1408, n_experts=4, top_k=2)
+    say("case grouped chunked down (d_ff 1408)")
+    w = mi.gen_layer_weights(cfg, 6, threads=4)
+    T = 64
+    x, _ = mi.gen_tokens(cfg, 6, T)
+    ids, scores = random_routing(T, cfg.top_k, cfg.n_experts, seed=64)
+    check(cfg, w, x, ids, scores, "grouped chunked down")
+
+
 def test_grouped_rejects_unsupported_formats():
     import quantized_moe_decode_amd as q
     cfg = small_cfg(d_in=256, d_ff=192, n_experts=6, top_k=2, bits_down=8)
