@@ -2,6 +2,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "api.hpp"
 #include "layer_kernel.hpp"
@@ -124,13 +127,27 @@ static moe_status plan_layer(const moe_layer_weights *w, int d_in_check, LayerPl
 
 // Workgroups of `k` that can be resident at once on the current device (0 if
 // the runtime cannot tell).
+// Workgroups of kernel k with lds bytes of dynamic LDS that fit on the
+// current device at once, asked of the runtime once per (kernel, LDS size,
+// device) and remembered; 0 if the runtime cannot tell.
 static int resident_capacity(LayerFn k, size_t lds) {
-    int dev = 0, cus = 0, per_cu = 0;
+    int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
+    static std::mutex mu;
+    static std::map<std::tuple<const void *, size_t, int>, int> known;
+    const auto key = std::make_tuple(reinterpret_cast<const void *>(k), lds, dev);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        const auto it = known.find(key);
+        if (it != known.end()) return it->second;
+    }
+    int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(k), kLayerThreads, lds) !=
         hipSuccess)
         return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    known[key] = cus * per_cu;
     return cus * per_cu;
 }
 
@@ -148,9 +165,9 @@ static int resident_capacity(LayerFn k, size_t lds) {
 // dots.llm1-shaped layer 50.7 us with single-pass B units that do not all
 // fit, 37.8 us with 4-pass B units and 2-pass A units; the Qwen1.5-shaped
 // layer is best with single-pass B units).  Ties go to single-stage A
-// units, then to fewer B passes; if nothing fits, the smallest grid.
-// cap1, cap2: resident capacity with single-stage and with pipelined units
-// (0 if unknown).
+// units, then to fewer B passes; if nothing fits, or the capacity is
+// unknown, the smallest grid.  cap1, cap2: resident capacity with
+// single-stage and with pipelined units (0 if unknown).
 static void fit_a_passes(LayerPlan &p, int cap1, int cap2) {
     LayerArgs &a = p.a;
     const int slots = a.K + a.S;
@@ -175,7 +192,7 @@ static void fit_a_passes(LayerPlan &p, int cap1, int cap2) {
         if (!have_small || grid < smallest.grid) { smallest = l; have_small = true; }
         // the router workgroups exit within ~2 us, long before routing is
         // done, so up to n_route units past the capacity start in their place
-        if (cap > 0 && grid > cap + a.n_route) return false;
+        if (cap <= 0 || grid > cap + a.n_route) return false;
         if (!have || l.cost < best.cost) { best = l; have = true; }
         return true;
     };
