@@ -130,13 +130,15 @@ moe_status moe_decode_route(const void *x, moe_dtype x_dtype, int32_t n_tokens, 
 size_t moe_decode_route_workspace_bytes(int32_t n_tokens, int32_t n_experts);
 
 /*
- * Status recorded in the workspace of moe_decode_route or moe_decode_layer.
+ * Status recorded in the workspace of moe_decode_route, moe_decode_layer or
+ * moe_decode_expert_ffn_grouped.
  * `head` is a host copy of the first MOE_WORKSPACE_HEAD_BYTES bytes of the
  * workspace, taken after the stream has passed the calls of interest (the
  * library itself never copies device memory).  Returns MOE_OK, or
  * MOE_ETIMEOUT when a wait inside some launch that used the workspace ran out
- * since the workspace was last zero-filled (that launch's results are
- * invalid); MOE_EINVAL for a null `head` or head_bytes <
+ * since the workspace was last zero-filled (route, layer) or within the last
+ * call (grouped expert FFN, whose calls clear the word); that launch's
+ * results are invalid.  MOE_EINVAL for a null `head` or head_bytes <
  * MOE_WORKSPACE_HEAD_BYTES.  Host-only; no device access.
  */
 #define MOE_WORKSPACE_HEAD_BYTES 4
@@ -221,8 +223,14 @@ size_t moe_decode_expert_ffn_noalloc_max_bytes(void);
  * fitted to the largest magnitude of each block of 128 of a pair's values
  * (exact, undone per group).  Within 2e-3 of the result's infinity norm.
  * workspace: moe_decode_expert_ffn_grouped_workspace_bytes() bytes (the work
- * lists and the fp16 copy of act), 16-byte aligned, no zeroing needed;
- * asynchronous on `stream`.
+ * lists, per-item counters and the fp16 copy of act), 16-byte aligned, no
+ * zeroing needed; asynchronous on `stream`.  Its first
+ * MOE_WORKSPACE_HEAD_BYTES bytes are an error word that each call clears:
+ * when act fits the down units' LDS the call runs gate/up and down in one
+ * launch, where a down unit waits (bounded) for the gate/up units of its
+ * work item; if such a wait ran out, that call's results are invalid and
+ * moe_decode_workspace_status on a host copy of the head reports
+ * MOE_ETIMEOUT.  Calls that may overlap need separate workspaces.
  */
 moe_status moe_decode_expert_ffn_grouped(const void *x, moe_dtype x_dtype, int32_t n_tokens,
                                          const moe_qmat *gate, const moe_qmat *up, const moe_qmat *down,

@@ -39,7 +39,18 @@
 // 128 values in the workgroup's row block (f16_stage_scale); the factor's
 // inverse is kept per (pair, block) and applied to each group's dot products
 // in kernel B (exact: a power of two).
+//
+// Launches: a bucketing workgroup, then (when act fits a down unit's LDS) one
+// launch of gate/up units followed by down units that wait per work item for
+// its gate/up units (ffn_grouped_fused), else a gate/up launch and a chunked
+// down launch.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "api.hpp"
 #include "common.hpp"
@@ -55,6 +66,7 @@ constexpr int kGChunk = kGChunkGroups * kGroup;  // 256 inputs
 constexpr int kGPad = kGChunk + 8;               // 16-bit values per staged token row
 constexpr int kGMinTok = 16;                     // smallest work item tile (sizes the workspace)
 constexpr int kGBucketThreads = 1024;
+constexpr int kGResIters = 8;                    // staging loads per thread, at most (resident x / act16, scales)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -74,8 +86,13 @@ struct GroupedArgs {
     const int32_t *work_begin;       // [max_work]: first index into pair_list
     const int32_t *work_count;       // [max_work]: pairs (1..NT)
     const int32_t *pair_list;        // [T*K] pair indices t*K + k, grouped by expert
-    int row_blocks;                  // workgroups per work item
-    int res_rb;                      // down_grouped_res: row blocks per workgroup
+    int row_blocks;                  // workgroups (units) per work item: gate/up kernel / unit
+    int res_rb;                      // resident down units: row blocks per unit
+    // the one-launch path (ffn_grouped_fused)
+    int row_blocks_b;                // down units per work item
+    int grid_a;                      // workgroups of gate/up units (a multiple of 8)
+    int32_t *err;                    // raised when a wait runs out
+    int32_t *done;                   // [max_work]: gate/up units finished per work item
 };
 
 // Pairs (v[p], v[p+4]) of 8 consecutive 16-bit inputs held as 4 words: the
@@ -112,11 +129,20 @@ __device__ __forceinline__ const u32x4 *code_pair_addr(const uint32_t *row, int 
     return reinterpret_cast<const u32x4 *>(row + min(G + (g >> 1), n_grp - 1) * 8 + 4 * (g & 1));
 }
 
+// A register copy the compiler keeps (a DPP move with the identity pattern).
+__device__ __forceinline__ uint32_t kept_copy(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xE4, 0xF, 0xF, false);
+}
+
+// The swaps act on copies of the loaded words: v_permlane32_swap overwrites
+// both its operands, and on the words themselves it led the register
+// allocator to keep a ring in other registers than the ones its loads write,
+// with a copy at the loop's end that waits for the loads just issued.
 __device__ __forceinline__ void spread_code_pair(const u32x4 &v, uint32_t (&w)[4]) {
     // v_permlane32_swap: lanes 32..63 of the first operand trade places with
     // lanes 0..31 of the second
-    const auto r02 = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
-    const auto r13 = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+    const auto r02 = __builtin_amdgcn_permlane32_swap(kept_copy(v.x), kept_copy(v.z), false, false);
+    const auto r13 = __builtin_amdgcn_permlane32_swap(kept_copy(v.y), kept_copy(v.w), false, false);
     w[0] = r02[0];
     w[2] = r02[1];
     w[1] = r13[0];
@@ -148,8 +174,8 @@ __device__ __forceinline__ float sum8(const uint32_t (&w)[4]) {
 // Workgroup -> (work item, row block): the row blocks of one item are eight
 // linear workgroup indices apart, so they share an XCD (workgroups are
 // dealt to the eight XCDs in turn).
-__device__ __forceinline__ void item_and_block(int row_blocks, int &w, int &rb) {
-    const int b = blockIdx.x, lane8 = b & 7, q = b >> 3;
+__device__ __forceinline__ void item_and_block(int row_blocks, int &w, int &rb, int b = blockIdx.x) {
+    const int lane8 = b & 7, q = b >> 3;
     rb = q % row_blocks;
     w = (q / row_blocks) * 8 + lane8;
 }
@@ -159,10 +185,14 @@ __device__ __forceinline__ void item_and_block(int row_blocks, int &w, int &rb) 
 // the ids outside [0, E)), each bucket cut into work items of at most nt
 // pairs.  The order of pairs inside a bucket does not matter: every pair's
 // results depend only on its own inputs.
+// It also clears the words the one-launch path counts with (the error word
+// and the per-item counters, max_work of them), so every call starts from
+// zero without a separate fill.
 __global__ __launch_bounds__(kGBucketThreads) void grouped_bucket_kernel(const int32_t *ids, int n_pairs, int E,
                                                                         int nt, int32_t *n_work,
                                                                         int32_t *work_expert, int32_t *work_begin,
-                                                                        int32_t *work_count, int32_t *pair_list) {
+                                                                        int32_t *work_count, int32_t *pair_list,
+                                                                        int32_t *err, int32_t *done, int max_work) {
     constexpr int kWaves = kGBucketThreads / kWave;
     constexpr int kPer = MOE_MAX_GROUPED_TOKENS * MOE_MAX_TOP_K / kGBucketThreads;   // ids per thread, at most
     __shared__ int cnt[2 * kGBucketThreads], base[2 * kGBucketThreads], tiles[2 * kGBucketThreads];
@@ -171,6 +201,8 @@ __global__ __launch_bounds__(kGBucketThreads) void grouped_bucket_kernel(const i
     const int per = (n_pairs + kGBucketThreads - 1) / kGBucketThreads;
     cnt[2 * tid] = 0;
     cnt[2 * tid + 1] = 0;
+    if (tid == 0) *err = 0;
+    for (int i = tid; i < max_work; i += kGBucketThreads) done[i] = 0;
     // this thread's pairs tid + i * kGBucketThreads: their buckets, all loads in flight at once
     int bk[kPer];
 #pragma unroll
@@ -308,18 +340,45 @@ __device__ __forceinline__ float row16_max(float v) {
 // A operand and the codes its B operand, so lane (j, g) of wave w ends with
 // D[4 g + r][j]: pairs 16 n + 4 g + r of weight row 16 w + j, and needs the
 // scales of that one row.
-template <int SB, int NB>
-__global__ __launch_bounds__(kGThreads) void gate_up_grouped(GroupedArgs a) {
+
+// Where act_cs goes (act16 likewise, see the end of gate_up_unit): plain
+// stores when the down projection is a later launch; device-scope (sc1)
+// stores, which another XCD's device-scope loads see, when a down unit of the
+// same launch reads them.
+template <bool AGENT>
+__device__ __forceinline__ void put_f32(float *p, float v) {
+    if constexpr (AGENT)
+        __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+
+// LDS of a gate/up unit.
+template <int NB>
+struct GUSmem {
+    static constexpr int NT = 16 * NB;
+    static constexpr size_t kX = 2 * NT * kGPad * 2, kSb = 2 * kGChunkGroups * kGRows * 4 * 4,
+                            kXs = 2 * kGChunkGroups * NT * 4, kMax = kGW * NT * 4, kInv = NT * 4, kPair = NT * 4;
+    static constexpr size_t kBytes = kX + kSb + kXs + kMax + kInv + kPair;
+    uint16_t *x;     // [2][NT][kGPad] staged inputs, pair order
+    float *sb;       // [2][group][row][sg, cg, su, cu]
+    float *xs;       // [2][group][slot] input group sums
+    float *mx;       // [wave][slot]
+    float *inv;      // [slot]
+    int *pair;       // [slot]
+    __device__ explicit GUSmem(unsigned char *p)
+        : x(reinterpret_cast<uint16_t *>(p)), sb(reinterpret_cast<float *>(p + kX)),
+          xs(reinterpret_cast<float *>(p + kX + kSb)), mx(reinterpret_cast<float *>(p + kX + kSb + kXs)),
+          inv(reinterpret_cast<float *>(p + kX + kSb + kXs + kMax)),
+          pair(reinterpret_cast<int *>(p + kX + kSb + kXs + kMax + kInv)) {}
+};
+
+// One gate/up unit: work item w, row block rb.  AGENT: act16 and act_cs with
+// device-scope stores (read by a down unit of the same launch).
+template <int SB, int NB, bool AGENT>
+__device__ __forceinline__ void gate_up_unit(const GroupedArgs &a, int w, int rb, GUSmem<NB> sm) {
     constexpr int NT = 16 * NB;
-    __shared__ __align__(16) uint16_t s_x[2][NT * kGPad];
-    __shared__ __align__(16) float s_sb[2][kGChunkGroups * kGRows * 4];      // [group][row][sg, cg, su, cu]
-    __shared__ __align__(16) float s_xs[2][kGChunkGroups * NT];             // [group][slot]
-    __shared__ float s_max[kGW][NT];
-    __shared__ float s_inv[NT];
-    __shared__ int s_pair[NT];
-    int w, rb;
-    item_and_block(a.row_blocks, w, rb);
-    if (w >= *a.n_work) return;
+    constexpr int kXBuf = NT * kGPad, kSbBuf = kGChunkGroups * kGRows * 4, kXsBuf = kGChunkGroups * NT;
     const int e = a.work_expert[w], begin = a.work_begin[w], count = a.work_count[w];
     const int row0 = rb * kGRows;
     if (e < 0) {
@@ -330,7 +389,7 @@ __global__ __launch_bounds__(kGThreads) void gate_up_grouped(GroupedArgs a) {
     const int g = lane >> 4, j = lane & 15;
     const int n_grp = a.d_in / kGroup, n_chunk = (n_grp + kGChunkGroups - 1) / kGChunkGroups;
     const int64_t erow = (int64_t)e * a.d_ff;
-    if (tid < NT) s_pair[tid] = tid < count ? a.pair_list[begin + tid] : -1;
+    if (tid < NT) sm.pair[tid] = tid < count ? a.pair_list[begin + tid] : -1;
     // staging roles: x rows of the slots this thread loads; scale row and kind
     int64_t xrow[NB];
     bool xlive[NB];
@@ -350,11 +409,15 @@ __global__ __launch_bounds__(kGThreads) void gate_up_grouped(GroupedArgs a) {
     const uint32_t *qg = a.gate.q + (erow + ra) * a.gate.wpr;
     const uint32_t *qu = a.up.q + (erow + ra) * a.up.wpr;
     const int xo = code_word_input(g);
-    u32x4 rg[2], ru[2];                                      // the chunk's code words, two groups each
+    // The code words of a chunk (two groups per entry) are requested one
+    // chunk before they are used, into two named register sets taken in turn
+    // (chunk c reads one and loads chunk c + 1 into the other), so no register
+    // copy at the loop's end waits for loads in flight.
+    u32x4 rg0[2], ru0[2], rg1[2], ru1[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        rg[p] = *code_pair_addr(qg, 2 * p, n_grp, g);
-        ru[p] = *code_pair_addr(qu, 2 * p, n_grp, g);
+        rg0[p] = *code_pair_addr(qg, 2 * p, n_grp, g);
+        ru0[p] = *code_pair_addr(qu, 2 * p, n_grp, g);
     }
     InStage<NB> st;
     uint16_t sbv[4];                                         // s, b of groups 2h and 2h + 1
@@ -370,17 +433,20 @@ __global__ __launch_bounds__(kGThreads) void gate_up_grouped(GroupedArgs a) {
         }
     };
     auto store_chunk = [&](int buf) {
-        in_store<NB, true>(st, s_x[buf], s_xs[buf]);
+        in_store<NB, true>(st, sm.x + buf * kXBuf, sm.xs + buf * kXsBuf);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {           // groups past the end: zero scale and bias
             const bool ok = sb_g0 + i < n_grp;
             const float sv = ok ? sb_to_float<SB>(sbv[2 * i]) : 0.f, bv = ok ? sb_to_float<SB>(sbv[2 * i + 1]) : 0.f;
-            *reinterpret_cast<float2 *>(&s_sb[buf][((2 * sb_h + i) * kGRows + sb_row) * 4 + 2 * sb_m]) =
+            *reinterpret_cast<float2 *>(&sm.sb[buf * kSbBuf + ((2 * sb_h + i) * kGRows + sb_row) * 4 + 2 * sb_m]) =
                 make_float2(sv, bv - 128.0f * sv);
         }
     };
+    // The inputs and scales of chunk c + 1 are requested at the end of chunk
+    // c - 1 and stored to LDS at the end of chunk c: a whole chunk in flight.
     load_chunk(0);
     store_chunk(0);
+    load_chunk(1);                                           // past the last chunk: clamped, unused
     __syncthreads();
 
     f32x4 acc_g[NB], acc_u[NB];
@@ -389,23 +455,24 @@ __global__ __launch_bounds__(kGThreads) void gate_up_grouped(GroupedArgs a) {
         acc_g[n] = f32x4{0.f, 0.f, 0.f, 0.f};
         acc_u[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    for (int c = 0; c < n_chunk; ++c) {
+    auto chunk = [&](int c, u32x4(&rg)[2], u32x4(&ru)[2], u32x4(&ng)[2], u32x4(&nu)[2]) {
         const int buf = c & 1;
-        if (c + 1 < n_chunk) load_chunk(c + 1);
+        const uint16_t *sx = sm.x + buf * kXBuf;
+        const float *ssb = sm.sb + buf * kSbBuf, *sxs = sm.xs + buf * kXsBuf;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             uint32_t wg[4], wu[4];
             spread_code_pair(rg[p], wg);
             spread_code_pair(ru[p], wu);
-            // refill the ring slot: no load sits behind a branch, so the wait
-            // counts stay exact across the chunk's end
-            rg[p] = *code_pair_addr(qg, (c + 1) * kGChunkGroups + 2 * p, n_grp, g);
-            ru[p] = *code_pair_addr(qu, (c + 1) * kGChunkGroups + 2 * p, n_grp, g);
+            // the next chunk's words (past the end: clamped, unused): no load
+            // sits behind a branch, so the wait counts stay exact
+            ng[p] = *code_pair_addr(qg, (c + 1) * kGChunkGroups + 2 * p, n_grp, g);
+            nu[p] = *code_pair_addr(qu, (c + 1) * kGChunkGroups + 2 * p, n_grp, g);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int d = 2 * p + h, G = c * kGChunkGroups + d;
                 if (G >= n_grp) continue;                    // the last chunk of a ragged d_in
-                const float2 sc = make_float2(s_sb[buf][(d * kGRows + rowl) * 4], s_sb[buf][(d * kGRows + rowl) * 4 + 2]);
+                const float2 sc = make_float2(ssb[(d * kGRows + rowl) * 4], ssb[(d * kGRows + rowl) * 4 + 2]);
                 uint32_t pg[2][4], pu[2][4];
                 nibble_pairs<0x43u>(wg[2 * h], pg[0]);
                 nibble_pairs<0x43u>(wg[2 * h + 1], pg[1]);
@@ -413,7 +480,7 @@ __global__ __launch_bounds__(kGThreads) void gate_up_grouped(GroupedArgs a) {
                 nibble_pairs<0x43u>(wu[2 * h + 1], pu[1]);
 #pragma unroll
                 for (int n = 0; n < NB; ++n) {
-                    const uint16_t *xr = s_x[buf] + (16 * n + j) * kGPad + d * kGroup + xo;
+                    const uint16_t *xr = sx + (16 * n + j) * kGPad + d * kGroup + xo;
                     f32x4 tg = {0.f, 0.f, 0.f, 0.f}, tu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
@@ -439,17 +506,24 @@ __global__ __launch_bounds__(kGThreads) void gate_up_grouped(GroupedArgs a) {
         // supplies xsum of pair 16 n + j and c of row j, both of group g; a
         // group past the end has both zero)
         {
-            const float cgv = s_sb[buf][(g * kGRows + rowl) * 4 + 1], cuv = s_sb[buf][(g * kGRows + rowl) * 4 + 3];
+            const float cgv = ssb[(g * kGRows + rowl) * 4 + 1], cuv = ssb[(g * kGRows + rowl) * 4 + 3];
 #pragma unroll
             for (int n = 0; n < NB; ++n) {
-                const float xv = s_xs[buf][g * NT + 16 * n + j];
+                const float xv = sxs[g * NT + 16 * n + j];
                 acc_g[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv, cgv, acc_g[n], 0, 0, 0);
                 acc_u[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv, cuv, acc_u[n], 0, 0, 0);
             }
         }
         if (c + 1 < n_chunk) store_chunk(buf ^ 1);
+        load_chunk(c + 2);                                   // past the last chunk: clamped, unused
         __syncthreads();
+    };
+    int c = 0;
+    for (; c + 1 < n_chunk; c += 2) {
+        chunk(c, rg0, ru0, rg1, ru1);
+        chunk(c + 1, rg1, ru1, rg0, ru0);
     }
+    if (c < n_chunk) chunk(c, rg0, ru0, rg1, ru1);
 
     // act in fp32, then the block's fp16 copy
     const int row = row0 + rowl;
@@ -462,31 +536,65 @@ __global__ __launch_bounds__(kGThreads) void gate_up_grouped(GroupedArgs a) {
             v[n][r] = acc_g[n][r] * sigmoidf_(acc_g[n][r]) * acc_u[n][r];
             const int t = 16 * n + 4 * g + r;
             const float m = row16_max(row_ok ? fabsf(v[n][r]) : 0.f);
-            if (j == 15) s_max[wave][t] = m;
-            if (t < count && row_ok) a.act[(int64_t)s_pair[t] * a.d_ff + row] = v[n][r];
+            if (j == 15) sm.mx[wave * NT + t] = m;
+            if (t < count && row_ok) a.act[(int64_t)sm.pair[t] * a.d_ff + row] = v[n][r];
         }
     }
     __syncthreads();
     if (tid < NT) {
         float m = 0.f;
 #pragma unroll
-        for (int q = 0; q < kGW; ++q) m = fmaxf(m, s_max[q][tid]);
+        for (int q = 0; q < kGW; ++q) m = fmaxf(m, sm.mx[q * NT + tid]);
         float inv;
         const float cs = f16_stage_scale(__float_as_uint(m), inv);
-        s_inv[tid] = inv;
-        if (tid < count) a.act_cs[(int64_t)s_pair[tid] * a.n_blk + rb] = cs;
+        sm.inv[tid] = inv;
+        if (tid < count) put_f32<AGENT>(a.act_cs + (int64_t)sm.pair[tid] * a.n_blk + rb, cs);
     }
     __syncthreads();
-    if (row_ok) {
+    if constexpr (!AGENT) {
+        if (row_ok) {
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * n + 4 * g + r;
+                    if (t < count)
+                        a.act16[(int64_t)sm.pair[t] * a.d_ff + row] = (uint16_t)f32_to_f16_bits(v[n][r] * sm.inv[t]);
+                }
+        }
+    } else {
+        // through LDS ([slot][128 rows], in the staging buffer, free by now),
+        // then out as 8-byte device-scope stores: each slot's 128 rows are
+        // 256 contiguous bytes, written as whole lines
+        uint16_t *tile = sm.x;
 #pragma unroll
         for (int n = 0; n < NB; ++n)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * n + 4 * g + r;
-                if (t < count)
-                    a.act16[(int64_t)s_pair[t] * a.d_ff + row] = (uint16_t)f32_to_f16_bits(v[n][r] * s_inv[t]);
+                tile[t * kGRows + rowl] = (uint16_t)f32_to_f16_bits(v[n][r] * sm.inv[t]);
             }
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            const int t = 16 * n + (tid >> 5), q = tid & 31;          // slot, 4-row piece
+            if (t < count && row0 + 4 * q < a.d_ff)
+                __hip_atomic_store(reinterpret_cast<uint64_t *>(a.act16 + (int64_t)sm.pair[t] * a.d_ff + row0 + 4 * q),
+                                   *reinterpret_cast<const uint64_t *>(tile + t * kGRows + 4 * q), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
+}
+
+// At most 128 VGPRs (four waves per SIMD: two workgroups per CU); the
+// compiler otherwise takes a few more with 32-pair items.
+template <int SB, int NB>
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(4))) void gate_up_grouped(GroupedArgs a) {
+    __shared__ __align__(16) unsigned char s_mem[GUSmem<NB>::kBytes];
+    int w, rb;
+    item_and_block(a.row_blocks, w, rb);
+    if (w >= *a.n_work) return;
+    gate_up_unit<SB, NB, false>(a, w, rb, GUSmem<NB>(s_mem));
 }
 
 // ------------------------------------------------------------------ kernel B
@@ -642,17 +750,12 @@ __global__ __launch_bounds__(kGThreads) void down_grouped(GroupedArgs a) {
     }
 }
 
-// Kernel B with the item's whole act resident in LDS (when it fits): act16,
-// its group sums and block factors staged once per workgroup, then res_rb
+// Down units with the item's whole act resident in LDS (when it fits):
+// act16, its group sums and block factors staged once per unit, then res_rb
 // row blocks of 128 rows in turn, each with all its groups' scales staged at
 // once, so the contraction runs without a barrier per chunk.  Same operand
 // roles and arithmetic as down_grouped.  Dynamic LDS: [NT][d_ff + 8] act16,
 // [n_grp][NT] sums, [n_blk][NT] factors, [n_grp][128][2] scales.
-// Row blocks per workgroup: 4 with at least 64 work items (1 / 2 / 4
-// measured on the Qwen3-shaped layer, 4 fastest from 128 tokens: 256 tokens
-// 125 -> 117 us per call), else 1 (with few experts touched, fewer
-// workgroups would leave CUs idle: 1 token 30 -> 40 us at 4).
-constexpr int kGResRBMany = 4, kGResManyItems = 64;
 constexpr size_t kGResLdsMax = 64 * 1024 - 512;    // dynamic LDS within the default per-workgroup limit
 
 __host__ __device__ constexpr int res_row_pad(int d_ff) { return d_ff + 8; }
@@ -663,15 +766,48 @@ static size_t res_lds_bytes(int nt, int d_ff) {
            (size_t)n_grp * kGRows * 8;
 }
 
-template <int SB, int NB>
-__global__ __launch_bounds__(kGThreads) void down_grouped_res(GroupedArgs a) {
+// The resident kernel applies: its LDS within the limit, and its staging
+// within kGResIters loads per thread and one block factor per thread.
+static bool res_fits(int nt, int d_ff) {
+    const int n_grp = d_ff / kGroup, n_blk = (d_ff + kGRows - 1) / kGRows;
+    return res_lds_bytes(nt, d_ff) <= kGResLdsMax && nt * (d_ff / 8) <= kGResIters * kGThreads &&
+           n_grp * kGRows <= kGResIters * kGThreads && n_blk * nt <= kGThreads;
+}
+
+constexpr uint32_t kGSpinLimit = 1u << 20;       // polls of a per-item counter before giving up
+
+// A 16-byte piece of act16 and a block factor: plain loads when act16 was
+// written by an earlier launch; device-scope (sc1) loads, which see the sc1
+// stores of another XCD, when a gate/up unit of the same launch wrote them.
+template <bool AGENT>
+__device__ __forceinline__ u32x4 get_piece(const uint16_t *p) {
+    if constexpr (AGENT) {
+        const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
+        const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+    } else {
+        return *reinterpret_cast<const u32x4 *>(p);
+    }
+}
+template <bool AGENT>
+__device__ __forceinline__ float get_f32(const float *p) {
+    if constexpr (AGENT)
+        return __uint_as_float(
+            __hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    else return *p;
+}
+
+// One resident down unit: work item w, row blocks res_rb * rbb .. (up to
+// n_rb).  dyn: the dynamic LDS (res_lds_bytes); pair, score: [NT].  AGENT:
+// act16 and act_cs come from gate/up units of the same launch; thread 0 first
+// waits until all row_blocks of them have finished the item (bounded: on
+// time-out the error word is raised and the unit goes on, its results
+// invalid).
+template <int SB, int NB, bool AGENT>
+__device__ __forceinline__ void down_unit(const GroupedArgs &a, int w, int rbb, unsigned char *dyn, int *s_pair,
+                                          float *s_score) {
     constexpr int NT = 16 * NB;
-    extern __shared__ __align__(16) unsigned char g_lds[];
-    __shared__ int s_pair[NT];
-    __shared__ float s_score[NT];
-    int w, rbb;
-    item_and_block(a.row_blocks, w, rbb);          // row_blocks counts groups of res_rb row blocks
-    if (w >= *a.n_work) return;
     const int e = a.work_expert[w], begin = a.work_begin[w], count = a.work_count[w];
     const int n_rb = (a.d_in + kGRows - 1) / kGRows;
     if (e < 0) {
@@ -683,8 +819,8 @@ __global__ __launch_bounds__(kGThreads) void down_grouped_res(GroupedArgs a) {
     const int g = lane >> 4, j = lane & 15;
     const int n = a.d_ff, n_grp = n / kGroup, n_chunk = (n_grp + kGChunkGroups - 1) / kGChunkGroups;
     const int pad = res_row_pad(n);
-    uint16_t *s_a = reinterpret_cast<uint16_t *>(g_lds);
-    float *s_as = reinterpret_cast<float *>(g_lds + ((size_t)NT * pad * 2 + 15) / 16 * 16);
+    uint16_t *s_a = reinterpret_cast<uint16_t *>(dyn);
+    float *s_as = reinterpret_cast<float *>(dyn + ((size_t)NT * pad * 2 + 15) / 16 * 16);
     float *s_cs = s_as + n_grp * NT;
     float *s_sb = s_cs + a.n_blk * NT;
     if (tid < NT) {
@@ -692,108 +828,233 @@ __global__ __launch_bounds__(kGThreads) void down_grouped_res(GroupedArgs a) {
         s_pair[tid] = p;
         s_score[tid] = p >= 0 && a.scores ? a.scores[p] : 1.0f;
     }
-    // the item's act16 rows: 16-byte pieces q = tid + 512 i, slot q / (n / 8),
-    // piece q % (n / 8) (eight consecutive lanes hold one group of 64), stored
-    // in the codes' pair order with their group sums
-    {
-        const int ppr = n / 8, n_pc = NT * ppr;
-        for (int q0 = 0; q0 < n_pc; q0 += kGThreads) {
-            const int q = q0 + tid, t = min(q / ppr, NT - 1), c = q % ppr;
-            const bool live = q < n_pc && t < count;
-            const int64_t row = (int64_t)a.pair_list[begin + (t < count ? t : 0)] * n;
-            uint32_t wv[4], wp[4];
-            words_of(*reinterpret_cast<const u32x4 *>(a.act16 + row + 8 * c), wv);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wv[i] = live ? wv[i] : 0u;
-            pair_inputs(wv, wp);
-            if (q < n_pc) *reinterpret_cast<u32x4 *>(s_a + t * pad + 8 * c) = u32x4{wp[0], wp[1], wp[2], wp[3]};
-            const float sm = group_sum_last<8>(sum8<false>(wv));
-            if (q < n_pc && (c & 7) == 0) s_as[(c >> 3) * NT + t] = sm;
-        }
-        for (int i = tid; i < a.n_blk * NT; i += kGThreads) {
-            const int blk = i / NT, t = i % NT;
-            s_cs[i] = t < count ? a.act_cs[(int64_t)a.pair_list[begin + t] * a.n_blk + blk] : 0.f;
-        }
-    }
     const f16x2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
     const int64_t erow = (int64_t)e * a.d_in;
     const int rowl = wave * 16 + j, xo = code_word_input(g);
-    for (int rbi = 0; rbi < a.res_rb; ++rbi) {
-        const int rb = rbb * a.res_rb + rbi;
-        if (rb >= n_rb) break;                               // uniform over the workgroup
-        const int row0 = rb * kGRows;
-        const int ra = min(row0 + rowl, a.d_in - 1);
-        const uint32_t *qd = a.down.q + (erow + ra) * a.down.wpr;
-        u32x4 rw[2];
+    const int rb0 = rbb * a.res_rb, n_rbw = min(a.res_rb, n_rb - rb0);   // this unit's row blocks (>= 1)
+    auto code_row = [&](int rbi) {
+        return a.down.q + (erow + min((rb0 + rbi) * kGRows + rowl, a.d_in - 1)) * a.down.wpr;
+    };
+    // Steps (row block, chunk) in order.  The code words of a step are
+    // requested LEAD steps before they are used (past the last step: the
+    // last one again, unused), into LEAD + 1 named register sets taken in
+    // turn, so no register copy at a loop's end waits for loads in flight and
+    // the next row block's first words are in flight while this one ends.
+    // Three steps ahead with 16-pair items, two with 32-pair items (what the
+    // registers allow at four waves per SIMD).  The first steps' words are
+    // requested before act is staged.
+    constexpr int LEAD = NB == 1 ? 3 : 2;
+    const int n_steps = n_rbw * n_chunk;
+    int l_rb = 0, l_c = 0;                                   // the next step whose words are requested
+    auto load_words = [&](u32x4(&dst)[2]) {
+        const uint32_t *qn = code_row(l_rb);
 #pragma unroll
-        for (int p = 0; p < 2; ++p) rw[p] = *code_pair_addr(qd, 2 * p, n_grp, g);
-        __syncthreads();                                     // the previous row block's scale readers are done
-        for (int i = tid; i < n_grp * kGRows; i += kGThreads) {
-            const int G = i / kGRows, r = i % kGRows;
-            const int64_t o = (erow + min(row0 + r, a.d_in - 1)) * a.down.gpr + G;
-            *reinterpret_cast<float2 *>(&s_sb[(G * kGRows + r) * 2]) =
-                make_float2(sb_to_float<SB>(a.down.s[o]), sb_to_float<SB>(a.down.b[o]));
+        for (int p = 0; p < 2; ++p) dst[p] = *code_pair_addr(qn, l_c * kGChunkGroups + 2 * p, n_grp, g);
+        if (++l_c == n_chunk) {
+            l_c = 0;
+            l_rb = min(l_rb + 1, n_rbw - 1);
         }
-        __syncthreads();
-        f32x4 acc[NB];
+    };
+    u32x4 rw0[2], rw1[2], rw2[2], rw3[2];
+    load_words(rw0);
+    load_words(rw1);
+    if constexpr (LEAD == 3) load_words(rw2);
+    if constexpr (AGENT) {
+        if (tid == 0) {
+            for (uint32_t spin = 0;
+                 __hip_atomic_load(a.done + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.row_blocks; ++spin) {
+                if (spin == kGSpinLimit) {
+                    __hip_atomic_fetch_or(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+    }
+    __syncthreads();
+    // the item's act16 rows: 16-byte pieces q = tid + 512 i, slot q / (n / 8),
+    // piece q % (n / 8) (eight consecutive lanes hold one group of 64), stored
+    // in the codes' pair order with their group sums.  Every thread issues
+    // kGResIters loads (indices past the end clamped to the last piece: one
+    // address for the whole wave) before the first store, so none waits for
+    // another (the host checks that kGResIters loads per thread cover act16)
+    {
+        const int ppr = n / 8, n_pc = NT * ppr, iters = (n_pc + kGThreads - 1) / kGThreads;
+        u32x4 v[kGResIters];
 #pragma unroll
-        for (int m = 0; m < NB; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int c = 0; c < n_chunk; ++c) {
+        for (int i = 0; i < kGResIters; ++i) {
+            const int q = min(tid + kGThreads * i, n_pc - 1), t = q / ppr, c = q - t * ppr;
+            const int64_t row = (int64_t)s_pair[t < count ? t : 0] * n;
+            v[i] = get_piece<AGENT>(a.act16 + row + 8 * c);
+        }
+        const int n_cs = a.n_blk * NT, ics = min(tid, n_cs - 1), t_cs = ics % NT;
+        const float csv = get_f32<AGENT>(a.act_cs + (int64_t)s_pair[t_cs < count ? t_cs : 0] * a.n_blk + ics / NT);
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                uint32_t wd[4];
-                spread_code_pair(rw[p], wd);
-                rw[p] = *code_pair_addr(qd, (c + 1) * kGChunkGroups + 2 * p, n_grp, g);
+        for (int i = 0; i < kGResIters; ++i) {
+            if (i < iters) {
+                const int q = tid + kGThreads * i, t = min(q / ppr, NT - 1), c = q % ppr;
+                const bool live = q < n_pc && t < count;
+                uint32_t wv[4], wp[4];
+                words_of(v[i], wv);
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int G = c * kGChunkGroups + 2 * p + h;
-                    if (G >= n_grp) continue;
-                    const float sd = s_sb[(G * kGRows + rowl) * 2];
-                    uint32_t pq[2][4];
-                    nibble_pairs<0x64u>(wd[2 * h], pq[0]);
-                    nibble_pairs<0x64u>(wd[2 * h + 1], pq[1]);
+                for (int k = 0; k < 4; ++k) wv[k] = live ? wv[k] : 0u;
+                pair_inputs(wv, wp);
+                if (q < n_pc) *reinterpret_cast<u32x4 *>(s_a + t * pad + 8 * c) = u32x4{wp[0], wp[1], wp[2], wp[3]};
+                const float sm = group_sum_last<8>(sum8<false>(wv));
+                if (q < n_pc && (c & 7) == 0) s_as[(c >> 3) * NT + t] = sm;
+            }
+        }
+        if (tid < n_cs) s_cs[tid] = t_cs < count ? csv : 0.f;
+    }
+    // a row block's scales and biases, [group][row][s, b]: kGResIters loads
+    // of each per thread (clamped as above) before the first store (the group
+    // index runs fastest, so a wave reads whole rows of the scale matrices)
+    auto stage_scales = [&](int row0) {
+        const int tot = n_grp * kGRows, iters = (tot + kGThreads - 1) / kGThreads;
+        uint32_t sv[kGResIters], bv[kGResIters];            // 16-bit values, one per register
+#pragma unroll
+        for (int i = 0; i < kGResIters; ++i) {
+            const int idx = min(tid + kGThreads * i, tot - 1), r = idx / n_grp, G = idx - r * n_grp;
+            const int64_t o = (erow + min(row0 + r, a.d_in - 1)) * a.down.gpr + G;
+            sv[i] = a.down.s[o];
+            bv[i] = a.down.b[o];
+        }
+#pragma unroll
+        for (int i = 0; i < kGResIters; ++i) {
+            const int idx = tid + kGThreads * i, r = idx / n_grp, G = idx - r * n_grp;
+            if (i < iters && idx < tot)
+                *reinterpret_cast<float2 *>(&s_sb[(G * kGRows + r) * 2]) =
+                    make_float2(sb_to_float<SB>((uint16_t)sv[i]), sb_to_float<SB>((uint16_t)bv[i]));
+        }
+    };
+    f32x4 acc[NB];
+    int rbi = 0, c = 0;                                      // the step being computed
+    auto step = [&](u32x4(&cur)[2], u32x4(&nxt)[2]) {
+        const int row0 = (rb0 + rbi) * kGRows;
+        if (c == 0) {
+            __syncthreads();                                 // act staged / the previous block's scale readers done
+            stage_scales(row0);
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < NB; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        uint32_t wd2[2][4];
+        spread_code_pair(cur[0], wd2[0]);
+        spread_code_pair(cur[1], wd2[1]);
+        load_words(nxt);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const uint32_t(&wd)[4] = wd2[p];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int G = c * kGChunkGroups + 2 * p + h;
+                if (G >= n_grp) continue;
+                const float sd = s_sb[(G * kGRows + rowl) * 2];
+                uint32_t pq[2][4];
+                nibble_pairs<0x64u>(wd[2 * h], pq[0]);
+                nibble_pairs<0x64u>(wd[2 * h + 1], pq[1]);
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        pq[s2][i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, pq[s2][i]) - off);
+#pragma unroll
+                for (int m = 0; m < NB; ++m) {
+                    const uint16_t *ar = s_a + (16 * m + j) * pad + G * kGroup + xo;
+                    f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2)
+                        t4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4 *>(ar + 8 * s2)),
+                            __builtin_bit_cast(f16x8_t, u32x4{pq[s2][0], pq[s2][1], pq[s2][2], pq[s2][3]}), t4,
+                            0, 0, 0);
+                    const f32x4 cs = *reinterpret_cast<const f32x4 *>(&s_cs[(G * kGroup / kGRows) * NT + 16 * m + 4 * g]);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            pq[s2][i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, pq[s2][i]) - off);
+                    for (int r = 0; r < 4; ++r) acc[m][r] += (cs[r] * sd) * t4[r];
+                }
+            }
+        }
+        // the chunk's bias terms as one fp32 16x16x4 MFMA per pair block (a
+        // group past the end: zero sum and zero bias)
+        const int Gb = c * kGChunkGroups + g;
+        const bool gok = Gb < n_grp;
+        const float bv = gok ? s_sb[(Gb * kGRows + rowl) * 2 + 1] : 0.f;
 #pragma unroll
-                    for (int m = 0; m < NB; ++m) {
-                        const uint16_t *ar = s_a + (16 * m + j) * pad + G * kGroup + xo;
-                        f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < NB; ++m) {
+            const float av = gok ? s_as[Gb * NT + 16 * m + j] * s_cs[(Gb * kGroup / kGRows) * NT + 16 * m + j] : 0.f;
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[m], 0, 0, 0);
+        }
+        if (c == n_chunk - 1) {
+            const int row = row0 + rowl;
+            if (row < a.d_in) {
 #pragma unroll
-                        for (int s2 = 0; s2 < 2; ++s2)
-                            t4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4 *>(ar + 8 * s2)),
-                                __builtin_bit_cast(f16x8_t, u32x4{pq[s2][0], pq[s2][1], pq[s2][2], pq[s2][3]}), t4,
-                                0, 0, 0);
-                        const f32x4 cs = *reinterpret_cast<const f32x4 *>(&s_cs[(G * kGroup / kGRows) * NT + 16 * m + 4 * g]);
+                for (int m = 0; m < NB; ++m)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[m][r] += (cs[r] * sd) * t4[r];
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 16 * m + 4 * g + r;
+                        if (t < count) a.partial[(int64_t)s_pair[t] * a.d_in + row] = s_score[t] * acc[m][r];
                     }
-                }
-            }
-            // the chunk's bias terms as one fp32 16x16x4 MFMA per pair block (a
-            // group past the end: zero sum and zero bias)
-            const int Gb = c * kGChunkGroups + g;
-            const bool gok = Gb < n_grp;
-            const float bv = gok ? s_sb[(Gb * kGRows + rowl) * 2 + 1] : 0.f;
-#pragma unroll
-            for (int m = 0; m < NB; ++m) {
-                const float av = gok ? s_as[Gb * NT + 16 * m + j] * s_cs[(Gb * kGroup / kGRows) * NT + 16 * m + j] : 0.f;
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[m], 0, 0, 0);
             }
         }
-        const int row = row0 + rowl;
-        if (row < a.d_in) {
-#pragma unroll
-            for (int m = 0; m < NB; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * m + 4 * g + r;
-                    if (t < count) a.partial[(int64_t)s_pair[t] * a.d_in + row] = s_score[t] * acc[m][r];
-                }
+        if (++c == n_chunk) {
+            c = 0;
+            ++rbi;
         }
+    };
+    int st = 0;
+    if constexpr (LEAD == 2) {
+        for (; st + 2 < n_steps; st += 3) {
+            step(rw0, rw2);
+            step(rw1, rw0);
+            step(rw2, rw1);
+        }
+        if (st < n_steps) step(rw0, rw2);
+        if (st + 1 < n_steps) step(rw1, rw0);
+    } else {
+        for (; st + 3 < n_steps; st += 4) {
+            step(rw0, rw3);
+            step(rw1, rw0);
+            step(rw2, rw1);
+            step(rw3, rw2);
+        }
+        if (st < n_steps) step(rw0, rw3);
+        if (st + 1 < n_steps) step(rw1, rw0);
+        if (st + 2 < n_steps) step(rw2, rw1);
+    }
+}
+
+// ------------------------------------------------------- the one-launch path
+// Gate/up and down of the whole call in one launch: workgroups 0 ..
+// grid_a - 1 are gate/up units (work item, row block), the rest down units
+// (work item, res_rb row blocks), both placed as the separate kernels place
+// them (an item's units on one XCD).  A down unit first waits until the
+// gate/up units of its item have finished (a per-item counter), so the last
+// gate/up units of the launch run beside the first down units instead of
+// leaving most of the chip idle at the end of a separate gate/up launch, and
+// only the last down units end alone.  Workgroups start in index order, so
+// every gate/up unit a down unit waits for has started before it, and gate/up
+// units never wait; the waits are bounded all the same (error word).  act16
+// and act_cs travel with device-scope stores and loads; each wave waits for
+// its stores before the item's counter moves.
+template <int SB, int NB>
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(4))) void ffn_grouped_fused(GroupedArgs a) {
+    extern __shared__ __align__(16) unsigned char g_lds[];
+    __shared__ int s_pair[16 * NB];
+    __shared__ float s_score[16 * NB];
+    const int n_work = *a.n_work;
+    if ((int)blockIdx.x < a.grid_a) {
+        int w, rb;
+        item_and_block(a.row_blocks, w, rb);
+        if (w >= n_work) return;
+        gate_up_unit<SB, NB, true>(a, w, rb, GUSmem<NB>(g_lds));
+        __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0): this wave's act16 / act_cs stores are done
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_fetch_add(a.done + w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        int w, rbb;
+        item_and_block(a.row_blocks_b, w, rbb, blockIdx.x - a.grid_a);
+        if (w >= n_work) return;
+        down_unit<SB, NB, true>(a, w, rbb, g_lds, s_pair, s_score);
     }
 }
 
@@ -807,7 +1068,11 @@ static int grouped_max_work(int n_pairs, int E, int nt) { return (n_pairs + nt -
 // (256 tokens 203 against 136 us, 1024 tokens 308 against 292 us).
 static int grouped_nb(int n_pairs, int E) { return n_pairs / E <= 9 ? 1 : 2; }
 
-// Workspace: the work lists (int32), then act16, then act_cs, each 256-byte aligned.
+// Workspace: the head (error word, n_work, two spare words),
+// the work lists and per-item counters (int32), then act16, then act_cs,
+// each 256-byte aligned.
+constexpr int kGHeadWords = 4;
+
 struct GroupedLayout {
     size_t act16, act_cs, total;
 };
@@ -816,28 +1081,57 @@ static GroupedLayout grouped_layout(int n_tokens, int top_k, int n_experts, int 
     GroupedLayout L;
     const size_t n_pairs = (size_t)n_tokens * top_k;
     const size_t mw = (size_t)grouped_max_work((int)n_pairs, n_experts, kGMinTok);
-    L.act16 = align_up((1 + 3 * mw + n_pairs) * sizeof(int32_t), 256);
+    L.act16 = align_up((kGHeadWords + 4 * mw + n_pairs) * sizeof(int32_t), 256);
     L.act_cs = L.act16 + align_up(n_pairs * d_ff * sizeof(uint16_t), 256);
     L.total = L.act_cs + align_up(n_pairs * ((d_ff + kGRows - 1) / kGRows) * sizeof(float), 256);
     return L;
 }
 
+// Dynamic LDS above the default 64 KB per workgroup is allowed per kernel
+// once (the largest size asked so far is remembered per kernel; gfx950 gives
+// a workgroup up to 160 KB).
+static void allow_dynamic_lds(const void *kernel, size_t bytes) {
+    if (bytes <= 64 * 1024) return;
+    static std::mutex mu;
+    static std::map<const void *, size_t> allowed;
+    std::lock_guard<std::mutex> lock(mu);
+    size_t &have = allowed[kernel];
+    if (have >= bytes) return;
+    if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess) have = bytes;
+}
+
+// Row blocks per down unit of the one-launch path: 4 when the call is
+// expected to touch at least 64 work items (expected distinct experts under
+// uniform routing, plus the items beyond 16 NB pairs), else 1 (with few items,
+// longer units leave CUs idle).  Measured on the Qwen3-shaped layer at 4, 2
+// and 1 row blocks: 32 tokens 97.9 / 100.3 / 105.7 us per call, 256 tokens
+// 115.1 / 122.3 / 134.9 us; 1 token 43 us at 4.
+static int fused_rb(int n_pairs, int E, int nt) {
+    const double items = E * (1.0 - std::exp(n_pairs * std::log1p(-1.0 / E))) + (double)n_pairs / nt;
+    return items >= 64.0 ? 4 : 1;
+}
+
 template <int SB, int NB>
 static void launch_grouped(const GroupedArgs &a, int mw, hipStream_t s) {
     const int items8 = (mw + 7) / 8 * 8;
-    GroupedArgs ga = a, gb = a;
-    ga.row_blocks = (a.d_ff + kGRows - 1) / kGRows;
-    hipLaunchKernelGGL((gate_up_grouped<SB, NB>), dim3(items8 * ga.row_blocks), dim3(kGThreads), 0, s, ga);
-    const int n_rb = (a.d_in + kGRows - 1) / kGRows;
-    const size_t lds = res_lds_bytes(16 * NB, a.d_ff);
-    if (lds <= kGResLdsMax) {
-        gb.res_rb = a.T * a.K / (16 * NB) >= kGResManyItems ? kGResRBMany : 1;
-        gb.row_blocks = (n_rb + gb.res_rb - 1) / gb.res_rb;
-        hipLaunchKernelGGL((down_grouped_res<SB, NB>), dim3(items8 * gb.row_blocks), dim3(kGThreads), lds, s, gb);
-    } else {
-        gb.row_blocks = n_rb;
-        hipLaunchKernelGGL((down_grouped<SB, NB>), dim3(items8 * gb.row_blocks), dim3(kGThreads), 0, s, gb);
+    const int ra = (a.d_ff + kGRows - 1) / kGRows, n_rb = (a.d_in + kGRows - 1) / kGRows;
+    if (res_fits(16 * NB, a.d_ff)) {
+        GroupedArgs f = a;
+        f.row_blocks = ra;
+        f.res_rb = fused_rb(a.T * a.K, a.E, 16 * NB);
+        f.row_blocks_b = (n_rb + f.res_rb - 1) / f.res_rb;
+        f.grid_a = items8 * ra;
+        const size_t lds = std::max(GUSmem<NB>::kBytes, res_lds_bytes(16 * NB, a.d_ff));
+        allow_dynamic_lds(reinterpret_cast<const void *>(&ffn_grouped_fused<SB, NB>), lds);
+        hipLaunchKernelGGL((ffn_grouped_fused<SB, NB>), dim3(items8 * (ra + f.row_blocks_b)), dim3(kGThreads), lds, s,
+                           f);
+        return;
     }
+    GroupedArgs ga = a, gb = a;
+    ga.row_blocks = ra;
+    hipLaunchKernelGGL((gate_up_grouped<SB, NB>), dim3(items8 * ga.row_blocks), dim3(kGThreads), 0, s, ga);
+    gb.row_blocks = n_rb;
+    hipLaunchKernelGGL((down_grouped<SB, NB>), dim3(items8 * gb.row_blocks), dim3(kGThreads), 0, s, gb);
 }
 
 }  // namespace moe
@@ -891,18 +1185,23 @@ extern "C" moe_status moe_decode_expert_ffn_grouped(const void *x, moe_dtype x_d
     a.scores = scores; a.act = act; a.partial = partial;
     char *wsb = reinterpret_cast<char *>(workspace);
     int32_t *ws = reinterpret_cast<int32_t *>(wsb);
-    a.n_work = ws;
-    a.work_expert = ws + 1;
-    a.work_begin = ws + 1 + mw_ws;
-    a.work_count = ws + 1 + 2 * mw_ws;
-    a.pair_list = ws + 1 + 3 * mw_ws;
+    a.err = ws;
+    a.n_work = ws + 1;
+    a.work_expert = ws + kGHeadWords;
+    a.work_begin = ws + kGHeadWords + mw_ws;
+    a.work_count = ws + kGHeadWords + 2 * mw_ws;
+    a.done = ws + kGHeadWords + 3 * mw_ws;
+    a.pair_list = ws + kGHeadWords + 4 * mw_ws;
     a.act16 = reinterpret_cast<uint16_t *>(wsb + L.act16);
     a.act_cs = reinterpret_cast<float *>(wsb + L.act_cs);
     a.row_blocks = 1;
     a.res_rb = 1;
+    a.row_blocks_b = 1;
+    a.grid_a = 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(grouped_bucket_kernel, dim3(1), dim3(kGBucketThreads), 0, s, expert_ids, n_pairs, E, nt, ws,
-                       ws + 1, ws + 1 + mw_ws, ws + 1 + 2 * mw_ws, ws + 1 + 3 * mw_ws);
+    hipLaunchKernelGGL(grouped_bucket_kernel, dim3(1), dim3(kGBucketThreads), 0, s, expert_ids, n_pairs, E, nt,
+                       ws + 1, ws + kGHeadWords, ws + kGHeadWords + mw_ws, ws + kGHeadWords + 2 * mw_ws,
+                       ws + kGHeadWords + 4 * mw_ws, a.err, a.done, mw_ws);
     const bool bf = sb == MOE_BF16;
     if (nb == 1)
         bf ? launch_grouped<MOE_BF16, 1>(a, mw, s) : launch_grouped<MOE_F16, 1>(a, mw, s);

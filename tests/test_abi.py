@@ -190,14 +190,15 @@ def test_token_limits_match_the_header():
 
 
 def test_grouped_workspace_bytes():
-    """The work lists (one count, then expert, first pair and pair count per
-    work item, at most ceil(pairs / 16) + n_experts + 1 items, then the pair
-    list, int32), the fp16 copy of act and one fp32 factor per pair and block
-    of 128 act values, each 256-byte aligned."""
+    """The head (error word, work-item count, unit counter, one spare word),
+    the work lists (expert, first pair and pair count per work item, at most
+    ceil(pairs / 16) + n_experts + 1 items), one counter per work item and the
+    pair list, int32; then the fp16 copy of act and one fp32 factor per pair
+    and block of 128 act values, each 256-byte aligned."""
     f = qmd.expert_ffn_grouped_workspace_bytes
     for T, K, E, F in [(1, 1, 1, 64), (256, 8, 128, 768), (1024, 32, 1024, 8192), (17, 3, 9, 704)]:
         mw = (T * K + 15) // 16 + E + 1
-        need = (1 + 3 * mw + T * K) * 4 + T * K * F * 2 + T * K * ((F + 127) // 128) * 4
+        need = (4 + 4 * mw + T * K) * 4 + T * K * F * 2 + T * K * ((F + 127) // 128) * 4
         assert need <= f(T, K, E, F) <= need + 3 * 256 and f(T, K, E, F) % 256 == 0
     assert f(0, 8, 128, 768) == 0 and f(4, 0, 128, 768) == 0 and f(4, 8, 0, 768) == 0 and f(4, 8, 8, 0) == 0
 

@@ -53,6 +53,7 @@ def run_grouped(cfg, w, x, ids, scores):
     ws = torch.zeros(q.expert_ffn_grouped_workspace_bytes(T, K, cfg.n_experts, cfg.d_ff), device=DEV, dtype=torch.uint8)
     q.moe_decode_expert_ffn_grouped(xd, g, u, d, idd, scd, act, part, ws)
     torch.cuda.synchronize()
+    assert q.workspace_status(ws) == q.MOE_OK, "a wait inside the grouped call ran out"
     return act.cpu().numpy(), part.cpu().numpy(), (xd, g, u, d, idd, scd, act, part, ws)
 
 
@@ -147,6 +148,45 @@ def test_grouped_full_size_256_tokens_and_repeatable():
     assert np.array_equal(act, act2) and np.array_equal(part, part2), "repeated call differs"
 
 
+def test_grouped_workspace_reused_eager_and_graph_replays():
+    """One workspace for many calls: the bucketing launch clears the unit
+    counter, the per-item counters and the error word of the one-launch path
+    at every call, so eager calls and replays of a captured call (eager work
+    between the replays) all give the first call's bits."""
+    import quantized_moe_decode_amd as q
+    cfg = mi.QWEN3
+    say("case grouped workspace reused, eager and graph replays")
+    w = mi.gen_layer_weights(cfg, 2)
+    T = 64
+    x, _ = mi.gen_tokens(cfg, 2, T)
+    ids, scores = random_routing(T, cfg.top_k, cfg.n_experts, seed=64)
+    act0, part0, args = run_grouped(cfg, w, x, ids, scores)
+    xd, g, u, d, idd, scd, act, part, ws = args
+    for _ in range(5):
+        act.fill_(-7.0)
+        part.fill_(-7.0)
+        q.moe_decode_expert_ffn_grouped(xd, g, u, d, idd, scd, act, part, ws)
+    torch.cuda.synchronize()
+    assert q.workspace_status(ws) == q.MOE_OK
+    assert np.array_equal(act.cpu().numpy(), act0) and np.array_equal(part.cpu().numpy(), part0)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        q.moe_decode_expert_ffn_grouped(xd, g, u, d, idd, scd, act, part, ws)   # warm-up on the capture stream
+        stream.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            q.moe_decode_expert_ffn_grouped(xd, g, u, d, idd, scd, act, part, ws)
+    for rep in range(3):
+        act.fill_(-7.0)
+        part.fill_(-7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert q.workspace_status(ws) == q.MOE_OK, f"replay {rep}: a wait ran out"
+        assert np.array_equal(act.cpu().numpy(), act0), f"replay {rep}: act differs"
+        assert np.array_equal(part.cpu().numpy(), part0), f"replay {rep}: partial differs"
+
+
 def test_grouped_full_size_1024_tokens():
     """1024 tokens x top-8 on the Qwen3-30B-A3B-shaped layer: 64 pairs per
     expert on average, the 64-pair work items; 16 tokens checked."""
@@ -160,9 +200,10 @@ def test_grouped_full_size_1024_tokens():
 
 
 def test_grouped_resident_down_many_items_ragged_row_blocks():
-    """512 tokens x top-4 on 9 experts (64 work items of 32 pairs): the down
-    kernel keeps act resident in LDS and takes four row blocks per workgroup;
-    d_in 1088 has 9 row blocks, so the last workgroup of an item has one."""
+    """512 tokens x top-4 on 9 experts (64 work items of 32 pairs) in the
+    one-launch path: each down unit keeps act resident in LDS and takes two
+    row blocks; d_in 1088 has 9 row blocks, so the last unit of an item has
+    one."""
     cfg = small_cfg(d_in=1088, d_ff=704, n_experts=9, top_k=4)
     say("case grouped resident down, 4 row blocks per workgroup, ragged")
     w = mi.gen_layer_weights(cfg, 5, threads=4)
@@ -173,8 +214,9 @@ def test_grouped_resident_down_many_items_ragged_row_blocks():
 
 
 def test_grouped_chunked_down_when_act_does_not_fit():
-    """d_ff 1408 with 32-pair items: act (89 KB as fp16) does not fit the
-    resident kernel's LDS, so the down projection takes the chunked kernel."""
+    """d_ff 1408 with 32-pair items: act (89 KB as fp16) does not fit a
+    resident down unit's LDS, so the call takes two launches, gate/up and the
+    chunked down kernel."""
     cfg = small_cfg(d_in=256, d_ff=1408, n_experts=4, top_k=2)
     say("case grouped chunked down (d_ff 1408)")
     w = mi.gen_layer_weights(cfg, 6, threads=4)
