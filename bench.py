@@ -67,8 +67,7 @@ ALL_CONFIGS = [HEADLINE, "qwen3_30b_a3b_moe_batch32", "qwen3_30b_a3b_moe_prefill
                "qwen1.5_moe_a2.7b", "dots_llm1_mixed_bit"]
 FUSED_KERNEL = "moe::layer_kernel"
 BATCH_GATE_UP_KERNEL = "moe::gate_up_batch_q4"
-GROUPED_GATE_UP_KERNEL = "moe::gate_up_grouped"
-GROUPED_DOWN_KERNEL = "moe::down_grouped"
+GROUPED_FFN_KERNEL = "moe::ffn_grouped_fused"        # gate/up and down units of the grouped call, one launch
 GROUPED_BUCKET_KERNEL = "moe::grouped_bucket_kernel"
 MAX_DECODE_TOKENS = 32          # above this the layer takes the grouped (matrix-core) expert FFN
 COPY_KERNEL = "MulFunctor"
@@ -100,14 +99,15 @@ def counters_path(workload: str) -> str:
 def dominant_kernel(cfg) -> str:
     if cfg.n_tokens == 1:
         return FUSED_KERNEL
-    return BATCH_GATE_UP_KERNEL if cfg.n_tokens <= MAX_DECODE_TOKENS else GROUPED_GATE_UP_KERNEL
+    return BATCH_GATE_UP_KERNEL if cfg.n_tokens <= MAX_DECODE_TOKENS else GROUPED_FFN_KERNEL
 
 
 def unit_kernels(cfg) -> list:
     """The kernels of the roofline unit: the dominant kernel, or for the
-    grouped path the three launches of one grouped expert FFN call."""
+    grouped path the two launches of one grouped expert FFN call (bucketing,
+    then gate/up and down units in one launch)."""
     k = dominant_kernel(cfg)
-    return [GROUPED_BUCKET_KERNEL, k, GROUPED_DOWN_KERNEL] if k == GROUPED_GATE_UP_KERNEL else [k]
+    return [GROUPED_BUCKET_KERNEL, k] if k == GROUPED_FFN_KERNEL else [k]
 
 
 def summarize_counters(fetch_csv, write_csv, workload, copy_mib, command) -> dict:
@@ -481,7 +481,7 @@ def roofline_of(wl, meas, args):
         torch.cuda.synchronize()
         avg_s = e0.elapsed_time(e1) / 1000.0 / (reps * L)
         alg = sum(a_bytes[i % R] for i in range(reps)) / (reps * L)
-        name = ("expert_ffn_grouped (bucketing + gate_up_grouped + down_grouped: the matrix-core expert FFN "
+        name = ("expert_ffn_grouped (bucketing + ffn_grouped_fused: the matrix-core expert FFN "
                 "of every touched expert, per layer)" if grouped else
                 "gate_up_batch_q4 (kernel A: gate/up GEMV + SwiGLU for every token of a touched expert)")
         del graphs

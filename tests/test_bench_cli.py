@@ -47,7 +47,7 @@ def test_batch_workload_counts_its_gate_up_kernel():
     import moe_inputs as mi
     assert bench.dominant_kernel(mi.CONFIGS["qwen3_30b_a3b_moe_batch32"]) == bench.BATCH_GATE_UP_KERNEL
     assert bench.dominant_kernel(mi.CONFIGS["qwen3_30b_a3b_moe"]) == bench.FUSED_KERNEL
-    assert bench.dominant_kernel(mi.CONFIGS["qwen3_30b_a3b_moe_prefill256"]) == bench.GROUPED_GATE_UP_KERNEL
+    assert bench.dominant_kernel(mi.CONFIGS["qwen3_30b_a3b_moe_prefill256"]) == bench.GROUPED_FFN_KERNEL
 
 
 def test_prefill_workload_reuses_the_headline_weights_and_takes_the_grouped_path():
@@ -60,21 +60,19 @@ def test_prefill_workload_reuses_the_headline_weights_and_takes_the_grouped_path
     assert bench.ALL_CONFIGS.index("qwen3_30b_a3b_moe_prefill256") == 2
 
 
-def test_counter_summary_of_the_grouped_unit_sums_its_three_kernels(tmp_path):
+def test_counter_summary_of_the_grouped_unit_sums_its_kernels(tmp_path):
     """On the grouped path the roofline unit is one grouped expert FFN call:
-    bucketing + gate/up + down, per-dispatch means summed."""
-    b = "moe::grouped_bucket_kernel(int const*, int, int, int, int*, int*, int*, int*, int*)"
-    a = "void moe::gate_up_grouped<2, 2>(moe::GroupedArgs)"
-    d = "void moe::down_grouped<2, 2>(moe::GroupedArgs)"
+    bucketing + the gate/up-and-down launch, per-dispatch means summed."""
+    b = "moe::grouped_bucket_kernel(int const*, int, int, int, int*, int*, int*, int*, int*, int*, int*, int)"
+    f = "void moe::ffn_grouped_fused<2, 2>(moe::GroupedArgs)"
     c = "void at::native::vectorized_elementwise_kernel<4, MulFunctor<float> >"
     fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
-    _pmc_csv(fetch, "FETCH_SIZE", [(b, 1), (b, 3), (a, 1000), (a, 1000), (d, 500), (d, 500), (c, 256 * 1024),
+    _pmc_csv(fetch, "FETCH_SIZE", [(b, 1), (b, 3), (f, 1500), (f, 1500), (c, 256 * 1024),
                                    ("void moe::route_logits_mfma(moe::RouteArgs)", 77)])
-    _pmc_csv(write, "WRITE_SIZE", [(b, 0), (b, 0), (a, 100), (a, 100), (d, 200), (d, 200), (c, 256 * 1024)])
+    _pmc_csv(write, "WRITE_SIZE", [(b, 0), (b, 0), (f, 300), (f, 300), (c, 256 * 1024)])
     rec = bench.summarize_counters(str(fetch), str(write), "qwen3_30b_a3b_moe_prefill256", 256, "cmd")
-    assert rec["kernel"] == " + ".join([bench.GROUPED_BUCKET_KERNEL, bench.GROUPED_GATE_UP_KERNEL,
-                                         bench.GROUPED_DOWN_KERNEL])
-    assert rec["hbm_bytes_per_launch"] == (2 + 1000 + 500 + 100 + 200) * 1024
+    assert rec["kernel"] == " + ".join([bench.GROUPED_BUCKET_KERNEL, bench.GROUPED_FFN_KERNEL])
+    assert rec["hbm_bytes_per_launch"] == (2 + 1500 + 300) * 1024
     assert rec["launches"] == [2, 2]
 
 
