@@ -525,19 +525,6 @@ static int pick_lr_shift(int cpr) {
     return s;
 }
 
-// Lanes per row for the multi-token kernels: the power of two (8 to 64) that
-// leaves the fewest idle lanes over a row's chunks, the larger on a tie
-// (768 inputs, 24 chunks: 8 lanes looping three times rather than 32 lanes
-// of which 8 idle).
-static int pick_lr_shift_dense(int cpr) {
-    int best = 6, best_slots = ((cpr + 63) >> 6) << 6;
-    for (int s = 5; s >= 3; --s) {
-        const int slots = ((cpr + (1 << s) - 1) >> s) << s;
-        if (slots < best_slots) best = s, best_slots = slots;
-    }
-    return best;
-}
-
 static QM to_qm(const moe_qmat *m) {
     QM q;
     q.q = m->q;
@@ -642,20 +629,35 @@ static moe_status geometry(FfnArgs &a, int maxt, int cols, int bits, size_t &lds
     return MOE_OK;
 }
 
+// Lanes per row for the multi-token kernels: the largest power of two (8 to
+// 64) that still gives every lane at least four chunks of a row per pass, so
+// the cross-lane sums at the end of a pass (2 x rows x tokens values per
+// lane group) are spread over enough codes; 8 when rows are shorter.  The
+// kernels are VALU-bound at these sizes, and with 64 lanes on a 2048-input
+// row (one chunk per lane, then a 64-lane reduction) the sums took about as
+// many instructions as the dot products.  Measured on the 32-token
+// Qwen3-shaped expert call (gate/up at 2048 inputs, one pass): 8 / 16 / 32
+// / 64 lanes 99.6 / 92.4 / 96.3 / 101.3 us; down (768 inputs) keeps 8.
+static int pick_lr_shift_batch(int cpr) {
+    int s = 3;
+    while (s < 6 && (cpr >> (s + 1)) >= 4) ++s;
+    return s;
+}
+
 // The 4-bit multi-token kernels (batch.hip), when their LDS fits; rows_per_wg
 // covers `passes` row passes of a workgroup.  More passes amortise a
-// workgroup's staging of its tokens' inputs; measured on the 32-token
-// Qwen3-shaped step (per-launch averages): gate/up 68.8 / 61.5 / 59.3 /
-// 63.1 us at 1 / 2 / 4 / 8 passes.  Down (768 inputs: 8 lanes per row, 2
-// rows per lane group) is fastest with a single pass: its workgroups are
-// small and many, six per CU.
-constexpr int kBatchPassesA = 4;
+// workgroup's staging of its tokens' inputs, but with 16 lanes per row one
+// pass of gate/up is already 32 rows (2 passes measured 3% slower on the
+// 32-token Qwen3-shaped call); down (768 inputs: 8 lanes per row, 2 rows per
+// lane group) is fastest with a single pass: its workgroups are small and
+// many, six per CU.
+constexpr int kBatchPassesA = 1;
 constexpr int kBatchPassesB = 1;
 static KernelFn batch_geometry(FfnArgs &a, int cols, int bits, int nr, int passes, KernelFn k, size_t &lds) {
     if (bits != 4 || !k) return nullptr;
     lds = batch_lds_bytes(cols);
     if (lds > kLdsBudget) return nullptr;
-    a.lr_shift = pick_lr_shift_dense(cols / 32);
+    a.lr_shift = pick_lr_shift_batch(cols / 32);
     a.rows_per_wg = passes * 4 * (kWave >> a.lr_shift) * nr;
     a.tpp = kBatchTok;
     return k;
