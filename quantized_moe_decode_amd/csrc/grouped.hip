@@ -129,20 +129,42 @@ __device__ __forceinline__ const u32x4 *code_pair_addr(const uint32_t *row, int 
     return reinterpret_cast<const u32x4 *>(row + min(G + (g >> 1), n_grp - 1) * 8 + 4 * (g & 1));
 }
 
+// The same words addressed from the expert's first code word (uniform: in
+// scalar registers) plus a 32-bit byte offset per lane, so a load costs a few
+// 32-bit vector operations instead of a 64-bit address: off = the lane's row
+// * bytes per row + 16 (g & 1), lim = n_grp - 1 - (g >> 1).  Rows of at most
+// 8192 codes of at most 8192 rows per expert keep the offset within 32 bits.
+struct CodeLane {
+    uint32_t off;
+    int lim, gh;
+};
+__device__ __forceinline__ CodeLane code_lane(int row, int wpr, int n_grp, int g) {
+    return CodeLane{(uint32_t)__umul24((uint32_t)row, 4u * (uint32_t)wpr) + 16u * (uint32_t)(g & 1),
+                    n_grp - 1 - (g >> 1), g >> 1};
+}
+__device__ __forceinline__ u32x4 load_code_pair(const uint32_t *base, const CodeLane &l, int G) {
+    const uint32_t byte = l.off + 32u * (uint32_t)(min(G, l.lim) + l.gh);
+    return *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(base) + byte);
+}
+
 // A register copy the compiler keeps (a DPP move with the identity pattern).
 __device__ __forceinline__ uint32_t kept_copy(uint32_t x) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xE4, 0xF, 0xF, false);
 }
 
-// The swaps act on copies of the loaded words: v_permlane32_swap overwrites
-// both its operands, and on the words themselves it led the register
-// allocator to keep a ring in other registers than the ones its loads write,
-// with a copy at the loop's end that waits for the loads just issued.
+// KEEP: the swaps act on copies of the loaded words.  v_permlane32_swap
+// overwrites both its operands, and on the words themselves it led the
+// register allocator (in the down units) to keep a ring in other registers
+// than the ones its loads write, with a copy at the loop's end that waits for
+// the loads just issued; the gate/up units do without the copies.
+template <bool KEEP>
 __device__ __forceinline__ void spread_code_pair(const u32x4 &v, uint32_t (&w)[4]) {
     // v_permlane32_swap: lanes 32..63 of the first operand trade places with
     // lanes 0..31 of the second
-    const auto r02 = __builtin_amdgcn_permlane32_swap(kept_copy(v.x), kept_copy(v.z), false, false);
-    const auto r13 = __builtin_amdgcn_permlane32_swap(kept_copy(v.y), kept_copy(v.w), false, false);
+    const uint32_t x = KEEP ? kept_copy(v.x) : v.x, y = KEEP ? kept_copy(v.y) : v.y;
+    const uint32_t z = KEEP ? kept_copy(v.z) : v.z, ww = KEEP ? kept_copy(v.w) : v.w;
+    const auto r02 = __builtin_amdgcn_permlane32_swap(x, z, false, false);
+    const auto r13 = __builtin_amdgcn_permlane32_swap(y, ww, false, false);
     w[0] = r02[0];
     w[2] = r02[1];
     w[1] = r13[0];
@@ -293,15 +315,18 @@ struct InStage {
 // is replaced by zeros when the slot is empty or the piece lies past n.  No
 // load sits behind a branch, so the wait counts stay exact and the code word
 // ring stays in flight across the chunk's end).
+// (row[r]: the row's first element as a 32-bit offset from src, which is
+// uniform, so the loads take src from scalar registers and a 32-bit byte
+// offset per lane; the inputs of a call stay far below 2^31 elements)
 template <int NB>
-__device__ __forceinline__ void in_load(InStage<NB> &st, const uint16_t *src, const int64_t (&row)[NB],
+__device__ __forceinline__ void in_load(InStage<NB> &st, const uint16_t *src, const uint32_t (&row)[NB],
                                         const bool (&live)[NB], int k0, int n) {
     const int c = 8 * (threadIdx.x & 31);
     const bool in_range = k0 + c < n;
-    const int kc = in_range ? k0 + c : n - 8;
+    const uint32_t kc = (uint32_t)(in_range ? k0 + c : n - 8);
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
-        st.v[r] = *reinterpret_cast<const u32x4 *>(src + row[r] + kc);
+        st.v[r] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(src) + 2u * (row[r] + kc));
         st.ok[r] = live[r] && in_range;
     }
 }
@@ -391,23 +416,26 @@ __device__ __forceinline__ void gate_up_unit(const GroupedArgs &a, int w, int rb
     const int64_t erow = (int64_t)e * a.d_ff;
     if (tid < NT) sm.pair[tid] = tid < count ? a.pair_list[begin + tid] : -1;
     // staging roles: x rows of the slots this thread loads; scale row and kind
-    int64_t xrow[NB];
+    uint32_t xrow[NB];
     bool xlive[NB];
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
         const int t = (tid >> 5) + 16 * r;
         xlive[r] = t < count;
-        xrow[r] = (int64_t)(a.pair_list[begin + (xlive[r] ? t : 0)] / a.K) * a.d_in;
+        xrow[r] = (uint32_t)(a.pair_list[begin + (xlive[r] ? t : 0)] / a.K) * (uint32_t)a.d_in;
     }
-    // scale staging: thread -> (row, matrix, pair of groups); c = b - 128 s
+    // scale staging: thread -> (row, matrix, pair of groups), a 32-bit byte
+    // offset per lane from the expert's scales; c = b - 128 s (one matrix per
+    // wave instead, so that its base stayed scalar, measured 3-6% slower)
     const int sb_row = tid >> 2, sb_m = (tid >> 1) & 1, sb_h = tid & 1;
-    const int64_t sb_off = (erow + min(row0 + sb_row, a.d_ff - 1)) * a.gate.gpr;
-    const uint16_t *sb_s = (sb_m ? a.up.s : a.gate.s) + sb_off, *sb_b = (sb_m ? a.up.b : a.gate.b) + sb_off;
+    const uint16_t *sb_s = (sb_m ? a.up.s : a.gate.s) + erow * a.gate.gpr;
+    const uint16_t *sb_b = (sb_m ? a.up.b : a.gate.b) + erow * a.gate.gpr;
+    const uint32_t sb_off = 2u * (uint32_t)__umul24((uint32_t)min(row0 + sb_row, a.d_ff - 1), (uint32_t)a.gate.gpr);
     // the lane's weight row and its code words
     const int rowl = wave * 16 + j;
     const int ra = min(row0 + rowl, a.d_ff - 1);
-    const uint32_t *qg = a.gate.q + (erow + ra) * a.gate.wpr;
-    const uint32_t *qu = a.up.q + (erow + ra) * a.up.wpr;
+    const uint32_t *qg = a.gate.q + erow * a.gate.wpr, *qu = a.up.q + erow * a.up.wpr;   // the expert's codes
+    const CodeLane cl = code_lane(ra, a.gate.wpr, n_grp, g);                             // (same layout for up)
     const int xo = code_word_input(g);
     // The code words of a chunk (two groups per entry) are requested one
     // chunk before they are used, into two named register sets taken in turn
@@ -416,8 +444,8 @@ __device__ __forceinline__ void gate_up_unit(const GroupedArgs &a, int w, int rb
     u32x4 rg0[2], ru0[2], rg1[2], ru1[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        rg0[p] = *code_pair_addr(qg, 2 * p, n_grp, g);
-        ru0[p] = *code_pair_addr(qu, 2 * p, n_grp, g);
+        rg0[p] = load_code_pair(qg, cl, 2 * p);
+        ru0[p] = load_code_pair(qu, cl, 2 * p);
     }
     InStage<NB> st;
     uint16_t sbv[4];                                         // s, b of groups 2h and 2h + 1
@@ -427,9 +455,9 @@ __device__ __forceinline__ void gate_up_unit(const GroupedArgs &a, int w, int rb
         sb_g0 = c * kGChunkGroups + 2 * sb_h;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int G = min(sb_g0 + i, n_grp - 1);
-            sbv[2 * i] = sb_s[G];
-            sbv[2 * i + 1] = sb_b[G];
+            const uint32_t o = sb_off + 2u * (uint32_t)min(sb_g0 + i, n_grp - 1);
+            sbv[2 * i] = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(sb_s) + o);
+            sbv[2 * i + 1] = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(sb_b) + o);
         }
     };
     auto store_chunk = [&](int buf) {
@@ -462,12 +490,12 @@ __device__ __forceinline__ void gate_up_unit(const GroupedArgs &a, int w, int rb
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             uint32_t wg[4], wu[4];
-            spread_code_pair(rg[p], wg);
-            spread_code_pair(ru[p], wu);
+            spread_code_pair<false>(rg[p], wg);
+            spread_code_pair<false>(ru[p], wu);
             // the next chunk's words (past the end: clamped, unused): no load
             // sits behind a branch, so the wait counts stay exact
-            ng[p] = *code_pair_addr(qg, (c + 1) * kGChunkGroups + 2 * p, n_grp, g);
-            nu[p] = *code_pair_addr(qu, (c + 1) * kGChunkGroups + 2 * p, n_grp, g);
+            ng[p] = load_code_pair(qg, cl, (c + 1) * kGChunkGroups + 2 * p);
+            nu[p] = load_code_pair(qu, cl, (c + 1) * kGChunkGroups + 2 * p);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int d = 2 * p + h, G = c * kGChunkGroups + d;
@@ -629,13 +657,13 @@ __global__ __launch_bounds__(kGThreads) void down_grouped(GroupedArgs a) {
         s_pair[tid] = p;
         s_score[tid] = p >= 0 && a.scores ? a.scores[p] : 1.0f;
     }
-    int64_t arow[NB];
+    uint32_t arow[NB];
     bool alive[NB];
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
         const int t = (tid >> 5) + 16 * r;
         alive[r] = t < count;
-        arow[r] = (int64_t)a.pair_list[begin + (alive[r] ? t : 0)] * n;
+        arow[r] = (uint32_t)a.pair_list[begin + (alive[r] ? t : 0)] * (uint32_t)n;
     }
     // scale staging, threads < 256: (row, pair of groups)
     const int sb_row = (tid >> 1) & (kGRows - 1), sb_h = tid & 1;
@@ -693,7 +721,7 @@ __global__ __launch_bounds__(kGThreads) void down_grouped(GroupedArgs a) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             uint32_t wd[4];
-            spread_code_pair(rw[p], wd);
+            spread_code_pair<true>(rw[p], wd);
             rw[p] = *code_pair_addr(qd, (c + 1) * kGChunkGroups + 2 * p, n_grp, g);   // as in kernel A
             // groups 2p and 2p + 1 are act16 block p of the chunk
 #pragma unroll
@@ -832,9 +860,8 @@ __device__ __forceinline__ void down_unit(const GroupedArgs &a, int w, int rbb, 
     const int64_t erow = (int64_t)e * a.d_in;
     const int rowl = wave * 16 + j, xo = code_word_input(g);
     const int rb0 = rbb * a.res_rb, n_rbw = min(a.res_rb, n_rb - rb0);   // this unit's row blocks (>= 1)
-    auto code_row = [&](int rbi) {
-        return a.down.q + (erow + min((rb0 + rbi) * kGRows + rowl, a.d_in - 1)) * a.down.wpr;
-    };
+    const uint32_t *qd = a.down.q + erow * a.down.wpr;      // the expert's codes
+    auto code_lane_of = [&](int rbi) { return code_lane(min((rb0 + rbi) * kGRows + rowl, a.d_in - 1), a.down.wpr, n_grp, g); };
     // Steps (row block, chunk) in order.  The code words of a step are
     // requested LEAD steps before they are used (past the last step: the
     // last one again, unused), into LEAD + 1 named register sets taken in
@@ -847,9 +874,9 @@ __device__ __forceinline__ void down_unit(const GroupedArgs &a, int w, int rbb, 
     const int n_steps = n_rbw * n_chunk;
     int l_rb = 0, l_c = 0;                                   // the next step whose words are requested
     auto load_words = [&](u32x4(&dst)[2]) {
-        const uint32_t *qn = code_row(l_rb);
+        const CodeLane cl = code_lane_of(l_rb);
 #pragma unroll
-        for (int p = 0; p < 2; ++p) dst[p] = *code_pair_addr(qn, l_c * kGChunkGroups + 2 * p, n_grp, g);
+        for (int p = 0; p < 2; ++p) dst[p] = load_code_pair(qd, cl, l_c * kGChunkGroups + 2 * p);
         if (++l_c == n_chunk) {
             l_c = 0;
             l_rb = min(l_rb + 1, n_rbw - 1);
@@ -939,8 +966,8 @@ __device__ __forceinline__ void down_unit(const GroupedArgs &a, int w, int rbb, 
             for (int m = 0; m < NB; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         uint32_t wd2[2][4];
-        spread_code_pair(cur[0], wd2[0]);
-        spread_code_pair(cur[1], wd2[1]);
+        spread_code_pair<true>(cur[0], wd2[0]);
+        spread_code_pair<true>(cur[1], wd2[1]);
         load_words(nxt);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
