@@ -13,7 +13,8 @@
 //   kernel A: bf16 x, codes as bf16 128 + q, bias folded as b - 128 s;
 //   kernel B: act rounded to fp16 after a power-of-two factor (2^8, or one
 //             fitted to the token's vector if that would overflow fp16),
-//             codes as exact fp16 q, the token's sums scaled back when stored.
+//             codes as fp16 1024 + q, bias folded as b - 1024 s, the token's
+//             sums scaled back when stored.
 #include <hip/hip_runtime.h>
 
 #include "api.hpp"
@@ -161,12 +162,15 @@ __device__ __forceinline__ void stage_act_f16(char *lds, int nt, int cpr, const 
     __syncthreads();
 }
 
-// fn(tag) for a workgroup-uniform nt in 1..kBatchTok, with ::value = 2 for
+// fn(tag) for a workgroup-uniform nt in 1..kBatchTok, with ::value = nt for
 // nt <= 2 and 4 otherwise: the compute loops see a compile-time token count
 // NT >= nt and run all NT tokens (tokens past nt compute on stale LDS and are
-// never stored).  Two instantiations rather than four: the code of all four
-// in one kernel needed 155 VGPRs (three waves per SIMD), these two 125 (four),
-// for a 5% faster 32-token step despite the dots of the padding tokens.
+// never stored).  Three instantiations rather than four: with a three-token
+// one as well, kernel A needs 139 VGPRs (three waves per SIMD) instead of
+// 123 (four), and the 32-token step measured 3.6% slower; the one-token
+// instantiation (a single pair per work item is the commonest case at 32
+// tokens with top-8 of 128 experts) took that step 4.84 -> 4.73 ms together
+// with kernel B's folded code offset.
 template <int N>
 struct TokC {
     static constexpr int value = N;
@@ -174,7 +178,8 @@ struct TokC {
 template <typename Fn>
 __device__ __forceinline__ void with_tokens(int nt, Fn fn) {
     static_assert(kBatchTok == 4, "token dispatch covers 1..4");
-    if (nt <= 2) fn(TokC<2>{});
+    if (nt == 1) fn(TokC<1>{});
+    else if (nt == 2) fn(TokC<2>{});
     else fn(TokC<4>{});
 }
 
@@ -352,7 +357,6 @@ __global__ __launch_bounds__(kBatchThreads, 6) void down_batch_q4(FfnArgs a) {
     const int lr = 1 << a.lr_shift, j = lane & (lr - 1), rsub = lane >> a.lr_shift, rpw = kWave >> a.lr_shift;
     const QM mats[1] = {a.down};
     const int64_t erow0 = (int64_t)wk.e * a.d_in;
-    const f16x2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
     with_tokens(nt, [&](auto ntc) {
         constexpr int NT = decltype(ntc)::value;
         for (int rb = row0 + wave * rpw * NR; rb < row_end; rb += 4 * rpw * NR) {
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(kBatchThreads, 6) void down_batch_q4(FfnArgs a) {
                         nibble_pairs<0x64u>(R.w[0][n].w[k], qw);
 #pragma unroll
                         for (int p = 0; p < 4; ++p) {
-                            const f16x2_t q = __builtin_bit_cast(f16x2_t, qw[p]) - off;
+                            const f16x2_t q = __builtin_bit_cast(f16x2_t, qw[p]);      // 1024 + q
 #pragma unroll
                             for (int t = 0; t < NT; ++t)
                                 d[n][t] = __builtin_amdgcn_fdot2(q, __builtin_bit_cast(f16x2_t, xk[t][p]), d[n][t],
@@ -400,7 +404,7 @@ __global__ __launch_bounds__(kBatchThreads, 6) void down_batch_q4(FfnArgs a) {
                     for (int n = 0; n < NR; ++n) {
                         const float s = R.live[n] ? sb_to_float<SB>(R.sr[0][n]) : 0.f;
                         const float b = R.live[n] ? sb_to_float<SB>(R.br[0][n]) : 0.f;
-                        acc[n][t] += s * d[n][t] + b * asum;
+                        acc[n][t] += s * d[n][t] + (b - 1024.0f * s) * asum;
                     }
                 }
             }

@@ -24,10 +24,12 @@
 // blocks of one work item run on one XCD and share its L2 copy of the inputs.
 //
 // Codes stay exact: kernel A turns a 4-bit code q into the bf16 number 128 + q
-// (nibble_pairs), kernel B into the fp16 number q (1024 + q, minus 1024 in a
-// packed fp16 subtraction), so every product in the matrix core is exact and
-// the affine scale and bias are applied per group of 64 inputs afterwards:
-//   sum_i (s q_i + b) x_i = s * sum_i (128 + q_i) x_i + (b - 128 s) * sum_i x_i.
+// (nibble_pairs), kernel B into the fp16 number 1024 + q, so every product in
+// the matrix core is exact and the affine scale and bias are applied per group
+// of 64 inputs afterwards, with the offset folded into the bias term:
+//   sum_i (s q_i + b) x_i = s * sum_i (128 + q_i) x_i + (b - 128 s) * sum_i x_i
+// (1024 and b - 1024 s for kernel B; its group sums are those of the fp16
+// values it multiplies, so the offset cancels up to fp32 rounding).
 // A lane's 8 values of a k-step are one code word; its nibble pairs come in
 // the order (q0, q4, q1, q5, q2, q6, q3, q7) and the inputs are permuted to
 // the same order (pair_inputs), which leaves the dot products unchanged.  Each
@@ -701,8 +703,10 @@ __global__ __launch_bounds__(kGThreads) void down_grouped(GroupedArgs a) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {       // groups past the end: zero scale and bias
                 const bool ok = sb_g0 + i < n_grp;
+                const float sv = ok ? sb_to_float<SB>(sbv[2 * i]) : 0.f;
+                const float bv = ok ? sb_to_float<SB>(sbv[2 * i + 1]) : 0.f;
                 *reinterpret_cast<float2 *>(&s_sb[buf][((2 * sb_h + i) * kGRows + sb_row) * 2]) =
-                    make_float2(ok ? sb_to_float<SB>(sbv[2 * i]) : 0.f, ok ? sb_to_float<SB>(sbv[2 * i + 1]) : 0.f);
+                    make_float2(sv, bv - 1024.0f * sv);      // the codes enter as 1024 + q
             }
         }
         if (tid < kBlkPerChunk * NT) s_cs[buf][cs_k * NT + cs_t] = cs_live && blk < a.n_blk ? csv : 0.f;
@@ -711,7 +715,6 @@ __global__ __launch_bounds__(kGThreads) void down_grouped(GroupedArgs a) {
     store_chunk(0);
     __syncthreads();
 
-    const f16x2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
     f32x4 acc[NB];
 #pragma unroll
     for (int m = 0; m < NB; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -732,11 +735,6 @@ __global__ __launch_bounds__(kGThreads) void down_grouped(GroupedArgs a) {
                 uint32_t pq[2][4];
                 nibble_pairs<0x64u>(wd[2 * h], pq[0]);
                 nibble_pairs<0x64u>(wd[2 * h + 1], pq[1]);
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        pq[s][i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, pq[s][i]) - off);
 #pragma unroll
                 for (int m = 0; m < NB; ++m) {
                     const uint16_t *ar = s_a[buf] + (16 * m + j) * kGPad + d * kGroup + xo;
@@ -856,7 +854,6 @@ __device__ __forceinline__ void down_unit(const GroupedArgs &a, int w, int rbb, 
         s_pair[tid] = p;
         s_score[tid] = p >= 0 && a.scores ? a.scores[p] : 1.0f;
     }
-    const f16x2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
     const int64_t erow = (int64_t)e * a.d_in;
     const int rowl = wave * 16 + j, xo = code_word_input(g);
     const int rb0 = rbb * a.res_rb, n_rbw = min(a.res_rb, n_rb - rb0);   // this unit's row blocks (>= 1)
@@ -949,9 +946,11 @@ __device__ __forceinline__ void down_unit(const GroupedArgs &a, int w, int rbb, 
 #pragma unroll
         for (int i = 0; i < kGResIters; ++i) {
             const int idx = tid + kGThreads * i, r = idx / n_grp, G = idx - r * n_grp;
-            if (i < iters && idx < tot)
+            if (i < iters && idx < tot) {
+                const float sf = sb_to_float<SB>((uint16_t)sv[i]);
                 *reinterpret_cast<float2 *>(&s_sb[(G * kGRows + r) * 2]) =
-                    make_float2(sb_to_float<SB>((uint16_t)sv[i]), sb_to_float<SB>((uint16_t)bv[i]));
+                    make_float2(sf, sb_to_float<SB>((uint16_t)bv[i]) - 1024.0f * sf);   // codes as 1024 + q
+            }
         }
     };
     f32x4 acc[NB];
@@ -980,11 +979,6 @@ __device__ __forceinline__ void down_unit(const GroupedArgs &a, int w, int rbb, 
                 uint32_t pq[2][4];
                 nibble_pairs<0x64u>(wd[2 * h], pq[0]);
                 nibble_pairs<0x64u>(wd[2 * h + 1], pq[1]);
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        pq[s2][i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, pq[s2][i]) - off);
 #pragma unroll
                 for (int m = 0; m < NB; ++m) {
                     const uint16_t *ar = s_a + (16 * m + j) * pad + G * kGroup + xo;
